@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the self-conditioning soft embedding on one MI355X.
+
+A step is one pass of the whole hot path over one canvas batch: se_row_stats over
+the full-width fp32 logits, then se_soft_embed_fused over the rank's vocab slice
+(probabilities rebuilt in the GEMM prologue), both on one stream.  Inputs are
+seeded synthetic data already resident in HBM when the timed region starts.
+
+Default workload: one tensor-parallel rank's share at its real shape (L_c = 256
+canvas positions, full-width logits over V = 262,144, slice [65536, 131072) of a
+bf16 table padded to 262,400 rows, d = 2,816, gamma = sqrt(2816)).
+
+Prints ONE JSON line.  ``value`` is soft-embed GFLOP/s over the whole step
+(2 L (e - s) d FLOP per step / step time); the same line carries steps/s, the
+fused call's GFLOP/s, per-kernel times, the roofline of the dominant call, and
+the fp64 oracle timed on this host as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "soft-embed GFLOP/s + steps/s at L_c=256,V=262144,d=2816; % of roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_soft_embed_fused_rank.json")
+KERNEL_SOURCES = ["soft_embed.hip", "se_device.h", "se_launch.h", "api.cpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "diffusion_self_conditioning_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def fused_call_bytes(w) -> int:
+    """Algorithmic HBM bytes of one fused call: the bf16 shard slice once, the fp32 logits
+    slice once, the fp32 output once."""
+    return 2 * w.k * w.d + 4 * w.rows * w.k + 4 * w.rows * w.d
+
+
+def row_stats_bytes(w) -> int:
+    return 4 * w.rows * w.vocab + 16 * w.rows
+
+
+def measured_traffic(nbytes_launch_hint: int):
+    """HBM bytes per fused call from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("bytes_per_call")
+
+
+def cpu_baseline(w, x_np, bits, budget_s: float = 12.0):
+    """The fp64 oracle (row stats + slice contraction) on a bounded row sample of the same
+    workload, on this host's cores; scaled to GFLOP/s of the soft embedding."""
+    import oracle
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    shard = bits[w.vocab_start:w.vocab_end]
+    rows = max(1, cores)
+    t0 = time.perf_counter()
+    oracle.row_stats(x_np[:rows])
+    oracle.soft_embed(x_np[:rows], w.vocab_start, w.vocab_end, shard, w.gamma)
+    dt = time.perf_counter() - t0
+    if dt < budget_s / 3:
+        rows = min(w.rows, max(rows, int(rows * budget_s / max(dt, 1e-3))) // cores * cores or cores)
+        t0 = time.perf_counter()
+        oracle.row_stats(x_np[:rows])
+        oracle.soft_embed(x_np[:rows], w.vocab_start, w.vocab_end, shard, w.gamma)
+        dt = time.perf_counter() - t0
+    flops = 2 * rows * w.k * w.d
+    return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{rows} of {w.rows} rows of the {w.name} workload (row stats over "
+                      f"V={w.vocab} + fp64 contraction over the {w.k}-row slice), {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="rank", choices=["rank", "full", "conv", "batch", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time se_probs_bf16 + se_soft_embed instead of the fused call")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the soft embedding of one tensor-parallel rank needs no second GPU; the "
+              "cross-rank all-reduce is not part of this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(1)
+    from diffusion_self_conditioning_amd import _binding as B
+    from diffusion_self_conditioning_amd import api
+    from diffusion_self_conditioning_amd import workloads as wl
+
+    w = wl.get(args.workload)
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    x_np = wl.make_logits(w)
+    bits, _ = wl.make_table(w)
+    x = torch.from_numpy(x_np).to(dev)
+    table = torch.from_numpy(bits).to(dev)
+    shard = table[w.vocab_start:w.vocab_end]
+    L, d = w.rows, w.d
+    mx = torch.empty(L, device=dev)
+    lse = torch.empty(L, device=dev)
+    ent = torch.empty(L, device=dev)
+    am = torch.empty(L, device=dev, dtype=torch.int32)
+    out = torch.empty((L, d), device=dev)
+    ws = api.workspace(L, w.vocab_start, w.vocab_end, d, dev)
+    probs = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16) if args.unfused else None
+
+    def stats():
+        B.se_row_stats(x, mx, lse, ent, am)
+
+    def embed():
+        if args.unfused:
+            B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, probs)
+            B.se_soft_embed(probs, w.vocab_start, w.vocab_end, shard, w.gamma, out, ws)
+        else:
+            B.se_soft_embed_fused(x, lse, w.vocab_start, w.vocab_end, shard, w.gamma, out, ws)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        stats()
+        embed()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, events around each call on the launch stream
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record()
+    for k in range(K):
+        ev[k][0].record()
+        stats()
+        ev[k][1].record()
+        embed()
+        ev[k][2].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / K
+    us_stats = [ev[k][0].elapsed_time(ev[k][1]) * 1e3 for k in range(K)]
+    us_embed = [ev[k][1].elapsed_time(ev[k][2]) * 1e3 for k in range(K)]
+    us_stats_avg = sum(us_stats) / K
+    us_embed_avg = sum(us_embed) / K
+
+    flops = w.flops()
+    gflops_step = flops / (ms_step * 1e-3) / 1e9
+    gflops_call = flops / (us_embed_avg * 1e-6) / 1e9
+    call_bytes = fused_call_bytes(w)
+    achieved_gbs = call_bytes / (us_embed_avg * 1e-6) / 1e9
+    t_roof_call_us = max(flops / (PEAK_BF16_TFLOPS * 1e12), call_bytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+    step_bytes = call_bytes + row_stats_bytes(w)
+    t_roof_step_us = (row_stats_bytes(w) / (PEAK_HBM_GBS * 1e9) + t_roof_call_us * 1e-6) * 1e6
+    mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > call_bytes / (PEAK_HBM_GBS * 1e9)
+    traffic = measured_traffic(call_bytes)
+    roof = {"bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(gflops_call / 1e3 if mfma_bound else achieved_gbs, 2),
+            "peak": PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "traffic": traffic}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = ("se_probs_bf16+se_soft_embed" if args.unfused else "se_soft_embed_fused") + \
+        " call (soft_embed_kernel + splitk_reduce_kernel)"
+    roof["algorithmic_bytes"] = call_bytes
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, x_np, bits)
+
+    line = {
+        "metric": METRIC, "value": round(gflops_step, 2), "unit": "GFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: L_c={L} rows, full-width fp32 logits V={w.vocab}, "
+                               f"slice [{w.vocab_start},{w.vocab_end}) of a bf16 table "
+                               f"[{w.table_rows}, {d}], gamma={w.gamma:.6g}"
+                               + (" (unfused)" if args.unfused else " (fused)"),
+                   "rows": L, "vocab": w.vocab, "vocab_start": w.vocab_start,
+                   "vocab_end": w.vocab_end, "d": d, "seed": w.seed},
+        "steps_per_s": round(1e3 / ms_step, 2),
+        "gflops_fused_call": round(gflops_call, 2),
+        "kernel_us": {"se_row_stats": round(us_stats_avg, 2),
+                      "se_soft_embed" + ("" if args.unfused else "_fused"): round(us_embed_avg, 2)},
+        "roofline": roof,
+        "roofline_step": {"t_roof_us": round(t_roof_step_us, 2),
+                          "frac": round(t_roof_step_us / (ms_step * 1e3), 4),
+                          "algorithmic_bytes": step_bytes},
+        "roofline_call_t_roof_us": round(t_roof_call_us, 2),
+        "wall_s_timed": round(wall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

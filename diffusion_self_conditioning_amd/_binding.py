@@ -1,0 +1,152 @@
+"""ctypes binding of libsoftembed (include/softembed.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libsoftembed.so``.  PyTorch supplies device memory and the stream;
+the functions below turn tensors into pointers, leading dimensions and sizes,
+call the C entry point of the same name, and raise on a non-OK status.  There
+is no fallback: if the library is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library binds to (same soname)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsoftembed.so")
+
+SE_OK, SE_ERR_NULL, SE_ERR_SHAPE, SE_ERR_SLICE, SE_ERR_ALIGN, SE_ERR_WORKSPACE, SE_ERR_HIP = range(7)
+STATUS_NAMES = ["SE_OK", "SE_ERR_NULL", "SE_ERR_SHAPE", "SE_ERR_SLICE", "SE_ERR_ALIGN",
+                "SE_ERR_WORKSPACE", "SE_ERR_HIP"]
+
+EXPORTS = ("se_status_string", "se_version", "se_row_stats", "se_probs_bf16",
+           "se_soft_embed_workspace_bytes", "se_soft_embed", "se_soft_embed_fused")
+
+
+class SoftEmbedError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def _declare(lib):
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    f32 = ctypes.c_float
+    lib.se_status_string.argtypes = [ctypes.c_int]
+    lib.se_status_string.restype = ctypes.c_char_p
+    lib.se_version.argtypes = []
+    lib.se_version.restype = ctypes.c_char_p
+    lib.se_row_stats.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.se_probs_bf16.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, i64, vp]
+    lib.se_soft_embed_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.se_soft_embed_workspace_bytes.restype = sz
+    lib.se_soft_embed.argtypes = [vp, i64, i64, i64, i64, i64, vp, i64, i64, i64, f32, vp, i64,
+                                  vp, sz, vp]
+    lib.se_soft_embed_fused.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, i64, i64, i64, f32,
+                                        vp, i64, vp, sz, vp]
+    for fn in ("se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused"):
+        getattr(lib, fn).restype = ctypes.c_int
+    return lib
+
+
+def load_library(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"libsoftembed.so not built at {path}; run "
+                          "`python -m diffusion_self_conditioning_amd.build`")
+    return _declare(ctypes.CDLL(path))
+
+
+lib = load_library()
+
+
+def _check(fn: str, status: int):
+    if status != SE_OK:
+        raise SoftEmbedError(fn, status, lib.se_status_string(status).decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _as_u16(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint16) if t.dtype == torch.bfloat16 else t
+
+
+def se_status_string(status: int) -> str:
+    return lib.se_status_string(status).decode()
+
+
+def se_version() -> str:
+    return lib.se_version().decode()
+
+
+def se_row_stats(logits, row_max, row_lse, row_entropy, row_argmax, *, vocab=None, stream=None):
+    """Row max / log-sum-exp / entropy / argmax of fp32 logits [n_rows, >= vocab]."""
+    n, v = logits.shape
+    vocab = v if vocab is None else vocab
+    _check("se_row_stats", lib.se_row_stats(_ptr(logits), _ld(logits), n, vocab, _ptr(row_max),
+                                            _ptr(row_lse), _ptr(row_entropy), _ptr(row_argmax),
+                                            _stream(stream)))
+
+
+def se_probs_bf16(logits, row_lse, vocab_start, vocab_end, probs, *, vocab=None, stream=None):
+    """probs[:, s:e] = bf16(exp(logits[:, s:e] - lse)); ``probs`` is bf16 or uint16."""
+    n, v = logits.shape
+    vocab = v if vocab is None else vocab
+    probs = _as_u16(probs)
+    _check("se_probs_bf16", lib.se_probs_bf16(_ptr(logits), _ld(logits), _ptr(row_lse), n, vocab,
+                                              vocab_start, vocab_end, _ptr(probs), _ld(probs),
+                                              _stream(stream)))
+
+
+def se_soft_embed_workspace_bytes(n_rows: int, vocab_start: int, vocab_end: int, d: int) -> int:
+    return int(lib.se_soft_embed_workspace_bytes(n_rows, vocab_start, vocab_end, d))
+
+
+def se_soft_embed(probs, vocab_start, vocab_end, w_shard, gamma, out, workspace=None, *,
+                  vocab=None, d=None, w_rows=None, stream=None):
+    """out[:, :d] = gamma * probs[:, s:e] @ w_shard[: e - s, :d]  (bf16 inputs, fp32 out)."""
+    probs, w_shard = _as_u16(probs), _as_u16(w_shard)
+    n, v = probs.shape
+    vocab = v if vocab is None else vocab
+    d = w_shard.shape[1] if d is None else d
+    w_rows = w_shard.shape[0] if w_rows is None else w_rows
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("se_soft_embed", lib.se_soft_embed(
+        _ptr(probs), _ld(probs), n, vocab, vocab_start, vocab_end, _ptr(w_shard), w_rows,
+        _ld(w_shard), d, float(gamma), _ptr(out), _ld(out), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def se_soft_embed_fused(logits, row_lse, vocab_start, vocab_end, w_shard, gamma, out,
+                        workspace=None, *, vocab=None, d=None, w_rows=None, stream=None):
+    """out[:, :d] = gamma * bf16(softmax(logits))[:, s:e] @ w_shard[: e - s, :d], P never stored."""
+    w_shard = _as_u16(w_shard)
+    n, v = logits.shape
+    vocab = v if vocab is None else vocab
+    d = w_shard.shape[1] if d is None else d
+    w_rows = w_shard.shape[0] if w_rows is None else w_rows
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("se_soft_embed_fused", lib.se_soft_embed_fused(
+        _ptr(logits), _ld(logits), _ptr(row_lse), n, vocab, vocab_start, vocab_end,
+        _ptr(w_shard), w_rows, _ld(w_shard), d, float(gamma), _ptr(out), _ld(out),
+        _ptr(workspace), ws_bytes, _stream(stream)))

@@ -1,0 +1,52 @@
+"""Tensor-level calls of libsoftembed.
+
+Each function allocates its outputs with torch on the input's device and calls
+the C entry point of the same family through the ctypes binding; all arithmetic
+runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._binding import (SoftEmbedError, se_probs_bf16, se_row_stats, se_soft_embed,  # noqa: F401
+                       se_soft_embed_fused, se_soft_embed_workspace_bytes, se_status_string,
+                       se_version)
+
+
+def row_stats(logits: torch.Tensor, stream=None):
+    """(row_max, row_lse, row_entropy, row_argmax) of fp32 logits [L, V] over the full width."""
+    n = logits.shape[0]
+    f = dict(device=logits.device, dtype=torch.float32)
+    mx, lse, ent = torch.empty(n, **f), torch.empty(n, **f), torch.empty(n, **f)
+    am = torch.empty(n, device=logits.device, dtype=torch.int32)
+    se_row_stats(logits, mx, lse, ent, am, stream=stream)
+    return mx, lse, ent, am
+
+
+def probs_bf16(logits, row_lse, vocab_start, vocab_end, stream=None):
+    """bf16 probability matrix [L, V]; only columns [vocab_start, vocab_end) are written."""
+    p = torch.zeros(logits.shape, device=logits.device, dtype=torch.bfloat16)
+    se_probs_bf16(logits, row_lse, vocab_start, vocab_end, p, stream=stream)
+    return p
+
+
+def workspace(n_rows, vocab_start, vocab_end, d, device):
+    nbytes = se_soft_embed_workspace_bytes(n_rows, vocab_start, vocab_end, d)
+    return torch.empty((nbytes + 3) // 4, device=device, dtype=torch.float32) if nbytes else None
+
+
+def soft_embed(logits, row_lse, vocab_start, vocab_end, w_shard, gamma, *, fused=True,
+               out=None, ws=None, stream=None):
+    """gamma * softmax(logits)[:, s:e] @ w_shard[: e - s]: one rank's partial, fp32 [L, d]."""
+    n, d = logits.shape[0], w_shard.shape[1]
+    if out is None:
+        out = torch.empty((n, d), device=logits.device, dtype=torch.float32)
+    if ws is None:
+        ws = workspace(n, vocab_start, vocab_end, d, logits.device)
+    if fused:
+        se_soft_embed_fused(logits, row_lse, vocab_start, vocab_end, w_shard, gamma, out, ws,
+                            stream=stream)
+    else:
+        p = probs_bf16(logits, row_lse, vocab_start, vocab_end, stream=stream)
+        se_soft_embed(p, vocab_start, vocab_end, w_shard, gamma, out, ws, stream=stream)
+    return out

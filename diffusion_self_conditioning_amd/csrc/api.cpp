@@ -1,0 +1,193 @@
+// api.cpp -- the C ABI of libsoftembed: argument checks, work decomposition,
+// launches.  Every check runs on the host before anything is enqueued, so a
+// rejected call launches nothing and touches no output.  The one runtime
+// condition the pages document as a failure -- a contraction whose two sides
+// disagree in length (calvarado04.com, "The symptom": the [65536, 2816] shard
+// against full-width probabilities) -- is SE_ERR_SLICE here.
+#include "../../include/softembed.h"
+#include "se_launch.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <climits>
+
+namespace se {
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+  GemmPlan g{};
+  g.tiles_m = (M + kBM - 1) / kBM;
+  g.tiles_n = (N + kBN - 1) / kBN;
+  g.tiles = g.tiles_m * g.tiles_n;
+  g.ksteps = (K + kBK - 1) / kBK;
+  g.splits = 1;
+  if (g.tiles > 0 && g.tiles < kTargetCUs) {
+    int64_t s = kTargetCUs / g.tiles;
+    const int64_t cap = g.ksteps / kMinStepsPerSplit;
+    if (s > cap) s = cap;
+    g.splits = s < 1 ? 1 : s;
+  }
+  g.grid = g.tiles * g.splits;
+  g.ws_bytes = g.splits > 1 ? (size_t)(g.splits * g.tiles * kTileFloats) * sizeof(float) : 0;
+  return g;
+}
+
+}  // namespace se
+
+namespace {
+
+inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+inline bool aligned4(const void* ptr) { return ((uintptr_t)ptr & 3u) == 0; }
+
+// Rows of the helper kernels go in grid.y, which is limited to 65535.
+constexpr int64_t kMaxGridY = 65535;
+
+se_status from_hip(hipError_t e) { return e == hipSuccess ? SE_OK : SE_ERR_HIP; }
+
+se_status check_slice_common(int64_t n_rows, int64_t vocab, int64_t s, int64_t e, int64_t w_rows,
+                             int64_t d, int64_t ld_w, int64_t ld_out, const void* w,
+                             const void* out) {
+  if (n_rows < 0 || vocab < 1 || d < 1 || w_rows < 0) return SE_ERR_SHAPE;
+  if (vocab > INT32_MAX || d > INT32_MAX || n_rows > INT32_MAX) return SE_ERR_SHAPE;
+  if (ld_w < d || ld_out < d) return SE_ERR_SHAPE;
+  if (s < 0 || e < s || e > vocab || e - s > w_rows) return SE_ERR_SLICE;
+  if (!aligned16(w) || !aligned16(out)) return SE_ERR_ALIGN;
+  if ((s % 8) != 0 || (d % 8) != 0 || (ld_w % 8) != 0 || (ld_out % 4) != 0) return SE_ERR_ALIGN;
+  return SE_OK;
+}
+
+se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* lse, int64_t n_rows,
+                         int64_t s, int64_t e, const uint16_t* w, int64_t ldw, int64_t d,
+                         float gamma, float* out, int64_t ld_out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  const se::GemmPlan g = se::plan_gemm(n_rows, d, e - s);
+  if (g.grid > INT32_MAX) return SE_ERR_SHAPE;
+  if (ws_bytes < g.ws_bytes) return SE_ERR_WORKSPACE;
+  if (g.ws_bytes > 0 && (ws == nullptr)) return SE_ERR_NULL;
+  if (g.ws_bytes > 0 && !aligned16(ws)) return SE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n_rows == 0) return SE_OK;
+  if (e == s) {
+    for (int64_t r0 = 0; r0 < n_rows; r0 += kMaxGridY) {
+      const int64_t nr = (n_rows - r0) < kMaxGridY ? (n_rows - r0) : kMaxGridY;
+      se_status rc = from_hip(se::launch_zero_rows(out + r0 * ld_out, ld_out, nr, d, st));
+      if (rc != SE_OK) return rc;
+    }
+    return SE_OK;
+  }
+  se::GemmParams p{};
+  p.a = a;
+  p.lda = lda;
+  p.lse = lse;
+  p.col0 = s;
+  p.w = w;
+  p.ldw = ldw;
+  p.M = n_rows;
+  p.N = d;
+  p.K = e - s;
+  p.gamma = gamma;
+  p.out = out;
+  p.ldo = ld_out;
+  p.ws = static_cast<float*>(ws);
+  p.tiles_n = (int)g.tiles_n;
+  p.tiles = (int)g.tiles;
+  p.splits = (int)g.splits;
+  p.ksteps = (int)g.ksteps;
+  return from_hip(se::launch_soft_embed(p, fused, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* se_status_string(se_status s) {
+  switch (s) {
+    case SE_OK: return "SE_OK";
+    case SE_ERR_NULL: return "SE_ERR_NULL: a required pointer is NULL";
+    case SE_ERR_SHAPE: return "SE_ERR_SHAPE: invalid size or leading dimension";
+    case SE_ERR_SLICE: return "SE_ERR_SLICE: vocab slice out of range or longer than the shard";
+    case SE_ERR_ALIGN: return "SE_ERR_ALIGN: pointer, pitch, vocab_start or d misaligned";
+    case SE_ERR_WORKSPACE: return "SE_ERR_WORKSPACE: workspace too small";
+    case SE_ERR_HIP: return "SE_ERR_HIP: HIP runtime error at launch";
+  }
+  return "unknown se_status";
+}
+
+const char* se_version(void) {
+  return "libsoftembed 0.1 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused)";
+}
+
+se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
+                       float* row_max, float* row_lse, float* row_entropy, int32_t* row_argmax,
+                       void* stream) {
+  if (!logits || !row_max || !row_lse || !row_entropy || !row_argmax) return SE_ERR_NULL;
+  if (n_rows < 0 || vocab < 1 || vocab > INT32_MAX || n_rows > INT32_MAX) return SE_ERR_SHAPE;
+  if (ld_logits < vocab) return SE_ERR_SHAPE;
+  if (!aligned16(logits) || (ld_logits % 4) != 0) return SE_ERR_ALIGN;
+  if (!aligned4(row_max) || !aligned4(row_lse) || !aligned4(row_entropy) || !aligned4(row_argmax))
+    return SE_ERR_ALIGN;
+  if (n_rows == 0) return SE_OK;
+  return from_hip(se::launch_row_stats(logits, ld_logits, n_rows, (int)vocab, row_max, row_lse,
+                                       row_entropy, row_argmax,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+se_status se_probs_bf16(const float* logits, int64_t ld_logits, const float* row_lse,
+                        int64_t n_rows, int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                        uint16_t* probs, int64_t ld_probs, void* stream) {
+  if (!logits || !row_lse || !probs) return SE_ERR_NULL;
+  if (n_rows < 0 || vocab < 1 || vocab > INT32_MAX || n_rows > INT32_MAX) return SE_ERR_SHAPE;
+  if (ld_logits < vocab || ld_probs < vocab) return SE_ERR_SHAPE;
+  if (vocab_start < 0 || vocab_end < vocab_start || vocab_end > vocab) return SE_ERR_SLICE;
+  if (!aligned16(logits) || !aligned16(probs) || !aligned4(row_lse)) return SE_ERR_ALIGN;
+  if ((ld_logits % 4) != 0 || (ld_probs % 8) != 0 || (vocab_start % 8) != 0) return SE_ERR_ALIGN;
+  const int64_t K = vocab_end - vocab_start;
+  if (n_rows == 0 || K == 0) return SE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int64_t r0 = 0; r0 < n_rows; r0 += kMaxGridY) {
+    const int64_t nr = (n_rows - r0) < kMaxGridY ? (n_rows - r0) : kMaxGridY;
+    se_status rc = from_hip(se::launch_probs_bf16(logits + r0 * ld_logits, ld_logits,
+                                                  row_lse + r0, nr, vocab_start, K,
+                                                  probs + r0 * ld_probs, ld_probs, st));
+    if (rc != SE_OK) return rc;
+  }
+  return SE_OK;
+}
+
+size_t se_soft_embed_workspace_bytes(int64_t n_rows, int64_t vocab_start, int64_t vocab_end,
+                                     int64_t d) {
+  if (n_rows < 0 || d < 1 || vocab_start < 0 || vocab_end < vocab_start) return 0;
+  if (n_rows > INT32_MAX || d > INT32_MAX || vocab_end > INT32_MAX) return 0;
+  if (n_rows == 0 || vocab_end == vocab_start) return 0;
+  return se::plan_gemm(n_rows, d, vocab_end - vocab_start).ws_bytes;
+}
+
+se_status se_soft_embed(const uint16_t* probs, int64_t ld_probs, int64_t n_rows, int64_t vocab,
+                        int64_t vocab_start, int64_t vocab_end, const uint16_t* w_shard,
+                        int64_t w_rows, int64_t ld_w, int64_t d, float gamma, float* out,
+                        int64_t ld_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!probs || !w_shard || !out) return SE_ERR_NULL;
+  se_status rc = check_slice_common(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w,
+                                    ld_out, w_shard, out);
+  if (rc != SE_OK) return rc;
+  if (ld_probs < vocab) return SE_ERR_SHAPE;
+  if (!aligned16(probs) || (ld_probs % 8) != 0) return SE_ERR_ALIGN;
+  return run_soft_embed(false, probs, ld_probs, nullptr, n_rows, vocab_start, vocab_end, w_shard,
+                        ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
+}
+
+se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const float* row_lse,
+                              int64_t n_rows, int64_t vocab, int64_t vocab_start,
+                              int64_t vocab_end, const uint16_t* w_shard, int64_t w_rows,
+                              int64_t ld_w, int64_t d, float gamma, float* out, int64_t ld_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !row_lse || !w_shard || !out) return SE_ERR_NULL;
+  se_status rc = check_slice_common(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w,
+                                    ld_out, w_shard, out);
+  if (rc != SE_OK) return rc;
+  if (ld_logits < vocab) return SE_ERR_SHAPE;
+  if (!aligned16(logits) || (ld_logits % 4) != 0 || !aligned4(row_lse)) return SE_ERR_ALIGN;
+  return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start, vocab_end, w_shard,
+                        ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// row_stats.hip -- one streaming pass over each full-width fp32 logits row:
+// running max, sum of 2^(t), sum of 2^(t) * t with t = (l - m) * log2(e), and
+// the first index of the maximum.  These give the log-sum-exp and the entropy
+// of the row's softmax:
+//     lse = m + ln Z,     H = ln Z - S1 / Z,   Z = sum e^(l-m),  S1 = sum e^(l-m)(l-m)
+// (H = -sum p ln p rewritten with ln p = (l - m) - ln Z; no 0*log 0 and no
+// cancellation between two large numbers).  The softmax is over the whole
+// vocabulary as on calvarado04.com, "Where the shapes stop agreeing" (the
+// sampler runs on gathered, full-width logits); entropy and argmax are what the
+// DiffusionGemma sampler's acceptance and convergence tests consume (agentlenshq
+// overview, "sampling loop and entropy-bound denoising").
+//
+// Partial states are merged with the online-normaliser rule (Milakov &
+// Gimelshein, "Online normalizer calculation for softmax", 2018), extended to
+// carry S1 and the argmax.  One workgroup of 1024 threads owns one row; each
+// thread streams 16-byte loads, 4 in flight, then wavefront shuffles and LDS
+// combine the 16 wave states in a fixed order.
+#include "se_device.h"
+#include "se_launch.h"
+
+#include <climits>
+
+namespace se {
+
+namespace {
+
+struct RowState {
+  float m;    // running max (natural units)
+  float z;    // sum 2^(t_v), t_v = (l_v - m) * log2e
+  float s1;   // sum 2^(t_v) * t_v   (log2 units)
+  int idx;    // first index of m
+};
+
+constexpr int kRowThreads = 1024;
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ void merge(RowState& a, RowState b) {
+  const bool take_b = (b.m > a.m) || (b.m == a.m && b.idx < a.idx);
+  if (take_b) { RowState t = a; a = b; b = t; }
+  if (b.z > 0.f) {                     // b holds at least one element
+    const float dm = (b.m - a.m) * kLog2e;   // <= 0
+    const float f = exp2_hw(dm);
+    a.z = __builtin_fmaf(f, b.z, a.z);
+    a.s1 = __builtin_fmaf(f, __builtin_fmaf(dm, b.z, b.s1), a.s1);
+  }
+}
+
+// Rescale the state to a new, larger maximum `nm`.
+__device__ __forceinline__ void raise_max(RowState& st, float nm, int nidx) {
+  if (st.z > 0.f) {
+    const float dm = (st.m - nm) * kLog2e;
+    const float f = exp2_hw(dm);
+    st.s1 = f * __builtin_fmaf(dm, st.z, st.s1);
+    st.z = f * st.z;
+  }
+  st.m = nm;
+  st.idx = nidx;
+}
+
+__device__ __forceinline__ void accum(RowState& st, float v, float nml) {
+  const float t = __builtin_fmaf(v, kLog2e, nml);
+  const float e = exp2_hw(t);
+  st.z += e;
+  st.s1 = __builtin_fmaf(e, t, st.s1);
+}
+
+__device__ __forceinline__ RowState shfl_xor_state(const RowState& s, int mask) {
+  RowState o;
+  o.m = __shfl_xor(s.m, mask);
+  o.z = __shfl_xor(s.z, mask);
+  o.s1 = __shfl_xor(s.s1, mask);
+  o.idx = __shfl_xor(s.idx, mask);
+  return o;
+}
+
+__global__ void __launch_bounds__(kRowThreads)
+row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
+                 float* __restrict__ row_max, float* __restrict__ row_lse,
+                 float* __restrict__ row_entropy, int32_t* __restrict__ row_argmax) {
+  const int64_t row = blockIdx.x;
+  const float* __restrict__ x = logits + row * ld;
+  const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x);
+  const int tid = threadIdx.x;
+  const int n4 = vocab >> 2;
+
+  RowState st{-INFINITY, 0.f, 0.f, INT_MAX};
+  int c = tid;
+  // Each thread visits its chunks in increasing index order, so a strict ">"
+  // keeps the first occurrence of the maximum.
+  for (; c + (kUnroll - 1) * kRowThreads < n4; c += kUnroll * kRowThreads) {
+    float4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = x4[c + u * kRowThreads];
+    float cm = v[0].x;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      cm = fmaxf(fmaxf(fmaxf(cm, v[u].x), fmaxf(v[u].y, v[u].z)), v[u].w);
+    if (cm > st.m) {
+      int idx = 0;
+#pragma unroll
+      for (int u = kUnroll - 1; u >= 0; --u) {
+        const int b = 4 * (c + u * kRowThreads);
+        idx = (v[u].w == cm) ? b + 3 : idx;
+        idx = (v[u].z == cm) ? b + 2 : idx;
+        idx = (v[u].y == cm) ? b + 1 : idx;
+        idx = (v[u].x == cm) ? b : idx;
+      }
+      raise_max(st, cm, idx);
+    }
+    const float nml = -(st.m * kLog2e);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      accum(st, v[u].x, nml);
+      accum(st, v[u].y, nml);
+      accum(st, v[u].z, nml);
+      accum(st, v[u].w, nml);
+    }
+  }
+  for (; c < n4; c += kRowThreads) {
+    const float4 v = x4[c];
+    const float cm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    if (cm > st.m) {
+      const int b = 4 * c;
+      const int idx = (v.x == cm) ? b : (v.y == cm) ? b + 1 : (v.z == cm) ? b + 2 : b + 3;
+      raise_max(st, cm, idx);
+    }
+    const float nml = -(st.m * kLog2e);
+    accum(st, v.x, nml);
+    accum(st, v.y, nml);
+    accum(st, v.z, nml);
+    accum(st, v.w, nml);
+  }
+  if (tid == 0) {
+    // the last vocab % 4 columns, after every chunk this thread has seen
+    for (int j = 4 * n4; j < vocab; ++j) {
+      const float v = x[j];
+      if (v > st.m) raise_max(st, v, j);
+      accum(st, v, -(st.m * kLog2e));
+    }
+  }
+
+  // wavefront reduction (fixed butterfly order)
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) merge(st, shfl_xor_state(st, mask));
+
+  __shared__ RowState partial[kRowThreads / 64];
+  const int wave = tid >> 6, lane = tid & 63;
+  if (lane == 0) partial[wave] = st;
+  __syncthreads();
+  if (wave == 0) {
+    RowState r = (lane < kRowThreads / 64) ? partial[lane]
+                                           : RowState{-INFINITY, 0.f, 0.f, INT_MAX};
+#pragma unroll
+    for (int mask = 8; mask >= 1; mask >>= 1) merge(r, shfl_xor_state(r, mask));
+    if (lane == 0) {
+      const float lnz = logf(r.z);
+      row_max[row] = r.m;
+      row_argmax[row] = r.idx;
+      row_lse[row] = r.m + lnz;
+      row_entropy[row] = lnz - (r.s1 * kLn2) / r.z;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int vocab,
+                            float* row_max, float* row_lse, float* row_entropy,
+                            int32_t* row_argmax, hipStream_t stream) {
+  hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)n_rows), dim3(kRowThreads), 0, stream,
+                     logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax);
+  return hipGetLastError();
+}
+
+}  // namespace se

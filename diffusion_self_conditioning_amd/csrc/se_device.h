@@ -1,0 +1,34 @@
+// se_device.h -- device-side helpers shared by the libsoftembed kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace se {
+
+constexpr float kLog2e = 1.4426950408889634f;   // log2(e)
+constexpr float kLn2 = 0.6931471805599453f;     // ln(2)
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// p = e^(l - lse) as 2^(l*log2e - lse*log2e); `nl` = -(lse * log2e) is computed
+// once per row by the caller.  Both the materialising kernel and the fused
+// prologue use exactly this sequence so their bf16 probabilities are equal.
+__device__ __forceinline__ float prob_from_logit(float l, float nl) {
+  return exp2_hw(__builtin_fmaf(l, kLog2e, nl));
+}
+
+__device__ __forceinline__ float neg_lse_log2(float lse) { return -(lse * kLog2e); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
+  uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
+  return a | (b << 16);
+}
+
+}  // namespace se

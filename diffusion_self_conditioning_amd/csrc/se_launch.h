@@ -1,0 +1,60 @@
+// se_launch.h -- internal interface between the C ABI layer (api.cpp) and the
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace se {
+
+// ---- work decomposition of the slice contraction (pure host logic) -------------
+// The output [M, N] is cut into BM x BN tiles; the contracted (vocab) axis into
+// BK-wide steps, and the steps of each tile into `splits` contiguous ranges
+// (split-K over the vocabulary axis, the in-GPU form of the partition identity on
+// calvarado04.com, "The fix").  Every tile uses the same split boundaries, and
+// workgroup b takes tile b % tiles, split b / tiles, so the workgroups that read
+// the same probability columns run side by side.
+constexpr int kBM = 256;
+constexpr int kBN = 256;
+constexpr int kBK = 64;
+constexpr int kGemmThreads = 512;
+constexpr int kTargetCUs = 256;          // MI355X compute units: sizes the split count
+constexpr int kMinStepsPerSplit = 4;
+constexpr int64_t kTileFloats = (int64_t)kBM * kBN;
+
+struct GemmPlan {
+  int64_t tiles_m, tiles_n, tiles, ksteps, splits, grid;
+  size_t ws_bytes;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+
+struct GemmParams {
+  const void* a;          // fused: fp32 logits; unfused: bf16 probabilities
+  int64_t lda;            // elements
+  const float* lse;       // fused only: per-row log-sum-exp
+  int64_t col0;           // vocab_start: column of `a` holding slice position 0
+  const uint16_t* w;      // bf16 shard, row 0 = slice position 0
+  int64_t ldw;
+  int64_t M, N, K;
+  float gamma;
+  float* out;
+  int64_t ldo;
+  float* ws;              // split partials [splits][tiles][kTileFloats]
+  int tiles_n, tiles, splits, ksteps;
+};
+
+hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int vocab,
+                            float* row_max, float* row_lse, float* row_entropy,
+                            int32_t* row_argmax, hipStream_t stream);
+
+hipError_t launch_probs_bf16(const float* logits, int64_t ld, const float* row_lse,
+                             int64_t n_rows, int64_t col0, int64_t K, uint16_t* probs,
+                             int64_t ldp, hipStream_t stream);
+
+hipError_t launch_soft_embed(const GemmParams& p, bool fused, hipStream_t stream);
+
+hipError_t launch_zero_rows(float* out, int64_t ldo, int64_t M, int64_t N, hipStream_t stream);
+
+}  // namespace se

@@ -1,0 +1,158 @@
+/*
+ * softembed.h -- C ABI of libsoftembed: DiffusionGemma's self-conditioning soft
+ * embedding on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (calvarado04.com/tag/vllm, section "Where the shapes stop
+ * agreeing", the expected-token-embedding equation, and section "The fix", the
+ * per-rank partial S^(r) and the normaliser gamma):
+ *
+ *     p_i      = softmax(logits_i)               over the FULL vocabulary [0, vocab)
+ *     out_i,:  = gamma * sum_{v=s}^{e-1} p_iv * W_shard[v - s, :]
+ *
+ * One call on the slice [vocab_start, vocab_end) = [s, e) yields exactly one
+ * tensor-parallel rank's partial gamma * S^(r).  Summing the calls of a
+ * disjoint, exhaustive partition gives the full product (same section, the
+ * partition equation).  There is no collective in this library.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers (hipMalloc'd or equivalent) owned
+ *    by the caller.  The library never allocates, frees, synchronises or reads
+ *    device memory from the host.  Work is enqueued on `stream` (a hipStream_t;
+ *    NULL = the null stream).  Outputs are valid once that stream is
+ *    synchronised; inputs must stay alive and unmodified until then.
+ *  - Matrices are row-major with a leading dimension (`ld_*`, in elements).
+ *    Vocabulary-wide matrices (logits, probs) have column j = vocab id j and are
+ *    read only at the columns an entry point documents.  The embedding shard
+ *    has row 0 = vocab id `vocab_start`.
+ *  - bf16 values are passed as uint16_t bit patterns (IEEE binary32 top half).
+ *  - Outputs must not alias inputs or the workspace.
+ *  - Every argument check happens synchronously on the host BEFORE anything is
+ *    enqueued; on any error nothing is launched and the outputs are untouched.
+ *  - Results are bitwise reproducible for the same inputs and shapes: the work
+ *    decomposition depends only on the shapes, and every reduction runs in a
+ *    fixed order.
+ *  - Logits must be finite (not checked on the device).
+ *  - Calls are thread-safe and capture-safe (no allocation, no sync, no host
+ *    read of device data).
+ */
+#ifndef SOFTEMBED_H
+#define SOFTEMBED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SE_OK = 0,
+    SE_ERR_NULL = 1,      /* a required pointer is NULL                                  */
+    SE_ERR_SHAPE = 2,     /* negative/zero size where one is required, ld too small,      */
+                          /* vocab or d above INT32_MAX                                   */
+    SE_ERR_SLICE = 3,     /* not 0 <= vocab_start <= vocab_end <= vocab, or the slice is  */
+                          /* longer than the shard (vocab_end - vocab_start > w_rows)     */
+    SE_ERR_ALIGN = 4,     /* pointer not 16-byte aligned, a row pitch not a multiple of   */
+                          /* 16 bytes, vocab_start % 8 != 0, or d % 8 != 0                */
+    SE_ERR_WORKSPACE = 5, /* workspace smaller than se_soft_embed_workspace_bytes()       */
+    SE_ERR_HIP = 6        /* the HIP runtime reported an error when launching             */
+} se_status;
+
+/* Human-readable name of a status code (static storage). */
+const char* se_status_string(se_status s);
+
+/* Number of kernels / version, for diagnostics. */
+const char* se_version(void);
+
+/*
+ * se_row_stats -- softmax statistics of each logits row over the full width.
+ *
+ * Definitions (agentlenshq DiffusionGemma overview, "sampling loop and
+ * entropy-bound denoising": acceptance orders positions by confidence and the
+ * convergence test uses a stable argmax and the mean per-token entropy; the
+ * softmax itself is over the full vocabulary as on calvarado04.com, "Where the
+ * shapes stop agreeing"):
+ *     row_max[i]     = max_v l_iv
+ *     row_argmax[i]  = smallest v with l_iv = row_max[i]
+ *     row_lse[i]     = log sum_v exp(l_iv)                       (natural log)
+ *     row_entropy[i] = -sum_v p_iv log p_iv, p = softmax(l_i)    (nats)
+ *
+ * logits:  fp32 [n_rows, ld_logits], columns [0, vocab) are read.
+ * outputs: fp32 row_max/row_lse/row_entropy [n_rows], int32 row_argmax [n_rows].
+ * n_rows == 0 is a no-op.  Requires vocab >= 1, ld_logits >= vocab,
+ * logits 16-byte aligned and ld_logits % 4 == 0; outputs 4-byte aligned.
+ */
+se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
+                       float* row_max, float* row_lse, float* row_entropy,
+                       int32_t* row_argmax, void* stream);
+
+/*
+ * se_probs_bf16 -- materialise the probability slice for the unfused path.
+ *
+ *     probs[i, v] = bf16_rne( exp(logits[i, v] - row_lse[i]) )   for v in [s, e)
+ *
+ * (calvarado04.com, "The fix": the probability slice is cast to the embedding
+ * dtype before the product; rounding is to nearest, ties to even.)
+ * Only columns [s, e) of probs are written.  row_lse comes from se_row_stats.
+ * Requires 0 <= s <= e <= vocab, s % 8 == 0, ld_logits % 4 == 0,
+ * ld_probs % 8 == 0, ld_* >= vocab, 16-byte aligned logits/probs.
+ */
+se_status se_probs_bf16(const float* logits, int64_t ld_logits, const float* row_lse,
+                        int64_t n_rows, int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                        uint16_t* probs, int64_t ld_probs, void* stream);
+
+/*
+ * se_soft_embed_workspace_bytes -- device workspace the two soft-embed entry
+ * points need for this shape (0 when the contraction is not split).  It
+ * depends only on the shape.  Returns 0 for shapes the calls would reject.
+ */
+size_t se_soft_embed_workspace_bytes(int64_t n_rows, int64_t vocab_start, int64_t vocab_end,
+                                     int64_t d);
+
+/*
+ * se_soft_embed -- gamma * P[:, s:e] W_shard[0:e-s, :] from materialised bf16
+ * probabilities (calvarado04.com, "The fix": the slice of the gathered
+ * probabilities times the local shard, then the normaliser).
+ *
+ * probs:   bf16 [n_rows, ld_probs]; columns [s, e) are read.
+ * w_shard: bf16 [w_rows, ld_w]; rows [0, e - s) and columns [0, d) are read.
+ *          Rows at or past e - s (the next rank's rows, or padding) are never
+ *          read, so padding may hold anything.
+ * out:     fp32 [n_rows, ld_out]; columns [0, d) are written (fp32 accumulate).
+ * workspace: device buffer of at least se_soft_embed_workspace_bytes() bytes
+ *          (may be NULL when that is 0); its contents are scratch.
+ * An empty slice (s == e) writes zeros.  n_rows == 0 is a no-op.
+ * Requires 0 <= s <= e <= vocab, e - s <= w_rows, s % 8 == 0, d % 8 == 0,
+ * ld_probs % 8 == 0, ld_w % 8 == 0, ld_out % 4 == 0, ld_probs >= vocab,
+ * ld_w >= d, ld_out >= d, 16-byte aligned pointers.
+ */
+se_status se_soft_embed(const uint16_t* probs, int64_t ld_probs, int64_t n_rows, int64_t vocab,
+                        int64_t vocab_start, int64_t vocab_end,
+                        const uint16_t* w_shard, int64_t w_rows, int64_t ld_w, int64_t d,
+                        float gamma, float* out, int64_t ld_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * se_soft_embed_fused -- as se_soft_embed, but the bf16 probabilities are
+ * rebuilt from the fp32 logits and row_lse inside the contraction, so the
+ * probability matrix is never written to memory.  Same rounding as
+ * se_probs_bf16 (bf16 nearest-even of exp(l - lse)), same accumulation.
+ *
+ * logits:  fp32 [n_rows, ld_logits]; columns [s, e) are read.
+ * row_lse: fp32 [n_rows] from se_row_stats over the FULL width [0, vocab).
+ * Other arguments and requirements as se_soft_embed, with ld_logits % 4 == 0
+ * and ld_logits >= vocab.
+ */
+se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const float* row_lse,
+                              int64_t n_rows, int64_t vocab, int64_t vocab_start,
+                              int64_t vocab_end,
+                              const uint16_t* w_shard, int64_t w_rows, int64_t ld_w, int64_t d,
+                              float gamma, float* out, int64_t ld_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOFTEMBED_H */

@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads without a GPU; every argument check runs before any HIP
+call, so each error code can be provoked here with placeholder pointers.  No
+call in this file reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from diffusion_self_conditioning_amd import _binding as b
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "softembed.h")
+lib = b.lib
+
+# 16-byte aligned placeholder addresses: never dereferenced (calls below fail validation)
+P1, P2, P3, P4, P5 = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(se_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(b.EXPORTS)
+    raw = ctypes.CDLL(b.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings():
+    for code, name in enumerate(b.STATUS_NAMES):
+        assert b.se_status_string(code).startswith(name)
+    assert "gfx950" in b.se_version()
+
+
+def fused(**kw):
+    a = dict(logits=P1, ld=262144, lse=P2, n=256, vocab=262144, s=65536, e=131072, w=P3,
+             w_rows=65536, ldw=2816, d=2816, gamma=53.0, out=P4, ldo=2816, ws=P5,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.se_soft_embed_fused(a["logits"], a["ld"], a["lse"], a["n"], a["vocab"], a["s"],
+                                   a["e"], a["w"], a["w_rows"], a["ldw"], a["d"], a["gamma"],
+                                   a["out"], a["ldo"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def unfused(**kw):
+    a = dict(probs=P1, ld=262144, n=256, vocab=262144, s=65536, e=131072, w=P3, w_rows=65536,
+             ldw=2816, d=2816, gamma=53.0, out=P4, ldo=2816, ws=P5, ws_bytes=1 << 40,
+             stream=None)
+    a.update(kw)
+    return lib.se_soft_embed(a["probs"], a["ld"], a["n"], a["vocab"], a["s"], a["e"], a["w"],
+                             a["w_rows"], a["ldw"], a["d"], a["gamma"], a["out"], a["ldo"],
+                             a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_the_pages_failure_is_an_error_code():
+    """Full-width probabilities against a 65,536-row shard (calvarado04.com, 'The symptom')."""
+    assert fused(s=0, e=262144) == b.SE_ERR_SLICE
+    assert unfused(s=0, e=262144) == b.SE_ERR_SLICE
+
+
+@pytest.mark.parametrize("call", [fused, unfused])
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), b.SE_ERR_NULL),
+    (dict(out=None), b.SE_ERR_NULL),
+    (dict(n=-1), b.SE_ERR_SHAPE),
+    (dict(d=0), b.SE_ERR_SHAPE),
+    (dict(vocab=0), b.SE_ERR_SHAPE),
+    (dict(vocab=1 << 31), b.SE_ERR_SHAPE),
+    (dict(ld=262143), b.SE_ERR_SHAPE),
+    (dict(ldw=2815), b.SE_ERR_SHAPE),
+    (dict(ldo=2808), b.SE_ERR_SHAPE),
+    (dict(s=-8), b.SE_ERR_SLICE),
+    (dict(s=131072, e=65536), b.SE_ERR_SLICE),
+    (dict(e=262152), b.SE_ERR_SLICE),
+    (dict(w_rows=65535), b.SE_ERR_SLICE),
+    (dict(s=65540, e=131072, w_rows=70000), b.SE_ERR_ALIGN),
+    (dict(d=2812, ldw=2816, ldo=2816), b.SE_ERR_ALIGN),
+    (dict(ldw=2820), b.SE_ERR_ALIGN),
+    (dict(ldo=2818), b.SE_ERR_ALIGN),
+    (dict(w=P3 + 8), b.SE_ERR_ALIGN),
+    (dict(out=P4 + 4), b.SE_ERR_ALIGN),
+    (dict(ws_bytes=1024), b.SE_ERR_WORKSPACE),
+    (dict(ws=None), b.SE_ERR_NULL),
+])
+def test_argument_errors(call, kw, code):
+    assert call(**kw) == code
+
+
+def test_input_specific_errors():
+    assert fused(lse=None) == b.SE_ERR_NULL
+    assert fused(logits=P1 + 4) == b.SE_ERR_ALIGN
+    assert fused(ld=262146) == b.SE_ERR_ALIGN
+    assert unfused(probs=None) == b.SE_ERR_NULL
+    assert unfused(ld=262148) == b.SE_ERR_ALIGN
+    assert unfused(probs=P1 + 2) == b.SE_ERR_ALIGN
+
+
+def test_empty_rows_is_a_noop():
+    assert fused(n=0, ws=None, ws_bytes=0) == b.SE_OK
+    assert unfused(n=0, ws=None, ws_bytes=0) == b.SE_OK
+    assert lib.se_row_stats(P1, 64, 0, 64, P2, P3, P4, P5, None) == b.SE_OK
+    assert lib.se_probs_bf16(P1, 64, P2, 0, 64, 0, 64, P3, 64, None) == b.SE_OK
+    assert lib.se_probs_bf16(P1, 64, P2, 4, 64, 8, 8, P3, 64, None) == b.SE_OK   # empty slice
+
+
+def test_row_stats_errors():
+    rs = lib.se_row_stats
+    assert rs(None, 64, 4, 64, P2, P3, P4, P5, None) == b.SE_ERR_NULL
+    assert rs(P1, 64, 4, 64, P2, None, P4, P5, None) == b.SE_ERR_NULL
+    assert rs(P1, 60, 4, 64, P2, P3, P4, P5, None) == b.SE_ERR_SHAPE
+    assert rs(P1, 64, 4, 0, P2, P3, P4, P5, None) == b.SE_ERR_SHAPE
+    assert rs(P1, 66, 4, 64, P2, P3, P4, P5, None) == b.SE_ERR_ALIGN
+    assert rs(P1 + 4, 64, 4, 64, P2, P3, P4, P5, None) == b.SE_ERR_ALIGN
+    assert rs(P1, 64, 4, 64, P2 + 1, P3, P4, P5, None) == b.SE_ERR_ALIGN
+
+
+def test_probs_errors():
+    pb = lib.se_probs_bf16
+    assert pb(P1, 64, P2, 4, 64, 8, 72, P3, 64, None) == b.SE_ERR_SLICE
+    assert pb(P1, 64, P2, 4, 64, 4, 8, P3, 64, None) == b.SE_ERR_ALIGN
+    assert pb(P1, 64, P2, 4, 64, 8, 16, P3, 60, None) == b.SE_ERR_SHAPE
+    assert pb(P1, 64, P2, 4, 64, 8, 16, P3, 68, None) == b.SE_ERR_ALIGN
+
+
+def test_workspace_plan():
+    """256 x 256 output tiles, 64-wide vocab steps, split count = floor(256 / tiles) capped so
+    every split has at least 4 steps; partial tiles are fp32."""
+    tile = 256 * 256 * 4
+    ws = b.se_soft_embed_workspace_bytes
+    assert ws(256, 65536, 131072, 2816) == 23 * 11 * tile        # one rank: 11 tiles x 23 splits
+    assert ws(256, 0, 262144, 2816) == 23 * 11 * tile
+    assert ws(2048, 0, 262144, 2816) == 2 * 88 * tile            # 88 tiles x 2 splits
+    assert ws(16, 0, 4096, 256) == 16 * 1 * tile                 # 64 steps -> 16 splits
+    assert ws(16, 0, 64, 256) == 0                               # one step: no split
+    assert ws(16, 8, 8, 256) == 0                                # empty slice
+    assert ws(0, 0, 4096, 256) == 0
+
+
+def test_workspace_plan_large_m():
+    # 16 x 11 = 176 tiles: floor(256 / 176) = 1 split, no workspace
+    assert b.se_soft_embed_workspace_bytes(4096, 0, 262144, 2816) == 0
+    assert b.se_soft_embed_workspace_bytes(8192, 0, 262144, 2816) == 0
