@@ -43,13 +43,18 @@ constexpr int64_t kMaxGridY = 65535;
 
 se_status from_hip(hipError_t e) { return e == hipSuccess ? SE_OK : SE_ERR_HIP; }
 
-se_status check_slice_common(int64_t n_rows, int64_t vocab, int64_t s, int64_t e, int64_t w_rows,
-                             int64_t d, int64_t ld_w, int64_t ld_out, const void* w,
-                             const void* out) {
+// Shape and slice checks (no pointers involved).
+se_status check_slice_shape(int64_t n_rows, int64_t vocab, int64_t s, int64_t e, int64_t w_rows,
+                            int64_t d, int64_t ld_w, int64_t ld_out) {
   if (n_rows < 0 || vocab < 1 || d < 1 || w_rows < 0) return SE_ERR_SHAPE;
   if (vocab > INT32_MAX || d > INT32_MAX || n_rows > INT32_MAX) return SE_ERR_SHAPE;
   if (ld_w < d || ld_out < d) return SE_ERR_SHAPE;
   if (s < 0 || e < s || e > vocab || e - s > w_rows) return SE_ERR_SLICE;
+  return SE_OK;
+}
+
+se_status check_slice_layout(int64_t s, int64_t d, int64_t ld_w, int64_t ld_out, const void* w,
+                             const void* out) {
   if (!aligned16(w) || !aligned16(out)) return SE_ERR_ALIGN;
   if ((s % 8) != 0 || (d % 8) != 0 || (ld_w % 8) != 0 || (ld_out % 4) != 0) return SE_ERR_ALIGN;
   return SE_OK;
@@ -65,7 +70,6 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
   if (g.ws_bytes > 0 && (ws == nullptr)) return SE_ERR_NULL;
   if (g.ws_bytes > 0 && !aligned16(ws)) return SE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (n_rows == 0) return SE_OK;
   if (e == s) {
     for (int64_t r0 = 0; r0 < n_rows; r0 += kMaxGridY) {
       const int64_t nr = (n_rows - r0) < kMaxGridY ? (n_rows - r0) : kMaxGridY;
@@ -119,13 +123,13 @@ const char* se_version(void) {
 se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
                        float* row_max, float* row_lse, float* row_entropy, int32_t* row_argmax,
                        void* stream) {
-  if (!logits || !row_max || !row_lse || !row_entropy || !row_argmax) return SE_ERR_NULL;
   if (n_rows < 0 || vocab < 1 || vocab > INT32_MAX || n_rows > INT32_MAX) return SE_ERR_SHAPE;
   if (ld_logits < vocab) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  if (!logits || !row_max || !row_lse || !row_entropy || !row_argmax) return SE_ERR_NULL;
   if (!aligned16(logits) || (ld_logits % 4) != 0) return SE_ERR_ALIGN;
   if (!aligned4(row_max) || !aligned4(row_lse) || !aligned4(row_entropy) || !aligned4(row_argmax))
     return SE_ERR_ALIGN;
-  if (n_rows == 0) return SE_OK;
   return from_hip(se::launch_row_stats(logits, ld_logits, n_rows, (int)vocab, row_max, row_lse,
                                        row_entropy, row_argmax,
                                        static_cast<hipStream_t>(stream)));
@@ -134,14 +138,15 @@ se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, i
 se_status se_probs_bf16(const float* logits, int64_t ld_logits, const float* row_lse,
                         int64_t n_rows, int64_t vocab, int64_t vocab_start, int64_t vocab_end,
                         uint16_t* probs, int64_t ld_probs, void* stream) {
-  if (!logits || !row_lse || !probs) return SE_ERR_NULL;
   if (n_rows < 0 || vocab < 1 || vocab > INT32_MAX || n_rows > INT32_MAX) return SE_ERR_SHAPE;
   if (ld_logits < vocab || ld_probs < vocab) return SE_ERR_SHAPE;
   if (vocab_start < 0 || vocab_end < vocab_start || vocab_end > vocab) return SE_ERR_SLICE;
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  if (!logits || !row_lse || !probs) return SE_ERR_NULL;
   if (!aligned16(logits) || !aligned16(probs) || !aligned4(row_lse)) return SE_ERR_ALIGN;
   if ((ld_logits % 4) != 0 || (ld_probs % 8) != 0 || (vocab_start % 8) != 0) return SE_ERR_ALIGN;
   const int64_t K = vocab_end - vocab_start;
-  if (n_rows == 0 || K == 0) return SE_OK;
+  if (K == 0) return SE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   for (int64_t r0 = 0; r0 < n_rows; r0 += kMaxGridY) {
     const int64_t nr = (n_rows - r0) < kMaxGridY ? (n_rows - r0) : kMaxGridY;
@@ -165,11 +170,13 @@ se_status se_soft_embed(const uint16_t* probs, int64_t ld_probs, int64_t n_rows,
                         int64_t vocab_start, int64_t vocab_end, const uint16_t* w_shard,
                         int64_t w_rows, int64_t ld_w, int64_t d, float gamma, float* out,
                         int64_t ld_out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!probs || !w_shard || !out) return SE_ERR_NULL;
-  se_status rc = check_slice_common(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w,
-                                    ld_out, w_shard, out);
+  se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
   if (rc != SE_OK) return rc;
   if (ld_probs < vocab) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  if (!probs || !w_shard || !out) return SE_ERR_NULL;
+  rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_shard, out);
+  if (rc != SE_OK) return rc;
   if (!aligned16(probs) || (ld_probs % 8) != 0) return SE_ERR_ALIGN;
   return run_soft_embed(false, probs, ld_probs, nullptr, n_rows, vocab_start, vocab_end, w_shard,
                         ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
@@ -180,11 +187,13 @@ se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const floa
                               int64_t vocab_end, const uint16_t* w_shard, int64_t w_rows,
                               int64_t ld_w, int64_t d, float gamma, float* out, int64_t ld_out,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  if (!logits || !row_lse || !w_shard || !out) return SE_ERR_NULL;
-  se_status rc = check_slice_common(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w,
-                                    ld_out, w_shard, out);
+  se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
   if (rc != SE_OK) return rc;
   if (ld_logits < vocab) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  if (!logits || !row_lse || !w_shard || !out) return SE_ERR_NULL;
+  rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_shard, out);
+  if (rc != SE_OK) return rc;
   if (!aligned16(logits) || (ld_logits % 4) != 0 || !aligned4(row_lse)) return SE_ERR_ALIGN;
   return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start, vocab_end, w_shard,
                         ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);

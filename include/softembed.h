@@ -33,6 +33,7 @@
  *    decomposition depends only on the shapes, and every reduction runs in a
  *    fixed order.
  *  - Logits must be finite (not checked on the device).
+ *  - n_rows == 0 is a no-op that checks only sizes; its pointers may be NULL.
  *  - Calls are thread-safe and capture-safe (no allocation, no sync, no host
  *    read of device data).
  */

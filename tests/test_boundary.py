@@ -108,6 +108,12 @@ def test_empty_rows_is_a_noop():
     assert lib.se_row_stats(P1, 64, 0, 64, P2, P3, P4, P5, None) == b.SE_OK
     assert lib.se_probs_bf16(P1, 64, P2, 0, 64, 0, 64, P3, 64, None) == b.SE_OK
     assert lib.se_probs_bf16(P1, 64, P2, 4, 64, 8, 8, P3, 64, None) == b.SE_OK   # empty slice
+    # with no rows, no buffer is touched: NULL pointers are accepted
+    assert fused(n=0, logits=None, lse=None, w=None, out=None, ws=None, ws_bytes=0) == b.SE_OK
+    assert unfused(n=0, probs=None, w=None, out=None, ws=None, ws_bytes=0) == b.SE_OK
+    assert lib.se_row_stats(None, 64, 0, 64, None, None, None, None, None) == b.SE_OK
+    # ... but sizes are still checked
+    assert fused(n=0, s=0, e=262144, logits=None) == b.SE_ERR_SLICE
 
 
 def test_row_stats_errors():
