@@ -10,6 +10,7 @@ constexpr float kLog2e = 1.4426950408889634f;   // log2(e)
 constexpr float kLn2 = 0.6931471805599453f;     // ln(2)
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 // 2^x on the transcendental unit (v_exp_f32).

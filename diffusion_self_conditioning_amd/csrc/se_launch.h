@@ -17,10 +17,17 @@ namespace se {
 // the same probability columns run side by side.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 64;
+#ifndef SE_BK
+#define SE_BK 32
+#endif
+#ifndef SE_STAGES
+#define SE_STAGES 3
+#endif
+constexpr int kBK = SE_BK;                // vocab positions per main-loop step (32 or 64)
+constexpr int kStages = SE_STAGES;        // register stages of global loads in flight
 constexpr int kGemmThreads = 512;
 constexpr int kTargetCUs = 256;          // MI355X compute units: sizes the split count
-constexpr int kMinStepsPerSplit = 4;
+constexpr int kMinStepsPerSplit = 256 / kBK;   // at least 256 vocab positions per split
 constexpr int64_t kTileFloats = (int64_t)kBM * kBN;
 
 struct GemmPlan {
