@@ -18,11 +18,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   g.tiles_m = (M + kBM - 1) / kBM;
   g.tiles_n = (N + kBN - 1) / kBN;
   g.tiles = g.tiles_m * g.tiles_n;
-  g.ksteps = (K + kBK - 1) / kBK;
+  g.kblocks = (K + kSplitQuantum - 1) / kSplitQuantum;
   g.splits = 1;
   if (g.tiles > 0 && g.tiles < kTargetCUs) {
     int64_t s = kTargetCUs / g.tiles;
-    const int64_t cap = g.ksteps / kMinStepsPerSplit;
+    const int64_t cap = g.kblocks / kMinBlocksPerSplit;
     if (s > cap) s = cap;
     g.splits = s < 1 ? 1 : s;
   }
@@ -95,7 +95,7 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
   p.tiles_n = (int)g.tiles_n;
   p.tiles = (int)g.tiles;
   p.splits = (int)g.splits;
-  p.ksteps = (int)g.ksteps;
+  p.kblocks = (int)g.kblocks;
   return from_hip(se::launch_soft_embed(p, fused, st));
 }
 

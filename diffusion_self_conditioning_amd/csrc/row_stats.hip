@@ -31,8 +31,14 @@ struct RowState {
   int idx;    // first index of m
 };
 
-constexpr int kRowThreads = 1024;
-constexpr int kUnroll = 4;
+#ifndef SE_ROW_THREADS
+#define SE_ROW_THREADS 1024
+#endif
+#ifndef SE_ROW_UNROLL
+#define SE_ROW_UNROLL 4
+#endif
+constexpr int kRowThreads = SE_ROW_THREADS;
+constexpr int kUnroll = SE_ROW_UNROLL;
 
 __device__ __forceinline__ void merge(RowState& a, RowState b) {
   const bool take_b = (b.m > a.m) || (b.m == a.m && b.idx < a.idx);
@@ -90,7 +96,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
   for (; c + (kUnroll - 1) * kRowThreads < n4; c += kUnroll * kRowThreads) {
     float4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = x4[c + u * kRowThreads];
+    for (int u = 0; u < kUnroll; ++u) v[u] = load_stream_f4(x4 + c + u * kRowThreads);
     float cm = v[0].x;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
@@ -117,7 +123,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
     }
   }
   for (; c < n4; c += kRowThreads) {
-    const float4 v = x4[c];
+    const float4 v = load_stream_f4(x4 + c);
     const float cm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
     if (cm > st.m) {
       const int b = 4 * c;

@@ -13,6 +13,20 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte loads for data read once (nontemporal hint: no reuse expected,
+// keeps the stream from displacing data other workgroups re-read from L2).
+__device__ __forceinline__ uint4 load_stream_u4(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load_stream_f4(const void* p) {
+  const f32x4_t v = __builtin_nontemporal_load(static_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

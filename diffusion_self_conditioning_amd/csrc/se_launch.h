@@ -10,28 +10,23 @@ namespace se {
 
 // ---- work decomposition of the slice contraction (pure host logic) -------------
 // The output [M, N] is cut into BM x BN tiles; the contracted (vocab) axis into
-// BK-wide steps, and the steps of each tile into `splits` contiguous ranges
-// (split-K over the vocabulary axis, the in-GPU form of the partition identity on
-// calvarado04.com, "The fix").  Every tile uses the same split boundaries, and
-// workgroup b takes tile b % tiles, split b / tiles, so the workgroups that read
-// the same probability columns run side by side.
+// blocks of kSplitQuantum positions, and the blocks of each tile into `splits`
+// contiguous ranges (split-K over the vocabulary axis, the in-GPU form of the
+// partition identity on calvarado04.com, "The fix").  Every tile uses the same
+// split boundaries, and logical workgroup b takes tile b % tiles, split b / tiles,
+// so the workgroups that read the same probability columns run side by side.
+// Both contraction kernels use the same boundaries and add their MFMA products in
+// the same order, so fused and unfused results are bitwise identical.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-#ifndef SE_BK
-#define SE_BK 32
-#endif
-#ifndef SE_STAGES
-#define SE_STAGES 3
-#endif
-constexpr int kBK = SE_BK;                // vocab positions per main-loop step (32 or 64)
-constexpr int kStages = SE_STAGES;        // register stages of global loads in flight
 constexpr int kGemmThreads = 512;
-constexpr int kTargetCUs = 256;          // MI355X compute units: sizes the split count
-constexpr int kMinStepsPerSplit = 256 / kBK;   // at least 256 vocab positions per split
+constexpr int kSplitQuantum = 64;         // vocab positions per split block
+constexpr int kMinBlocksPerSplit = 4;     // at least 256 vocab positions per split
+constexpr int kTargetCUs = 256;           // MI355X compute units: sizes the split count
 constexpr int64_t kTileFloats = (int64_t)kBM * kBN;
 
 struct GemmPlan {
-  int64_t tiles_m, tiles_n, tiles, ksteps, splits, grid;
+  int64_t tiles_m, tiles_n, tiles, kblocks, splits, grid;
   size_t ws_bytes;
 };
 
@@ -49,7 +44,7 @@ struct GemmParams {
   float* out;
   int64_t ldo;
   float* ws;              // split partials [splits][tiles][kTileFloats]
-  int tiles_n, tiles, splits, ksteps;
+  int tiles_n, tiles, splits, kblocks;
 };
 
 hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int vocab,

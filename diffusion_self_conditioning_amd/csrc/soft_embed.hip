@@ -5,30 +5,35 @@
 // agreeing") restricted to one rank's vocab slice is that rank's partial S^(r);
 // the normaliser gamma scales it ("The fix").  Split-K is the partition identity
 // of the same section applied inside one GPU: each workgroup contracts one range
-// of vocabulary steps, and the partial tiles are summed in a fixed order.
+// of vocabulary positions, and the partial tiles are summed in a fixed order.
 //
-// Tiling (512 threads = 8 wave64s, one workgroup per CU):
-//   workgroup tile 256 (rows) x 256 (hidden) x 32 (vocab per step), double
-//   buffered in LDS (2 x 32 KiB).  Waves form a 2 x 4 grid; each owns a
-//   128 x 64 sub-tile = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16.
-// Global loads run kStages steps ahead through registers: the loads of step
-//   k + kStages are issued right after step k + 1 has been written to LDS, in the
-//   order in which they will be consumed, so each wait names exactly the loads
-//   it needs and the later ones stay in flight.
-// A operand (probabilities, vocab-contiguous rows) in LDS as [row][vocab]:
-//   fused   -- fp32 logits are loaded, turned into 2^(l log2e - lse log2e),
-//              rounded to bf16 and written to LDS; P never reaches memory.
-//   unfused -- bf16 probabilities are copied global -> LDS.
-//   A fragments are single ds_read_b128s.
-// B operand (embedding shard) in LDS as loaded, [vocab][hidden]: 16-byte
-//   chunks, no register shuffles.  The MFMA wants 8 vocab-consecutive values of
-//   one hidden column per lane; ds_read_b64_tr_b16 delivers them: in each group
-//   of 16 lanes, lane i names the 4-element piece (row kb + i/4, columns
-//   nb + 4 (i%4) .. +3) and lane j receives rows kb .. kb+3 of column nb + j.
-// Both LDS tiles XOR-swizzle their 16-byte chunk index by the row so that every
-//   write and every fragment read of a 16-lane group touches 64 distinct banks.
-// Rows past M, vocab positions past K and hidden columns past N are never read;
-// they enter the tile as exact zeros.
+// Tiling (512 threads = 8 wave64s, one workgroup per CU): a 256 (rows) x 256
+// (hidden) output tile, walked along the vocabulary in steps of BK (32 for the
+// fused variant, 64 for the bf16 one).  Waves form a 2 x 4 grid; each owns a
+// 128 x 64 sub-tile = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+//
+// LDS holds two buffers, each an A tile [256][BK] and a table tile [BK][256]:
+//   A (probabilities, vocab-contiguous rows): fused -- fp32 logits are loaded,
+//     turned into 2^(l log2e - lse log2e), rounded to bf16 and written to LDS, so
+//     P never reaches memory; unfused -- bf16 probabilities are copied.  A
+//     fragments are single ds_read_b128s.
+//   W (embedding shard) is stored as loaded, [vocab][hidden]: the MFMA wants 8
+//     vocab-consecutive values of one hidden column per lane and
+//     ds_read_b64_tr_b16 delivers them: in each group of 16 lanes, lane i names
+//     the 4-element piece (row kb + i/4, columns nb + 4 (i%4) .. +3) and lane j
+//     receives rows kb .. kb+3 of column nb + j; two such reads form a fragment.
+//   Both tiles XOR-swizzle their 16-byte chunk index with the row, so every write
+//   and every fragment read of a 16-lane group touches 64 distinct banks.
+//
+// Pipeline: two register stages of global loads.  While the waves multiply step
+// k out of one LDS buffer, piece by piece between the MFMAs they write step k + 1
+// from registers into the other buffer and refill those registers with step
+// k + 3; loads are issued in the order they are consumed, so every wait names
+// exactly the piece it needs.  The table is streamed with nontemporal loads.  The
+// main loop covers only full steps and has no load branches: rows past M and
+// columns past N are clamped (they only feed output rows / columns that are never
+// written).  A slice's last, partial step runs after the loop with guarded loads:
+// vocab positions past K enter as exact zeros and table rows past K are never read.
 #include "se_device.h"
 #include "se_launch.h"
 
@@ -36,22 +41,6 @@ namespace se {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kAStageBytes = kBM * kBK * 2;      // [256][kBK] bf16
-constexpr int kWStageBytes = kBK * kBN * 2;      // [kBK][256] bf16
-constexpr int kARowBytes = 2 * kBK;
-constexpr int kARowsPerBankLine = 256 / kARowBytes;   // rows sharing one 64-bank line
-constexpr int kAChunks = kBK / 8;                      // 16-byte chunks per A row
-// A fused: float4 per thread, kBK / 4 threads per row; A bf16 and W: 16 B per thread
-constexpr int kAFusedTpr = kBK / 4;
-constexpr int kAFusedPasses = kBM / (kGemmThreads / kAFusedTpr);
-constexpr int kABf16Tpr = kBK / 8;
-constexpr int kABf16Passes = kBM / (kGemmThreads / kABf16Tpr);
-constexpr int kWPasses = kBK / (kGemmThreads / 32);
-constexpr int kBufBytes = kAStageBytes + kWStageBytes;
-constexpr int kLdsBytes = 2 * kBufBytes;         // 64 KiB
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
 // Workgroups are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Renumber them so that each XCD owns a contiguous run of logical ids: the tiles
@@ -63,35 +52,60 @@ __device__ __forceinline__ int xcd_local_order(int b, int g) {
   return x * q + (x < r ? x : r) + slot;
 }
 
-// byte offset of A element (m, k): rows of 2 kBK bytes, 16-byte chunk index
-// (k / 8) XOR ((m / rows-per-bank-line) mod chunks-per-row)
-__device__ __forceinline__ int a_off(int m, int k) {
-  return m * kARowBytes + 16 * ((k >> 3) ^ ((m / kARowsPerBankLine) % kAChunks)) + 2 * (k & 7);
-}
-// byte offset of W element (k, n): rows of 512 bytes, chunk (n / 8) ^ (4 (k & 3))
+// byte offset of table element (k, n) in a [BK][256] LDS tile: rows of 512 bytes,
+// 16-byte chunk index (n / 8) XOR 4 (k % 4)
 __device__ __forceinline__ int w_off(int k, int n) {
   return k * 512 + 16 * ((n >> 3) ^ (4 * (k & 3))) + 2 * (n & 7);
 }
 
-template <bool FUSED>
-struct AStage;
-template <>
-struct AStage<true> {
-  float4 v[kAFusedPasses];   // fp32 logits, one float4 per pass
-};
-template <>
-struct AStage<false> {
-  uint4 v[kABf16Passes];     // bf16 probabilities, 8 per pass
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+
+template <bool FUSED, int BK>
+struct Cfg {
+  static constexpr int kKSub = BK / 16;                        // MFMA k-steps per step
+  static constexpr int kAStage = kBM * BK * 2;                 // bytes of the A tile
+  static constexpr int kWStage = BK * kBN * 2;                 // bytes of the table tile
+  static constexpr int kBuf = kAStage + kWStage;
+  static constexpr int kARowBytes = 2 * BK;
+  static constexpr int kARowsPerLine = 256 / kARowBytes;       // rows per 64-bank line
+  static constexpr int kAChunks = BK / 8;                      // 16-byte chunks per A row
+  // A loads: fused float4 per thread (BK/4 threads per row), bf16 16 B (BK/8 per row)
+  static constexpr int kATpr = FUSED ? BK / 4 : BK / 8;
+  static constexpr int kARowsPerPass = kGemmThreads / kATpr;
+  static constexpr int kAPasses = kBM / kARowsPerPass;
+  static constexpr int kWPasses = BK / (kGemmThreads / 32);    // 32 threads per table row
+  static constexpr int kAPiece = kAPasses / kKSub;
+  static constexpr int kWPiece = kWPasses / kKSub;
+  static_assert(kAPiece * kKSub == kAPasses && kWPiece * kKSub == kWPasses, "pieces");
+  static_assert(kSplitQuantum % BK == 0, "steps must tile the split quantum");
+
+  // byte offset of A element (m, k): 16-byte chunk index (k / 8) XOR a row function
+  __device__ static __forceinline__ int a_off(int m, int k) {
+    return m * kARowBytes + 16 * ((k >> 3) ^ ((m / kARowsPerLine) % kAChunks)) + 2 * (k & 7);
+  }
 };
 
-struct WStage {
-  uint4 v[kWPasses];         // bf16 table rows w_r + 16 i, columns 8 w_j .. +7
+template <bool FUSED, int BK>
+struct ARegs;
+template <int BK>
+struct ARegs<true, BK> {
+  float4 v[Cfg<true, BK>::kAPasses];      // fp32 logits
+};
+template <int BK>
+struct ARegs<false, BK> {
+  uint4 v[Cfg<false, BK>::kAPasses];      // bf16 probabilities
+};
+template <int BK>
+struct WRegs {
+  uint4 v[Cfg<true, BK>::kWPasses];       // bf16 table chunks
 };
 
-template <bool FUSED>
+template <bool FUSED, int BK>
 __global__ void __launch_bounds__(kGemmThreads)
 soft_embed_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  using C = Cfg<FUSED, BK>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * C::kBuf];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,67 +118,75 @@ soft_embed_kernel(const GemmParams p) {
   const int s = b / p.tiles;
   const int64_t m0 = (int64_t)(t / p.tiles_n) * kBM;
   const int64_t n0 = (int64_t)(t % p.tiles_n) * kBN;
-  const int ks0 = (int)(((int64_t)s * p.ksteps) / p.splits);
-  const int ks1 = (int)(((int64_t)(s + 1) * p.ksteps) / p.splits);
+  // this split's vocab range [k_lo, k_hi), in steps of BK: [s0, s1), full below sf
+  const int64_t k_lo = (((int64_t)s * p.kblocks) / p.splits) * kSplitQuantum;
+  const int64_t k_hi = min((((int64_t)(s + 1) * p.kblocks) / p.splits) * kSplitQuantum, p.K);
+  const int s0 = (int)(k_lo / BK);
+  const int s1 = (int)((k_hi + BK - 1) / BK);
+  const int sf = min(s1, (int)(p.K / BK));
 
-  // ---- per-thread load coordinates --------------------------------------------
-  // A fused: kBK/4 threads x float4 per row; A bf16: kBK/8 threads x 16 B per row;
-  // W: 32 threads x 16 B per row (256 bf16), 16 rows per pass.
-  constexpr int kATpr = FUSED ? kAFusedTpr : kABf16Tpr;
-  constexpr int kAPasses = FUSED ? kAFusedPasses : kABf16Passes;
-  constexpr int kARowsPerPass = kGemmThreads / kATpr;
-  const int a_c = tid % kATpr;
-  const int a_m = tid / kATpr;
+  // ---- per-thread load coordinates ----------------------------------------------
+  const int a_c = tid % C::kATpr;
+  const int a_m = tid / C::kATpr;
   const int w_j = tid & 31;
   const int w_r = tid >> 5;
 
   // Rows past M and columns past N only feed output rows / columns that are never
-  // written, so their loads are clamped to the last valid row / column instead of
-  // being guarded: the pipelined loads stay branch-free.
-  float nl[kAFusedPasses];
+  // written, so their loads are clamped to the last valid row / column.
+  auto a_row = [&](int i) -> int64_t { return min(m0 + a_m + C::kARowsPerPass * i, p.M - 1); };
+  float nl[C::kAPasses];
   if constexpr (FUSED) {
 #pragma unroll
-    for (int i = 0; i < kAFusedPasses; ++i) {
-      const int64_t row = min(m0 + a_m + kARowsPerPass * i, p.M - 1);
-      nl[i] = neg_lse_log2(p.lse[row]);
-    }
+    for (int i = 0; i < C::kAPasses; ++i) nl[i] = neg_lse_log2(p.lse[a_row(i)]);
   }
   const int64_t w_col = min(n0 + 8 * w_j, p.N - 8);
 
-  // Full step: every vocab position of the step is inside the slice.
-  auto load_full = [&](int ks, AStage<FUSED>& ra, WStage& rw) {
-    const int64_t kb = (int64_t)ks * kBK;
-    if constexpr (FUSED) {
-      const float* a = static_cast<const float*>(p.a) + p.col0 + kb + 4 * a_c;
+  // piece `pc` (of kKSub) of a full step
+  auto load_piece = [&](int ks, int pc, ARegs<FUSED, BK>& ra, WRegs<BK>& rw) {
+    const int64_t kb = (int64_t)ks * BK;
 #pragma unroll
-      for (int i = 0; i < kAPasses; ++i) {
-        const int64_t row = min(m0 + a_m + kARowsPerPass * i, p.M - 1);
-        ra.v[i] = *reinterpret_cast<const float4*>(a + row * p.lda);
-      }
-    } else {
-      const uint16_t* a = static_cast<const uint16_t*>(p.a) + p.col0 + kb + 8 * a_c;
-#pragma unroll
-      for (int i = 0; i < kAPasses; ++i) {
-        const int64_t row = min(m0 + a_m + kARowsPerPass * i, p.M - 1);
-        ra.v[i] = *reinterpret_cast<const uint4*>(a + row * p.lda);
+    for (int i = pc * C::kAPiece; i < (pc + 1) * C::kAPiece; ++i) {
+      if constexpr (FUSED) {
+        const float* a = static_cast<const float*>(p.a) + p.col0 + kb + 4 * a_c;
+        ra.v[i] = *reinterpret_cast<const float4*>(a + a_row(i) * p.lda);
+      } else {
+        const uint16_t* a = static_cast<const uint16_t*>(p.a) + p.col0 + kb + 8 * a_c;
+        ra.v[i] = *reinterpret_cast<const uint4*>(a + a_row(i) * p.lda);
       }
     }
 #pragma unroll
-    for (int i = 0; i < kWPasses; ++i)
-      rw.v[i] = *reinterpret_cast<const uint4*>(p.w + (kb + w_r + 16 * i) * p.ldw + w_col);
+    for (int i = pc * C::kWPiece; i < (pc + 1) * C::kWPiece; ++i)
+      rw.v[i] = load_stream_u4(p.w + (kb + w_r + 16 * i) * p.ldw + w_col);
   };
-
-  // Last, partial step: vocab positions past K enter as exact zeros (probability
-  // 0 from a -inf logit, or a zero bf16) and table rows past K are never read.
-  auto load_tail = [&](int ks, AStage<FUSED>& ra, WStage& rw) {
-    const int64_t kb = (int64_t)ks * kBK;
-    if constexpr (FUSED) {
-      const float* a = static_cast<const float*>(p.a);
-      const int64_t kk = kb + 4 * a_c;
+  auto store_piece = [&](int buf, int pc, const ARegs<FUSED, BK>& ra, const WRegs<BK>& rw) {
+    unsigned char* A = lds + buf * C::kBuf;
+    unsigned char* W = A + C::kAStage;
 #pragma unroll
-      for (int i = 0; i < kAPasses; ++i) {
-        const int64_t row = min(m0 + a_m + kARowsPerPass * i, p.M - 1);
-        const float* src = a + row * p.lda + p.col0 + kk;
+    for (int i = pc * C::kAPiece; i < (pc + 1) * C::kAPiece; ++i) {
+      const int m = a_m + C::kARowsPerPass * i;
+      if constexpr (FUSED) {
+        const float4 v = ra.v[i];
+        uint2 o;
+        o.x = pack_bf16x2(prob_from_logit(v.x, nl[i]), prob_from_logit(v.y, nl[i]));
+        o.y = pack_bf16x2(prob_from_logit(v.z, nl[i]), prob_from_logit(v.w, nl[i]));
+        *reinterpret_cast<uint2*>(A + C::a_off(m, 4 * a_c)) = o;
+      } else {
+        *reinterpret_cast<uint4*>(A + C::a_off(m, 8 * a_c)) = ra.v[i];
+      }
+    }
+#pragma unroll
+    for (int i = pc * C::kWPiece; i < (pc + 1) * C::kWPiece; ++i)
+      *reinterpret_cast<uint4*>(W + w_off(w_r + 16 * i, 8 * w_j)) = rw.v[i];
+  };
+  // the slice's last, partial step: positions past K are exact zeros (probability 0
+  // from a -inf logit, or a zero bf16); table rows past K are never read
+  auto load_tail = [&](int ks, ARegs<FUSED, BK>& ra, WRegs<BK>& rw) {
+    const int64_t kb = (int64_t)ks * BK;
+#pragma unroll
+    for (int i = 0; i < C::kAPasses; ++i) {
+      if constexpr (FUSED) {
+        const int64_t kk = kb + 4 * a_c;
+        const float* src = static_cast<const float*>(p.a) + a_row(i) * p.lda + p.col0 + kk;
         float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         if (kk + 4 <= p.K) {
           v = *reinterpret_cast<const float4*>(src);
@@ -174,14 +196,9 @@ soft_embed_kernel(const GemmParams p) {
           if (kk + 2 < p.K) v.z = src[2];
         }
         ra.v[i] = v;
-      }
-    } else {
-      const uint16_t* a = static_cast<const uint16_t*>(p.a);
-      const int64_t kk = kb + 8 * a_c;
-#pragma unroll
-      for (int i = 0; i < kAPasses; ++i) {
-        const int64_t row = min(m0 + a_m + kARowsPerPass * i, p.M - 1);
-        const uint16_t* src = a + row * p.lda + p.col0 + kk;
+      } else {
+        const int64_t kk = kb + 8 * a_c;
+        const uint16_t* src = static_cast<const uint16_t*>(p.a) + a_row(i) * p.lda + p.col0 + kk;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (kk + 8 <= p.K) {
           v = *reinterpret_cast<const uint4*>(src);
@@ -196,34 +213,12 @@ soft_embed_kernel(const GemmParams p) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < kWPasses; ++i) {
+    for (int i = 0; i < C::kWPasses; ++i) {
       const int64_t kr = kb + w_r + 16 * i;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (kr < p.K) v = *reinterpret_cast<const uint4*>(p.w + kr * p.ldw + w_col);
       rw.v[i] = v;
     }
-  };
-
-  auto store = [&](int buf, const AStage<FUSED>& ra, const WStage& rw) {
-    unsigned char* A = lds + buf * kBufBytes;
-    unsigned char* W = A + kAStageBytes;
-    if constexpr (FUSED) {
-#pragma unroll
-      for (int i = 0; i < kAPasses; ++i) {
-        const float4 v = ra.v[i];
-        uint2 o;
-        o.x = pack_bf16x2(prob_from_logit(v.x, nl[i]), prob_from_logit(v.y, nl[i]));
-        o.y = pack_bf16x2(prob_from_logit(v.z, nl[i]), prob_from_logit(v.w, nl[i]));
-        *reinterpret_cast<uint2*>(A + a_off(a_m + kARowsPerPass * i, 4 * a_c)) = o;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kAPasses; ++i)
-        *reinterpret_cast<uint4*>(A + a_off(a_m + kARowsPerPass * i, 8 * a_c)) = ra.v[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kWPasses; ++i)
-      *reinterpret_cast<uint4*>(W + w_off(w_r + 16 * i, 8 * w_j)) = rw.v[i];
   };
 
   f32x16 acc[4][2];
@@ -239,29 +234,27 @@ soft_embed_kernel(const GemmParams p) {
   const int half = lane >> 5;
   const int grp = lane >> 4;              // 16-lane group
   const int gi = lane & 15;
-  // transpose-read piece of this lane: row offset gi / 4, column offset 4 (gi % 4)
   const int tr_k = 8 * (grp >> 1) + (gi >> 2);
   const int tr_n = 16 * (grp & 1) + 4 * (gi & 3);
 
-  auto compute = [&](int buf) {
-    const unsigned char* A = lds + buf * kBufBytes;
-    const unsigned char* W = A + kAStageBytes;
+  // MFMAs of one step out of LDS buffer `buf`; `side(q)` runs after substep q
+  auto compute = [&](int buf, auto&& side) {
+    const unsigned char* A = lds + buf * C::kBuf;
+    const unsigned char* W = A + C::kAStage;
 #pragma unroll
-    for (int q = 0; q < kBK / 16; ++q) {
+    for (int q = 0; q < C::kKSub; ++q) {
       bf16x8 af[4], bfr[2];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int m = 128 * wm + 32 * mi + l32;
-        af[mi] = *reinterpret_cast<const bf16x8*>(A + a_off(m, 16 * q + 8 * half));
-      }
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8*>(A + C::a_off(128 * wm + 32 * mi + l32,
+                                                               16 * q + 8 * half));
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
         const int nb = 64 * wn + 32 * ni + tr_n;
         const int kb = 16 * q + tr_k;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_ptr)(W + w_off(kb, nb)));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_ptr)(W + w_off(kb + 4, nb)));
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(W + w_off(kb, nb)));
+        const v4i16 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(W + w_off(kb + 4, nb)));
         bfr[ni] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
                                           __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5,
                                           6, 7);
@@ -272,47 +265,53 @@ soft_embed_kernel(const GemmParams p) {
         for (int ni = 0; ni < 2; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni],
                                                                 0, 0, 0);
+      side(q);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- main loop: kStages register stages in flight, LDS double buffer ----------
-  // Steps [ks0, kf) are full.  Their loads are issued kStages steps ahead in
-  // consumption order; past the end the step index is clamped, so the loop body
-  // has no load branches (a few redundant in-bounds loads at the very end).
-  const int kf = min(ks1, (int)(p.K / kBK));
-  AStage<FUSED> ra[kStages];
-  WStage rw[kStages];
-  if (ks0 < kf) {
-    const int klast = kf - 1;
+  // ---- main loop over the full steps [s0, sf) --------------------------------------
+  ARegs<FUSED, BK> ra[2];
+  WRegs<BK> rw[2];
+  if (s0 < sf) {
+    const int slast = sf - 1;
 #pragma unroll
-    for (int j = 0; j < kStages; ++j) load_full(min(ks0 + j, klast), ra[j], rw[j]);
-    store(0, ra[0], rw[0]);
-    load_full(min(ks0 + kStages, klast), ra[0], rw[0]);
+    for (int pc = 0; pc < C::kKSub; ++pc) load_piece(s0, pc, ra[0], rw[0]);
+#pragma unroll
+    for (int pc = 0; pc < C::kKSub; ++pc) load_piece(min(s0 + 1, slast), pc, ra[1], rw[1]);
+#pragma unroll
+    for (int pc = 0; pc < C::kKSub; ++pc) {
+      store_piece(0, pc, ra[0], rw[0]);
+      load_piece(min(s0 + 2, slast), pc, ra[0], rw[0]);
+    }
     __syncthreads();
-    for (int base = ks0; base < kf; base += kStages) {
+    for (int base = s0; base < sf; base += 2) {
 #pragma unroll
-      for (int j = 0; j < kStages; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const int ks = base + j;
-        if (ks < kf) {
-          const int buf = (ks - ks0) & 1;
-          compute(buf);
-          const int nj = (j + 1) % kStages;
-          if (ks + 1 < kf) store(buf ^ 1, ra[nj], rw[nj]);
-          load_full(min(ks + 1 + kStages, klast), ra[nj], rw[nj]);
+        if (ks < sf) {
+          const int buf = (ks - s0) & 1;
+          const int nj = (j + 1) & 1;             // register stage holding step ks + 1
+          const bool more = ks + 1 < sf;
+          const int knext = min(ks + 3, slast);
+          compute(buf, [&](int q) {
+            if (more) store_piece(buf ^ 1, q, ra[nj], rw[nj]);
+            load_piece(knext, q, ra[nj], rw[nj]);
+          });
           __syncthreads();
         }
       }
     }
   }
-  if (kf < ks1) {
-    // the slice's last, partial step (only the final split has one)
-    load_tail(kf, ra[0], rw[0]);
-    store(0, ra[0], rw[0]);
+  if (sf < s1) {
+    load_tail(sf, ra[0], rw[0]);
+#pragma unroll
+    for (int pc = 0; pc < C::kKSub; ++pc) store_piece(0, pc, ra[0], rw[0]);
     __syncthreads();
-    compute(0);
+    compute(0, [](int) {});
   }
 
-  // ---- epilogue ---------------------------------------------------------------
+  // ---- epilogue ---------------------------------------------------------------------
   // 32x32 MFMA accumulator layout: register r of lane l holds
   //   row 8 (r / 4) + 4 (l / 32) + (r % 4),  column l % 32  of the block.
   if (p.splits == 1) {
@@ -320,10 +319,10 @@ soft_embed_kernel(const GemmParams p) {
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
-        const int64_t col = n0 + 64 * wn + 32 * ni + (lane & 31);
+        const int64_t col = n0 + 64 * wn + 32 * ni + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int64_t row = m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * half + (r & 3);
           if (row < p.M && col < p.N) p.out[row * p.ldo + col] = p.gamma * acc[mi][ni][r];
         }
       }
@@ -380,10 +379,11 @@ __global__ void zero_rows_kernel(float* __restrict__ out, int64_t ldo, int64_t N
 
 hipError_t launch_soft_embed(const GemmParams& p, bool fused, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles * p.splits));
+  // fused: 32 vocab positions per step (fp32 logits staging); bf16: 64
   if (fused)
-    hipLaunchKernelGGL(soft_embed_kernel<true>, grid, dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL((soft_embed_kernel<true, 32>), grid, dim3(kGemmThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(soft_embed_kernel<false>, grid, dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL((soft_embed_kernel<false, 64>), grid, dim3(kGemmThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));
