@@ -66,6 +66,12 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
                          void* stream) {
   const se::GemmPlan g = se::plan_gemm(n_rows, d, e - s);
   if (g.grid > INT32_MAX) return SE_ERR_SHAPE;
+  // the kernels address one tile's rows of `a` and a split's rows of the shard with
+  // 32-bit byte offsets
+  const int64_t esz = fused ? 4 : 2;
+  if ((int64_t)(se::kBM - 1) * lda * esz + (e - s) * esz > (int64_t)UINT32_MAX ||
+      (e - s) * ldw * 2 > (int64_t)UINT32_MAX)
+    return SE_ERR_SHAPE;
   if (ws_bytes < g.ws_bytes) return SE_ERR_WORKSPACE;
   if (g.ws_bytes > 0 && (ws == nullptr)) return SE_ERR_NULL;
   if (g.ws_bytes > 0 && !aligned16(ws)) return SE_ERR_ALIGN;

@@ -27,6 +27,36 @@ __device__ __forceinline__ float4 load_stream_f4(const void* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer resource over [base, base + bytes) for raw (unstructured) buffer loads:
+// the base sits in scalar registers, each load adds a 32-bit per-lane offset and a
+// 32-bit wave-uniform offset.  Dword 3 selects 32-bit raw access on gfx950.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// 16-byte raw buffer loads (LLVM's raw buffer-load intrinsic, bound by name: the
+// clang builtin of the same width drops all but one lane of the vector here).
+// `aux` 2 = nontemporal (streamed once).
+__device__ u32x4_t se_raw_buffer_load_u4(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
+                                         int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.v4i32");
+__device__ f32x4_t se_raw_buffer_load_f4(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
+                                         int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.v4f32");
+__device__ __forceinline__ uint4 buffer_load_u4(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint32_t soff) {
+  const u32x4_t v = se_raw_buffer_load_u4(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 buffer_load_u4_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                   uint32_t soff) {
+  const u32x4_t v = se_raw_buffer_load_u4(r, (int)voff, (int)soff, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 buffer_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+  const f32x4_t v = se_raw_buffer_load_f4(r, (int)voff, (int)soff, 0);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -39,11 +69,12 @@ __device__ __forceinline__ float prob_from_logit(float l, float nl) {
 
 __device__ __forceinline__ float neg_lse_log2(float lse) { return -(lse * kLog2e); }
 
-// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+// Two fp32 -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
-  uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-  return a | (b << 16);
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 }  // namespace se

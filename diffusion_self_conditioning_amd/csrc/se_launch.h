@@ -19,9 +19,9 @@ namespace se {
 // the same order, so fused and unfused results are bitwise identical.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kGemmThreads = 512;
-constexpr int kSplitQuantum = 64;         // vocab positions per split block
-constexpr int kMinBlocksPerSplit = 4;     // at least 256 vocab positions per split
+constexpr int kGemmThreads = 256;
+constexpr int kSplitQuantum = 128;        // vocab positions per split block
+constexpr int kMinBlocksPerSplit = 2;     // at least 256 vocab positions per split
 constexpr int kTargetCUs = 256;           // MI355X compute units: sizes the split count
 constexpr int64_t kTileFloats = (int64_t)kBM * kBN;
 

@@ -7,35 +7,51 @@
 // of the same section applied inside one GPU: each workgroup contracts one range
 // of vocabulary positions, and the partial tiles are summed in a fixed order.
 //
-// Tiling (512 threads = 8 wave64s, one workgroup per CU): a 256 (rows) x 256
-// (hidden) output tile, walked along the vocabulary in steps of BK (32 for the
-// fused variant, 64 for the bf16 one).  Waves form a 2 x 4 grid; each owns a
-// 128 x 64 sub-tile = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+// Tiling: one workgroup of 4 wave64s per CU, a 256 (rows) x 256 (hidden) output
+// tile.  The waves form a 2 x 2 grid; each owns a 128 x 128 sub-tile = 4 x 4
+// blocks of v_mfma_f32_32x32x16_bf16, i.e. 256 fp32 accumulators per lane.  Every
+// element of the probability tile and of the table tile is read from LDS by two
+// waves (the transposing table reads run at about half the rate of plain 16-byte
+// reads, so no wave layout reads the table more than twice).
 //
-// LDS holds two buffers, each an A tile [256][BK] and a table tile [BK][256]:
-//   A (probabilities, vocab-contiguous rows): fused -- fp32 logits are loaded,
-//     turned into 2^(l log2e - lse log2e), rounded to bf16 and written to LDS, so
-//     P never reaches memory; unfused -- bf16 probabilities are copied.  A
-//     fragments are single ds_read_b128s.
-//   W (embedding shard) is stored as loaded, [vocab][hidden]: the MFMA wants 8
-//     vocab-consecutive values of one hidden column per lane and
-//     ds_read_b64_tr_b16 delivers them: in each group of 16 lanes, lane i names
-//     the 4-element piece (row kb + i/4, columns nb + 4 (i%4) .. +3) and lane j
-//     receives rows kb .. kb+3 of column nb + j; two such reads form a fragment.
-//   Both tiles XOR-swizzle their 16-byte chunk index with the row, so every write
-//   and every fragment read of a 16-lane group touches 64 distinct banks.
+// The vocabulary is walked in steps of 32 positions grouped into super-steps of
+// 128.  LDS holds (160 KB):
+//   two probability tiles P [256][128] bf16, one per super-step (current / next).
+//     A fragment (8 consecutive positions of one row) is one ds_read_b128.
+//     fused: fp32 logits become 2^(l log2e - lse log2e) rounded to bf16 and are
+//     written here, so P never reaches memory; unfused: bf16 probabilities are
+//     copied.  The probability rows are loaded 512 (fused) or 256 (unfused) bytes
+//     at a time -- each load instruction covers 2 (4) rows, not 8 (16): the vector
+//     memory path serves few long runs much faster than many short ones.
+//   two table tiles W [32][256] bf16, one per step (current / next).  W is stored
+//     as loaded, [vocab][hidden]; the MFMA wants 8 vocab-consecutive values of one
+//     hidden column per lane, which ds_read_b64_tr_b16 delivers: in each group of
+//     16 lanes, lane i names the 4-element piece (row kb + i/4, columns
+//     nb + 4 (i%4) .. +3) and lane j receives rows kb .. kb+3 of column nb + j;
+//     two such reads form a fragment.
+//   Both tiles XOR-swizzle their 16-byte chunk index with the row, so the writes
+//   and the fragment reads of every 16-lane group hit distinct banks.
 //
-// Pipeline: two register stages of global loads.  While the waves multiply step
-// k out of one LDS buffer, piece by piece between the MFMAs they write step k + 1
-// from registers into the other buffer and refill those registers with step
-// k + 3; loads are issued in the order they are consumed, so every wait names
-// exactly the piece it needs.  The table is streamed with nontemporal loads.  The
-// main loop covers only full steps and has no load branches: rows past M and
-// columns past N are clamped (they only feed output rows / columns that are never
-// written).  A slice's last, partial step runs after the loop with guarded loads:
-// vocab positions past K enter as exact zeros and table rows past K are never read.
+// Pipeline.  Table: two register stages; while step k is multiplied, step k + 1
+// goes from registers to LDS and the registers are refilled with step k + 3.
+// Probabilities: two register sets of one quarter super-step each; during step q
+// of super-step S, quarter q of super-step S + 1 is converted into the other P tile
+// and its registers are refilled two quarters ahead.  All of it is interleaved
+// with the MFMAs.  Per-lane addresses are 32-bit offsets from wave-uniform buffer
+// bases, so advancing a step costs only scalar arithmetic.  The main loop covers
+// whole super-steps and has no load branches: loads past the split's end are
+// clamped to its last super-step (the data lands in a tile that is never read).
+// A slice's last, partial super-step runs after the loop with guarded loads:
+// positions past K enter as exact zeros, table rows past K are never read.  Rows
+// past M are clamped (they only feed output rows that are never written); that
+// path computes addresses per load and is used only when M is not a multiple of
+// 256.
 #include "se_device.h"
 #include "se_launch.h"
+
+#ifndef SE_SCHED
+#define SE_SCHED 3
+#endif
 
 namespace se {
 namespace {
@@ -52,263 +68,344 @@ __device__ __forceinline__ int xcd_local_order(int b, int g) {
   return x * q + (x < r ? x : r) + slot;
 }
 
-// byte offset of table element (k, n) in a [BK][256] LDS tile: rows of 512 bytes,
-// 16-byte chunk index (n / 8) XOR 4 (k % 4)
+constexpr int kBK = 32;                          // vocab positions per step
+constexpr int kQ = 4;                            // steps per super-step
+constexpr int kSS = kBK * kQ;                    // vocab positions per super-step
+constexpr int kPBuf = kBM * kSS * 2;             // bf16 probability tile of a super-step
+constexpr int kWBuf = kBK * kBN * 2;             // bf16 table tile of a step
+constexpr int kWBase = 2 * kPBuf;                // LDS: [P0][P1][W0][W1]
+constexpr int kLds = 2 * kPBuf + 2 * kWBuf;
+static_assert(kLds <= 160 * 1024, "LDS budget of one CU");
+static_assert(kSplitQuantum % kSS == 0, "super-steps must tile the split quantum");
+static_assert(kGemmThreads == 256, "4 waves in a 2 x 2 grid");
+
+// byte offset of P element (m, k) in a [256][128] tile: 256-byte rows, 16-byte
+// chunk index (k / 8) XOR (m % 16)
+__device__ __forceinline__ int p_off(int m, int k) {
+  return m * 256 + 16 * ((k >> 3) ^ (m & 15)) + 2 * (k & 7);
+}
+// byte offset of W element (k, n) in a [32][256] tile: 512-byte rows, 16-byte
+// chunk index (n / 8) XOR 4 (k % 4)
 __device__ __forceinline__ int w_off(int k, int n) {
   return k * 512 + 16 * ((n >> 3) ^ (4 * (k & 3))) + 2 * (n & 7);
 }
 
+// Probability producer geometry, per wave and super-step (the wave's 64 rows).
+//   fused: 32 loads of 4 fp32; load i covers rows 64 wave + 2 i + lane/32,
+//          positions 4 (lane % 32) .. +3.
+//   unfused: 16 loads of 8 bf16; load i covers rows 64 wave + 4 i + lane/16,
+//          positions 8 (lane % 16) .. +7.
+// A quarter (one step's share) is 8 (4) loads; two register sets of a quarter.
+template <bool FUSED>
+struct AGeo;
+template <>
+struct AGeo<true> {
+  static constexpr int kLoads = 32, kPerQ = 8, kRowsPerLoad = 2, kEsz = 4;
+  typedef float4 reg_t;
+  __device__ static int row(int i, int lane) { return 2 * i + (lane >> 5); }
+  __device__ static int pos(int lane) { return 4 * (lane & 31); }
+};
+template <>
+struct AGeo<false> {
+  static constexpr int kLoads = 16, kPerQ = 4, kRowsPerLoad = 4, kEsz = 2;
+  typedef uint4 reg_t;
+  __device__ static int row(int i, int lane) { return 4 * i + (lane >> 4); }
+  __device__ static int pos(int lane) { return 8 * (lane & 15); }
+};
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
-template <bool FUSED, int BK>
-struct Cfg {
-  static constexpr int kKSub = BK / 16;                        // MFMA k-steps per step
-  static constexpr int kAStage = kBM * BK * 2;                 // bytes of the A tile
-  static constexpr int kWStage = BK * kBN * 2;                 // bytes of the table tile
-  static constexpr int kBuf = kAStage + kWStage;
-  static constexpr int kARowBytes = 2 * BK;
-  static constexpr int kARowsPerLine = 256 / kARowBytes;       // rows per 64-bank line
-  static constexpr int kAChunks = BK / 8;                      // 16-byte chunks per A row
-  // A loads: fused float4 per thread (BK/4 threads per row), bf16 16 B (BK/8 per row)
-  static constexpr int kATpr = FUSED ? BK / 4 : BK / 8;
-  static constexpr int kARowsPerPass = kGemmThreads / kATpr;
-  static constexpr int kAPasses = kBM / kARowsPerPass;
-  static constexpr int kWPasses = BK / (kGemmThreads / 32);    // 32 threads per table row
-  static constexpr int kAPiece = kAPasses / kKSub;
-  static constexpr int kWPiece = kWPasses / kKSub;
-  static_assert(kAPiece * kKSub == kAPasses && kWPiece * kKSub == kWPasses, "pieces");
-  static_assert(kSplitQuantum % BK == 0, "steps must tile the split quantum");
-
-  // byte offset of A element (m, k): 16-byte chunk index (k / 8) XOR a row function
-  __device__ static __forceinline__ int a_off(int m, int k) {
-    return m * kARowBytes + 16 * ((k >> 3) ^ ((m / kARowsPerLine) % kAChunks)) + 2 * (k & 7);
-  }
-};
-
-template <bool FUSED, int BK>
-struct ARegs;
-template <int BK>
-struct ARegs<true, BK> {
-  float4 v[Cfg<true, BK>::kAPasses];      // fp32 logits
-};
-template <int BK>
-struct ARegs<false, BK> {
-  uint4 v[Cfg<false, BK>::kAPasses];      // bf16 probabilities
-};
-template <int BK>
-struct WRegs {
-  uint4 v[Cfg<true, BK>::kWPasses];       // bf16 table chunks
-};
-
-template <bool FUSED, int BK>
-__global__ void __launch_bounds__(kGemmThreads)
+template <bool FUSED, bool FULL>
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 soft_embed_kernel(const GemmParams p) {
-  using C = Cfg<FUSED, BK>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * C::kBuf];
+  using G = AGeo<FUSED>;
+  using AReg = typename G::reg_t;
+  constexpr int kEsz = G::kEsz;
+  constexpr int kPerQ = G::kPerQ;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2;          // 0..1 : 128-row half
-  const int wn = wave & 3;           // 0..3 : 64-column quarter
+  const int wm = wave >> 1;          // 128-row half
+  const int wn = wave & 1;           // 128-column half
 
   const int b = xcd_local_order((int)blockIdx.x, (int)gridDim.x);
   const int t = b % p.tiles;
   const int s = b / p.tiles;
-  const int64_t m0 = (int64_t)(t / p.tiles_n) * kBM;
-  const int64_t n0 = (int64_t)(t % p.tiles_n) * kBN;
-  // this split's vocab range [k_lo, k_hi), in steps of BK: [s0, s1), full below sf
+  const int m0 = (t / p.tiles_n) * kBM;
+  const int n0 = (t % p.tiles_n) * kBN;
+  // this split's vocab range [k_lo, k_hi): full super-steps [S0, Sf), then (last
+  // split only) the partial super-step Sf, whose steps end at ks_end
   const int64_t k_lo = (((int64_t)s * p.kblocks) / p.splits) * kSplitQuantum;
   const int64_t k_hi = min((((int64_t)(s + 1) * p.kblocks) / p.splits) * kSplitQuantum, p.K);
-  const int s0 = (int)(k_lo / BK);
-  const int s1 = (int)((k_hi + BK - 1) / BK);
-  const int sf = min(s1, (int)(p.K / BK));
+  const int S0 = (int)(k_lo / kSS);
+  const int Sf = (int)(min(k_hi, (p.K / kSS) * kSS) / kSS);
+  const int ks_end = (int)((k_hi + kBK - 1) / kBK);
+  const int M = (int)p.M, N = (int)p.N;
+  const int tile_rows = min(kBM, M - m0);
 
-  // ---- per-thread load coordinates ----------------------------------------------
-  const int a_c = tid % C::kATpr;
-  const int a_m = tid / C::kATpr;
-  const int w_j = tid & 31;
-  const int w_r = tid >> 5;
-
-  // Rows past M and columns past N only feed output rows / columns that are never
-  // written, so their loads are clamped to the last valid row / column.
-  auto a_row = [&](int i) -> int64_t { return min(m0 + a_m + C::kARowsPerPass * i, p.M - 1); };
-  float nl[C::kAPasses];
-  if constexpr (FUSED) {
-#pragma unroll
-    for (int i = 0; i < C::kAPasses; ++i) nl[i] = neg_lse_log2(p.lse[a_row(i)]);
-  }
-  const int64_t w_col = min(n0 + 8 * w_j, p.N - 8);
-
-  // piece `pc` (of kKSub) of a full step
-  auto load_piece = [&](int ks, int pc, ARegs<FUSED, BK>& ra, WRegs<BK>& rw) {
-    const int64_t kb = (int64_t)ks * BK;
-#pragma unroll
-    for (int i = pc * C::kAPiece; i < (pc + 1) * C::kAPiece; ++i) {
-      if constexpr (FUSED) {
-        const float* a = static_cast<const float*>(p.a) + p.col0 + kb + 4 * a_c;
-        ra.v[i] = *reinterpret_cast<const float4*>(a + a_row(i) * p.lda);
-      } else {
-        const uint16_t* a = static_cast<const uint16_t*>(p.a) + p.col0 + kb + 8 * a_c;
-        ra.v[i] = *reinterpret_cast<const uint4*>(a + a_row(i) * p.lda);
-      }
-    }
-#pragma unroll
-    for (int i = pc * C::kWPiece; i < (pc + 1) * C::kWPiece; ++i)
-      rw.v[i] = load_stream_u4(p.w + (kb + w_r + 16 * i) * p.ldw + w_col);
+  // ---- probability producer: buffer resource at (row m0, column col0) -----------------
+  const int64_t a_ld = p.lda * kEsz;
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(
+      static_cast<const unsigned char*>(p.a) + ((int64_t)m0 * p.lda + p.col0) * kEsz,
+      (uint32_t)min((int64_t)(tile_rows - 1) * a_ld + p.K * kEsz, (int64_t)UINT32_MAX));
+  const int a_row0 = 64 * wave;
+  const uint32_t a_lo = (uint32_t)((a_row0 + G::row(0, lane)) * a_ld) + kEsz * G::pos(lane);
+  // -(lse log2e) of row 64 wave + lane; load i fetches its rows' values with a
+  // cross-lane permute (no LDS storage)
+  float nl_lane = 0.f;
+  if constexpr (FUSED) nl_lane = neg_lse_log2(p.lse[m0 + min(a_row0 + lane, tile_rows - 1)]);
+  auto nl_of = [&](int i) -> float {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                         4 * G::row(i, lane), __builtin_bit_cast(int, nl_lane)));
   };
-  auto store_piece = [&](int buf, int pc, const ARegs<FUSED, BK>& ra, const WRegs<BK>& rw) {
-    unsigned char* A = lds + buf * C::kBuf;
-    unsigned char* W = A + C::kAStage;
-#pragma unroll
-    for (int i = pc * C::kAPiece; i < (pc + 1) * C::kAPiece; ++i) {
-      const int m = a_m + C::kARowsPerPass * i;
-      if constexpr (FUSED) {
-        const float4 v = ra.v[i];
-        uint2 o;
-        o.x = pack_bf16x2(prob_from_logit(v.x, nl[i]), prob_from_logit(v.y, nl[i]));
-        o.y = pack_bf16x2(prob_from_logit(v.z, nl[i]), prob_from_logit(v.w, nl[i]));
-        *reinterpret_cast<uint2*>(A + C::a_off(m, 4 * a_c)) = o;
-      } else {
-        *reinterpret_cast<uint4*>(A + C::a_off(m, 8 * a_c)) = ra.v[i];
-      }
+  // LDS store offset of load i (within a P tile).  Row 64 wave + R i + r (r = this
+  // lane's row within the load) has swizzle (R i + r) % 16 = (R (i % (16 / R))) ^ r,
+  // so the offset is a per-lane base with the chunk bits XORed by 16 R (i % (16 / R)).
+  constexpr int kR = G::kRowsPerLoad;
+  const int a_r = G::row(0, lane);
+  const uint32_t a_st_row = (uint32_t)(a_row0 + a_r) * 256;
+  const uint32_t a_st_chk = 16u * (uint32_t)((G::pos(lane) >> 3) ^ a_r) + 2u * (G::pos(lane) & 7);
+
+  // load i of super-step S (clamped by the caller)
+  auto load_a = [&](int S, int i) -> AReg {
+    uint32_t voff, soff = (uint32_t)S * (kSS * kEsz);
+    if constexpr (FULL) {
+      voff = a_lo;
+      soff += (uint32_t)(i * G::kRowsPerLoad * a_ld);
+    } else {
+      const int row = min(a_row0 + G::row(i, lane), tile_rows - 1);
+      voff = (uint32_t)(row * a_ld) + kEsz * G::pos(lane);
     }
-#pragma unroll
-    for (int i = pc * C::kWPiece; i < (pc + 1) * C::kWPiece; ++i)
-      *reinterpret_cast<uint4*>(W + w_off(w_r + 16 * i, 8 * w_j)) = rw.v[i];
+    if constexpr (FUSED) return buffer_load_f4(a_rsrc, voff, soff);
+    else return buffer_load_u4(a_rsrc, voff, soff);
   };
-  // the slice's last, partial step: positions past K are exact zeros (probability 0
-  // from a -inf logit, or a zero bf16); table rows past K are never read
-  auto load_tail = [&](int ks, ARegs<FUSED, BK>& ra, WRegs<BK>& rw) {
-    const int64_t kb = (int64_t)ks * BK;
-#pragma unroll
-    for (int i = 0; i < C::kAPasses; ++i) {
-      if constexpr (FUSED) {
-        const int64_t kk = kb + 4 * a_c;
-        const float* src = static_cast<const float*>(p.a) + a_row(i) * p.lda + p.col0 + kk;
-        float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (kk + 4 <= p.K) {
-          v = *reinterpret_cast<const float4*>(src);
-        } else {
-          if (kk + 0 < p.K) v.x = src[0];
-          if (kk + 1 < p.K) v.y = src[1];
-          if (kk + 2 < p.K) v.z = src[2];
-        }
-        ra.v[i] = v;
-      } else {
-        const int64_t kk = kb + 8 * a_c;
-        const uint16_t* src = static_cast<const uint16_t*>(p.a) + a_row(i) * p.lda + p.col0 + kk;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (kk + 8 <= p.K) {
-          v = *reinterpret_cast<const uint4*>(src);
-        } else if (kk < p.K) {
-          uint32_t h[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) h[j] = (kk + j < p.K) ? (uint32_t)src[j] : 0u;
-          v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                         h[6] | (h[7] << 16));
-        }
-        ra.v[i] = v;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::kWPasses; ++i) {
-      const int64_t kr = kb + w_r + 16 * i;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (kr < p.K) v = *reinterpret_cast<const uint4*>(p.w + kr * p.ldw + w_col);
-      rw.v[i] = v;
+  // convert / copy load i (register r) into P tile `pbuf`
+  auto store_a = [&](int pbuf, int i, const AReg& r, float nl) {
+    unsigned char* dst = lds + pbuf * kPBuf + a_st_row + i * kR * 256 +
+                         (a_st_chk ^ (uint32_t)(16 * kR * (i % (16 / kR))));
+    if constexpr (FUSED) {
+      uint2 o;
+      o.x = pack_bf16x2(prob_from_logit(r.x, nl), prob_from_logit(r.y, nl));
+      o.y = pack_bf16x2(prob_from_logit(r.z, nl), prob_from_logit(r.w, nl));
+      *reinterpret_cast<uint2*>(dst) = o;
+    } else {
+      *reinterpret_cast<uint4*>(dst) = r;
     }
   };
 
-  f32x16 acc[4][2];
+  // ---- table producer: buffer resource at shard row k_lo -------------------------------
+  // step ks, piece j (0..3): rows 8 wave + 2 j + lane/32, columns 8 (lane % 32) .. +7
+  const int64_t w_ld = p.ldw * 2;
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      make_rsrc(reinterpret_cast<const unsigned char*>(p.w) + k_lo * w_ld,
+                (uint32_t)min((k_hi - k_lo) * w_ld, (int64_t)UINT32_MAX));
+  const uint32_t w_lo = (uint32_t)((8 * wave + (lane >> 5)) * w_ld) +
+                        2 * (uint32_t)min(n0 + 8 * (lane & 31), N - 8);
+  uint32_t w_st[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    w_st[e] = kWBase + w_off(8 * wave + 2 * e + (lane >> 5), 8 * (lane & 31)) - 1024 * e;
+  auto load_w = [&](int ks, int j) -> uint4 {
+    return buffer_load_u4_nt(w_rsrc, w_lo,
+                             (uint32_t)(((int64_t)ks * kBK - k_lo + 2 * j) * w_ld));
+  };
+  auto store_w = [&](int wbuf, int j, const uint4& r) {
+    *reinterpret_cast<uint4*>(lds + wbuf * kWBuf + w_st[j & 1] + 1024 * j) = r;
+  };
+
+  f32x16 acc[4][4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  // per-lane fragment coordinates
-  const int l32 = lane & 31;
-  const int half = lane >> 5;
-  const int grp = lane >> 4;              // 16-lane group
-  const int gi = lane & 15;
-  const int tr_k = 8 * (grp >> 1) + (gi >> 2);
-  const int tr_n = 16 * (grp & 1) + 4 * (gi & 3);
-
-  // MFMAs of one step out of LDS buffer `buf`; `side(q)` runs after substep q
-  auto compute = [&](int buf, auto&& side) {
-    const unsigned char* A = lds + buf * C::kBuf;
-    const unsigned char* W = A + C::kAStage;
+  // ---- fragments ---------------------------------------------------------------------
+  // A, substep u (0..7) of a super-step: row 128 wm + 32 mi + lane % 32, positions
+  // 16 u + 8 (lane / 32) .. +7
+  // p_off(row, 16 u + 8 h) with row % 16 = lane % 16 is rd_row + (rd_chk ^ 32 u)
+  const uint32_t rd_row = (uint32_t)(128 * wm + (lane & 31)) * 256;
+  const uint32_t rd_chk = 16u * (uint32_t)((lane >> 5) ^ (lane & 15));
+  // W: 16-lane group g, lane i: piece (row 8 (g/2) + i/4, columns 32 ni + 16 (g%2) + 4 (i%4))
+  uint32_t b_rd[4];
+  {
+    const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-    for (int q = 0; q < C::kKSub; ++q) {
-      bf16x8 af[4], bfr[2];
+    for (int ni = 0; ni < 4; ++ni)
+      b_rd[ni] = kWBase + w_off(8 * (g >> 1) + (i >> 2), 128 * wn + 32 * ni + 16 * (g & 1) + 4 * (i & 3));
+  }
+  auto frag_read = [&](int pbuf, int wbuf, int u, int q, bf16x8 (&af)[4], bf16x8 (&bf)[4]) {
+    const unsigned char* pa = lds + pbuf * kPBuf + rd_row + (rd_chk ^ (uint32_t)(32 * u));
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(A + C::a_off(128 * wm + 32 * mi + l32,
-                                                               16 * q + 8 * half));
+    for (int mi = 0; mi < 4; ++mi) af[mi] = *reinterpret_cast<const bf16x8*>(pa + 8192 * mi);
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int nb = 64 * wn + 32 * ni + tr_n;
-        const int kb = 16 * q + tr_k;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(W + w_off(kb, nb)));
-        const v4i16 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(W + w_off(kb + 4, nb)));
-        bfr[ni] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
-                                          __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5,
-                                          6, 7);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni],
-                                                                0, 0, 0);
-      side(q);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int ni = 0; ni < 4; ++ni) {
+      const unsigned char* wp = lds + wbuf * kWBuf + b_rd[ni] + 8192 * q;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp + 2048));
+      bf[ni] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
+                                       __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
+  auto mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+  };
 
-  // ---- main loop over the full steps [s0, sf) --------------------------------------
-  ARegs<FUSED, BK> ra[2];
-  WRegs<BK> rw[2];
-  if (s0 < sf) {
-    const int slast = sf - 1;
+  // One step: the 2 substeps' fragments are read up front; side(q) is interleaved
+  // with substep q's 16 MFMAs.
+  auto compute = [&](int pbuf, int wbuf, int qstep, auto&& side) {
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    frag_read(pbuf, wbuf, 2 * qstep, 0, a0, b0);
+    frag_read(pbuf, wbuf, 2 * qstep + 1, 1, a1, b1);
+    mfmas(a0, b0);
+    side(0);
+#if SE_SCHED
+    // substep 0 fragment reads, then (fused) the lse permutes of this half's conversions
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
-    for (int pc = 0; pc < C::kKSub; ++pc) load_piece(s0, pc, ra[0], rw[0]);
-#pragma unroll
-    for (int pc = 0; pc < C::kKSub; ++pc) load_piece(min(s0 + 1, slast), pc, ra[1], rw[1]);
-#pragma unroll
-    for (int pc = 0; pc < C::kKSub; ++pc) {
-      store_piece(0, pc, ra[0], rw[0]);
-      load_piece(min(s0 + 2, slast), pc, ra[0], rw[0]);
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, SE_SCHED, 0);  // VALU
+      if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // substep 1 reads
+      if (i >= 4 && i < 10) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS writes
+      if (i >= 8 && i < 14) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // loads
     }
-    __syncthreads();
-    for (int base = s0; base < sf; base += 2) {
+#endif
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a1, b1);
+    side(1);
+#if SE_SCHED
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int ks = base + j;
-        if (ks < sf) {
-          const int buf = (ks - s0) & 1;
-          const int nj = (j + 1) & 1;             // register stage holding step ks + 1
-          const bool more = ks + 1 < sf;
-          const int knext = min(ks + 3, slast);
-          compute(buf, [&](int q) {
-            if (more) store_piece(buf ^ 1, q, ra[nj], rw[nj]);
-            load_piece(knext, q, ra[nj], rw[nj]);
-          });
-          __syncthreads();
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, SE_SCHED, 0);
+      if (i >= 2 && i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (i >= 6 && i < 12) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+#endif
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- main loop over the full super-steps [S0, Sf) ------------------------------------
+  AReg ra[2][kPerQ];                 // quarter registers: set q % 2
+  uint4 rw[2][4];                    // table register stages
+  if (S0 < Sf) {
+    const int Slast = Sf - 1;
+    const int kslast = 4 * Sf - 1;
+    const int ks0 = 4 * S0;
+    // prologue: P tile of S0 complete, quarters 0 / 1 of S0 + 1 in flight; table
+    // step ks0 in LDS, ks0 + 1 / ks0 + 2 in flight
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+#pragma unroll
+      for (int i = 0; i < kPerQ; ++i) ra[q & 1][i] = load_a(S0, q * kPerQ + i);
+#pragma unroll
+      for (int i = 0; i < kPerQ; ++i) store_a(S0 & 1, q * kPerQ + i, ra[q & 1][i], nl_of(q * kPerQ + i));
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < kPerQ; ++i) ra[q][i] = load_a(min(S0 + 1, Slast), q * kPerQ + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rw[0][j] = load_w(ks0, j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rw[1][j] = load_w(min(ks0 + 1, kslast), j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store_w(0, j, rw[0][j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rw[0][j] = load_w(min(ks0 + 2, kslast), j);
+    __syncthreads();
+
+    for (int S = S0; S < Sf; ++S) {
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int ks = 4 * S + q;
+        uint4 (&rwn)[4] = rw[(q + 1) & 1];            // table step ks + 1
+        AReg (&rq)[kPerQ] = ra[q & 1];                // quarter q of super-step S + 1
+        // refill: quarter q + 2 of S + 1, or quarter q - 2 of S + 2
+        const int Sr = min(q < 2 ? S + 1 : S + 2, Slast);
+        const int qr = (q + 2) & 3;
+        const int kn = min(ks + 3, kslast);
+        float nlq[FUSED ? kPerQ : 1];
+        if constexpr (FUSED) {
+#pragma unroll
+          for (int i = 0; i < kPerQ; ++i) nlq[i] = nl_of(q * kPerQ + i);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        compute(S & 1, q & 1, q, [&](int h) {
+#pragma unroll
+          for (int j = 2 * h; j < 2 * h + 2; ++j) store_w((q + 1) & 1, j, rwn[j]);
+#pragma unroll
+          for (int i = h * kPerQ / 2; i < (h + 1) * kPerQ / 2; ++i)
+            store_a((S + 1) & 1, q * kPerQ + i, rq[i], nlq[FUSED ? i : 0]);
+#pragma unroll
+          for (int j = 2 * h; j < 2 * h + 2; ++j) rwn[j] = load_w(kn, j);
+#pragma unroll
+          for (int i = h * kPerQ / 2; i < (h + 1) * kPerQ / 2; ++i) rq[i] = load_a(Sr, qr * kPerQ + i);
+        });
+        __syncthreads();
       }
     }
   }
-  if (sf < s1) {
-    load_tail(sf, ra[0], rw[0]);
+
+  // ---- the partial last super-step (last split only) -------------------------------------
+  if (4 * Sf < ks_end) {
+    const int64_t kb = (int64_t)Sf * kSS;
+    const unsigned char* abase = static_cast<const unsigned char*>(p.a) +
+                                 ((int64_t)m0 * p.lda + p.col0 + kb) * kEsz;
 #pragma unroll
-    for (int pc = 0; pc < C::kKSub; ++pc) store_piece(0, pc, ra[0], rw[0]);
-    __syncthreads();
-    compute(0, [](int) {});
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int row = min(a_row0 + G::row(i, lane), tile_rows - 1);
+      const int64_t kk = kb + G::pos(lane);
+      const unsigned char* src = abase + (int64_t)row * a_ld + kEsz * G::pos(lane);
+      AReg v;
+      if constexpr (FUSED) {
+        const float* f = reinterpret_cast<const float*>(src);
+        v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (kk + 4 <= p.K) {
+          v = *reinterpret_cast<const float4*>(f);
+        } else {
+          if (kk + 0 < p.K) v.x = f[0];
+          if (kk + 1 < p.K) v.y = f[1];
+          if (kk + 2 < p.K) v.z = f[2];
+        }
+      } else {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(src);
+        v = make_uint4(0u, 0u, 0u, 0u);
+        if (kk + 8 <= p.K) {
+          v = *reinterpret_cast<const uint4*>(h);
+        } else if (kk < p.K) {
+          uint32_t e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e[j] = (kk + j < p.K) ? (uint32_t)h[j] : 0u;
+          v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                         e[6] | (e[7] << 16));
+        }
+      }
+      store_a(0, i, v, nl_of(i));
+    }
+    for (int ks = 4 * Sf; ks < ks_end; ++ks) {
+      const int64_t kr0 = (int64_t)ks * kBK;
+      const unsigned char* wb = reinterpret_cast<const unsigned char*>(p.w) + kr0 * w_ld;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t kr = kr0 + 8 * wave + 2 * j + (lane >> 5);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (kr < p.K) v = *reinterpret_cast<const uint4*>(wb + (int64_t)(2 * j) * w_ld + w_lo);
+        store_w(0, j, v);
+      }
+      __syncthreads();
+      compute(0, 0, ks - 4 * Sf, [](int) {});
+      __syncthreads();
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------------------
@@ -318,12 +415,12 @@ soft_embed_kernel(const GemmParams p) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int64_t col = n0 + 64 * wn + 32 * ni + l32;
+      for (int ni = 0; ni < 4; ++ni) {
+        const int col = n0 + 128 * wn + 32 * ni + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (row < p.M && col < p.N) p.out[row * p.ldo + col] = p.gamma * acc[mi][ni][r];
+          const int row = m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < M && col < N) p.out[(int64_t)row * p.ldo + col] = p.gamma * acc[mi][ni][r];
         }
       }
   } else {
@@ -332,10 +429,10 @@ soft_embed_kernel(const GemmParams p) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          dst[((wave * 8 + mi * 2 + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
+          dst[((wave * 16 + mi * 4 + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
   }
 }
 
@@ -352,12 +449,12 @@ splitk_reduce_kernel(const float* __restrict__ ws, int tiles, int tiles_n, int s
   const int e0 = ((blockIdx.x % kBlocksPerTile) * kReduceThreads + threadIdx.x) * 4;
   const int l0 = e0 & 63;
   const int r = (e0 >> 6) & 15;
-  const int blk = e0 >> 10;
-  const int wave = blk >> 3, mi = (blk >> 1) & 3, ni = blk & 1;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int blk = e0 >> 10;                       // wave * 16 + mi * 4 + ni
+  const int wave = blk >> 4, mi = (blk >> 2) & 3, ni = blk & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int64_t row = (int64_t)(t / tiles_n) * kBM + 128 * wm + 32 * mi + 8 * (r >> 2) +
                       4 * (l0 >> 5) + (r & 3);
-  const int64_t col = (int64_t)(t % tiles_n) * kBN + 64 * wn + 32 * ni + (l0 & 31);
+  const int64_t col = (int64_t)(t % tiles_n) * kBN + 128 * wn + 32 * ni + (l0 & 31);
   if (row >= M || col >= N) return;
   const float* src = ws + (int64_t)t * kTileFloats + e0;
   float4 a = *reinterpret_cast<const float4*>(src);
@@ -379,11 +476,16 @@ __global__ void zero_rows_kernel(float* __restrict__ out, int64_t ldo, int64_t N
 
 hipError_t launch_soft_embed(const GemmParams& p, bool fused, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles * p.splits));
-  // fused: 32 vocab positions per step (fp32 logits staging); bf16: 64
-  if (fused)
-    hipLaunchKernelGGL((soft_embed_kernel<true, 32>), grid, dim3(kGemmThreads), 0, stream, p);
+  // whole 256-row tiles take the path with per-lane addresses fixed for the kernel
+  const bool full = p.M % kBM == 0;
+  if (fused && full)
+    hipLaunchKernelGGL((soft_embed_kernel<true, true>), grid, dim3(kGemmThreads), 0, stream, p);
+  else if (fused)
+    hipLaunchKernelGGL((soft_embed_kernel<true, false>), grid, dim3(kGemmThreads), 0, stream, p);
+  else if (full)
+    hipLaunchKernelGGL((soft_embed_kernel<false, true>), grid, dim3(kGemmThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((soft_embed_kernel<false, 64>), grid, dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL((soft_embed_kernel<false, false>), grid, dim3(kGemmThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));

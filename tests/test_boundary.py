@@ -136,15 +136,15 @@ def test_probs_errors():
 
 
 def test_workspace_plan():
-    """256 x 256 output tiles, 64-wide vocab steps, split count = floor(256 / tiles) capped so
-    every split has at least 4 steps; partial tiles are fp32."""
+    """256 x 256 output tiles, vocab split in blocks of 128 positions, split count =
+    floor(256 / tiles) capped so every split has at least 2 blocks; partial tiles are fp32."""
     tile = 256 * 256 * 4
     ws = b.se_soft_embed_workspace_bytes
     assert ws(256, 65536, 131072, 2816) == 23 * 11 * tile        # one rank: 11 tiles x 23 splits
     assert ws(256, 0, 262144, 2816) == 23 * 11 * tile
     assert ws(2048, 0, 262144, 2816) == 2 * 88 * tile            # 88 tiles x 2 splits
-    assert ws(16, 0, 4096, 256) == 16 * 1 * tile                 # 64 steps -> 16 splits
-    assert ws(16, 0, 64, 256) == 0                               # one step: no split
+    assert ws(16, 0, 4096, 256) == 16 * 1 * tile                 # 32 blocks -> 16 splits
+    assert ws(16, 0, 64, 256) == 0                               # one block: no split
     assert ws(16, 8, 8, 256) == 0                                # empty slice
     assert ws(0, 0, 4096, 256) == 0
 
