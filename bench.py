@@ -205,6 +205,32 @@ def main():
         " call (soft_embed_kernel + splitk_reduce_kernel)"
     roof["algorithmic_bytes"] = call_bytes
 
+    # side measurement (not part of `value`): the unfused call on the same inputs,
+    # se_probs_bf16 (bf16 probability slice written to memory) + se_soft_embed
+    side = None
+    if not args.unfused:
+        pr = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16)
+        out_u = torch.empty_like(out)
+
+        def unfused():
+            B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, pr)
+            B.se_soft_embed(pr, w.vocab_start, w.vocab_end, shard, w.gamma, out_u, ws)
+
+        for _ in range(args.warmup):
+            unfused()
+        evu = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        torch.cuda.synchronize()
+        evu[0].record()
+        for k in range(K):
+            unfused()
+            evu[k + 1].record()
+        torch.cuda.synchronize()
+        us_u = sum(evu[k].elapsed_time(evu[k + 1]) for k in range(K)) * 1e3 / K
+        side = {"unfused_call_us": round(us_u, 2),
+                "gflops_unfused_call": round(flops / (us_u * 1e-6) / 1e9, 2),
+                "unfused_equals_fused": bool(torch.equal(out_u, out))}
+        del pr, out_u
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
@@ -231,6 +257,7 @@ def main():
                           "algorithmic_bytes": step_bytes},
         "roofline_call_t_roof_us": round(t_roof_call_us, 2),
         "wall_s_timed": round(wall, 4),
+        "unfused": side,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -19,7 +19,10 @@ namespace se {
 // the same order, so fused and unfused results are bitwise identical.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kGemmThreads = 256;
+#ifndef SE_WAVES
+#define SE_WAVES 8          // waves per contraction workgroup: 4 (2 x 2 grid) or 8 (2 x 4)
+#endif
+constexpr int kGemmThreads = 64 * SE_WAVES;
 constexpr int kSplitQuantum = 128;        // vocab positions per split block
 constexpr int kMinBlocksPerSplit = 2;     // at least 256 vocab positions per split
 constexpr int kTargetCUs = 256;           // MI355X compute units: sizes the split count

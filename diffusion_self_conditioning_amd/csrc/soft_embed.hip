@@ -7,12 +7,12 @@
 // of the same section applied inside one GPU: each workgroup contracts one range
 // of vocabulary positions, and the partial tiles are summed in a fixed order.
 //
-// Tiling: one workgroup of 4 wave64s per CU, a 256 (rows) x 256 (hidden) output
-// tile.  The waves form a 2 x 2 grid; each owns a 128 x 128 sub-tile = 4 x 4
-// blocks of v_mfma_f32_32x32x16_bf16, i.e. 256 fp32 accumulators per lane.  Every
-// element of the probability tile and of the table tile is read from LDS by two
-// waves (the transposing table reads run at about half the rate of plain 16-byte
-// reads, so no wave layout reads the table more than twice).
+// Tiling: one workgroup per CU, a 256 (rows) x 256 (hidden) output tile, in
+// 8 wave64s (default; two per SIMD, so one wave's MFMAs run while the other waits
+// on memory) forming a 2 x 4 grid of 128 x 64 wave tiles (4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16, 128 fp32 accumulators per lane), or 4 waves in a 2 x 2
+// grid of 128 x 128 tiles (256 accumulators in AGPRs).  Both give bitwise equal
+// results: every output element adds the same products in the same order.
 //
 // The vocabulary is walked in steps of 32 positions grouped into super-steps of
 // 128.  LDS holds (160 KB):
@@ -50,7 +50,10 @@
 #include "se_launch.h"
 
 #ifndef SE_SCHED
-#define SE_SCHED 3
+#define SE_SCHED 0            // VALU instructions placed after each MFMA (0: compiler's order)
+#endif
+#ifndef SE_W_LOAD
+#define SE_W_LOAD buffer_load_u4_nt   // the table is streamed once: nontemporal loads
 #endif
 
 namespace se {
@@ -77,7 +80,16 @@ constexpr int kWBase = 2 * kPBuf;                // LDS: [P0][P1][W0][W1]
 constexpr int kLds = 2 * kPBuf + 2 * kWBuf;
 static_assert(kLds <= 160 * 1024, "LDS budget of one CU");
 static_assert(kSplitQuantum % kSS == 0, "super-steps must tile the split quantum");
-static_assert(kGemmThreads == 256, "4 waves in a 2 x 2 grid");
+// Waves: 2 rows x kWN columns of wave tiles, each 128 x kTN (kMI x kNI MFMA blocks)
+constexpr int kWaves = kGemmThreads / 64;
+static_assert(kWaves == 4 || kWaves == 8, "4 (2 x 2) or 8 (2 x 4) waves");
+constexpr int kWN = kWaves / 2;
+constexpr int kTN = kBN / kWN;
+constexpr int kMI = 4;
+constexpr int kNI = kTN / 32;
+constexpr int kArows = kBM / kWaves;             // probability rows produced per wave
+constexpr int kWrows = kBK / kWaves;             // table rows per wave and step
+constexpr int kWJ = kWrows / 2;                  // table loads per wave and step
 
 // byte offset of P element (m, k) in a [256][128] tile: 256-byte rows, 16-byte
 // chunk index (k / 8) XOR (m % 16)
@@ -90,24 +102,25 @@ __device__ __forceinline__ int w_off(int k, int n) {
   return k * 512 + 16 * ((n >> 3) ^ (4 * (k & 3))) + 2 * (n & 7);
 }
 
-// Probability producer geometry, per wave and super-step (the wave's 64 rows).
-//   fused: 32 loads of 4 fp32; load i covers rows 64 wave + 2 i + lane/32,
+// Probability producer geometry, per wave and super-step (the wave's kArows rows).
+//   fused: loads of 4 fp32; load i covers rows kArows wave + 2 i + lane/32,
 //          positions 4 (lane % 32) .. +3.
-//   unfused: 16 loads of 8 bf16; load i covers rows 64 wave + 4 i + lane/16,
+//   unfused: loads of 8 bf16; load i covers rows kArows wave + 4 i + lane/16,
 //          positions 8 (lane % 16) .. +7.
-// A quarter (one step's share) is 8 (4) loads; two register sets of a quarter.
+// A quarter (one step's share) is a quarter of the loads; two register sets of a
+// quarter.
 template <bool FUSED>
 struct AGeo;
 template <>
 struct AGeo<true> {
-  static constexpr int kLoads = 32, kPerQ = 8, kRowsPerLoad = 2, kEsz = 4;
+  static constexpr int kRowsPerLoad = 2, kEsz = 4, kLoads = kArows / 2, kPerQ = kLoads / 4;
   typedef float4 reg_t;
   __device__ static int row(int i, int lane) { return 2 * i + (lane >> 5); }
   __device__ static int pos(int lane) { return 4 * (lane & 31); }
 };
 template <>
 struct AGeo<false> {
-  static constexpr int kLoads = 16, kPerQ = 4, kRowsPerLoad = 4, kEsz = 2;
+  static constexpr int kRowsPerLoad = 4, kEsz = 2, kLoads = kArows / 4, kPerQ = kLoads / 4;
   typedef uint4 reg_t;
   __device__ static int row(int i, int lane) { return 4 * i + (lane >> 4); }
   __device__ static int pos(int lane) { return 8 * (lane & 15); }
@@ -117,7 +130,8 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
 template <bool FUSED, bool FULL>
-__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kGemmThreads)
+__attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 soft_embed_kernel(const GemmParams p) {
   using G = AGeo<FUSED>;
   using AReg = typename G::reg_t;
@@ -128,8 +142,8 @@ soft_embed_kernel(const GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;          // 128-row half
-  const int wn = wave & 1;           // 128-column half
+  const int wm = wave / kWN;         // 128-row half
+  const int wn = wave % kWN;         // kTN-column slice
 
   const int b = xcd_local_order((int)blockIdx.x, (int)gridDim.x);
   const int t = b % p.tiles;
@@ -151,9 +165,9 @@ soft_embed_kernel(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(
       static_cast<const unsigned char*>(p.a) + ((int64_t)m0 * p.lda + p.col0) * kEsz,
       (uint32_t)min((int64_t)(tile_rows - 1) * a_ld + p.K * kEsz, (int64_t)UINT32_MAX));
-  const int a_row0 = 64 * wave;
+  const int a_row0 = kArows * wave;
   const uint32_t a_lo = (uint32_t)((a_row0 + G::row(0, lane)) * a_ld) + kEsz * G::pos(lane);
-  // -(lse log2e) of row 64 wave + lane; load i fetches its rows' values with a
+  // -(lse log2e) of row kArows wave + lane; load i fetches its rows' values with a
   // cross-lane permute (no LDS storage)
   float nl_lane = 0.f;
   if constexpr (FUSED) nl_lane = neg_lse_log2(p.lse[m0 + min(a_row0 + lane, tile_rows - 1)]);
@@ -161,7 +175,7 @@ soft_embed_kernel(const GemmParams p) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
                                          4 * G::row(i, lane), __builtin_bit_cast(int, nl_lane)));
   };
-  // LDS store offset of load i (within a P tile).  Row 64 wave + R i + r (r = this
+  // LDS store offset of load i (within a P tile).  Row kArows wave + R i + r (r = this
   // lane's row within the load) has swizzle (R i + r) % 16 = (R (i % (16 / R))) ^ r,
   // so the offset is a per-lane base with the chunk bits XORed by 16 R (i % (16 / R)).
   constexpr int kR = G::kRowsPerLoad;
@@ -197,30 +211,30 @@ soft_embed_kernel(const GemmParams p) {
   };
 
   // ---- table producer: buffer resource at shard row k_lo -------------------------------
-  // step ks, piece j (0..3): rows 8 wave + 2 j + lane/32, columns 8 (lane % 32) .. +7
+  // step ks, piece j (< kWJ): rows kWrows wave + 2 j + lane/32, columns 8 (lane % 32) ..
   const int64_t w_ld = p.ldw * 2;
   const __amdgpu_buffer_rsrc_t w_rsrc =
       make_rsrc(reinterpret_cast<const unsigned char*>(p.w) + k_lo * w_ld,
                 (uint32_t)min((k_hi - k_lo) * w_ld, (int64_t)UINT32_MAX));
-  const uint32_t w_lo = (uint32_t)((8 * wave + (lane >> 5)) * w_ld) +
+  const uint32_t w_lo = (uint32_t)((kWrows * wave + (lane >> 5)) * w_ld) +
                         2 * (uint32_t)min(n0 + 8 * (lane & 31), N - 8);
   uint32_t w_st[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e)
-    w_st[e] = kWBase + w_off(8 * wave + 2 * e + (lane >> 5), 8 * (lane & 31)) - 1024 * e;
+    w_st[e] = kWBase + w_off(kWrows * wave + 2 * e + (lane >> 5), 8 * (lane & 31)) - 1024 * e;
   auto load_w = [&](int ks, int j) -> uint4 {
-    return buffer_load_u4_nt(w_rsrc, w_lo,
+    return SE_W_LOAD(w_rsrc, w_lo,
                              (uint32_t)(((int64_t)ks * kBK - k_lo + 2 * j) * w_ld));
   };
   auto store_w = [&](int wbuf, int j, const uint4& r) {
     *reinterpret_cast<uint4*>(lds + wbuf * kWBuf + w_st[j & 1] + 1024 * j) = r;
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[kMI][kNI];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
@@ -231,19 +245,19 @@ soft_embed_kernel(const GemmParams p) {
   const uint32_t rd_row = (uint32_t)(128 * wm + (lane & 31)) * 256;
   const uint32_t rd_chk = 16u * (uint32_t)((lane >> 5) ^ (lane & 15));
   // W: 16-lane group g, lane i: piece (row 8 (g/2) + i/4, columns 32 ni + 16 (g%2) + 4 (i%4))
-  uint32_t b_rd[4];
+  uint32_t b_rd[kNI];
   {
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      b_rd[ni] = kWBase + w_off(8 * (g >> 1) + (i >> 2), 128 * wn + 32 * ni + 16 * (g & 1) + 4 * (i & 3));
+    for (int ni = 0; ni < kNI; ++ni)
+      b_rd[ni] = kWBase + w_off(8 * (g >> 1) + (i >> 2), kTN * wn + 32 * ni + 16 * (g & 1) + 4 * (i & 3));
   }
-  auto frag_read = [&](int pbuf, int wbuf, int u, int q, bf16x8 (&af)[4], bf16x8 (&bf)[4]) {
+  auto frag_read = [&](int pbuf, int wbuf, int u, int q, bf16x8 (&af)[kMI], bf16x8 (&bf)[kNI]) {
     const unsigned char* pa = lds + pbuf * kPBuf + rd_row + (rd_chk ^ (uint32_t)(32 * u));
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) af[mi] = *reinterpret_cast<const bf16x8*>(pa + 8192 * mi);
+    for (int mi = 0; mi < kMI; ++mi) af[mi] = *reinterpret_cast<const bf16x8*>(pa + 8192 * mi);
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 0; ni < kNI; ++ni) {
       const unsigned char* wp = lds + wbuf * kWBuf + b_rd[ni] + 8192 * q;
       const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp));
       const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp + 2048));
@@ -251,32 +265,36 @@ soft_embed_kernel(const GemmParams p) {
                                        __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
-  auto mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) {
+  auto mfmas = [&](const bf16x8 (&af)[kMI], const bf16x8 (&bf)[kNI]) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < kNI; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
   };
 
   // One step: the 2 substeps' fragments are read up front; side(q) is interleaved
-  // with substep q's 16 MFMAs.
+  // with substep q's MFMAs.
+  constexpr int kMF = kMI * kNI;                     // MFMAs per substep
+  constexpr int kFR = kMI + 2 * kNI;                 // fragment reads per substep
+  constexpr int kSide = kWJ / 2 + G::kPerQ / 2;      // LDS writes (and loads) per half
   auto compute = [&](int pbuf, int wbuf, int qstep, auto&& side) {
-    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    bf16x8 a0[kMI], b0[kNI], a1[kMI], b1[kNI];
     frag_read(pbuf, wbuf, 2 * qstep, 0, a0, b0);
     frag_read(pbuf, wbuf, 2 * qstep + 1, 1, a1, b1);
     mfmas(a0, b0);
     side(0);
 #if SE_SCHED
-    // substep 0 fragment reads, then (fused) the lse permutes of this half's conversions
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kFR, 0);     // substep 0 fragment reads
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+    for (int i = 0; i < kMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, SE_SCHED, 0);  // VALU
-      if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // substep 1 reads
-      if (i >= 4 && i < 10) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS writes
-      if (i >= 8 && i < 14) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // loads
+      if (i < kFR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // substep 1 reads
+      if (i >= kMF / 4 && i < kMF / 4 + kSide)
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS writes
+      if (i >= kMF / 2 && i < kMF / 2 + kSide)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // loads
     }
 #endif
     __builtin_amdgcn_sched_barrier(0);
@@ -284,11 +302,12 @@ soft_embed_kernel(const GemmParams p) {
     side(1);
 #if SE_SCHED
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, SE_SCHED, 0);
-      if (i >= 2 && i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      if (i >= 6 && i < 12) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i >= kMF / 8 && i < kMF / 8 + kSide) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (i >= 3 * kMF / 8 && i < 3 * kMF / 8 + kSide)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
 #endif
     __builtin_amdgcn_sched_barrier(0);
@@ -296,7 +315,7 @@ soft_embed_kernel(const GemmParams p) {
 
   // ---- main loop over the full super-steps [S0, Sf) ------------------------------------
   AReg ra[2][kPerQ];                 // quarter registers: set q % 2
-  uint4 rw[2][4];                    // table register stages
+  uint4 rw[2][kWJ];                  // table register stages
   if (S0 < Sf) {
     const int Slast = Sf - 1;
     const int kslast = 4 * Sf - 1;
@@ -315,20 +334,20 @@ soft_embed_kernel(const GemmParams p) {
 #pragma unroll
       for (int i = 0; i < kPerQ; ++i) ra[q][i] = load_a(min(S0 + 1, Slast), q * kPerQ + i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rw[0][j] = load_w(ks0, j);
+    for (int j = 0; j < kWJ; ++j) rw[0][j] = load_w(ks0, j);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rw[1][j] = load_w(min(ks0 + 1, kslast), j);
+    for (int j = 0; j < kWJ; ++j) rw[1][j] = load_w(min(ks0 + 1, kslast), j);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) store_w(0, j, rw[0][j]);
+    for (int j = 0; j < kWJ; ++j) store_w(0, j, rw[0][j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rw[0][j] = load_w(min(ks0 + 2, kslast), j);
+    for (int j = 0; j < kWJ; ++j) rw[0][j] = load_w(min(ks0 + 2, kslast), j);
     __syncthreads();
 
     for (int S = S0; S < Sf; ++S) {
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
         const int ks = 4 * S + q;
-        uint4 (&rwn)[4] = rw[(q + 1) & 1];            // table step ks + 1
+        uint4 (&rwn)[kWJ] = rw[(q + 1) & 1];          // table step ks + 1
         AReg (&rq)[kPerQ] = ra[q & 1];                // quarter q of super-step S + 1
         // refill: quarter q + 2 of S + 1, or quarter q - 2 of S + 2
         const int Sr = min(q < 2 ? S + 1 : S + 2, Slast);
@@ -342,12 +361,12 @@ soft_embed_kernel(const GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);
         compute(S & 1, q & 1, q, [&](int h) {
 #pragma unroll
-          for (int j = 2 * h; j < 2 * h + 2; ++j) store_w((q + 1) & 1, j, rwn[j]);
+          for (int j = h * kWJ / 2; j < (h + 1) * kWJ / 2; ++j) store_w((q + 1) & 1, j, rwn[j]);
 #pragma unroll
           for (int i = h * kPerQ / 2; i < (h + 1) * kPerQ / 2; ++i)
             store_a((S + 1) & 1, q * kPerQ + i, rq[i], nlq[FUSED ? i : 0]);
 #pragma unroll
-          for (int j = 2 * h; j < 2 * h + 2; ++j) rwn[j] = load_w(kn, j);
+          for (int j = h * kWJ / 2; j < (h + 1) * kWJ / 2; ++j) rwn[j] = load_w(kn, j);
 #pragma unroll
           for (int i = h * kPerQ / 2; i < (h + 1) * kPerQ / 2; ++i) rq[i] = load_a(Sr, qr * kPerQ + i);
         });
@@ -396,8 +415,8 @@ soft_embed_kernel(const GemmParams p) {
       const int64_t kr0 = (int64_t)ks * kBK;
       const unsigned char* wb = reinterpret_cast<const unsigned char*>(p.w) + kr0 * w_ld;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t kr = kr0 + 8 * wave + 2 * j + (lane >> 5);
+      for (int j = 0; j < kWJ; ++j) {
+        const int64_t kr = kr0 + kWrows * wave + 2 * j + (lane >> 5);
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (kr < p.K) v = *reinterpret_cast<const uint4*>(wb + (int64_t)(2 * j) * w_ld + w_lo);
         store_w(0, j, v);
@@ -413,10 +432,10 @@ soft_embed_kernel(const GemmParams p) {
   //   row 8 (r / 4) + 4 (l / 32) + (r % 4),  column l % 32  of the block.
   if (p.splits == 1) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int col = n0 + 128 * wn + 32 * ni + (lane & 31);
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int col = n0 + kTN * wn + 32 * ni + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -427,12 +446,12 @@ soft_embed_kernel(const GemmParams p) {
     // partial tile in register order: fully coalesced 256-byte stores
     float* dst = p.ws + ((int64_t)s * p.tiles + t) * kTileFloats;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          dst[((wave * 16 + mi * 4 + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
+          dst[((wave * kMF + mi * kNI + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
   }
 }
 
@@ -449,12 +468,12 @@ splitk_reduce_kernel(const float* __restrict__ ws, int tiles, int tiles_n, int s
   const int e0 = ((blockIdx.x % kBlocksPerTile) * kReduceThreads + threadIdx.x) * 4;
   const int l0 = e0 & 63;
   const int r = (e0 >> 6) & 15;
-  const int blk = e0 >> 10;                       // wave * 16 + mi * 4 + ni
-  const int wave = blk >> 4, mi = (blk >> 2) & 3, ni = blk & 3;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int blk = e0 >> 10;                       // (wave * kMI + mi) * kNI + ni
+  const int wave = blk / (kMI * kNI), mi = (blk / kNI) % kMI, ni = blk % kNI;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int64_t row = (int64_t)(t / tiles_n) * kBM + 128 * wm + 32 * mi + 8 * (r >> 2) +
                       4 * (l0 >> 5) + (r & 3);
-  const int64_t col = (int64_t)(t % tiles_n) * kBN + 128 * wn + 32 * ni + (l0 & 31);
+  const int64_t col = (int64_t)(t % tiles_n) * kBN + kTN * wn + 32 * ni + (l0 & 31);
   if (row >= M || col >= N) return;
   const float* src = ws + (int64_t)t * kTileFloats + e0;
   float4 a = *reinterpret_cast<const float4*>(src);
