@@ -231,6 +231,35 @@ def main():
                 "unfused_equals_fused": bool(torch.equal(out_u, out))}
         del pr, out_u
 
+    # side measurement: the sampler's acceptance / convergence step on this step's row
+    # statistics (canvases of 256 positions)
+    acc_side = None
+    if L % 256 == 0:
+        nc = L // 256
+        st = {"acc": torch.zeros(L, dtype=torch.uint8, device=dev),
+              "prev": torch.full((L,), -1, dtype=torch.int32, device=dev),
+              "sc": torch.zeros(nc, dtype=torch.int32, device=dev),
+              "stc": torch.zeros(nc, dtype=torch.int32, device=dev),
+              "new": torch.empty(L, dtype=torch.uint8, device=dev),
+              "conv": torch.empty(nc, dtype=torch.uint8, device=dev)}
+
+        def accept_step():
+            B.se_accept_converge(ent, am, 256, 8.0, 3, 0.05, 64, st["acc"], st["prev"], st["sc"],
+                                 st["stc"], st["new"], st["conv"])
+
+        for _ in range(args.warmup):
+            accept_step()
+        eva = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        torch.cuda.synchronize()
+        eva[0].record()
+        for k in range(K):
+            accept_step()
+            eva[k + 1].record()
+        torch.cuda.synchronize()
+        acc_side = {"accept_converge_us": round(
+            sum(eva[k].elapsed_time(eva[k + 1]) for k in range(K)) * 1e3 / K, 2),
+            "canvases": nc, "accepted_last_step": int(st["new"].sum().item())}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
@@ -258,6 +287,7 @@ def main():
         "roofline_call_t_roof_us": round(t_roof_call_us, 2),
         "wall_s_timed": round(wall, 4),
         "unfused": side,
+        "accept_converge": acc_side,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -21,7 +21,8 @@ STATUS_NAMES = ["SE_OK", "SE_ERR_NULL", "SE_ERR_SHAPE", "SE_ERR_SLICE", "SE_ERR_
                 "SE_ERR_WORKSPACE", "SE_ERR_HIP"]
 
 EXPORTS = ("se_status_string", "se_version", "se_row_stats", "se_probs_bf16",
-           "se_soft_embed_workspace_bytes", "se_soft_embed", "se_soft_embed_fused")
+           "se_soft_embed_workspace_bytes", "se_soft_embed", "se_soft_embed_fused",
+           "se_accept_converge")
 
 
 class SoftEmbedError(RuntimeError):
@@ -45,7 +46,11 @@ def _declare(lib):
                                   vp, sz, vp]
     lib.se_soft_embed_fused.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, i64, i64, i64, f32,
                                         vp, i64, vp, sz, vp]
-    for fn in ("se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused"):
+    f64, i32 = ctypes.c_double, ctypes.c_int32
+    lib.se_accept_converge.argtypes = [vp, vp, i64, i64, f64, i32, f64, i32, vp, vp, vp, vp, vp,
+                                       vp, vp]
+    for fn in ("se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
+               "se_accept_converge"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -150,3 +155,22 @@ def se_soft_embed_fused(logits, row_lse, vocab_start, vocab_end, w_shard, gamma,
         _ptr(logits), _ld(logits), _ptr(row_lse), n, vocab, vocab_start, vocab_end,
         _ptr(w_shard), w_rows, _ld(w_shard), d, float(gamma), _ptr(out), _ld(out),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def se_accept_converge(row_entropy, row_argmax, canvas_len, entropy_budget, stable_steps,
+                       entropy_tau, step_limit, accepted, prev_argmax, stable_count, step_count,
+                       newly_accepted, converged, *, stream=None):
+    """Entropy-bound acceptance + convergence test over canvases of ``canvas_len`` rows.
+
+    ``row_entropy`` fp32 / ``row_argmax`` int32 of n_canvas * canvas_len positions; state
+    tensors ``accepted`` (uint8), ``prev_argmax`` (int32), ``stable_count`` / ``step_count``
+    (int32 per canvas) are updated in place; ``newly_accepted`` (uint8) and ``converged``
+    (uint8 per canvas) are written."""
+    n = row_entropy.numel()
+    if n % canvas_len:
+        raise ValueError("row count is not a multiple of canvas_len")
+    _check("se_accept_converge", lib.se_accept_converge(
+        _ptr(row_entropy), _ptr(row_argmax), n // canvas_len, canvas_len, float(entropy_budget),
+        int(stable_steps), float(entropy_tau), int(step_limit), _ptr(accepted),
+        _ptr(prev_argmax), _ptr(stable_count), _ptr(step_count), _ptr(newly_accepted),
+        _ptr(converged), _stream(stream)))

@@ -123,7 +123,7 @@ const char* se_status_string(se_status s) {
 }
 
 const char* se_version(void) {
-  return "libsoftembed 0.1 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused)";
+  return "libsoftembed 0.2 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge)";
 }
 
 se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
@@ -203,6 +203,29 @@ se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const floa
   if (!aligned16(logits) || (ld_logits % 4) != 0 || !aligned4(row_lse)) return SE_ERR_ALIGN;
   return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start, vocab_end, w_shard,
                         ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
+}
+
+se_status se_accept_converge(const float* row_entropy, const int32_t* row_argmax,
+                             int64_t n_canvas, int64_t canvas_len, double entropy_budget,
+                             int32_t stable_steps, double entropy_tau, int32_t step_limit,
+                             uint8_t* accepted, int32_t* prev_argmax, int32_t* stable_count,
+                             int32_t* step_count, uint8_t* newly_accepted, uint8_t* converged,
+                             void* stream) {
+  if (n_canvas < 0 || n_canvas > INT32_MAX || canvas_len < 1 || canvas_len > 1024) return SE_ERR_SHAPE;
+  if (stable_steps < 1 || step_limit < 1) return SE_ERR_SHAPE;
+  if (entropy_budget != entropy_budget || entropy_tau != entropy_tau) return SE_ERR_SHAPE;
+  if (n_canvas == 0) return SE_OK;
+  if (!row_entropy || !row_argmax || !accepted || !prev_argmax || !stable_count || !step_count ||
+      !newly_accepted || !converged)
+    return SE_ERR_NULL;
+  if (!aligned4(row_entropy) || !aligned4(row_argmax) || !aligned4(prev_argmax) ||
+      !aligned4(stable_count) || !aligned4(step_count))
+    return SE_ERR_ALIGN;
+  return from_hip(se::launch_accept_converge(row_entropy, row_argmax, n_canvas, (int)canvas_len,
+                                             entropy_budget, stable_steps, entropy_tau,
+                                             step_limit, accepted, prev_argmax, stable_count,
+                                             step_count, newly_accepted, converged,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

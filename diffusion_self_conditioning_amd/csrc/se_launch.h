@@ -60,6 +60,13 @@ hipError_t launch_probs_bf16(const float* logits, int64_t ld, const float* row_l
 
 hipError_t launch_soft_embed(const GemmParams& p, bool fused, hipStream_t stream);
 
+hipError_t launch_accept_converge(const float* row_entropy, const int32_t* row_argmax,
+                                  int64_t n_canvas, int len, double budget, int stable_steps,
+                                  double tau, int step_limit, uint8_t* accepted,
+                                  int32_t* prev_argmax, int32_t* stable_count,
+                                  int32_t* step_count, uint8_t* newly, uint8_t* converged,
+                                  hipStream_t stream);
+
 hipError_t launch_zero_rows(float* out, int64_t ldo, int64_t M, int64_t N, hipStream_t stream);
 
 }  // namespace se

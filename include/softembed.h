@@ -152,6 +152,50 @@ se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const floa
                               float gamma, float* out, int64_t ld_out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * se_accept_converge -- entropy-bound acceptance and the convergence test of the
+ * diffusion sampler, on the statistics se_row_stats produces (agentlenshq overview
+ * of DiffusionGemma in vLLM, section on the sampling loop and entropy-bound
+ * denoising: tokens are accepted from the most to the least confident until the
+ * cumulative entropy exceeds a fixed budget; a canvas has converged when its argmax
+ * prediction has been stable for several steps and its mean per-token entropy is
+ * below a threshold, or when a step limit is reached).
+ *
+ * The rows are n_canvas canvases of canvas_len consecutive positions each
+ * (row c * canvas_len + i is position i of canvas c).  Per canvas, one call:
+ *   1. candidates = positions with accepted[] == 0, ordered by entropy ascending,
+ *      ties by lower position;
+ *   2. entropies enter as exact fixed-point integers q = round_half_even(H * 2^32)
+ *      (2^-32 nat resolution), so cumulative sums are exact and order-free;
+ *   3. the candidates taken are the prefix of that order before the first one whose
+ *      cumulative sum exceeds entropy_budget * 2^32 (compared in double), but at
+ *      least one when any candidate is left; they get newly_accepted = 1 and
+ *      accepted = 1 (every other position: newly_accepted = 0);
+ *   4. stable_count = (row_argmax == prev_argmax at every position) ?
+ *      stable_count + 1 : 0;  prev_argmax = row_argmax;  step_count += 1;
+ *   5. converged = (stable_count >= stable_steps && sum(q) < entropy_tau *
+ *      canvas_len * 2^32) || step_count >= step_limit.
+ * The budget, stable_steps, tau and step_limit values are the caller's: the pages
+ * give none.
+ *
+ * row_entropy: fp32 [n_canvas * canvas_len] (nats); row_argmax: int32, same size.
+ * State (in/out, caller-owned, initialise once per canvas: accepted = 0,
+ * prev_argmax = -1, stable_count = 0, step_count = 0):
+ *   accepted: uint8 [n_canvas * canvas_len]; prev_argmax: int32, same size;
+ *   stable_count, step_count: int32 [n_canvas].
+ * Outputs: newly_accepted: uint8 [n_canvas * canvas_len]; converged: uint8 [n_canvas].
+ * Errors: SE_ERR_SHAPE if n_canvas < 0, canvas_len < 1 or > 1024, stable_steps < 1,
+ * step_limit < 1, or entropy_budget / entropy_tau is NaN; SE_ERR_NULL for a NULL
+ * pointer (n_canvas > 0); SE_ERR_ALIGN if an int32 or fp32 array is not 4-byte
+ * aligned.  n_canvas == 0 is a no-op.
+ */
+se_status se_accept_converge(const float* row_entropy, const int32_t* row_argmax,
+                             int64_t n_canvas, int64_t canvas_len, double entropy_budget,
+                             int32_t stable_steps, double entropy_tau, int32_t step_limit,
+                             uint8_t* accepted, int32_t* prev_argmax, int32_t* stable_count,
+                             int32_t* step_count, uint8_t* newly_accepted, uint8_t* converged,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -153,3 +153,29 @@ def test_workspace_plan_large_m():
     # 16 x 11 = 176 tiles: floor(256 / 176) = 1 split, no workspace
     assert b.se_soft_embed_workspace_bytes(4096, 0, 262144, 2816) == 0
     assert b.se_soft_embed_workspace_bytes(8192, 0, 262144, 2816) == 0
+
+
+def accept(**kw):
+    a = dict(ent=P1, am=P2, n=8, L=256, budget=1.0, k=2, tau=0.5, limit=16, acc=P3, prev=P4,
+             sc=P5, stc=P5 + 64, newly=P5 + 128, conv=P5 + 192, stream=None)
+    a.update(kw)
+    return lib.se_accept_converge(a["ent"], a["am"], a["n"], a["L"], a["budget"], a["k"],
+                                  a["tau"], a["limit"], a["acc"], a["prev"], a["sc"], a["stc"],
+                                  a["newly"], a["conv"], a["stream"])
+
+
+def test_accept_converge_errors():
+    assert accept(n=-1) == b.SE_ERR_SHAPE
+    assert accept(L=0) == b.SE_ERR_SHAPE
+    assert accept(L=1025) == b.SE_ERR_SHAPE
+    assert accept(k=0) == b.SE_ERR_SHAPE
+    assert accept(limit=0) == b.SE_ERR_SHAPE
+    assert accept(budget=float("nan")) == b.SE_ERR_SHAPE
+    assert accept(tau=float("nan")) == b.SE_ERR_SHAPE
+    assert accept(ent=None) == b.SE_ERR_NULL
+    assert accept(conv=None) == b.SE_ERR_NULL
+    assert accept(am=P2 + 2) == b.SE_ERR_ALIGN
+    assert accept(sc=P5 + 1) == b.SE_ERR_ALIGN
+    # bytes (accepted, newly, converged) need no alignment; no canvases is a no-op
+    assert accept(n=0, ent=None, am=None, acc=None, prev=None, sc=None, stc=None, newly=None,
+                  conv=None) == b.SE_OK
