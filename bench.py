@@ -260,6 +260,25 @@ def main():
             sum(eva[k].elapsed_time(eva[k + 1]) for k in range(K)) * 1e3 / K, 2),
             "canvases": nc, "accepted_last_step": int(st["new"].sum().item())}
 
+    # side measurement: the on-device sum of 4 per-rank partials of this output shape,
+    # written as fp32 and bf16
+    parts4 = torch.randn((4, L, d), device=dev)
+    red_f = torch.empty((L, d), device=dev)
+    red_b = torch.empty((L, d), dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        B.se_reduce_partials(parts4, out=red_f, out_bf16=red_b)
+    evr = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evr[0].record()
+    for k in range(K):
+        B.se_reduce_partials(parts4, out=red_f, out_bf16=red_b)
+        evr[k + 1].record()
+    torch.cuda.synchronize()
+    red_us = sum(evr[k].elapsed_time(evr[k + 1]) for k in range(K)) * 1e3 / K
+    red_side = {"reduce_partials_us": round(red_us, 2), "parts": 4,
+                "gbs": round((4 * 4 + 4 + 2) * L * d / (red_us * 1e-6) / 1e9, 1)}
+    del parts4, red_f, red_b
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
@@ -288,6 +307,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "unfused": side,
         "accept_converge": acc_side,
+        "reduce_partials": red_side,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

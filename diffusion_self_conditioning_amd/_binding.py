@@ -22,7 +22,7 @@ STATUS_NAMES = ["SE_OK", "SE_ERR_NULL", "SE_ERR_SHAPE", "SE_ERR_SLICE", "SE_ERR_
 
 EXPORTS = ("se_status_string", "se_version", "se_row_stats", "se_probs_bf16",
            "se_soft_embed_workspace_bytes", "se_soft_embed", "se_soft_embed_fused",
-           "se_accept_converge")
+           "se_accept_converge", "se_reduce_partials")
 
 
 class SoftEmbedError(RuntimeError):
@@ -49,8 +49,9 @@ def _declare(lib):
     f64, i32 = ctypes.c_double, ctypes.c_int32
     lib.se_accept_converge.argtypes = [vp, vp, i64, i64, f64, i32, f64, i32, vp, vp, vp, vp, vp,
                                        vp, vp]
+    lib.se_reduce_partials.argtypes = [vp, i64, i64, i64, i64, i64, vp, i64, vp, i64, vp]
     for fn in ("se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
-               "se_accept_converge"):
+               "se_accept_converge", "se_reduce_partials"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -174,3 +175,17 @@ def se_accept_converge(row_entropy, row_argmax, canvas_len, entropy_budget, stab
         int(stable_steps), float(entropy_tau), int(step_limit), _ptr(accepted),
         _ptr(prev_argmax), _ptr(stable_count), _ptr(step_count), _ptr(newly_accepted),
         _ptr(converged), _stream(stream)))
+
+
+def se_reduce_partials(parts, out=None, out_bf16=None, *, stream=None):
+    """Sum fp32 partials ``parts`` [T, n_rows, >= d] in order r = 0..T-1 into ``out`` (fp32)
+    and / or ``out_bf16`` (bfloat16), both [n_rows, >= d]."""
+    if parts.dim() != 3 or parts.stride(2) != 1:
+        raise ValueError("parts must be [T, rows, d] with unit column stride")
+    t, n, d = parts.shape
+    dst = out if out is not None else out_bf16
+    d = dst.shape[1]
+    _check("se_reduce_partials", lib.se_reduce_partials(
+        _ptr(parts), t, parts.stride(0), n, d, parts.stride(1), _ptr(out),
+        _ld(out) if out is not None else 0, _ptr(out_bf16),
+        _ld(out_bf16) if out_bf16 is not None else 0, _stream(stream)))

@@ -123,7 +123,7 @@ const char* se_status_string(se_status s) {
 }
 
 const char* se_version(void) {
-  return "libsoftembed 0.2 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge)";
+  return "libsoftembed 0.2 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials)";
 }
 
 se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
@@ -226,6 +226,25 @@ se_status se_accept_converge(const float* row_entropy, const int32_t* row_argmax
                                              step_limit, accepted, prev_argmax, stable_count,
                                              step_count, newly_accepted, converged,
                                              static_cast<hipStream_t>(stream)));
+}
+
+se_status se_reduce_partials(const float* parts, int64_t n_parts, int64_t part_stride,
+                             int64_t n_rows, int64_t d, int64_t ld_part, float* out,
+                             int64_t ld_out, uint16_t* out_bf16, int64_t ld_bf16, void* stream) {
+  if (n_parts < 1 || n_rows < 0 || d < 1 || ld_part < d) return SE_ERR_SHAPE;
+  if (n_rows > kMaxGridY || d > INT32_MAX) return SE_ERR_SHAPE;
+  if (out && ld_out < d) return SE_ERR_SHAPE;
+  if (out_bf16 && ld_bf16 < d) return SE_ERR_SHAPE;
+  if (n_parts > 1 && part_stride < n_rows * ld_part) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;
+  if (!parts || (!out && !out_bf16)) return SE_ERR_NULL;
+  if ((d % 4) != 0 || (ld_part % 4) != 0 || (n_parts > 1 && (part_stride % 4) != 0))
+    return SE_ERR_ALIGN;
+  if (!aligned16(parts) || (out && (!aligned16(out) || (ld_out % 4) != 0))) return SE_ERR_ALIGN;
+  if (out_bf16 && ((((uintptr_t)out_bf16) & 7u) != 0 || (ld_bf16 % 4) != 0)) return SE_ERR_ALIGN;
+  return from_hip(se::launch_reduce_parts(parts, n_parts, part_stride, n_rows, d, ld_part, out,
+                                          ld_out, out_bf16, ld_bf16,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -67,6 +67,11 @@ hipError_t launch_accept_converge(const float* row_entropy, const int32_t* row_a
                                   int32_t* step_count, uint8_t* newly, uint8_t* converged,
                                   hipStream_t stream);
 
+hipError_t launch_reduce_parts(const float* parts, int64_t n_parts, int64_t part_stride,
+                               int64_t n_rows, int64_t d, int64_t ld_part, float* out,
+                               int64_t ld_out, uint16_t* out_bf16, int64_t ld_bf16,
+                               hipStream_t stream);
+
 hipError_t launch_zero_rows(float* out, int64_t ldo, int64_t M, int64_t N, hipStream_t stream);
 
 }  // namespace se

@@ -196,6 +196,25 @@ se_status se_accept_converge(const float* row_entropy, const int32_t* row_argmax
                              int32_t* step_count, uint8_t* newly_accepted, uint8_t* converged,
                              void* stream);
 
+/*
+ * se_reduce_partials -- E^sc = sum_r S^(r) over T partials that sit on one GPU
+ * (calvarado04.com/tag/vllm, section "The fix": the per-rank partials are summed
+ * by one all-reduce and the result is in the embedding dtype).  Each partial is
+ * the output of one slice call (gamma already applied); part r is the fp32 matrix
+ * [n_rows, d] at parts + r * part_stride with row pitch ld_part.  Parts are added
+ * in the order r = 0 .. n_parts-1 in fp32.  The sum is written to out (fp32, row
+ * pitch ld_out) and / or to out_bf16 (bf16 bits, round to nearest even, row pitch
+ * ld_bf16); either output may be NULL, not both.
+ * Errors: SE_ERR_SHAPE if n_parts < 1, n_rows < 0, d < 1, a pitch < d, or
+ * part_stride < n_rows * ld_part; SE_ERR_NULL if parts is NULL or both outputs are
+ * (n_rows > 0); SE_ERR_ALIGN if d or a pitch (or part_stride) is not a multiple of
+ * 4, or parts / out is not 16-byte or out_bf16 not 8-byte aligned.  n_rows == 0
+ * is a no-op.
+ */
+se_status se_reduce_partials(const float* parts, int64_t n_parts, int64_t part_stride,
+                             int64_t n_rows, int64_t d, int64_t ld_part, float* out,
+                             int64_t ld_out, uint16_t* out_bf16, int64_t ld_bf16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,6 +33,17 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(raw, n), n
 
 
+def test_every_entry_point_has_declared_argument_types():
+    """Undeclared ctypes argument types would pass int64 sizes as 32-bit ints."""
+    for n in b.EXPORTS:
+        fn = getattr(lib, n)
+        assert fn.argtypes is not None, n
+        decl = re.search(r"(?:se_status|size_t|const char\*)\s+" + n + r"\s*\(([^)]*)\)",
+                         open(HEADER).read())
+        params = [x for x in decl.group(1).split(",") if x.strip() not in ("", "void")]
+        assert len(fn.argtypes) == len(params), n
+
+
 def test_status_strings():
     for code, name in enumerate(b.STATUS_NAMES):
         assert b.se_status_string(code).startswith(name)
@@ -179,3 +190,24 @@ def test_accept_converge_errors():
     # bytes (accepted, newly, converged) need no alignment; no canvases is a no-op
     assert accept(n=0, ent=None, am=None, acc=None, prev=None, sc=None, stc=None, newly=None,
                   conv=None) == b.SE_OK
+
+
+def test_reduce_partials_errors():
+    rp = lib.se_reduce_partials
+    ok = dict(parts=P1, t=4, stride=256 * 2816, n=256, d=2816, ldp=2816, out=P2, ldo=2816,
+              ob=P3, ldb=2816)
+
+    def call(**kw):
+        a = dict(ok); a.update(kw)
+        return rp(a["parts"], a["t"], a["stride"], a["n"], a["d"], a["ldp"], a["out"], a["ldo"],
+                  a["ob"], a["ldb"], None)
+    assert call(t=0) == b.SE_ERR_SHAPE
+    assert call(ldp=2812) == b.SE_ERR_SHAPE
+    assert call(stride=100) == b.SE_ERR_SHAPE
+    assert call(ldo=2000) == b.SE_ERR_SHAPE
+    assert call(parts=None) == b.SE_ERR_NULL
+    assert call(out=None, ob=None) == b.SE_ERR_NULL
+    assert call(d=2814, ldp=2816, ldo=2816, ldb=2816) == b.SE_ERR_ALIGN
+    assert call(out=P2 + 8) == b.SE_ERR_ALIGN
+    assert call(ob=P3 + 4) == b.SE_ERR_ALIGN
+    assert call(n=0, parts=None, out=None, ob=None) == b.SE_OK
