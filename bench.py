@@ -48,6 +48,27 @@ def fused_call_bytes(w) -> int:
     return 2 * w.k * w.d + 4 * w.rows * w.k + 4 * w.rows * w.d
 
 
+def fp8_call_bytes(w) -> int:
+    """Algorithmic HBM bytes of one fused call on the e4m3 table: the codes and row scales of
+    the slice once, the fp32 logits slice once, the fp32 output once."""
+    return w.k * w.d + 4 * w.k + 4 * w.rows * w.k + 4 * w.rows * w.d
+
+
+def event_time_us(fn, K: int, warmup: int) -> float:
+    """Average time of fn() over K back-to-back calls, from events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for k in range(K):
+        fn()
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    return sum(ev[k].elapsed_time(ev[k + 1]) for k in range(K)) * 1e3 / K
+
+
 def row_stats_bytes(w) -> int:
     return 4 * w.rows * w.vocab + 16 * w.rows
 
@@ -216,16 +237,7 @@ def main():
             B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, pr)
             B.se_soft_embed(pr, w.vocab_start, w.vocab_end, shard, w.gamma, out_u, ws)
 
-        for _ in range(args.warmup):
-            unfused()
-        evu = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-        torch.cuda.synchronize()
-        evu[0].record()
-        for k in range(K):
-            unfused()
-            evu[k + 1].record()
-        torch.cuda.synchronize()
-        us_u = sum(evu[k].elapsed_time(evu[k + 1]) for k in range(K)) * 1e3 / K
+        us_u = event_time_us(unfused, K, args.warmup)
         side = {"unfused_call_us": round(us_u, 2),
                 "gflops_unfused_call": round(flops / (us_u * 1e-6) / 1e9, 2),
                 "unfused_equals_fused": bool(torch.equal(out_u, out))}
@@ -247,37 +259,44 @@ def main():
             B.se_accept_converge(ent, am, 256, 8.0, 3, 0.05, 64, st["acc"], st["prev"], st["sc"],
                                  st["stc"], st["new"], st["conv"])
 
-        for _ in range(args.warmup):
-            accept_step()
-        eva = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-        torch.cuda.synchronize()
-        eva[0].record()
-        for k in range(K):
-            accept_step()
-            eva[k + 1].record()
-        torch.cuda.synchronize()
-        acc_side = {"accept_converge_us": round(
-            sum(eva[k].elapsed_time(eva[k + 1]) for k in range(K)) * 1e3 / K, 2),
-            "canvases": nc, "accepted_last_step": int(st["new"].sum().item())}
+        acc_side = {"accept_converge_us": round(event_time_us(accept_step, K, args.warmup), 2),
+                    "canvases": nc, "accepted_last_step": int(st["new"].sum().item())}
 
     # side measurement: the on-device sum of 4 per-rank partials of this output shape,
     # written as fp32 and bf16
     parts4 = torch.randn((4, L, d), device=dev)
     red_f = torch.empty((L, d), device=dev)
     red_b = torch.empty((L, d), dtype=torch.bfloat16, device=dev)
-    for _ in range(args.warmup):
-        B.se_reduce_partials(parts4, out=red_f, out_bf16=red_b)
-    evr = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    evr[0].record()
-    for k in range(K):
-        B.se_reduce_partials(parts4, out=red_f, out_bf16=red_b)
-        evr[k + 1].record()
-    torch.cuda.synchronize()
-    red_us = sum(evr[k].elapsed_time(evr[k + 1]) for k in range(K)) * 1e3 / K
+    red_us = event_time_us(lambda: B.se_reduce_partials(parts4, out=red_f, out_bf16=red_b), K,
+                           args.warmup)
     red_side = {"reduce_partials_us": round(red_us, 2), "parts": 4,
                 "gbs": round((4 * 4 + 4 + 2) * L * d / (red_us * 1e-6) / 1e9, 1)}
     del parts4, red_f, red_b
+
+    # side measurement: the same calls on the e4m3 form of the shard (quantized once on the
+    # GPU, untimed), fused and unfused, with the fused call's HBM roofline
+    codes = torch.empty((w.k, d), dtype=torch.uint8, device=dev)
+    wscale = torch.empty(w.k, device=dev)
+    B.se_quantize_table_fp8(shard, codes, wscale)
+    out8 = torch.empty_like(out)
+    pr8 = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16)
+    B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, pr8)
+    us_f8 = event_time_us(lambda: B.se_soft_embed_fp8_fused(
+        x, lse, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, ws), K, args.warmup)
+    us_u8 = event_time_us(lambda: B.se_soft_embed_fp8(
+        pr8, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, ws), K, args.warmup)
+    us_q = event_time_us(lambda: B.se_quantize_table_fp8(shard, codes, wscale), 3, 1)
+    f8_bytes = fp8_call_bytes(w)
+    fp8_side = {"fused_call_us": round(us_f8, 2),
+                "gflops_fused_call": round(flops / (us_f8 * 1e-6) / 1e9, 2),
+                "unfused_gemm_only_us": round(us_u8, 2),
+                "roofline_fused_call": {"bound": "hbm", "algorithmic_bytes": f8_bytes,
+                                        "achieved": round(f8_bytes / (us_f8 * 1e-6) / 1e9, 2),
+                                        "peak": PEAK_HBM_GBS,
+                                        "frac": round(f8_bytes / (us_f8 * 1e-6) / 1e9
+                                                      / PEAK_HBM_GBS, 4)},
+                "quantize_shard_us": round(us_q, 2)}
+    del codes, wscale, out8, pr8
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -308,6 +327,7 @@ def main():
         "unfused": side,
         "accept_converge": acc_side,
         "reduce_partials": red_side,
+        "fp8_table": fp8_side,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

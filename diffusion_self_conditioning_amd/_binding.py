@@ -22,7 +22,8 @@ STATUS_NAMES = ["SE_OK", "SE_ERR_NULL", "SE_ERR_SHAPE", "SE_ERR_SLICE", "SE_ERR_
 
 EXPORTS = ("se_status_string", "se_version", "se_row_stats", "se_probs_bf16",
            "se_soft_embed_workspace_bytes", "se_soft_embed", "se_soft_embed_fused",
-           "se_accept_converge", "se_reduce_partials")
+           "se_accept_converge", "se_reduce_partials", "se_quantize_table_fp8",
+           "se_soft_embed_fp8", "se_soft_embed_fp8_fused")
 
 
 class SoftEmbedError(RuntimeError):
@@ -50,8 +51,14 @@ def _declare(lib):
     lib.se_accept_converge.argtypes = [vp, vp, i64, i64, f64, i32, f64, i32, vp, vp, vp, vp, vp,
                                        vp, vp]
     lib.se_reduce_partials.argtypes = [vp, i64, i64, i64, i64, i64, vp, i64, vp, i64, vp]
+    lib.se_quantize_table_fp8.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+    lib.se_soft_embed_fp8.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, i64, i64, i64, f32, vp,
+                                      i64, vp, sz, vp]
+    lib.se_soft_embed_fp8_fused.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, vp, i64, i64, i64,
+                                            f32, vp, i64, vp, sz, vp]
     for fn in ("se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
-               "se_accept_converge", "se_reduce_partials"):
+               "se_accept_converge", "se_reduce_partials", "se_quantize_table_fp8",
+               "se_soft_embed_fp8", "se_soft_embed_fp8_fused"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -189,3 +196,42 @@ def se_reduce_partials(parts, out=None, out_bf16=None, *, stream=None):
         _ptr(parts), t, parts.stride(0), n, d, parts.stride(1), _ptr(out),
         _ld(out) if out is not None else 0, _ptr(out_bf16),
         _ld(out_bf16) if out_bf16 is not None else 0, _stream(stream)))
+
+
+def se_quantize_table_fp8(w, codes, row_scale, *, d=None, stream=None):
+    """e4m3 codes (uint8 [rows, >= d]) and power-of-two row scales (fp32 [rows]) of the
+    bf16 table ``w`` [rows, >= d]."""
+    w = _as_u16(w)
+    rows = w.shape[0]
+    d = w.shape[1] if d is None else d
+    _check("se_quantize_table_fp8", lib.se_quantize_table_fp8(
+        _ptr(w), _ld(w), rows, d, _ptr(codes), _ld(codes), _ptr(row_scale), _stream(stream)))
+
+
+def se_soft_embed_fp8(probs, vocab_start, vocab_end, w_codes, w_scale, gamma, out, workspace=None,
+                      *, vocab=None, d=None, w_rows=None, stream=None):
+    """se_soft_embed with the shard as e4m3 codes [w_rows, >= d] and fp32 row scales."""
+    probs = _as_u16(probs)
+    n, v = probs.shape
+    vocab = v if vocab is None else vocab
+    d = w_codes.shape[1] if d is None else d
+    w_rows = w_codes.shape[0] if w_rows is None else w_rows
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("se_soft_embed_fp8", lib.se_soft_embed_fp8(
+        _ptr(probs), _ld(probs), n, vocab, vocab_start, vocab_end, _ptr(w_codes), _ptr(w_scale),
+        w_rows, _ld(w_codes), d, float(gamma), _ptr(out), _ld(out), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def se_soft_embed_fp8_fused(logits, row_lse, vocab_start, vocab_end, w_codes, w_scale, gamma, out,
+                            workspace=None, *, vocab=None, d=None, w_rows=None, stream=None):
+    """se_soft_embed_fused with the shard as e4m3 codes [w_rows, >= d] and fp32 row scales."""
+    n, v = logits.shape
+    vocab = v if vocab is None else vocab
+    d = w_codes.shape[1] if d is None else d
+    w_rows = w_codes.shape[0] if w_rows is None else w_rows
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("se_soft_embed_fp8_fused", lib.se_soft_embed_fp8_fused(
+        _ptr(logits), _ld(logits), _ptr(row_lse), n, vocab, vocab_start, vocab_end,
+        _ptr(w_codes), _ptr(w_scale), w_rows, _ld(w_codes), d, float(gamma), _ptr(out), _ld(out),
+        _ptr(workspace), ws_bytes, _stream(stream)))

@@ -8,7 +8,8 @@ from __future__ import annotations
 
 import torch
 
-from ._binding import (SoftEmbedError, se_probs_bf16, se_row_stats, se_soft_embed,  # noqa: F401
+from ._binding import (SoftEmbedError, se_probs_bf16, se_quantize_table_fp8,  # noqa: F401
+                       se_row_stats, se_soft_embed, se_soft_embed_fp8, se_soft_embed_fp8_fused,
                        se_soft_embed_fused, se_soft_embed_workspace_bytes, se_status_string,
                        se_version)
 
@@ -49,4 +50,31 @@ def soft_embed(logits, row_lse, vocab_start, vocab_end, w_shard, gamma, *, fused
     else:
         p = probs_bf16(logits, row_lse, vocab_start, vocab_end, stream=stream)
         se_soft_embed(p, vocab_start, vocab_end, w_shard, gamma, out, ws, stream=stream)
+    return out
+
+
+def quantize_table_fp8(w, stream=None):
+    """(codes uint8 [rows, d], row_scale fp32 [rows]): the e4m3 form of a bf16 table."""
+    rows, d = w.shape
+    codes = torch.empty((rows, d), device=w.device, dtype=torch.uint8)
+    scale = torch.empty(rows, device=w.device, dtype=torch.float32)
+    se_quantize_table_fp8(w, codes, scale, stream=stream)
+    return codes, scale
+
+
+def soft_embed_fp8(logits, row_lse, vocab_start, vocab_end, w_codes, w_scale, gamma, *,
+                   fused=True, out=None, ws=None, stream=None):
+    """soft_embed with the shard in e4m3 form (codes [rows, d], power-of-two row scales)."""
+    n, d = logits.shape[0], w_codes.shape[1]
+    if out is None:
+        out = torch.empty((n, d), device=logits.device, dtype=torch.float32)
+    if ws is None:
+        ws = workspace(n, vocab_start, vocab_end, d, logits.device)
+    if fused:
+        se_soft_embed_fp8_fused(logits, row_lse, vocab_start, vocab_end, w_codes, w_scale, gamma,
+                                out, ws, stream=stream)
+    else:
+        p = probs_bf16(logits, row_lse, vocab_start, vocab_end, stream=stream)
+        se_soft_embed_fp8(p, vocab_start, vocab_end, w_codes, w_scale, gamma, out, ws,
+                          stream=stream)
     return out

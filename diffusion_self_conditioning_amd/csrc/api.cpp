@@ -60,17 +60,26 @@ se_status check_slice_layout(int64_t s, int64_t d, int64_t ld_w, int64_t ld_out,
   return SE_OK;
 }
 
+// The e4m3 table's extra checks: codes in 16-byte pieces of 16 columns, one fp32
+// scale per shard row.
+se_status check_fp8_layout(int64_t d, int64_t ld_w, const float* w_scale) {
+  if (!w_scale) return SE_ERR_NULL;
+  if (!aligned4(w_scale) || (d % 16) != 0 || (ld_w % 16) != 0) return SE_ERR_ALIGN;
+  return SE_OK;
+}
+
 se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* lse, int64_t n_rows,
-                         int64_t s, int64_t e, const uint16_t* w, int64_t ldw, int64_t d,
-                         float gamma, float* out, int64_t ld_out, void* ws, size_t ws_bytes,
-                         void* stream) {
+                         int64_t s, int64_t e, const void* w, const float* w_scale, int64_t ldw,
+                         int64_t d, float gamma, float* out, int64_t ld_out, void* ws,
+                         size_t ws_bytes, void* stream) {
   const se::GemmPlan g = se::plan_gemm(n_rows, d, e - s);
   if (g.grid > INT32_MAX) return SE_ERR_SHAPE;
   // the kernels address one tile's rows of `a` and a split's rows of the shard with
   // 32-bit byte offsets
   const int64_t esz = fused ? 4 : 2;
+  const int64_t wsz = w_scale ? 1 : 2;
   if ((int64_t)(se::kBM - 1) * lda * esz + (e - s) * esz > (int64_t)UINT32_MAX ||
-      (e - s) * ldw * 2 > (int64_t)UINT32_MAX)
+      (e - s) * ldw * wsz > (int64_t)UINT32_MAX)
     return SE_ERR_SHAPE;
   if (ws_bytes < g.ws_bytes) return SE_ERR_WORKSPACE;
   if (g.ws_bytes > 0 && (ws == nullptr)) return SE_ERR_NULL;
@@ -90,6 +99,7 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
   p.lse = lse;
   p.col0 = s;
   p.w = w;
+  p.wscale = w_scale;
   p.ldw = ldw;
   p.M = n_rows;
   p.N = d;
@@ -102,7 +112,7 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
   p.tiles = (int)g.tiles;
   p.splits = (int)g.splits;
   p.kblocks = (int)g.kblocks;
-  return from_hip(se::launch_soft_embed(p, fused, st));
+  return from_hip(se::launch_soft_embed(p, fused, w_scale != nullptr, st));
 }
 
 }  // namespace
@@ -123,7 +133,7 @@ const char* se_status_string(se_status s) {
 }
 
 const char* se_version(void) {
-  return "libsoftembed 0.2 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials)";
+  return "libsoftembed 0.3 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table)";
 }
 
 se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
@@ -185,7 +195,7 @@ se_status se_soft_embed(const uint16_t* probs, int64_t ld_probs, int64_t n_rows,
   if (rc != SE_OK) return rc;
   if (!aligned16(probs) || (ld_probs % 8) != 0) return SE_ERR_ALIGN;
   return run_soft_embed(false, probs, ld_probs, nullptr, n_rows, vocab_start, vocab_end, w_shard,
-                        ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
+                        nullptr, ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
 }
 
 se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const float* row_lse,
@@ -202,7 +212,59 @@ se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const floa
   if (rc != SE_OK) return rc;
   if (!aligned16(logits) || (ld_logits % 4) != 0 || !aligned4(row_lse)) return SE_ERR_ALIGN;
   return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start, vocab_end, w_shard,
-                        ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
+                        nullptr, ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
+}
+
+se_status se_quantize_table_fp8(const uint16_t* w, int64_t ld_w, int64_t rows, int64_t d,
+                                uint8_t* codes, int64_t ld_codes, float* row_scale,
+                                void* stream) {
+  if (rows < 0 || d < 1 || d > INT32_MAX || ld_w < d || ld_codes < d) return SE_ERR_SHAPE;
+  if (rows / 4 >= (int64_t)INT32_MAX) return SE_ERR_SHAPE;
+  if (rows == 0) return SE_OK;
+  if (!w || !codes || !row_scale) return SE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned4(row_scale)) return SE_ERR_ALIGN;
+  if ((d % 16) != 0 || (ld_w % 8) != 0 || (ld_codes % 16) != 0) return SE_ERR_ALIGN;
+  return from_hip(se::launch_quantize_fp8(w, ld_w, rows, d, codes, ld_codes, row_scale,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+se_status se_soft_embed_fp8(const uint16_t* probs, int64_t ld_probs, int64_t n_rows, int64_t vocab,
+                            int64_t vocab_start, int64_t vocab_end, const uint8_t* w_codes,
+                            const float* w_scale, int64_t w_rows, int64_t ld_w, int64_t d,
+                            float gamma, float* out, int64_t ld_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
+  if (rc != SE_OK) return rc;
+  if (ld_probs < vocab) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  if (!probs || !w_codes || !out) return SE_ERR_NULL;
+  rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_codes, out);
+  if (rc != SE_OK) return rc;
+  rc = check_fp8_layout(d, ld_w, w_scale);
+  if (rc != SE_OK) return rc;
+  if (!aligned16(probs) || (ld_probs % 8) != 0) return SE_ERR_ALIGN;
+  return run_soft_embed(false, probs, ld_probs, nullptr, n_rows, vocab_start, vocab_end, w_codes,
+                        w_scale, ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
+}
+
+se_status se_soft_embed_fp8_fused(const float* logits, int64_t ld_logits, const float* row_lse,
+                                  int64_t n_rows, int64_t vocab, int64_t vocab_start,
+                                  int64_t vocab_end, const uint8_t* w_codes, const float* w_scale,
+                                  int64_t w_rows, int64_t ld_w, int64_t d, float gamma,
+                                  float* out, int64_t ld_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
+  if (rc != SE_OK) return rc;
+  if (ld_logits < vocab) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  if (!logits || !row_lse || !w_codes || !out) return SE_ERR_NULL;
+  rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_codes, out);
+  if (rc != SE_OK) return rc;
+  rc = check_fp8_layout(d, ld_w, w_scale);
+  if (rc != SE_OK) return rc;
+  if (!aligned16(logits) || (ld_logits % 4) != 0 || !aligned4(row_lse)) return SE_ERR_ALIGN;
+  return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start, vocab_end, w_codes,
+                        w_scale, ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
 }
 
 se_status se_accept_converge(const float* row_entropy, const int32_t* row_argmax,

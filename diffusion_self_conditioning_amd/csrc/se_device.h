@@ -56,6 +56,12 @@ __device__ __forceinline__ float4 buffer_load_f4(__amdgpu_buffer_rsrc_t r, uint3
   const f32x4_t v = se_raw_buffer_load_f4(r, (int)voff, (int)soff, 0);
   return make_float4(v.x, v.y, v.z, v.w);
 }
+__device__ float se_raw_buffer_load_f1(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
+                                      int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.f32");
+__device__ __forceinline__ float buffer_load_f1(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint32_t soff) {
+  return se_raw_buffer_load_f1(r, (int)voff, (int)soff, 0);
+}
 
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -75,6 +81,20 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// 16 OCP e4m3 codes (byte j of `c` = element j) times a power-of-two `scale`, as 16
+// bf16 values: elements 0..7 in `lo`, 8..15 in `hi`.  Every e4m3 value times a power
+// of two in the normal range is a bf16 value, so the conversion is exact.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t c, float scale, bool high) {
+  return high ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, false));
+}
+__device__ __forceinline__ void fp8x16_to_bf16(const uint4& c, float scale, uint4& lo, uint4& hi) {
+  lo = make_uint4(fp8x2_to_bf16x2(c.x, scale, false), fp8x2_to_bf16x2(c.x, scale, true),
+                  fp8x2_to_bf16x2(c.y, scale, false), fp8x2_to_bf16x2(c.y, scale, true));
+  hi = make_uint4(fp8x2_to_bf16x2(c.z, scale, false), fp8x2_to_bf16x2(c.z, scale, true),
+                  fp8x2_to_bf16x2(c.w, scale, false), fp8x2_to_bf16x2(c.w, scale, true));
 }
 
 }  // namespace se

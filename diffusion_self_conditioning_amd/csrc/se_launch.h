@@ -40,8 +40,9 @@ struct GemmParams {
   int64_t lda;            // elements
   const float* lse;       // fused only: per-row log-sum-exp
   int64_t col0;           // vocab_start: column of `a` holding slice position 0
-  const uint16_t* w;      // bf16 shard, row 0 = slice position 0
-  int64_t ldw;
+  const void* w;          // shard, row 0 = slice position 0: bf16, or e4m3 codes
+  const float* wscale;    // e4m3 table only: power-of-two scale of each shard row
+  int64_t ldw;            // elements (bytes for e4m3 codes)
   int64_t M, N, K;
   float gamma;
   float* out;
@@ -58,7 +59,12 @@ hipError_t launch_probs_bf16(const float* logits, int64_t ld, const float* row_l
                              int64_t n_rows, int64_t col0, int64_t K, uint16_t* probs,
                              int64_t ldp, hipStream_t stream);
 
-hipError_t launch_soft_embed(const GemmParams& p, bool fused, hipStream_t stream);
+// fused: `a` holds fp32 logits (else bf16 probabilities); w8: `w` holds e4m3 codes
+// with per-row scales (else bf16)
+hipError_t launch_soft_embed(const GemmParams& p, bool fused, bool w8, hipStream_t stream);
+
+hipError_t launch_quantize_fp8(const uint16_t* w, int64_t ldw, int64_t rows, int64_t d,
+                               uint8_t* codes, int64_t ldq, float* row_scale, hipStream_t stream);
 
 hipError_t launch_accept_converge(const float* row_entropy, const int32_t* row_argmax,
                                   int64_t n_canvas, int len, double budget, int stable_steps,

@@ -46,6 +46,14 @@
 // past M are clamped (they only feed output rows that are never written); that
 // path computes addresses per load and is used only when M is not a multiple of
 // 256.
+//
+// e4m3 table (W8): the shard arrives as OCP FP8 E4M3 codes with one power-of-two
+// scale per vocabulary row (the FP8 weights of the agentlenshq overview, section on
+// performance and quantization).  Each lane loads 16 codes of one row per step and
+// that row's scale; v_cvt_scalef32_pk_bf16_fp8 turns them into bf16 (exactly: code x
+// power of two is a bf16 value) on the way into the same LDS tile, so everything after
+// the LDS write is the bf16 kernel and the two agree bit for bit on the dequantized
+// table.
 #include "se_device.h"
 #include "se_launch.h"
 
@@ -89,7 +97,6 @@ constexpr int kMI = 4;
 constexpr int kNI = kTN / 32;
 constexpr int kArows = kBM / kWaves;             // probability rows produced per wave
 constexpr int kWrows = kBK / kWaves;             // table rows per wave and step
-constexpr int kWJ = kWrows / 2;                  // table loads per wave and step
 
 // byte offset of P element (m, k) in a [256][128] tile: 256-byte rows, 16-byte
 // chunk index (k / 8) XOR (m % 16)
@@ -126,14 +133,37 @@ struct AGeo<false> {
   __device__ static int pos(int lane) { return 8 * (lane & 15); }
 };
 
+// Table producer geometry, per wave and step (the wave's kWrows rows of the step).
+//   bf16: loads of 8 values; load j covers rows 2 j + lane/32, columns 8 (lane % 32) ..
+//   e4m3: loads of 16 codes; load j covers rows 4 j + lane/16, columns 16 (lane % 16) ..;
+//         they become bf16 (times the row's scale) on the way into LDS, so the LDS
+//         tile, the fragment reads and the MFMAs are the same for both tables.
+template <bool W8>
+struct WGeo;
+template <>
+struct WGeo<false> {
+  static constexpr int kRowsPerLoad = 2, kEsz = 2, kCols = 8, kLoads = kWrows / 2;
+  __device__ static int row(int lane) { return lane >> 5; }
+  __device__ static int col(int lane) { return 8 * (lane & 31); }
+};
+template <>
+struct WGeo<true> {
+  static constexpr int kRowsPerLoad = 4, kEsz = 1, kCols = 16, kLoads = kWrows / 4;
+  __device__ static int row(int lane) { return lane >> 4; }
+  __device__ static int col(int lane) { return 16 * (lane & 15); }
+};
+static_assert(WGeo<true>::kLoads >= 1, "an e4m3 load covers 4 table rows");
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
-template <bool FUSED, bool FULL>
+template <bool FUSED, bool FULL, bool W8>
 __global__ void __launch_bounds__(kGemmThreads)
 __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 soft_embed_kernel(const GemmParams p) {
   using G = AGeo<FUSED>;
+  using WG = WGeo<W8>;
+  constexpr int kWJ = WG::kLoads;                // table loads per wave and step
   using AReg = typename G::reg_t;
   constexpr int kEsz = G::kEsz;
   constexpr int kPerQ = G::kPerQ;
@@ -210,24 +240,47 @@ soft_embed_kernel(const GemmParams p) {
     }
   };
 
-  // ---- table producer: buffer resource at shard row k_lo -------------------------------
-  // step ks, piece j (< kWJ): rows kWrows wave + 2 j + lane/32, columns 8 (lane % 32) ..
-  const int64_t w_ld = p.ldw * 2;
+  // ---- table producer: buffer resources at shard row k_lo ------------------------------
+  // step ks, load j (< kWJ): rows kWrows wave + WG::kRowsPerLoad j + WG::row(lane)
+  const int64_t w_ld = p.ldw * WG::kEsz;
   const __amdgpu_buffer_rsrc_t w_rsrc =
-      make_rsrc(reinterpret_cast<const unsigned char*>(p.w) + k_lo * w_ld,
+      make_rsrc(static_cast<const unsigned char*>(p.w) + k_lo * w_ld,
                 (uint32_t)min((k_hi - k_lo) * w_ld, (int64_t)UINT32_MAX));
-  const uint32_t w_lo = (uint32_t)((kWrows * wave + (lane >> 5)) * w_ld) +
-                        2 * (uint32_t)min(n0 + 8 * (lane & 31), N - 8);
+  const int w_r = kWrows * wave + WG::row(lane);   // this lane's row in load 0 of a step
+  const uint32_t w_lo =
+      (uint32_t)(w_r * w_ld) + WG::kEsz * (uint32_t)min(n0 + WG::col(lane), N - WG::kCols);
+  // LDS store offsets.  bf16: the rows of loads j and j + 1 differ in swizzle phase
+  // (row % 4); e4m3: every load of a lane has the same phase and fills two chunks.
   uint32_t w_st[2];
+  if constexpr (W8) {
+    w_st[0] = kWBase + w_off(w_r, WG::col(lane));
+    w_st[1] = kWBase + w_off(w_r, WG::col(lane) + 8);
+  } else {
 #pragma unroll
-  for (int e = 0; e < 2; ++e)
-    w_st[e] = kWBase + w_off(kWrows * wave + 2 * e + (lane >> 5), 8 * (lane & 31)) - 1024 * e;
+    for (int e = 0; e < 2; ++e) w_st[e] = kWBase + w_off(w_r + 2 * e, WG::col(lane)) - 1024 * e;
+  }
+  // e4m3 row scales of the split, one fp32 per lane and load
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      make_rsrc(W8 ? static_cast<const void*>(p.wscale + k_lo) : p.w,
+                W8 ? (uint32_t)min((k_hi - k_lo) * 4, (int64_t)UINT32_MAX) : 0u);
   auto load_w = [&](int ks, int j) -> uint4 {
     return SE_W_LOAD(w_rsrc, w_lo,
-                             (uint32_t)(((int64_t)ks * kBK - k_lo + 2 * j) * w_ld));
+                     (uint32_t)(((int64_t)ks * kBK - k_lo + WG::kRowsPerLoad * j) * w_ld));
   };
-  auto store_w = [&](int wbuf, int j, const uint4& r) {
-    *reinterpret_cast<uint4*>(lds + wbuf * kWBuf + w_st[j & 1] + 1024 * j) = r;
+  auto load_s = [&](int ks, int j) -> float {
+    return buffer_load_f1(s_rsrc, 4u * (uint32_t)w_r,
+                          (uint32_t)(((int64_t)ks * kBK - k_lo + WG::kRowsPerLoad * j) * 4));
+  };
+  auto store_w = [&](int wbuf, int j, const uint4& r, float sc) {
+    unsigned char* base = lds + wbuf * kWBuf;
+    if constexpr (W8) {
+      uint4 lo, hi;
+      fp8x16_to_bf16(r, sc, lo, hi);
+      *reinterpret_cast<uint4*>(base + w_st[0] + 512 * WG::kRowsPerLoad * j) = lo;
+      *reinterpret_cast<uint4*>(base + w_st[1] + 512 * WG::kRowsPerLoad * j) = hi;
+    } else {
+      *reinterpret_cast<uint4*>(base + w_st[j & 1] + 1024 * j) = r;
+    }
   };
 
   f32x16 acc[kMI][kNI];
@@ -316,6 +369,7 @@ soft_embed_kernel(const GemmParams p) {
   // ---- main loop over the full super-steps [S0, Sf) ------------------------------------
   AReg ra[2][kPerQ];                 // quarter registers: set q % 2
   uint4 rw[2][kWJ];                  // table register stages
+  float rs[2][kWJ];                  // e4m3 row scales of those stages
   if (S0 < Sf) {
     const int Slast = Sf - 1;
     const int kslast = 4 * Sf - 1;
@@ -334,13 +388,19 @@ soft_embed_kernel(const GemmParams p) {
 #pragma unroll
       for (int i = 0; i < kPerQ; ++i) ra[q][i] = load_a(min(S0 + 1, Slast), q * kPerQ + i);
 #pragma unroll
-    for (int j = 0; j < kWJ; ++j) rw[0][j] = load_w(ks0, j);
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int j = 0; j < kWJ; ++j) rw[1][j] = load_w(min(ks0 + 1, kslast), j);
+      for (int j = 0; j < kWJ; ++j) {
+        rw[st][j] = load_w(min(ks0 + st, kslast), j);
+        rs[st][j] = W8 ? load_s(min(ks0 + st, kslast), j) : 0.f;
+      }
 #pragma unroll
-    for (int j = 0; j < kWJ; ++j) store_w(0, j, rw[0][j]);
+    for (int j = 0; j < kWJ; ++j) store_w(0, j, rw[0][j], rs[0][j]);
 #pragma unroll
-    for (int j = 0; j < kWJ; ++j) rw[0][j] = load_w(min(ks0 + 2, kslast), j);
+    for (int j = 0; j < kWJ; ++j) {
+      rw[0][j] = load_w(min(ks0 + 2, kslast), j);
+      rs[0][j] = W8 ? load_s(min(ks0 + 2, kslast), j) : 0.f;
+    }
     __syncthreads();
 
     for (int S = S0; S < Sf; ++S) {
@@ -348,6 +408,7 @@ soft_embed_kernel(const GemmParams p) {
       for (int q = 0; q < kQ; ++q) {
         const int ks = 4 * S + q;
         uint4 (&rwn)[kWJ] = rw[(q + 1) & 1];          // table step ks + 1
+        float (&rsn)[kWJ] = rs[(q + 1) & 1];
         AReg (&rq)[kPerQ] = ra[q & 1];                // quarter q of super-step S + 1
         // refill: quarter q + 2 of S + 1, or quarter q - 2 of S + 2
         const int Sr = min(q < 2 ? S + 1 : S + 2, Slast);
@@ -360,13 +421,19 @@ soft_embed_kernel(const GemmParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         compute(S & 1, q & 1, q, [&](int h) {
+          // table loads j in [ceil(h kWJ / 2), ceil((h + 1) kWJ / 2)): a single load
+          // goes with the first half
 #pragma unroll
-          for (int j = h * kWJ / 2; j < (h + 1) * kWJ / 2; ++j) store_w((q + 1) & 1, j, rwn[j]);
+          for (int j = (h * kWJ + 1) / 2; j < ((h + 1) * kWJ + 1) / 2; ++j)
+            store_w((q + 1) & 1, j, rwn[j], rsn[j]);
 #pragma unroll
           for (int i = h * kPerQ / 2; i < (h + 1) * kPerQ / 2; ++i)
             store_a((S + 1) & 1, q * kPerQ + i, rq[i], nlq[FUSED ? i : 0]);
 #pragma unroll
-          for (int j = h * kWJ / 2; j < (h + 1) * kWJ / 2; ++j) rwn[j] = load_w(kn, j);
+          for (int j = (h * kWJ + 1) / 2; j < ((h + 1) * kWJ + 1) / 2; ++j) {
+            rwn[j] = load_w(kn, j);
+            if constexpr (W8) rsn[j] = load_s(kn, j);
+          }
 #pragma unroll
           for (int i = h * kPerQ / 2; i < (h + 1) * kPerQ / 2; ++i) rq[i] = load_a(Sr, qr * kPerQ + i);
         });
@@ -416,10 +483,14 @@ soft_embed_kernel(const GemmParams p) {
       const unsigned char* wb = reinterpret_cast<const unsigned char*>(p.w) + kr0 * w_ld;
 #pragma unroll
       for (int j = 0; j < kWJ; ++j) {
-        const int64_t kr = kr0 + kWrows * wave + 2 * j + (lane >> 5);
+        const int64_t kr = kr0 + w_r + WG::kRowsPerLoad * j;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (kr < p.K) v = *reinterpret_cast<const uint4*>(wb + (int64_t)(2 * j) * w_ld + w_lo);
-        store_w(0, j, v);
+        float sc = 0.f;
+        if (kr < p.K) {
+          v = *reinterpret_cast<const uint4*>(wb + (int64_t)(WG::kRowsPerLoad * j) * w_ld + w_lo);
+          if constexpr (W8) sc = p.wscale[kr];
+        }
+        store_w(0, j, v, sc);
       }
       __syncthreads();
       compute(0, 0, ks - 4 * Sf, [](int) {});
@@ -493,18 +564,25 @@ __global__ void zero_rows_kernel(float* __restrict__ out, int64_t ldo, int64_t N
 
 }  // namespace
 
-hipError_t launch_soft_embed(const GemmParams& p, bool fused, hipStream_t stream) {
+namespace {
+
+template <bool FUSED, bool W8>
+void launch_contraction(const GemmParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles * p.splits));
   // whole 256-row tiles take the path with per-lane addresses fixed for the kernel
-  const bool full = p.M % kBM == 0;
-  if (fused && full)
-    hipLaunchKernelGGL((soft_embed_kernel<true, true>), grid, dim3(kGemmThreads), 0, stream, p);
-  else if (fused)
-    hipLaunchKernelGGL((soft_embed_kernel<true, false>), grid, dim3(kGemmThreads), 0, stream, p);
-  else if (full)
-    hipLaunchKernelGGL((soft_embed_kernel<false, true>), grid, dim3(kGemmThreads), 0, stream, p);
+  if (p.M % kBM == 0)
+    hipLaunchKernelGGL((soft_embed_kernel<FUSED, true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((soft_embed_kernel<false, false>), grid, dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL((soft_embed_kernel<FUSED, false, W8>), grid, dim3(kGemmThreads), 0, stream, p);
+}
+
+}  // namespace
+
+hipError_t launch_soft_embed(const GemmParams& p, bool fused, bool w8, hipStream_t stream) {
+  if (fused && w8) launch_contraction<true, true>(p, stream);
+  else if (fused) launch_contraction<true, false>(p, stream);
+  else if (w8) launch_contraction<false, true>(p, stream);
+  else launch_contraction<false, false>(p, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));

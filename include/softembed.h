@@ -153,6 +153,62 @@ se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const floa
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * se_quantize_table_fp8 -- the e4m3 form of a bf16 embedding table (the pages serve
+ * the model with FP8 weights: agentlenshq overview of DiffusionGemma in vLLM,
+ * section on performance and quantization, quantized checkpoints).
+ *
+ * Per row v:  k_v = the smallest integer >= -126 with max_j |w[v, j]| <= 448 * 2^k_v
+ *             (k_v = 0 for an all-zero row; 448 is the largest finite e4m3 value),
+ *             row_scale[v] = 2^k_v (an exact power of two),
+ *             codes[v, j]  = e4m3_rne(w[v, j] * 2^-k_v)   (OCP FP8 E4M3: 1 sign,
+ *                            4 exponent bits with bias 7, 3 mantissa bits, no
+ *                            infinities; nearest value, ties to even code; the sign
+ *                            of a zero result is the input's).
+ * code * scale is exactly representable in bf16, so the e4m3 table dequantizes
+ * exactly to bf16.
+ *
+ * w: bf16 [rows, ld_w], columns [0, d) read; values must be finite.
+ * codes: uint8 [rows, ld_codes], columns [0, d) written.  row_scale: fp32 [rows].
+ * Errors: SE_ERR_SHAPE if rows < 0, d < 1, ld_w < d or ld_codes < d; SE_ERR_NULL for
+ * a NULL pointer (rows > 0); SE_ERR_ALIGN unless d % 16 == 0, ld_w % 8 == 0,
+ * ld_codes % 16 == 0, w and codes 16-byte and row_scale 4-byte aligned.
+ * rows == 0 is a no-op.
+ */
+se_status se_quantize_table_fp8(const uint16_t* w, int64_t ld_w, int64_t rows, int64_t d,
+                                uint8_t* codes, int64_t ld_codes, float* row_scale,
+                                void* stream);
+
+/*
+ * se_soft_embed_fp8 / se_soft_embed_fp8_fused -- se_soft_embed / se_soft_embed_fused
+ * with the shard in the e4m3 form of se_quantize_table_fp8:
+ *
+ *     out_i,: = gamma * sum_{v=s}^{e-1} p_iv * (codes[v - s, :] * w_scale[v - s])
+ *
+ * The table enters the bf16 MFMA contraction as code * scale, which is exact, so
+ * the result equals se_soft_embed(_fused) on the dequantized bf16 table bit for bit
+ * (same probabilities, same accumulation order).
+ *
+ * w_codes: uint8 [w_rows, ld_w], rows [0, e - s) and columns [0, d) read.
+ * w_scale: fp32 [w_rows], entries [0, e - s) read; each must be a power of two in
+ *          the normal range (as se_quantize_table_fp8 writes them).
+ * Other arguments, the workspace and the errors as se_soft_embed(_fused), and in
+ * addition: SE_ERR_NULL if w_scale is NULL; SE_ERR_ALIGN unless d % 16 == 0,
+ * ld_w % 16 == 0 and w_scale is 4-byte aligned.
+ */
+se_status se_soft_embed_fp8(const uint16_t* probs, int64_t ld_probs, int64_t n_rows, int64_t vocab,
+                            int64_t vocab_start, int64_t vocab_end, const uint8_t* w_codes,
+                            const float* w_scale, int64_t w_rows, int64_t ld_w, int64_t d,
+                            float gamma, float* out, int64_t ld_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+se_status se_soft_embed_fp8_fused(const float* logits, int64_t ld_logits, const float* row_lse,
+                                  int64_t n_rows, int64_t vocab, int64_t vocab_start,
+                                  int64_t vocab_end, const uint8_t* w_codes, const float* w_scale,
+                                  int64_t w_rows, int64_t ld_w, int64_t d, float gamma,
+                                  float* out, int64_t ld_out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * se_accept_converge -- entropy-bound acceptance and the convergence test of the
  * diffusion sampler, on the statistics se_row_stats produces (agentlenshq overview
  * of DiffusionGemma in vLLM, section on the sampling loop and entropy-bound

@@ -211,3 +211,52 @@ def test_reduce_partials_errors():
     assert call(out=P2 + 8) == b.SE_ERR_ALIGN
     assert call(ob=P3 + 4) == b.SE_ERR_ALIGN
     assert call(n=0, parts=None, out=None, ob=None) == b.SE_OK
+
+
+def fp8_call(fused_call, **kw):
+    a = dict(a=P1, ld=262144, lse=P2, n=256, vocab=262144, s=65536, e=131072, w=P3, sc=P5 + 256,
+             w_rows=65536, ldw=2816, d=2816, gamma=53.0, out=P4, ldo=2816, ws=P5,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    if fused_call:
+        return lib.se_soft_embed_fp8_fused(a["a"], a["ld"], a["lse"], a["n"], a["vocab"], a["s"],
+                                           a["e"], a["w"], a["sc"], a["w_rows"], a["ldw"], a["d"],
+                                           a["gamma"], a["out"], a["ldo"], a["ws"], a["ws_bytes"],
+                                           a["stream"])
+    return lib.se_soft_embed_fp8(a["a"], a["ld"], a["n"], a["vocab"], a["s"], a["e"], a["w"],
+                                 a["sc"], a["w_rows"], a["ldw"], a["d"], a["gamma"], a["out"],
+                                 a["ldo"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("fused_call", [True, False])
+@pytest.mark.parametrize("kw,code", [
+    (dict(sc=None), b.SE_ERR_NULL),
+    (dict(w=None), b.SE_ERR_NULL),
+    (dict(sc=P5 + 2), b.SE_ERR_ALIGN),
+    (dict(d=2808, ldw=2816, ldo=2816), b.SE_ERR_ALIGN),      # d % 16
+    (dict(ldw=2824), b.SE_ERR_ALIGN),                         # ld_w % 16
+    (dict(w=P3 + 8), b.SE_ERR_ALIGN),
+    (dict(s=0, e=262144), b.SE_ERR_SLICE),
+    (dict(w_rows=65535), b.SE_ERR_SLICE),
+    (dict(ws_bytes=1024), b.SE_ERR_WORKSPACE),
+    (dict(n=0, a=None, lse=None, w=None, sc=None, out=None, ws=None, ws_bytes=0), b.SE_OK),
+])
+def test_fp8_soft_embed_errors(fused_call, kw, code):
+    assert fp8_call(fused_call, **kw) == code
+
+
+def test_quantize_table_fp8_errors():
+    q = lib.se_quantize_table_fp8
+    assert q(P1, 2816, -1, 2816, P2, 2816, P3, None) == b.SE_ERR_SHAPE
+    assert q(P1, 2816, 16, 0, P2, 2816, P3, None) == b.SE_ERR_SHAPE
+    assert q(P1, 2808, 16, 2816, P2, 2816, P3, None) == b.SE_ERR_SHAPE
+    assert q(P1, 2816, 16, 2816, P2, 2800, P3, None) == b.SE_ERR_SHAPE
+    assert q(None, 2816, 16, 2816, P2, 2816, P3, None) == b.SE_ERR_NULL
+    assert q(P1, 2816, 16, 2816, P2, 2816, None, None) == b.SE_ERR_NULL
+    assert q(P1, 2816, 16, 2808, P2, 2816, P3, None) == b.SE_ERR_ALIGN    # d % 16
+    assert q(P1, 2820, 16, 2816, P2, 2816, P3, None) == b.SE_ERR_ALIGN    # ld_w % 8
+    assert q(P1, 2816, 16, 2816, P2, 2824, P3, None) == b.SE_ERR_ALIGN    # ld_codes % 16
+    assert q(P1 + 2, 2816, 16, 2816, P2, 2816, P3, None) == b.SE_ERR_ALIGN
+    assert q(P1, 2816, 16, 2816, P2 + 8, 2816, P3, None) == b.SE_ERR_ALIGN
+    assert q(P1, 2816, 16, 2816, P2, 2816, P3 + 1, None) == b.SE_ERR_ALIGN
+    assert q(None, 2816, 0, 2816, None, 2816, None, None) == b.SE_OK

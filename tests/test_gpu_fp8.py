@@ -1,0 +1,249 @@
+"""GPU parity of the e4m3 table path: se_quantize_table_fp8, se_soft_embed_fp8 and
+se_soft_embed_fp8_fused (MI355X), all through the C ABI.
+
+Bars:
+  quantizer                codes and scales bit-exact with oracle.fp8.quantize_table
+  contraction vs oracle    relative Frobenius <= 5e-3 against the fp64 soft embedding of
+                           the oracle's dequantized table (the gate of the bf16 path)
+  contraction vs bf16 path bit-exact: the e4m3 kernels on the oracle's codes equal the
+                           bf16 kernels on the oracle's dequantized bf16 table (code x
+                           power-of-two scale is exact in bf16; same accumulation order)
+  decode                   a one-hot probability row returns code value x scale exactly,
+                           for every finite code
+The table inputs of the GPU contraction are the oracle's codes, never the GPU
+quantizer's, so no expected value depends on the HIP path.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+from diffusion_self_conditioning_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from diffusion_self_conditioning_amd import _binding as B
+    from diffusion_self_conditioning_amd import api
+
+DEV = "cuda:0"
+GATE = 5e-3
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def rel_fro(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    n = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (n if n > 0 else 1.0)
+
+
+def padded(a, ld, fill):
+    """2-D device tensor view [rows, cols] of a buffer with row pitch ld, padding = fill."""
+    rows, cols = a.shape
+    buf = np.full((rows, ld), fill, dtype=a.dtype)
+    buf[:, :cols] = a
+    return dev(buf)[:, :cols]
+
+
+def gpu_quantize(bits, ld_w=None, ld_q=None):
+    rows, d = bits.shape
+    w_t = padded(bits, ld_w or d, np.uint16(0x7FC0))
+    c_t = padded(np.zeros((rows, d), np.uint8), ld_q or d, np.uint8(0xA5))
+    s_t = torch.full((rows,), float("nan"), device=DEV)
+    B.se_quantize_table_fp8(w_t, c_t, s_t)
+    torch.cuda.synchronize()
+    return c_t, s_t
+
+
+def check_quantizer(bits, ld_w=None, ld_q=None):
+    c_t, s_t = gpu_quantize(bits, ld_w, ld_q)
+    codes, scale = fp8.quantize_table(bits)
+    got_c, got_s = c_t.cpu().numpy(), s_t.cpu().numpy()
+    bad = np.argwhere(got_c != codes)
+    assert bad.size == 0, [(tuple(i), hex(got_c[tuple(i)]), hex(codes[tuple(i)]),
+                            hex(bits[tuple(i)])) for i in bad[:8]]
+    np.testing.assert_array_equal(got_s, scale)
+    if ld_q:   # the pitch padding of the codes buffer is untouched
+        full = c_t.as_strided((c_t.shape[0], ld_q), (ld_q, 1)).cpu().numpy()
+        assert np.all(full[:, bits.shape[1]:] == 0xA5)
+
+
+def crafted_table(d=64):
+    """Rows that exercise every rounding case of the quantizer."""
+    mags = fp8._MAGS
+    mids = (mags[1:] + mags[:-1]) / 2                 # exact ties, 5 significant bits at most
+    base = np.concatenate([[448.0], mids, -mids[::3], mags[::5]])
+    rows = []
+    rows.append(np.zeros(d))                          # all zero
+    rows.append(-np.zeros(d))                         # negative zeros
+    r = np.zeros(d); r[7] = 1.0; rows.append(r)       # a single one
+    for j in (-20, -8, 0, 5, 100):                    # ties at several scales
+        for o in range(0, len(base), d):
+            chunk = base[o:o + d]
+            rr = np.zeros(d); rr[:len(chunk)] = chunk; rr[0] = 448.0
+            rows.append(rr * 2.0 ** j)
+    rows.append(np.linspace(-3e38, 3e38, d))          # near the bf16 maximum
+    rows.append(np.full(d, 1.5 * 2.0 ** -130))        # bf16 subnormals: k clamps at -126
+    rows.append(np.linspace(-1e-30, 1e-30, d))
+    rng = np.random.default_rng(21)
+    rows.extend(rng.standard_normal((20, d)) * 0.02)
+    t = np.array(rows, dtype=np.float32)
+    return (t.view(np.uint32) >> 16).astype(np.uint16)   # all values above are bf16-exact
+
+
+def test_quantizer_tiny_table():
+    w = wl.get("tiny")
+    bits, _ = wl.make_table(w)
+    say("quantize tiny", bits.shape)
+    check_quantizer(bits)
+
+
+@pytest.mark.parametrize("d,ld_w,ld_q", [(64, None, None), (64, 72, 80), (16, 24, 32), (48, None, 64)])
+def test_quantizer_crafted_rows(d, ld_w, ld_q):
+    bits = crafted_table(d)
+    say("quantize crafted", bits.shape, ld_w, ld_q)
+    check_quantizer(bits, ld_w, ld_q)
+
+
+def test_decode_every_code_one_hot():
+    """Row i of P is one-hot at vocab i (exactly 1.0 in bf16): out[i] = code x scale."""
+    K, d = 256, 16
+    codes = ((np.arange(K)[:, None] + 16 * np.arange(d)[None, :]) % 256).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x00               # NaN codes are not table values
+    scale = np.float32(2.0) ** (np.arange(K) % 41 - 20).astype(np.float32)
+    want = fp8.dequantize(codes, scale)
+    c_t, s_t = dev(codes), dev(scale)
+    probs = np.zeros((K, K), np.uint16)
+    probs[np.arange(K), np.arange(K)] = 0x3F80
+    out = torch.full((K, d), float("nan"), device=DEV)
+    ws = api.workspace(K, 0, K, d, DEV)
+    say("decode unfused")
+    B.se_soft_embed_fp8(dev(probs), 0, K, c_t, s_t, 1.0, out, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().astype(np.float64), want)
+    say("decode fused")
+    x = wl.one_hot_logits(K, K, np.arange(K), hot=0.0, cold=-200.0)
+    x_t = dev(x)
+    _, lse, _, _ = api.row_stats(x_t)
+    out2 = torch.full((K, d), float("nan"), device=DEV)
+    B.se_soft_embed_fp8_fused(x_t, lse, 0, K, c_t, s_t, 1.0, out2, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out2.cpu().numpy().astype(np.float64), want)
+
+
+def _pair(x, s, e, codes, scale, gamma, pad_rows=0, d_view=None):
+    """(fp8 fused, fp8 unfused, bf16 fused, bf16 unfused) outputs on the same inputs; the
+    e4m3 shard gets pad_rows rows of NaN codes / NaN scales after the slice."""
+    K, d = codes.shape[0], codes.shape[1]
+    cpad = np.concatenate([codes, np.full((pad_rows, d), 0x7F, np.uint8)])
+    spad = np.concatenate([scale, np.full(pad_rows, np.nan, np.float32)])
+    dq = fp8.dequantize_bf16_bits(codes, scale)
+    c_t, s_t, dq_t = dev(cpad), dev(spad), dev(dq)
+    x_t = dev(x)
+    L = x.shape[0]
+    _, lse, _, _ = api.row_stats(x_t)
+    ws = api.workspace(L, s, e, d, DEV)
+    outs = []
+    for fn in ("fp8_fused", "fp8", "bf16_fused", "bf16"):
+        o = torch.full((L, d), float("nan"), device=DEV)
+        if fn == "fp8_fused":
+            B.se_soft_embed_fp8_fused(x_t, lse, s, e, c_t, s_t, gamma, o, ws)
+        elif fn == "bf16_fused":
+            B.se_soft_embed_fused(x_t, lse, s, e, dq_t, gamma, o, ws)
+        else:
+            V = x.shape[1]
+            p = torch.zeros((L, ((V + 7) // 8) * 8), device=DEV, dtype=torch.bfloat16)[:, :V]
+            B.se_probs_bf16(x_t, lse, s, e, p)
+            if fn == "fp8":
+                B.se_soft_embed_fp8(p, s, e, c_t, s_t, gamma, o, ws)
+            else:
+                B.se_soft_embed(p, s, e, dq_t, gamma, o, ws)
+        torch.cuda.synchronize()
+        outs.append(o)
+    return outs, dq
+
+
+CASES = {
+    # name: (L, V, s, e, d, seed)
+    "tiny": (16, 4096, 0, 4096, 256, 1),
+    "ragged": (17, 20008, 8, 20008, 48, 2),
+    "slice-1": (5, 1000, 16, 17, 16, 3),
+    "slice-63": (33, 1000, 64, 127, 2816, 4),
+    "slice-4097": (255, 8200, 8, 4105, 272, 5),
+    "two-tiles-rows": (300, 2048, 0, 2048, 512, 6),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_fp8_contraction_parity(case):
+    L, V, s, e, d, seed = CASES[case]
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    tab = (rng.standard_normal((e - s, d)) * 0.02).astype(np.float32)
+    bits = (tab.view(np.uint32) >> 16).astype(np.uint16)
+    codes, scale = fp8.quantize_table(bits)
+    say("fp8 contraction", case, (L, V, s, e, d))
+    (f8f, f8u, bff, bfu), dq = _pair(x, s, e, codes, scale, 7.5, pad_rows=24)
+    assert torch.equal(f8f, bff), "fp8 fused != bf16 fused on the dequantized table"
+    assert torch.equal(f8u, bfu), "fp8 != bf16 on the dequantized table"
+    assert torch.equal(f8f, f8u), "fp8 fused != fp8 unfused"
+    ref = oracle.soft_embed(x, s, e, fp8.dequantize(codes, scale).astype(np.float32), 7.5)
+    r = rel_fro(f8f.cpu().numpy(), ref)
+    say("rel_fro", f"{r:.3e}")
+    assert r <= GATE
+
+
+def test_fp8_quantization_error_against_the_bf16_table():
+    """Not a parity bar: the size of the e4m3 table's effect on the soft embedding."""
+    L, V, d = 64, 8192, 256
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    bits = ((rng.standard_normal((V, d)) * 0.02).astype(np.float32).view(np.uint32) >> 16
+            ).astype(np.uint16)
+    codes, scale = fp8.quantize_table(bits)
+    (f8f, _, _, _), _ = _pair(x, 0, V, codes, scale, 16.0)
+    ref_bf16 = oracle.soft_embed(x, 0, V, bits, 16.0)
+    r = rel_fro(f8f.cpu().numpy(), ref_bf16)
+    say("e4m3 vs bf16 table rel_fro", f"{r:.3e}")
+    assert r < 0.05
+
+
+def test_fp8_rank_full_size():
+    """One tensor-parallel rank at its real shape (L=256, slice [65536, 131072) of the
+    262,400-row table, d=2816): the quantizer over the whole shard bit-exact with the
+    oracle, the e4m3 fused call bit-exact with the bf16 fused call on the dequantized
+    table, and sampled rows against the fp64 oracle."""
+    w = wl.get("rank")
+    say("fp8 rank: generating table")
+    bits, _ = wl.make_table(w)
+    shard = np.ascontiguousarray(bits[w.vocab_start:w.vocab_end])
+    del bits
+    say("fp8 rank: gpu quantize")
+    c_t, s_t = gpu_quantize(shard)
+    say("fp8 rank: oracle quantize")
+    codes, scale = fp8.quantize_table(shard)
+    assert np.array_equal(c_t.cpu().numpy(), codes)
+    np.testing.assert_array_equal(s_t.cpu().numpy(), scale)
+    del c_t, s_t
+    x = wl.make_logits(w)
+    say("fp8 rank: gpu calls")
+    (f8f, f8u, bff, bfu), dq = _pair(x, w.vocab_start, w.vocab_end, codes, scale, w.gamma)
+    assert torch.equal(f8f, bff)
+    assert torch.equal(f8u, bfu)
+    rows = np.array([0, 100, 255])
+    say("fp8 rank: oracle rows", list(rows))
+    ref = oracle.soft_embed(x[rows], w.vocab_start, w.vocab_end, dq, w.gamma)
+    r = rel_fro(f8f.cpu().numpy()[rows], ref)
+    say("rel_fro", f"{r:.3e}")
+    assert r <= GATE
