@@ -298,6 +298,32 @@ def main():
                 "quantize_shard_us": round(us_q, 2)}
     del codes, wscale, out8, pr8
 
+    # side measurement: the one-pass call over the same slice (softmax over the slice, row
+    # statistics from the same read of the logits), and the merge of 4 slice results.  For
+    # a slice that is the whole vocabulary the one-pass call is a whole step.
+    wso = api.onepass_workspace(L, w.vocab_start, w.vocab_end, d, dev)
+    oo = torch.empty((L, d), device=dev)
+    so = [torch.empty(L, device=dev) for _ in range(3)]
+    ao = torch.empty(L, device=dev, dtype=torch.int32)
+    us_o = event_time_us(lambda: B.se_soft_embed_onepass(
+        x, w.vocab_start, w.vocab_end, shard, w.gamma, oo, so[0], so[1], so[2], ao, wso), K,
+        args.warmup)
+    outs4 = torch.randn((4, L, d), device=dev)
+    st4 = [torch.randn((4, L), device=dev) for _ in range(3)]
+    am4 = torch.zeros((4, L), device=dev, dtype=torch.int32)
+    us_m = event_time_us(lambda: B.se_merge_slices(outs4, st4[0], st4[1], st4[2], am4, oo, so[0],
+                                                   so[1], so[2], ao), K, args.warmup)
+    o_bytes = fused_call_bytes(w) + 16 * L
+    onepass_side = {"call_us": round(us_o, 2),
+                    "gflops_call": round(flops / (us_o * 1e-6) / 1e9, 2),
+                    "roofline_call": {"bound": "hbm", "algorithmic_bytes": o_bytes,
+                                      "achieved": round(o_bytes / (us_o * 1e-6) / 1e9, 2),
+                                      "peak": PEAK_HBM_GBS,
+                                      "frac": round(o_bytes / (us_o * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                                    4)},
+                    "merge_4_slices_us": round(us_m, 2)}
+    del wso, oo, so, ao, outs4, st4, am4
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
@@ -328,6 +354,7 @@ def main():
         "accept_converge": acc_side,
         "reduce_partials": red_side,
         "fp8_table": fp8_side,
+        "onepass": onepass_side,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

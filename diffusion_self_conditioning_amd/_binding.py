@@ -23,7 +23,8 @@ STATUS_NAMES = ["SE_OK", "SE_ERR_NULL", "SE_ERR_SHAPE", "SE_ERR_SLICE", "SE_ERR_
 EXPORTS = ("se_status_string", "se_version", "se_row_stats", "se_probs_bf16",
            "se_soft_embed_workspace_bytes", "se_soft_embed", "se_soft_embed_fused",
            "se_accept_converge", "se_reduce_partials", "se_quantize_table_fp8",
-           "se_soft_embed_fp8", "se_soft_embed_fp8_fused")
+           "se_soft_embed_fp8", "se_soft_embed_fp8_fused", "se_soft_embed_onepass_workspace_bytes",
+           "se_soft_embed_onepass", "se_merge_slices")
 
 
 class SoftEmbedError(RuntimeError):
@@ -56,9 +57,16 @@ def _declare(lib):
                                       i64, vp, sz, vp]
     lib.se_soft_embed_fp8_fused.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, vp, i64, i64, i64,
                                             f32, vp, i64, vp, sz, vp]
+    lib.se_soft_embed_onepass_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.se_soft_embed_onepass_workspace_bytes.restype = sz
+    lib.se_soft_embed_onepass.argtypes = [vp, i64, i64, i64, i64, i64, vp, i64, i64, i64, f32, vp,
+                                          i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.se_merge_slices.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp, vp,
+                                    vp, vp, vp]
     for fn in ("se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
                "se_accept_converge", "se_reduce_partials", "se_quantize_table_fp8",
-               "se_soft_embed_fp8", "se_soft_embed_fp8_fused"):
+               "se_soft_embed_fp8", "se_soft_embed_fp8_fused", "se_soft_embed_onepass",
+               "se_merge_slices"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -235,3 +243,40 @@ def se_soft_embed_fp8_fused(logits, row_lse, vocab_start, vocab_end, w_codes, w_
         _ptr(logits), _ld(logits), _ptr(row_lse), n, vocab, vocab_start, vocab_end,
         _ptr(w_codes), _ptr(w_scale), w_rows, _ld(w_codes), d, float(gamma), _ptr(out), _ld(out),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def se_soft_embed_onepass_workspace_bytes(n_rows: int, vocab_start: int, vocab_end: int,
+                                          d: int) -> int:
+    return int(lib.se_soft_embed_onepass_workspace_bytes(n_rows, vocab_start, vocab_end, d))
+
+
+def se_soft_embed_onepass(logits, vocab_start, vocab_end, w_shard, gamma, out, row_max, row_lse,
+                          row_entropy, row_argmax, workspace, *, vocab=None, d=None, w_rows=None,
+                          stream=None):
+    """Slice-normalised soft embedding and slice row statistics from one read of the logits."""
+    w_shard = _as_u16(w_shard)
+    n, v = logits.shape
+    vocab = v if vocab is None else vocab
+    d = w_shard.shape[1] if d is None else d
+    w_rows = w_shard.shape[0] if w_rows is None else w_rows
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("se_soft_embed_onepass", lib.se_soft_embed_onepass(
+        _ptr(logits), _ld(logits), n, vocab, vocab_start, vocab_end, _ptr(w_shard), w_rows,
+        _ld(w_shard), d, float(gamma), _ptr(out), _ld(out), _ptr(row_max), _ptr(row_lse),
+        _ptr(row_entropy), _ptr(row_argmax), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def se_merge_slices(outs, part_max, part_lse, part_entropy, part_argmax, out, row_max, row_lse,
+                    row_entropy, row_argmax, *, stream=None):
+    """Merge T slice results: ``outs`` [T, n_rows, >= d] fp32, statistics [T, n_rows]."""
+    if outs.dim() != 3 or outs.stride(2) != 1:
+        raise ValueError("outs must be [T, rows, d] with unit column stride")
+    t, n, _ = outs.shape
+    d = out.shape[1]
+    for a in (part_max, part_lse, part_entropy, part_argmax):
+        if tuple(a.shape) != (t, n) or not a.is_contiguous():
+            raise ValueError("slice statistics must be contiguous [T, rows]")
+    _check("se_merge_slices", lib.se_merge_slices(
+        _ptr(outs), t, outs.stride(0), n, d, outs.stride(1), _ptr(part_max), _ptr(part_lse),
+        _ptr(part_entropy), _ptr(part_argmax), _ptr(out), _ld(out), _ptr(row_max),
+        _ptr(row_lse), _ptr(row_entropy), _ptr(row_argmax), _stream(stream)))

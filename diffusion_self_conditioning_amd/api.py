@@ -8,10 +8,11 @@ from __future__ import annotations
 
 import torch
 
-from ._binding import (SoftEmbedError, se_probs_bf16, se_quantize_table_fp8,  # noqa: F401
-                       se_row_stats, se_soft_embed, se_soft_embed_fp8, se_soft_embed_fp8_fused,
-                       se_soft_embed_fused, se_soft_embed_workspace_bytes, se_status_string,
-                       se_version)
+from ._binding import (SoftEmbedError, se_merge_slices, se_probs_bf16,  # noqa: F401
+                       se_quantize_table_fp8, se_row_stats, se_soft_embed, se_soft_embed_fp8,
+                       se_soft_embed_fp8_fused, se_soft_embed_fused, se_soft_embed_onepass,
+                       se_soft_embed_onepass_workspace_bytes, se_soft_embed_workspace_bytes,
+                       se_status_string, se_version)
 
 
 def row_stats(logits: torch.Tensor, stream=None):
@@ -78,3 +79,22 @@ def soft_embed_fp8(logits, row_lse, vocab_start, vocab_end, w_codes, w_scale, ga
         se_soft_embed_fp8(p, vocab_start, vocab_end, w_codes, w_scale, gamma, out, ws,
                           stream=stream)
     return out
+
+
+def onepass_workspace(n_rows, vocab_start, vocab_end, d, device):
+    nbytes = se_soft_embed_onepass_workspace_bytes(n_rows, vocab_start, vocab_end, d)
+    return torch.empty((nbytes + 3) // 4, device=device, dtype=torch.float32)
+
+
+def soft_embed_onepass(logits, vocab_start, vocab_end, w_shard, gamma, *, ws=None, stream=None):
+    """(out, row_max, row_lse, row_entropy, row_argmax) over the slice [s, e), one logits read."""
+    n, d = logits.shape[0], w_shard.shape[1]
+    f = dict(device=logits.device, dtype=torch.float32)
+    out = torch.empty((n, d), **f)
+    mx, lse, ent = torch.empty(n, **f), torch.empty(n, **f), torch.empty(n, **f)
+    am = torch.empty(n, device=logits.device, dtype=torch.int32)
+    if ws is None:
+        ws = onepass_workspace(n, vocab_start, vocab_end, d, logits.device)
+    se_soft_embed_onepass(logits, vocab_start, vocab_end, w_shard, gamma, out, mx, lse, ent, am,
+                          ws, stream=stream)
+    return out, mx, lse, ent, am

@@ -31,6 +31,22 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   return g;
 }
 
+// Workspace of the one-pass call: bf16 probabilities [n_rows, ldp] of the slice, the
+// split partials (kept even for one split), and per-(split, row) statistics.
+OnepassLayout onepass_layout(int64_t n_rows, int64_t K, int64_t d) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  OnepassLayout o{};
+  o.g = plan_gemm(n_rows, d, K);
+  o.ldp = (K + 7) / 8 * 8;
+  o.rows_pad = o.g.tiles_m * kBM;
+  o.off_probs = 0;
+  o.off_parts = up((size_t)(n_rows * o.ldp) * 2);
+  o.off_stats = o.off_parts + up((size_t)(o.g.splits * o.g.tiles * kTileFloats) * 4);
+  o.off_arg = o.off_stats + up((size_t)(o.g.splits * o.rows_pad) * 16);
+  o.total = o.off_arg + up((size_t)(o.g.splits * o.rows_pad) * 4);
+  return o;
+}
+
 }  // namespace se
 
 namespace {
@@ -112,6 +128,7 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
   p.tiles = (int)g.tiles;
   p.splits = (int)g.splits;
   p.kblocks = (int)g.kblocks;
+  p.keep_partials = false;
   return from_hip(se::launch_soft_embed(p, fused, w_scale != nullptr, st));
 }
 
@@ -133,7 +150,7 @@ const char* se_status_string(se_status s) {
 }
 
 const char* se_version(void) {
-  return "libsoftembed 0.3 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table)";
+  return "libsoftembed 0.3 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table, one-pass)";
 }
 
 se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
@@ -265,6 +282,104 @@ se_status se_soft_embed_fp8_fused(const float* logits, int64_t ld_logits, const 
   if (!aligned16(logits) || (ld_logits % 4) != 0 || !aligned4(row_lse)) return SE_ERR_ALIGN;
   return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start, vocab_end, w_codes,
                         w_scale, ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
+}
+
+size_t se_soft_embed_onepass_workspace_bytes(int64_t n_rows, int64_t vocab_start,
+                                             int64_t vocab_end, int64_t d) {
+  if (n_rows < 1 || d < 1 || vocab_start < 0 || vocab_end <= vocab_start) return 0;
+  if (n_rows > INT32_MAX || d > INT32_MAX || vocab_end > INT32_MAX) return 0;
+  return se::onepass_layout(n_rows, vocab_end - vocab_start, d).total;
+}
+
+se_status se_soft_embed_onepass(const float* logits, int64_t ld_logits, int64_t n_rows,
+                                int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                                const uint16_t* w_shard, int64_t w_rows, int64_t ld_w, int64_t d,
+                                float gamma, float* out, int64_t ld_out, float* row_max,
+                                float* row_lse, float* row_entropy, int32_t* row_argmax,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
+  if (rc != SE_OK) return rc;
+  if (ld_logits < vocab) return SE_ERR_SHAPE;
+  if (vocab_end == vocab_start) return SE_ERR_SLICE;   // a softmax over no positions
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  if (!logits || !w_shard || !out || !row_max || !row_lse || !row_entropy || !row_argmax)
+    return SE_ERR_NULL;
+  rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_shard, out);
+  if (rc != SE_OK) return rc;
+  if (!aligned16(logits) || (ld_logits % 4) != 0) return SE_ERR_ALIGN;
+  if (!aligned4(row_max) || !aligned4(row_lse) || !aligned4(row_entropy) || !aligned4(row_argmax))
+    return SE_ERR_ALIGN;
+  const int64_t K = vocab_end - vocab_start;
+  const se::OnepassLayout o = se::onepass_layout(n_rows, K, d);
+  if (o.g.grid > INT32_MAX || n_rows * o.g.splits > INT32_MAX) return SE_ERR_SHAPE;
+  if ((int64_t)(se::kBM - 1) * o.ldp * 2 + K * 2 > (int64_t)UINT32_MAX ||
+      K * ld_w * 2 > (int64_t)UINT32_MAX)
+    return SE_ERR_SHAPE;
+  if (workspace_bytes < o.total) return SE_ERR_WORKSPACE;
+  if (!workspace) return SE_ERR_NULL;
+  if (!aligned16(workspace)) return SE_ERR_ALIGN;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t* probs = reinterpret_cast<uint16_t*>(ws + o.off_probs);
+  float* stats = reinterpret_cast<float*>(ws + o.off_stats);
+  int32_t* stat_arg = reinterpret_cast<int32_t*>(ws + o.off_arg);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = from_hip(se::launch_split_sweep(logits, ld_logits, vocab_start, K, n_rows,
+                                       (int)o.g.splits, (int)o.g.kblocks, probs, o.ldp, stats,
+                                       stat_arg, o.rows_pad, st));
+  if (rc != SE_OK) return rc;
+  se::GemmParams p{};
+  p.a = probs;
+  p.lda = o.ldp;
+  p.col0 = 0;
+  p.w = w_shard;
+  p.ldw = ld_w;
+  p.M = n_rows;
+  p.N = d;
+  p.K = K;
+  p.gamma = gamma;
+  p.out = out;
+  p.ldo = ld_out;
+  p.ws = reinterpret_cast<float*>(ws + o.off_parts);
+  p.tiles_n = (int)o.g.tiles_n;
+  p.tiles = (int)o.g.tiles;
+  p.splits = (int)o.g.splits;
+  p.kblocks = (int)o.g.kblocks;
+  p.keep_partials = true;
+  p.stats = stats;
+  p.stat_arg = stat_arg;
+  p.rows_pad = o.rows_pad;
+  rc = from_hip(se::launch_soft_embed(p, false, false, st));
+  if (rc != SE_OK) return rc;
+  return from_hip(se::launch_onepass_reduce(p, row_max, row_lse, row_entropy, row_argmax,
+                                            vocab_start, st));
+}
+
+se_status se_merge_slices(const float* outs, int64_t n_parts, int64_t part_stride,
+                          int64_t n_rows, int64_t d, int64_t ld_part, const float* part_max,
+                          const float* part_lse, const float* part_entropy,
+                          const int32_t* part_argmax, float* out, int64_t ld_out,
+                          float* row_max, float* row_lse, float* row_entropy,
+                          int32_t* row_argmax, void* stream) {
+  if (n_parts < 1 || n_parts > INT32_MAX || n_rows < 0 || d < 1 || ld_part < d || ld_out < d)
+    return SE_ERR_SHAPE;
+  if (n_rows > kMaxGridY || d > INT32_MAX) return SE_ERR_SHAPE;
+  if (n_parts > 1 && part_stride < n_rows * ld_part) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;
+  if (!outs || !part_max || !part_lse || !part_entropy || !part_argmax || !out || !row_max ||
+      !row_lse || !row_entropy || !row_argmax)
+    return SE_ERR_NULL;
+  if ((d % 4) != 0 || (ld_part % 4) != 0 || (ld_out % 4) != 0 ||
+      (n_parts > 1 && (part_stride % 4) != 0))
+    return SE_ERR_ALIGN;
+  if (!aligned16(outs) || !aligned16(out)) return SE_ERR_ALIGN;
+  if (!aligned4(part_max) || !aligned4(part_lse) || !aligned4(part_entropy) ||
+      !aligned4(part_argmax) || !aligned4(row_max) || !aligned4(row_lse) ||
+      !aligned4(row_entropy) || !aligned4(row_argmax))
+    return SE_ERR_ALIGN;
+  return from_hip(se::launch_merge_slices(outs, n_parts, part_stride, n_rows, d, ld_part,
+                                          part_max, part_lse, part_entropy, part_argmax, out,
+                                          ld_out, row_max, row_lse, row_entropy, row_argmax,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 se_status se_accept_converge(const float* row_entropy, const int32_t* row_argmax,

@@ -1,0 +1,208 @@
+// onepass.hip -- the single sweep over the logits of the one-pass soft embedding.
+//
+// The expected token embedding needs softmax(logits) (calvarado04.com, "Where the
+// shapes stop agreeing"), and the sampler needs each row's max, log-sum-exp, entropy
+// and argmax (agentlenshq overview of DiffusionGemma in vLLM, sampling loop).  The
+// two-pass path reads the full-width logits once for those statistics and again for
+// the probabilities.  Here the vocabulary slice is cut into the contraction's split-K
+// ranges, and each range is normalised against its own maximum m_s:
+//     P[i, k] = bf16_rne(e^(l[i, k] - m_s)),  Z_s = sum e^(l - m_s),
+//     S1_s = sum e^(l - m_s) (l - m_s),  argmax_s = first position of m_s,
+// so the probabilities can be written before any other range has been seen.  The
+// contraction of P runs unchanged per split, and the split reduction rescales every
+// split by e^(m_s - M), M = max_s m_s, and divides by Z = sum_s e^(m_s - M) Z_s: the
+// merge rule of the partition identity ("The fix") written for softmax numerators.
+//
+// One wave per (row, split range): a first pass finds the range's maximum and its
+// first position (16-byte loads, 256 positions per instruction, then a cross-lane
+// reduction); a second pass over the same, now cache-resident, range forms the
+// probabilities, writes them as bf16 and sums Z_s and S1_s in fp32.
+#include "se_device.h"
+#include "se_launch.h"
+
+namespace se {
+namespace {
+
+constexpr int kSweepThreads = 256;                  // 4 waves: 4 (row, split) ranges
+constexpr int kSweepWaves = kSweepThreads / 64;
+
+// whole-wave reductions (64 lanes) on top of the half-wave ones
+__device__ __forceinline__ float wave_sum(float v) {
+  v = half_sum(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  half_argmax(v, i);
+  const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const int i1 = __builtin_amdgcn_readlane(i, 32);
+  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  i = __builtin_amdgcn_readlane(i, 0);
+  argmax_step(v, i, v1, i1);
+}
+
+__global__ void __launch_bounds__(kSweepThreads)
+split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, int64_t K,
+                   int64_t n_rows, int splits, int kblocks, uint16_t* __restrict__ probs,
+                   int64_t ldp, float4* __restrict__ stats, int32_t* __restrict__ stat_arg,
+                   int64_t rows_pad) {
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = (int64_t)blockIdx.x * kSweepWaves + (threadIdx.x >> 6);
+  if (unit >= n_rows * splits) return;              // uniform per wave
+  const int64_t row = unit % n_rows;
+  const int s = (int)(unit / n_rows);
+  // the contraction's split boundaries (positions of the slice)
+  const int64_t k_lo = (((int64_t)s * kblocks) / splits) * kSplitQuantum;
+  const int64_t k_hi = min((((int64_t)(s + 1) * kblocks) / splits) * kSplitQuantum, K);
+  const float* __restrict__ x = logits + row * ld + col0;
+  uint16_t* __restrict__ p = probs + row * ldp;
+
+  // pass 1: maximum and its first position; four 16-byte loads in flight per lane
+  float mv = -INFINITY;
+  int mi = 0;
+  auto max4 = [&](const float4& v, int64_t k) {
+    argmax_step(mv, mi, v.x, (int)k);
+    argmax_step(mv, mi, v.y, (int)k + 1);
+    argmax_step(mv, mi, v.z, (int)k + 2);
+    argmax_step(mv, mi, v.w, (int)k + 3);
+  };
+  int64_t k = k_lo + 4 * lane;
+  for (; k + 3 * 256 + 4 <= k_hi; k += 4 * 256) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(x + k + 256 * u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) max4(v[u], k + 256 * u);
+  }
+  for (; k < k_hi; k += 256) {
+    if (k + 4 <= k_hi) {
+      max4(*reinterpret_cast<const float4*>(x + k), k);
+    } else {
+      for (int64_t j = k; j < k_hi; ++j) argmax_step(mv, mi, x[j], (int)j);
+    }
+  }
+  wave_argmax(mv, mi);
+  const float nl = neg_lse_log2(mv);
+
+  // pass 2: probabilities against the range maximum, Z and S1 (log2 units)
+  float z = 0.f, s1 = 0.f;
+  auto prob4 = [&](const float4& v, int64_t k) {
+    const float t0 = __builtin_fmaf(v.x, kLog2e, nl), t1 = __builtin_fmaf(v.y, kLog2e, nl);
+    const float t2 = __builtin_fmaf(v.z, kLog2e, nl), t3 = __builtin_fmaf(v.w, kLog2e, nl);
+    const float q0 = exp2_hw(t0), q1 = exp2_hw(t1), q2 = exp2_hw(t2), q3 = exp2_hw(t3);
+    z += (q0 + q1) + (q2 + q3);
+    s1 = __builtin_fmaf(q0, t0, __builtin_fmaf(q1, t1, __builtin_fmaf(q2, t2, __builtin_fmaf(q3, t3, s1))));
+    uint2 o;
+    o.x = pack_bf16x2(q0, q1);
+    o.y = pack_bf16x2(q2, q3);
+    *reinterpret_cast<uint2*>(p + k) = o;
+  };
+  k = k_lo + 4 * lane;
+  for (; k + 3 * 256 + 4 <= k_hi; k += 4 * 256) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(x + k + 256 * u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) prob4(v[u], k + 256 * u);
+  }
+  for (; k < k_hi; k += 256) {
+    if (k + 4 <= k_hi) {
+      prob4(*reinterpret_cast<const float4*>(x + k), k);
+    } else {
+      for (int64_t j = k; j < k_hi; ++j) {
+        const float t = __builtin_fmaf(x[j], kLog2e, nl);
+        const float q = exp2_hw(t);
+        z += q;
+        s1 = __builtin_fmaf(q, t, s1);
+        p[j] = __builtin_bit_cast(uint16_t, (__bf16)q);
+      }
+    }
+  }
+  z = wave_sum(z);
+  s1 = wave_sum(s1);
+  if (lane == 0) {
+    stats[(int64_t)s * rows_pad + row] = make_float4(mv, z, s1 * kLn2, mv);
+    stat_arg[(int64_t)s * rows_pad + row] = mi;
+  }
+}
+
+// Merge of T slice results (one-pass calls on disjoint vocabulary slices, in vocabulary
+// order) into the result over their union.  With lse = ln sum_r e^(lse_r), slice r
+// carries probability mass pi_r = e^(lse_r - lse):
+//   out = sum_r pi_r out_r,   H = sum_r pi_r (H_r - ln pi_r),
+//   max = max_r max_r, argmax = the first slice's argmax among those reaching max.
+// Each thread produces 4 consecutive columns of one row; slices are added in order.
+constexpr int kMergeThreads = 256;
+
+__global__ void __launch_bounds__(kMergeThreads)
+merge_slices_kernel(const float* __restrict__ outs, int n_parts, int64_t part_stride,
+                    int64_t n_rows, int64_t d, int64_t ld_part, const float* __restrict__ pmax,
+                    const float* __restrict__ plse, const float* __restrict__ pent,
+                    const int32_t* __restrict__ parg, float* __restrict__ out, int64_t ld_out,
+                    float* __restrict__ row_max, float* __restrict__ row_lse,
+                    float* __restrict__ row_entropy, int32_t* __restrict__ row_argmax) {
+  const int64_t row = blockIdx.y;
+  const int64_t c = ((int64_t)blockIdx.x * kMergeThreads + threadIdx.x) * 4;
+  if (c >= d) return;
+  float top = -INFINITY;
+  for (int r = 0; r < n_parts; ++r) top = fmaxf(top, plse[r * n_rows + row]);
+  float zs = 0.f;
+  for (int r = 0; r < n_parts; ++r) zs += exp2_hw((plse[r * n_rows + row] - top) * kLog2e);
+  const float lse = top + logf(zs);
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float h = 0.f;
+  for (int r = 0; r < n_parts; ++r) {
+    const float lp = plse[r * n_rows + row] - lse;          // ln pi_r
+    const float pi = exp2_hw(lp * kLog2e);
+    const float4 v = *reinterpret_cast<const float4*>(outs + r * part_stride + row * ld_part + c);
+    a.x = __builtin_fmaf(pi, v.x, a.x);
+    a.y = __builtin_fmaf(pi, v.y, a.y);
+    a.z = __builtin_fmaf(pi, v.z, a.z);
+    a.w = __builtin_fmaf(pi, v.w, a.w);
+    h = __builtin_fmaf(pi, pent[r * n_rows + row] - lp, h);
+  }
+  *reinterpret_cast<float4*>(out + row * ld_out + c) = a;
+  if (c == 0) {
+    float mx = -INFINITY;
+    int32_t am = 0;
+    for (int r = 0; r < n_parts; ++r) {
+      const float m = pmax[r * n_rows + row];
+      if (m > mx) { mx = m; am = parg[r * n_rows + row]; }
+    }
+    row_max[row] = mx;
+    row_lse[row] = lse;
+    row_entropy[row] = h;
+    row_argmax[row] = am;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_stride,
+                               int64_t n_rows, int64_t d, int64_t ld_part,
+                               const float* part_max, const float* part_lse,
+                               const float* part_entropy, const int32_t* part_argmax,
+                               float* out, int64_t ld_out, float* row_max, float* row_lse,
+                               float* row_entropy, int32_t* row_argmax, hipStream_t stream) {
+  const int64_t groups = (d + 3) / 4;
+  const dim3 grid((unsigned)((groups + kMergeThreads - 1) / kMergeThreads), (unsigned)n_rows);
+  hipLaunchKernelGGL(merge_slices_kernel, grid, dim3(kMergeThreads), 0, stream, outs,
+                     (int)n_parts, part_stride, n_rows, d, ld_part, part_max, part_lse,
+                     part_entropy, part_argmax, out, ld_out, row_max, row_lse, row_entropy,
+                     row_argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int64_t K,
+                              int64_t n_rows, int splits, int kblocks, uint16_t* probs,
+                              int64_t ldp, float* stats, int32_t* stat_arg, int64_t rows_pad,
+                              hipStream_t stream) {
+  const int64_t units = n_rows * splits;
+  const dim3 grid((unsigned)((units + kSweepWaves - 1) / kSweepWaves));
+  hipLaunchKernelGGL(split_sweep_kernel, grid, dim3(kSweepThreads), 0, stream, logits, ld, col0,
+                     K, n_rows, splits, kblocks, probs, ldp, reinterpret_cast<float4*>(stats),
+                     stat_arg, rows_pad);
+  return hipGetLastError();
+}
+
+}  // namespace se

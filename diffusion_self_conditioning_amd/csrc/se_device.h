@@ -83,6 +83,50 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+// ---- reductions over each half (32 lanes) of a wave ------------------------------------
+// Lanes 0-31 and 32-63 reduce separately and every lane ends with its half's result:
+// four DPP exchanges inside each 16-lane row (xor 1, xor 2, half-row mirror, row
+// mirror), then one swizzle that swaps the two rows of a half (xor 16).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl,
+                                                            0xF, 0xF, true));
+}
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, kCtrl, 0xF, 0xF, true);
+}
+__device__ __forceinline__ float swz16_f(float v) {     // lane ^ 16 within 32 lanes
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+__device__ __forceinline__ int swz16_i(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
+
+__device__ __forceinline__ float half_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return v + swz16_f(v);
+}
+__device__ __forceinline__ float half_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(v, swz16_f(v));
+}
+// (value, index) maximum, ties to the lower index
+__device__ __forceinline__ void argmax_step(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+__device__ __forceinline__ void half_argmax(float& v, int& i) {
+  argmax_step(v, i, dpp_f<0xB1>(v), dpp_i<0xB1>(i));
+  argmax_step(v, i, dpp_f<0x4E>(v), dpp_i<0x4E>(i));
+  argmax_step(v, i, dpp_f<0x141>(v), dpp_i<0x141>(i));
+  argmax_step(v, i, dpp_f<0x140>(v), dpp_i<0x140>(i));
+  argmax_step(v, i, swz16_f(v), swz16_i(i));
+}
+
 // 16 OCP e4m3 codes (byte j of `c` = element j) times a power-of-two `scale`, as 16
 // bf16 values: elements 0..7 in `lo`, 8..15 in `hi`.  Every e4m3 value times a power
 // of two in the normal range is a bf16 value, so the conversion is exact.

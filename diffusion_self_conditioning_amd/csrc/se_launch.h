@@ -35,6 +35,14 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 
+struct OnepassLayout {
+  GemmPlan g;
+  int64_t ldp, rows_pad;
+  size_t off_probs, off_parts, off_stats, off_arg, total;
+};
+
+OnepassLayout onepass_layout(int64_t n_rows, int64_t K, int64_t d);
+
 struct GemmParams {
   const void* a;          // fused: fp32 logits; unfused: bf16 probabilities
   int64_t lda;            // elements
@@ -49,6 +57,14 @@ struct GemmParams {
   int64_t ldo;
   float* ws;              // split partials [splits][tiles][kTileFloats]
   int tiles_n, tiles, splits, kblocks;
+  // one-pass: partials are written even for one split and left for
+  // launch_onepass_reduce, which reads the per-(split, row) statistics
+  // stats[s * rows_pad + row] = {reference, Z, S1 (nats), max}, stat_arg = the max's
+  // slice position
+  bool keep_partials;
+  const float* stats;
+  const int32_t* stat_arg;
+  int64_t rows_pad;
 };
 
 hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int vocab,
@@ -62,6 +78,25 @@ hipError_t launch_probs_bf16(const float* logits, int64_t ld, const float* row_l
 // fused: `a` holds fp32 logits (else bf16 probabilities); w8: `w` holds e4m3 codes
 // with per-row scales (else bf16)
 hipError_t launch_soft_embed(const GemmParams& p, bool fused, bool w8, hipStream_t stream);
+
+// one-pass sweep: per (row, split range) maximum, Z, S1 and argmax, and the bf16
+// probabilities against the range maximum (probs [n_rows, ldp], slice position 0 at
+// column 0)
+hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int64_t K,
+                              int64_t n_rows, int splits, int kblocks, uint16_t* probs,
+                              int64_t ldp, float* stats, int32_t* stat_arg, int64_t rows_pad,
+                              hipStream_t stream);
+
+hipError_t launch_onepass_reduce(const GemmParams& p, float* row_max, float* row_lse,
+                                 float* row_entropy, int32_t* row_argmax, int64_t col0,
+                                 hipStream_t stream);
+
+hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_stride,
+                               int64_t n_rows, int64_t d, int64_t ld_part,
+                               const float* part_max, const float* part_lse,
+                               const float* part_entropy, const int32_t* part_argmax,
+                               float* out, int64_t ld_out, float* row_max, float* row_lse,
+                               float* row_entropy, int32_t* row_argmax, hipStream_t stream);
 
 hipError_t launch_quantize_fp8(const uint16_t* w, int64_t ldw, int64_t rows, int64_t d,
                                uint8_t* codes, int64_t ldq, float* row_scale, hipStream_t stream);

@@ -501,7 +501,7 @@ soft_embed_kernel(const GemmParams p) {
   // ---- epilogue ---------------------------------------------------------------------
   // 32x32 MFMA accumulator layout: register r of lane l holds
   //   row 8 (r / 4) + 4 (l / 32) + (r % 4),  column l % 32  of the block.
-  if (p.splits == 1) {
+  if (p.splits == 1 && !p.keep_partials) {
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
@@ -556,6 +556,63 @@ splitk_reduce_kernel(const float* __restrict__ ws, int tiles, int tiles_n, int s
       make_float4(gamma * a.x, gamma * a.y, gamma * a.z, gamma * a.w);
 }
 
+// One-pass reduction.  Split s holds the partial U_s of probabilities taken against a
+// reference m_s, with Z_s and S1_s against the same reference and its maximum M_s
+// (stats[s][row] = {m_s, Z_s, S1_s, M_s}).  At the overall maximum M = max_s M_s:
+//   f_s = e^(m_s - M),  Z = sum_s f_s Z_s,  out = gamma sum_s f_s U_s / Z,
+//   lse = M + ln Z,  H = ln Z - sum_s f_s (S1_s + (m_s - M) Z_s) / Z,
+//   argmax = the position of the first split reaching M (splits are in vocabulary
+// order).  The splits are visited in order, so the result is bitwise repeatable.
+__global__ void __launch_bounds__(256)
+onepass_reduce_kernel(const float* __restrict__ ws, const float4* __restrict__ stats,
+                      const int32_t* __restrict__ stat_arg, int64_t rows_pad, int tiles,
+                      int tiles_n, int splits, int64_t M, int64_t N, float gamma, int64_t col0,
+                      float* __restrict__ out, int64_t ldo, float* __restrict__ row_max,
+                      float* __restrict__ row_lse, float* __restrict__ row_entropy,
+                      int32_t* __restrict__ row_argmax) {
+  constexpr int kBlocksPerTile = (int)(kTileFloats / (4 * 256));
+  const int t = blockIdx.x / kBlocksPerTile;
+  const int e0 = ((blockIdx.x % kBlocksPerTile) * 256 + threadIdx.x) * 4;
+  const int l0 = e0 & 63;
+  const int r = (e0 >> 6) & 15;
+  const int blk = e0 >> 10;
+  const int wave = blk / (kMI * kNI), mi = (blk / kNI) % kMI, ni = blk % kNI;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int64_t row = (int64_t)(t / tiles_n) * kBM + 128 * wm + 32 * mi + 8 * (r >> 2) +
+                      4 * (l0 >> 5) + (r & 3);
+  const int64_t col = (int64_t)(t % tiles_n) * kBN + kTN * wn + 32 * ni + (l0 & 31);
+  if (row >= M || col >= N) return;
+  float mx = -INFINITY;
+  int arg = 0;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float ms = stats[sp * rows_pad + row].w;
+    if (ms > mx) { mx = ms; arg = stat_arg[sp * rows_pad + row]; }
+  }
+  float z = 0.f, s1 = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* src = ws + (int64_t)t * kTileFloats + e0;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float4 st = stats[sp * rows_pad + row];
+    const float d = st.x - mx;
+    const float f = exp2_hw(d * kLog2e);
+    z = fmaf(f, st.y, z);
+    s1 = fmaf(f, fmaf(d, st.y, st.z), s1);
+    const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)sp * tiles * kTileFloats);
+    a.x = fmaf(f, v.x, a.x); a.y = fmaf(f, v.y, a.y);
+    a.z = fmaf(f, v.z, a.z); a.w = fmaf(f, v.w, a.w);
+  }
+  const float g = gamma / z;
+  *reinterpret_cast<float4*>(out + row * ldo + col) = make_float4(g * a.x, g * a.y, g * a.z, g * a.w);
+  if (col == 0) {
+    const float lz = logf(z);
+    row_max[row] = mx;
+    row_lse[row] = mx + lz;
+    row_entropy[row] = lz - s1 / z;
+    row_argmax[row] = (int32_t)(col0 + arg);
+  }
+}
+
+
 __global__ void zero_rows_kernel(float* __restrict__ out, int64_t ldo, int64_t N) {
   const int64_t row = blockIdx.y;
   const int64_t c = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -584,10 +641,21 @@ hipError_t launch_soft_embed(const GemmParams& p, bool fused, bool w8, hipStream
   else if (w8) launch_contraction<false, true>(p, stream);
   else launch_contraction<false, false>(p, stream);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
+  if (e != hipSuccess || p.splits == 1 || p.keep_partials) return e;
   const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(kReduceThreads), 0, stream, p.ws,
                      p.tiles, p.tiles_n, p.splits, p.M, p.N, p.gamma, p.out, p.ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_onepass_reduce(const GemmParams& p, float* row_max, float* row_lse,
+                                 float* row_entropy, int32_t* row_argmax, int64_t col0,
+                                 hipStream_t stream) {
+  const int blocks = p.tiles * (int)(kTileFloats / (4 * 256));
+  hipLaunchKernelGGL(onepass_reduce_kernel, dim3(blocks), dim3(256), 0, stream, p.ws,
+                     reinterpret_cast<const float4*>(p.stats), p.stat_arg, p.rows_pad, p.tiles,
+                     p.tiles_n, p.splits, p.M, p.N, p.gamma, col0, p.out, p.ldo, row_max,
+                     row_lse, row_entropy, row_argmax);
   return hipGetLastError();
 }
 

@@ -209,6 +209,68 @@ se_status se_soft_embed_fp8_fused(const float* logits, int64_t ld_logits, const 
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * se_soft_embed_onepass -- the soft embedding and the row statistics of a vocabulary
+ * slice from ONE read of its logits (no se_row_stats pass first).  The softmax is
+ * over the slice [s, e) itself:
+ *
+ *     q_iv     = e^(l_iv) / sum_{u=s}^{e-1} e^(l_iu)                 for v in [s, e)
+ *     out_i,:  = gamma * sum_{v=s}^{e-1} q_iv * W_shard[v - s, :]
+ *     row_max, row_argmax (a vocabulary id), row_lse, row_entropy: as se_row_stats,
+ *     over columns [s, e)
+ *
+ * With [s, e) = [0, vocab) this is se_row_stats followed by se_soft_embed_fused.  On
+ * a rank's slice it is the slice-local result that se_merge_slices combines across
+ * slices (calvarado04.com, "The fix": the vocabulary-sharded layout; each rank then
+ * needs only its own logits columns).  Internally the slice is cut into the
+ * contraction's split ranges; each range's probabilities are taken against the
+ * range's own maximum (bf16, round to nearest even), contracted in fp32, and the
+ * ranges are merged with the rescaling rule e^(m_r - m) before dividing by the sum.
+ *
+ * logits: fp32 [n_rows, ld_logits], columns [s, e) read.  Other arguments as
+ * se_soft_embed_fused, with row_max / row_lse / row_entropy (fp32) and row_argmax
+ * (int32) of [n_rows] written, and a workspace of se_soft_embed_onepass_workspace_bytes
+ * (it holds the bf16 probabilities of the slice, the split partials and per-split
+ * statistics: about 2 * n_rows * (e - s) bytes plus the partials).
+ * Errors as se_soft_embed_fused, and SE_ERR_SLICE for an empty slice (s == e);
+ * SE_ERR_NULL / SE_ERR_ALIGN for a NULL or misaligned statistics output or workspace.
+ */
+size_t se_soft_embed_onepass_workspace_bytes(int64_t n_rows, int64_t vocab_start,
+                                             int64_t vocab_end, int64_t d);
+
+se_status se_soft_embed_onepass(const float* logits, int64_t ld_logits, int64_t n_rows,
+                                int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                                const uint16_t* w_shard, int64_t w_rows, int64_t ld_w, int64_t d,
+                                float gamma, float* out, int64_t ld_out, float* row_max,
+                                float* row_lse, float* row_entropy, int32_t* row_argmax,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * se_merge_slices -- combine the se_soft_embed_onepass results of T disjoint slices,
+ * given in vocabulary order, into the result over their union (the full vocabulary
+ * when the slices partition it).  With lse = ln sum_r e^(lse_r), slice r carries the
+ * probability mass pi_r = e^(lse_r - lse) (calvarado04.com, "The fix": the partition
+ * of the product over vocabulary slices, here with each slice normalised by itself):
+ *
+ *     out = sum_r pi_r out_r,            row_lse = lse,
+ *     row_entropy = sum_r pi_r (H_r - ln pi_r),
+ *     row_max = max_r max_r,  row_argmax = the argmax of the first slice reaching it.
+ *
+ * Slice r's output is the fp32 matrix [n_rows, d] at outs + r * part_stride (row pitch
+ * ld_part); its statistics are part_max / part_lse / part_entropy / part_argmax
+ * [r * n_rows + i].  Slices are added in order r = 0 .. n_parts-1 (fp32).
+ * Errors: SE_ERR_SHAPE if n_parts < 1, n_rows < 0 or > 65535, d < 1, a pitch < d, or
+ * part_stride < n_rows * ld_part; SE_ERR_NULL for a NULL pointer (n_rows > 0);
+ * SE_ERR_ALIGN unless d, the pitches and part_stride are multiples of 4, outs / out
+ * are 16-byte and the statistics arrays 4-byte aligned.  n_rows == 0 is a no-op.
+ */
+se_status se_merge_slices(const float* outs, int64_t n_parts, int64_t part_stride,
+                          int64_t n_rows, int64_t d, int64_t ld_part, const float* part_max,
+                          const float* part_lse, const float* part_entropy,
+                          const int32_t* part_argmax, float* out, int64_t ld_out,
+                          float* row_max, float* row_lse, float* row_entropy,
+                          int32_t* row_argmax, void* stream);
+
+/*
  * se_accept_converge -- entropy-bound acceptance and the convergence test of the
  * diffusion sampler, on the statistics se_row_stats produces (agentlenshq overview
  * of DiffusionGemma in vLLM, section on the sampling loop and entropy-bound

@@ -260,3 +260,70 @@ def test_quantize_table_fp8_errors():
     assert q(P1, 2816, 16, 2816, P2 + 8, 2816, P3, None) == b.SE_ERR_ALIGN
     assert q(P1, 2816, 16, 2816, P2, 2816, P3 + 1, None) == b.SE_ERR_ALIGN
     assert q(None, 2816, 0, 2816, None, 2816, None, None) == b.SE_OK
+
+
+def onepass_call(**kw):
+    a = dict(x=P1, ld=262144, n=256, vocab=262144, s=0, e=262144, w=P3, w_rows=262144, ldw=2816,
+             d=2816, gamma=53.0, out=P4, ldo=2816, mx=P5, lse=P5 + 1024, ent=P5 + 2048,
+             am=P5 + 4096, ws=P2, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.se_soft_embed_onepass(a["x"], a["ld"], a["n"], a["vocab"], a["s"], a["e"], a["w"],
+                                     a["w_rows"], a["ldw"], a["d"], a["gamma"], a["out"],
+                                     a["ldo"], a["mx"], a["lse"], a["ent"], a["am"], a["ws"],
+                                     a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(s=8, e=8), b.SE_ERR_SLICE),                  # empty slice: no softmax
+    (dict(e=262152), b.SE_ERR_SLICE),
+    (dict(w_rows=1000), b.SE_ERR_SLICE),
+    (dict(n=-1), b.SE_ERR_SHAPE),
+    (dict(ld=100), b.SE_ERR_SHAPE),
+    (dict(mx=None), b.SE_ERR_NULL),
+    (dict(am=None), b.SE_ERR_NULL),
+    (dict(ws=None), b.SE_ERR_NULL),
+    (dict(ws_bytes=4096), b.SE_ERR_WORKSPACE),
+    (dict(lse=P5 + 1026), b.SE_ERR_ALIGN),
+    (dict(x=P1 + 4), b.SE_ERR_ALIGN),
+    (dict(ws=P2 + 8), b.SE_ERR_ALIGN),
+    (dict(s=4, e=1000), b.SE_ERR_ALIGN),
+    (dict(n=0, x=None, w=None, out=None, mx=None, lse=None, ent=None, am=None, ws=None,
+          ws_bytes=0), b.SE_OK),
+])
+def test_onepass_errors(kw, code):
+    assert onepass_call(**kw) == code
+
+
+def test_onepass_workspace_plan():
+    """bf16 probabilities of the slice (rows padded to 8 positions), partials of every split
+    (kept even for one split) and 20 bytes of statistics per (split, row)."""
+    ws = b.se_soft_embed_onepass_workspace_bytes
+    up = lambda x: (x + 255) // 256 * 256
+    tile = 256 * 256 * 4
+    assert ws(256, 0, 262144, 2816) == up(256 * 262144 * 2) + up(23 * 11 * tile) + \
+        up(23 * 256 * 16) + up(23 * 256 * 4)
+    assert ws(5, 16, 17, 16) == up(5 * 8 * 2) + up(tile) + up(256 * 16) + up(256 * 4)
+    assert ws(5, 16, 16, 16) == 0 and ws(0, 0, 64, 16) == 0
+
+
+def test_merge_slices_errors():
+    m = lib.se_merge_slices
+
+    def call(**kw):
+        a = dict(outs=P1, t=4, stride=256 * 2816, n=256, d=2816, ldp=2816, mx=P2, lse=P2 + 64,
+                 ent=P2 + 128, am=P2 + 192, out=P3, ldo=2816, rmx=P4, rlse=P4 + 64, rent=P4 + 128,
+                 ram=P4 + 192)
+        a.update(kw)
+        return m(a["outs"], a["t"], a["stride"], a["n"], a["d"], a["ldp"], a["mx"], a["lse"],
+                 a["ent"], a["am"], a["out"], a["ldo"], a["rmx"], a["rlse"], a["rent"], a["ram"],
+                 None)
+    assert call(t=0) == b.SE_ERR_SHAPE
+    assert call(n=70000) == b.SE_ERR_SHAPE
+    assert call(stride=100) == b.SE_ERR_SHAPE
+    assert call(ldo=100) == b.SE_ERR_SHAPE
+    assert call(outs=None) == b.SE_ERR_NULL
+    assert call(ram=None) == b.SE_ERR_NULL
+    assert call(d=2814) == b.SE_ERR_ALIGN
+    assert call(out=P3 + 8) == b.SE_ERR_ALIGN
+    assert call(ent=P2 + 130) == b.SE_ERR_ALIGN
+    assert call(n=0, outs=None, out=None) == b.SE_OK
