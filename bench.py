@@ -2,18 +2,23 @@
 """Benchmark of the self-conditioning soft embedding on one MI355X.
 
 A step is one pass of the whole hot path over one canvas batch: se_row_stats over
-the full-width fp32 logits, then se_soft_embed_fused over the rank's vocab slice
-(probabilities rebuilt in the GEMM prologue), both on one stream.  Inputs are
-seeded synthetic data already resident in HBM when the timed region starts.
+the full-width fp32 logits, then the rank's slice contraction, both on one stream.
+The contraction path is chosen with --path:
+  unfused  se_probs_bf16 + se_soft_embed (default: the fastest exact path at these
+           shapes; its output is bitwise the fused call's)
+  fused    se_soft_embed_fused (probabilities rebuilt in the GEMM prologue)
+  onepass  se_soft_embed_onepass, which forms the row statistics from the same read
+           of the logits (whole-vocabulary workloads only; no se_row_stats call)
+Inputs are seeded synthetic data already resident in HBM when the timed region starts.
 
 Default workload: one tensor-parallel rank's share at its real shape (L_c = 256
 canvas positions, full-width logits over V = 262,144, slice [65536, 131072) of a
 bf16 table padded to 262,400 rows, d = 2,816, gamma = sqrt(2816)).
 
 Prints ONE JSON line.  ``value`` is soft-embed GFLOP/s over the whole step
-(2 L (e - s) d FLOP per step / step time); the same line carries steps/s, the
-fused call's GFLOP/s, per-kernel times, the roofline of the dominant call, and
-the fp64 oracle timed on this host as a CPU baseline.
+(2 L (e - s) d FLOP per step / step time); the same line carries steps/s, per-call
+times, the roofline of the step's contraction call, every other path timed on the
+same inputs, and the fp64 oracle timed on this host as a CPU baseline.
 """
 from __future__ import annotations
 
@@ -30,8 +35,8 @@ sys.path.insert(0, ROOT)
 METRIC = "soft-embed GFLOP/s + steps/s at L_c=256,V=262144,d=2816; % of roofline"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_soft_embed_fused_rank.json")
-KERNEL_SOURCES = ["soft_embed.hip", "se_device.h", "se_launch.h", "api.cpp"]
+KERNEL_SOURCES = ["soft_embed.hip", "probs.hip", "onepass.hip", "se_device.h", "se_launch.h",
+                  "api.cpp"]
 
 
 def kernel_hash() -> str:
@@ -73,11 +78,11 @@ def row_stats_bytes(w) -> int:
     return 4 * w.rows * w.vocab + 16 * w.rows
 
 
-def measured_traffic(nbytes_launch_hint: int):
-    """HBM bytes per fused call from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel sources; else None."""
+def measured_traffic(path: str, workload: str):
+    """HBM bytes per call of the step's contraction path from the committed rocprofv3 counter
+    summary of this workload, if it was taken on the current kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(os.path.join(ROOT, "profiles", f"traffic_soft_embed_{path}_{workload}.json")) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -114,11 +119,16 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU needs tens of milliseconds of this work before its kernels run at their
+    # steady-state speed (measured: 5 warmup steps leave the rank step about 6% slow)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="rank", choices=["rank", "full", "conv", "batch", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--unfused", action="store_true",
-                    help="time se_probs_bf16 + se_soft_embed instead of the fused call")
+    ap.add_argument("--path", default="unfused", choices=["unfused", "fused", "onepass"],
+                    help="the step's contraction: se_probs_bf16 + se_soft_embed (default, the "
+                         "fastest exact path at these shapes), se_soft_embed_fused, or "
+                         "se_soft_embed_onepass (whole-vocabulary workloads; it forms the row "
+                         "statistics itself, so the step has no se_row_stats call)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference for scaling the HBM byte counters), then exit")
@@ -151,6 +161,11 @@ def main():
     from diffusion_self_conditioning_amd import workloads as wl
 
     w = wl.get(args.workload)
+    whole = w.vocab_start == 0 and w.vocab_end == w.vocab
+    if args.path == "onepass" and not whole:
+        print("--path onepass needs a workload whose slice is the whole vocabulary (its row "
+              "statistics are those of the slice)", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     x_np = wl.make_logits(w)
@@ -165,22 +180,34 @@ def main():
     am = torch.empty(L, device=dev, dtype=torch.int32)
     out = torch.empty((L, d), device=dev)
     ws = api.workspace(L, w.vocab_start, w.vocab_end, d, dev)
-    probs = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16) if args.unfused else None
+    probs = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16)
+    wso = api.onepass_workspace(L, w.vocab_start, w.vocab_end, d, dev)
 
     def stats():
         B.se_row_stats(x, mx, lse, ent, am)
 
-    def embed():
-        if args.unfused:
-            B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, probs)
-            B.se_soft_embed(probs, w.vocab_start, w.vocab_end, shard, w.gamma, out, ws)
-        else:
-            B.se_soft_embed_fused(x, lse, w.vocab_start, w.vocab_end, shard, w.gamma, out, ws)
+    def call_unfused(o):
+        B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, probs)
+        B.se_soft_embed(probs, w.vocab_start, w.vocab_end, shard, w.gamma, o, ws)
+
+    def call_fused(o):
+        B.se_soft_embed_fused(x, lse, w.vocab_start, w.vocab_end, shard, w.gamma, o, ws)
+
+    def call_onepass(o):
+        B.se_soft_embed_onepass(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse, ent,
+                                am, wso)
+
+    calls = {"unfused": call_unfused, "fused": call_fused, "onepass": call_onepass}
+    call_names = {"unfused": "se_probs_bf16 + se_soft_embed", "fused": "se_soft_embed_fused",
+                  "onepass": "se_soft_embed_onepass"}
+    embed = calls[args.path]
+    with_stats = args.path != "onepass"       # the one-pass call forms the statistics itself
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        stats()
-        embed()
+        if with_stats:
+            stats()
+        embed(out)
     torch.cuda.synchronize()
 
     # timed region: K whole steps, events around each call on the launch stream
@@ -192,9 +219,10 @@ def main():
     t_start.record()
     for k in range(K):
         ev[k][0].record()
-        stats()
+        if with_stats:
+            stats()
         ev[k][1].record()
-        embed()
+        embed(out)
         ev[k][2].record()
     t_end.record()
     torch.cuda.synchronize()
@@ -209,39 +237,35 @@ def main():
     flops = w.flops()
     gflops_step = flops / (ms_step * 1e-3) / 1e9
     gflops_call = flops / (us_embed_avg * 1e-6) / 1e9
-    call_bytes = fused_call_bytes(w)
+    call_bytes = fused_call_bytes(w) + (16 * L if args.path == "onepass" else 0)
     achieved_gbs = call_bytes / (us_embed_avg * 1e-6) / 1e9
     t_roof_call_us = max(flops / (PEAK_BF16_TFLOPS * 1e12), call_bytes / (PEAK_HBM_GBS * 1e9)) * 1e6
-    step_bytes = call_bytes + row_stats_bytes(w)
-    t_roof_step_us = (row_stats_bytes(w) / (PEAK_HBM_GBS * 1e9) + t_roof_call_us * 1e-6) * 1e6
+    stats_bytes = row_stats_bytes(w) if with_stats else 0
+    step_bytes = call_bytes + stats_bytes
+    t_roof_step_us = (stats_bytes / (PEAK_HBM_GBS * 1e9) + t_roof_call_us * 1e-6) * 1e6
     mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > call_bytes / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(call_bytes)
+    traffic = measured_traffic(args.path, w.name)
     roof = {"bound": "mfma" if mfma_bound else "hbm",
             "achieved": round(gflops_call / 1e3 if mfma_bound else achieved_gbs, 2),
             "peak": PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS,
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "traffic": traffic}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = ("se_probs_bf16+se_soft_embed" if args.unfused else "se_soft_embed_fused") + \
-        " call (soft_embed_kernel + splitk_reduce_kernel)"
+    roof["kernel"] = call_names[args.path] + " call"
     roof["algorithmic_bytes"] = call_bytes
 
-    # side measurement (not part of `value`): the unfused call on the same inputs,
-    # se_probs_bf16 (bf16 probability slice written to memory) + se_soft_embed
-    side = None
-    if not args.unfused:
-        pr = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16)
-        out_u = torch.empty_like(out)
-
-        def unfused():
-            B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, pr)
-            B.se_soft_embed(pr, w.vocab_start, w.vocab_end, shard, w.gamma, out_u, ws)
-
-        us_u = event_time_us(unfused, K, args.warmup)
-        side = {"unfused_call_us": round(us_u, 2),
-                "gflops_unfused_call": round(flops / (us_u * 1e-6) / 1e9, 2),
-                "unfused_equals_fused": bool(torch.equal(out_u, out))}
-        del pr, out_u
+    # side measurements (not part of `value`): every contraction path on the same inputs,
+    # each event-timed as one call; the unfused and fused outputs are compared bitwise
+    side = {}
+    ref_out = out.clone()
+    for name in ("unfused", "fused"):
+        o = torch.empty_like(out)
+        side[name + "_call_us"] = round(event_time_us(lambda: calls[name](o), K, args.warmup), 2)
+        if args.path != "onepass":
+            side[name + "_equals_step_output"] = bool(torch.equal(o, ref_out))
+        del o
+    side["gflops_unfused_call"] = round(flops / (side["unfused_call_us"] * 1e-6) / 1e9, 2)
+    side["gflops_fused_call"] = round(flops / (side["fused_call_us"] * 1e-6) / 1e9, 2)
 
     # side measurement: the sampler's acceptance / convergence step on this step's row
     # statistics (canvases of 256 positions)
@@ -301,7 +325,6 @@ def main():
     # side measurement: the one-pass call over the same slice (softmax over the slice, row
     # statistics from the same read of the logits), and the merge of 4 slice results.  For
     # a slice that is the whole vocabulary the one-pass call is a whole step.
-    wso = api.onepass_workspace(L, w.vocab_start, w.vocab_end, d, dev)
     oo = torch.empty((L, d), device=dev)
     so = [torch.empty(L, device=dev) for _ in range(3)]
     ao = torch.empty(L, device=dev, dtype=torch.int32)
@@ -322,7 +345,7 @@ def main():
                                       "frac": round(o_bytes / (us_o * 1e-6) / 1e9 / PEAK_HBM_GBS,
                                                     4)},
                     "merge_4_slices_us": round(us_m, 2)}
-    del wso, oo, so, ao, outs4, st4, am4
+    del oo, so, ao, outs4, st4, am4
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -337,20 +360,20 @@ def main():
         "config": {"workload": f"{w.name}: L_c={L} rows, full-width fp32 logits V={w.vocab}, "
                                f"slice [{w.vocab_start},{w.vocab_end}) of a bf16 table "
                                f"[{w.table_rows}, {d}], gamma={w.gamma:.6g}"
-                               + (" (unfused)" if args.unfused else " (fused)"),
+                               + f" ({args.path})",
                    "rows": L, "vocab": w.vocab, "vocab_start": w.vocab_start,
                    "vocab_end": w.vocab_end, "d": d, "seed": w.seed},
         "steps_per_s": round(1e3 / ms_step, 2),
-        "gflops_fused_call": round(gflops_call, 2),
-        "kernel_us": {"se_row_stats": round(us_stats_avg, 2),
-                      "se_soft_embed" + ("" if args.unfused else "_fused"): round(us_embed_avg, 2)},
+        "gflops_call": round(gflops_call, 2),
+        "kernel_us": {"se_row_stats": round(us_stats_avg, 2) if with_stats else None,
+                      call_names[args.path]: round(us_embed_avg, 2)},
         "roofline": roof,
         "roofline_step": {"t_roof_us": round(t_roof_step_us, 2),
                           "frac": round(t_roof_step_us / (ms_step * 1e3), 4),
                           "algorithmic_bytes": step_bytes},
         "roofline_call_t_roof_us": round(t_roof_call_us, 2),
         "wall_s_timed": round(wall, 4),
-        "unfused": side,
+        "paths": side,
         "accept_converge": acc_side,
         "reduce_partials": red_side,
         "fp8_table": fp8_side,

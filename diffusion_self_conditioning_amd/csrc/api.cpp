@@ -312,8 +312,10 @@ se_status se_soft_embed_onepass(const float* logits, int64_t ld_logits, int64_t 
   const int64_t K = vocab_end - vocab_start;
   const se::OnepassLayout o = se::onepass_layout(n_rows, K, d);
   if (o.g.grid > INT32_MAX || n_rows * o.g.splits > INT32_MAX) return SE_ERR_SHAPE;
+  // 32-bit byte offsets: a tile's rows of the probabilities, a split's table rows, and a
+  // row's range of logits in the sweep
   if ((int64_t)(se::kBM - 1) * o.ldp * 2 + K * 2 > (int64_t)UINT32_MAX ||
-      K * ld_w * 2 > (int64_t)UINT32_MAX)
+      K * ld_w * 2 > (int64_t)UINT32_MAX || K * 4 > (int64_t)UINT32_MAX)
     return SE_ERR_SHAPE;
   if (workspace_bytes < o.total) return SE_ERR_WORKSPACE;
   if (!workspace) return SE_ERR_NULL;

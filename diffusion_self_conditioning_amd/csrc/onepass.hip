@@ -13,18 +13,21 @@
 // split by e^(m_s - M), M = max_s m_s, and divides by Z = sum_s e^(m_s - M) Z_s: the
 // merge rule of the partition identity ("The fix") written for softmax numerators.
 //
-// One wave per (row, split range): a first pass finds the range's maximum and its
-// first position (16-byte loads, 256 positions per instruction, then a cross-lane
-// reduction); a second pass over the same, now cache-resident, range forms the
-// probabilities, writes them as bf16 and sums Z_s and S1_s in fp32.
+// One workgroup per (row, split range): a first pass reads the range once from memory
+// and finds its maximum and first position; a second pass over the same values, kept
+// in LDS, forms the probabilities, writes them as bf16 and sums Z_s and S1_s in fp32.
 #include "se_device.h"
 #include "se_launch.h"
 
 namespace se {
 namespace {
 
-constexpr int kSweepThreads = 256;                  // 4 waves: 4 (row, split) ranges
+constexpr int kSweepThreads = 512;                  // one workgroup per (row, split range)
 constexpr int kSweepWaves = kSweepThreads / 64;
+// The range is kept in LDS between the two passes when it fits (up to 60 KB of fp32,
+// 15,360 positions, within the 64 KB a launch gets by default); longer ranges read the
+// logits again in the second pass.
+constexpr int kSweepLdsMax = 61440;
 
 // whole-wave reductions (64 lanes) on top of the half-wave ones
 __device__ __forceinline__ float wave_sum(float v) {
@@ -41,52 +44,72 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   argmax_step(v, i, v1, i1);
 }
 
+// Pass 1 reads the range (16-byte buffer loads, eight in flight per lane), keeps it in
+// LDS when it fits, and finds the first maximum; pass 2
+// forms the probabilities against it from LDS (or from memory), writes them as bf16
+// and sums Z and S1.  Cross-wave reductions go through a small LDS array in wave
+// order, so the sums are independent of scheduling.
+template <bool KEEP>
 __global__ void __launch_bounds__(kSweepThreads)
 split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, int64_t K,
                    int64_t n_rows, int splits, int kblocks, uint16_t* __restrict__ probs,
                    int64_t ldp, float4* __restrict__ stats, int32_t* __restrict__ stat_arg,
                    int64_t rows_pad) {
-  const int lane = threadIdx.x & 63;
-  const int64_t unit = (int64_t)blockIdx.x * kSweepWaves + (threadIdx.x >> 6);
-  if (unit >= n_rows * splits) return;              // uniform per wave
-  const int64_t row = unit % n_rows;
-  const int s = (int)(unit / n_rows);
+  extern __shared__ float4 keep[];                    // the range (KEEP only)
+  __shared__ float red_v[kSweepWaves], red_w[kSweepWaves];
+  __shared__ int red_i[kSweepWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x % n_rows;
+  const int s = (int)(blockIdx.x / n_rows);
   // the contraction's split boundaries (positions of the slice)
   const int64_t k_lo = (((int64_t)s * kblocks) / splits) * kSplitQuantum;
   const int64_t k_hi = min((((int64_t)(s + 1) * kblocks) / splits) * kSplitQuantum, K);
-  const float* __restrict__ x = logits + row * ld + col0;
-  uint16_t* __restrict__ p = probs + row * ldp;
+  const int n = (int)(k_hi - k_lo);
+  const int n4 = n / 4;                               // whole 16-byte groups
+  const float* __restrict__ x = logits + row * ld + col0 + k_lo;
+  uint16_t* __restrict__ p = probs + row * ldp + k_lo;
 
-  // pass 1: maximum and its first position; four 16-byte loads in flight per lane
+  // pass 1
   float mv = -INFINITY;
   int mi = 0;
-  auto max4 = [&](const float4& v, int64_t k) {
-    argmax_step(mv, mi, v.x, (int)k);
-    argmax_step(mv, mi, v.y, (int)k + 1);
-    argmax_step(mv, mi, v.z, (int)k + 2);
-    argmax_step(mv, mi, v.w, (int)k + 3);
+  auto max4 = [&](const float4& v, int k) {
+    argmax_step(mv, mi, v.x, k);
+    argmax_step(mv, mi, v.y, k + 1);
+    argmax_step(mv, mi, v.z, k + 2);
+    argmax_step(mv, mi, v.w, k + 3);
   };
-  int64_t k = k_lo + 4 * lane;
-  for (; k + 3 * 256 + 4 <= k_hi; k += 4 * 256) {
-    float4 v[4];
+  // eight 16-byte loads in flight per lane; the buffer resource bounds them to the range
+  // (out-of-range lanes read zeros, which the mask below discards)
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)n4 * 16u);
+  for (int base = 0; base < n4; base += 8 * kSweepThreads) {
+    float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(x + k + 256 * u);
+    for (int u = 0; u < 8; ++u)
+      v[u] = buffer_load_f4(xr, (uint32_t)(base + u * kSweepThreads + tid) * 16u, 0u);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) max4(v[u], k + 256 * u);
-  }
-  for (; k < k_hi; k += 256) {
-    if (k + 4 <= k_hi) {
-      max4(*reinterpret_cast<const float4*>(x + k), k);
-    } else {
-      for (int64_t j = k; j < k_hi; ++j) argmax_step(mv, mi, x[j], (int)j);
+    for (int u = 0; u < 8; ++u) {
+      const int g = base + u * kSweepThreads + tid;
+      if (g < n4) {
+        if constexpr (KEEP) keep[g] = v[u];
+        max4(v[u], 4 * g);
+      }
     }
   }
+  for (int j = 4 * n4 + tid; j < n; j += kSweepThreads) argmax_step(mv, mi, x[j], j);
   wave_argmax(mv, mi);
+  if (lane == 0) { red_v[wave] = mv; red_i[wave] = mi; }
+  __syncthreads();
+  mv = red_v[0];
+  mi = red_i[0];
+  for (int w = 1; w < kSweepWaves; ++w) argmax_step(mv, mi, red_v[w], red_i[w]);
   const float nl = neg_lse_log2(mv);
 
-  // pass 2: probabilities against the range maximum, Z and S1 (log2 units)
+  // pass 2
   float z = 0.f, s1 = 0.f;
-  auto prob4 = [&](const float4& v, int64_t k) {
+  for (int g = tid; g < n4; g += kSweepThreads) {
+    float4 v;
+    if constexpr (KEEP) v = keep[g];
+    else v = reinterpret_cast<const float4*>(x)[g];
     const float t0 = __builtin_fmaf(v.x, kLog2e, nl), t1 = __builtin_fmaf(v.y, kLog2e, nl);
     const float t2 = __builtin_fmaf(v.z, kLog2e, nl), t3 = __builtin_fmaf(v.w, kLog2e, nl);
     const float q0 = exp2_hw(t0), q1 = exp2_hw(t1), q2 = exp2_hw(t2), q3 = exp2_hw(t3);
@@ -95,34 +118,25 @@ split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, i
     uint2 o;
     o.x = pack_bf16x2(q0, q1);
     o.y = pack_bf16x2(q2, q3);
-    *reinterpret_cast<uint2*>(p + k) = o;
-  };
-  k = k_lo + 4 * lane;
-  for (; k + 3 * 256 + 4 <= k_hi; k += 4 * 256) {
-    float4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(x + k + 256 * u);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) prob4(v[u], k + 256 * u);
+    reinterpret_cast<uint2*>(p)[g] = o;
   }
-  for (; k < k_hi; k += 256) {
-    if (k + 4 <= k_hi) {
-      prob4(*reinterpret_cast<const float4*>(x + k), k);
-    } else {
-      for (int64_t j = k; j < k_hi; ++j) {
-        const float t = __builtin_fmaf(x[j], kLog2e, nl);
-        const float q = exp2_hw(t);
-        z += q;
-        s1 = __builtin_fmaf(q, t, s1);
-        p[j] = __builtin_bit_cast(uint16_t, (__bf16)q);
-      }
-    }
+  for (int j = 4 * n4 + tid; j < n; j += kSweepThreads) {
+    const float t = __builtin_fmaf(x[j], kLog2e, nl);
+    const float q = exp2_hw(t);
+    z += q;
+    s1 = __builtin_fmaf(q, t, s1);
+    p[j] = __builtin_bit_cast(uint16_t, (__bf16)q);
   }
   z = wave_sum(z);
   s1 = wave_sum(s1);
-  if (lane == 0) {
-    stats[(int64_t)s * rows_pad + row] = make_float4(mv, z, s1 * kLn2, mv);
-    stat_arg[(int64_t)s * rows_pad + row] = mi;
+  __syncthreads();                                    // red_v / red_i reads are done
+  if (lane == 0) { red_v[wave] = z; red_w[wave] = s1; }
+  __syncthreads();
+  if (tid == 0) {
+    float zt = 0.f, st = 0.f;
+    for (int w = 0; w < kSweepWaves; ++w) { zt += red_v[w]; st += red_w[w]; }
+    stats[(int64_t)s * rows_pad + row] = make_float4(mv, zt, st * kLn2, mv);
+    stat_arg[(int64_t)s * rows_pad + row] = (int32_t)(k_lo + mi);
   }
 }
 
@@ -197,11 +211,18 @@ hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int
                               int64_t n_rows, int splits, int kblocks, uint16_t* probs,
                               int64_t ldp, float* stats, int32_t* stat_arg, int64_t rows_pad,
                               hipStream_t stream) {
-  const int64_t units = n_rows * splits;
-  const dim3 grid((unsigned)((units + kSweepWaves - 1) / kSweepWaves));
-  hipLaunchKernelGGL(split_sweep_kernel, grid, dim3(kSweepThreads), 0, stream, logits, ld, col0,
-                     K, n_rows, splits, kblocks, probs, ldp, reinterpret_cast<float4*>(stats),
-                     stat_arg, rows_pad);
+  // the longest split range: kSplitQuantum-position blocks dealt as evenly as possible
+  const int64_t longest = min((int64_t)((kblocks + splits - 1) / splits) * kSplitQuantum, K);
+  const size_t lds = (size_t)(longest / 4) * sizeof(float4);
+  const dim3 grid((unsigned)(n_rows * splits));
+  if (lds <= (size_t)kSweepLdsMax)
+    hipLaunchKernelGGL(split_sweep_kernel<true>, grid, dim3(kSweepThreads), lds, stream, logits,
+                       ld, col0, K, n_rows, splits, kblocks, probs, ldp,
+                       reinterpret_cast<float4*>(stats), stat_arg, rows_pad);
+  else
+    hipLaunchKernelGGL(split_sweep_kernel<false>, grid, dim3(kSweepThreads), 0, stream, logits,
+                       ld, col0, K, n_rows, splits, kblocks, probs, ldp,
+                       reinterpret_cast<float4*>(stats), stat_arg, rows_pad);
   return hipGetLastError();
 }
 

@@ -128,6 +128,17 @@ def test_onepass_special_rows(kind):
     check_slice(x, 0, V, table(V, d, 12), 3.0)
 
 
+def test_onepass_long_ranges_read_twice():
+    """Split ranges longer than the sweep keeps in LDS (300 rows x 11 n-tiles -> 11 splits of
+    about 18,000 positions): the second pass reads the logits from memory again."""
+    L, V, d = 300, 200000, 2816
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    x[np.arange(L), rng.integers(0, V, L)] += 9.0
+    say("onepass long ranges")
+    check_slice(x, 0, V, table(V, d, 18), 2.5, rows=np.array([0, 1, 150, 299]))
+
+
 def test_onepass_agrees_with_the_two_pass_path():
     """Over the whole vocabulary the one-pass statistics are se_row_stats' (argmax and max
     bitwise) and the embedding is within bf16 rounding of the fused call's."""
