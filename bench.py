@@ -124,7 +124,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="rank", choices=["rank", "full", "conv", "batch", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", default="unfused", choices=["unfused", "fused", "onepass"],
+    ap.add_argument("--path", default="unfused", choices=["unfused", "fused", "staged", "onepass"],
                     help="the step's contraction: se_probs_bf16 + se_soft_embed (default, the "
                          "fastest exact path at these shapes), se_soft_embed_fused, or "
                          "se_soft_embed_onepass (whole-vocabulary workloads; it forms the row "
@@ -182,6 +182,7 @@ def main():
     ws = api.workspace(L, w.vocab_start, w.vocab_end, d, dev)
     probs = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16)
     wso = api.onepass_workspace(L, w.vocab_start, w.vocab_end, d, dev)
+    wss = api.staged_workspace(L, w.vocab_start, w.vocab_end, d, dev)
 
     def stats():
         B.se_row_stats(x, mx, lse, ent, am)
@@ -193,13 +194,17 @@ def main():
     def call_fused(o):
         B.se_soft_embed_fused(x, lse, w.vocab_start, w.vocab_end, shard, w.gamma, o, ws)
 
+    def call_staged(o):
+        B.se_soft_embed_staged(x, lse, w.vocab_start, w.vocab_end, shard, w.gamma, o, wss)
+
     def call_onepass(o):
         B.se_soft_embed_onepass(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse, ent,
                                 am, wso)
 
-    calls = {"unfused": call_unfused, "fused": call_fused, "onepass": call_onepass}
+    calls = {"unfused": call_unfused, "fused": call_fused, "staged": call_staged,
+             "onepass": call_onepass}
     call_names = {"unfused": "se_probs_bf16 + se_soft_embed", "fused": "se_soft_embed_fused",
-                  "onepass": "se_soft_embed_onepass"}
+                  "staged": "se_soft_embed_staged", "onepass": "se_soft_embed_onepass"}
     embed = calls[args.path]
     with_stats = args.path != "onepass"       # the one-pass call forms the statistics itself
 
@@ -258,7 +263,7 @@ def main():
     # each event-timed as one call; the unfused and fused outputs are compared bitwise
     side = {}
     ref_out = out.clone()
-    for name in ("unfused", "fused"):
+    for name in ("unfused", "fused", "staged"):
         o = torch.empty_like(out)
         side[name + "_call_us"] = round(event_time_us(lambda: calls[name](o), K, args.warmup), 2)
         if args.path != "onepass":
@@ -266,6 +271,7 @@ def main():
         del o
     side["gflops_unfused_call"] = round(flops / (side["unfused_call_us"] * 1e-6) / 1e9, 2)
     side["gflops_fused_call"] = round(flops / (side["fused_call_us"] * 1e-6) / 1e9, 2)
+    side["gflops_staged_call"] = round(flops / (side["staged_call_us"] * 1e-6) / 1e9, 2)
 
     # side measurement: the sampler's acceptance / convergence step on this step's row
     # statistics (canvases of 256 positions)

@@ -11,7 +11,8 @@ import torch
 from ._binding import (SoftEmbedError, se_merge_slices, se_probs_bf16,  # noqa: F401
                        se_quantize_table_fp8, se_row_stats, se_soft_embed, se_soft_embed_fp8,
                        se_soft_embed_fp8_fused, se_soft_embed_fused, se_soft_embed_onepass,
-                       se_soft_embed_onepass_workspace_bytes, se_soft_embed_workspace_bytes,
+                       se_soft_embed_onepass_workspace_bytes, se_soft_embed_staged,
+                       se_soft_embed_staged_workspace_bytes, se_soft_embed_workspace_bytes,
                        se_status_string, se_version)
 
 
@@ -37,12 +38,24 @@ def workspace(n_rows, vocab_start, vocab_end, d, device):
     return torch.empty((nbytes + 3) // 4, device=device, dtype=torch.float32) if nbytes else None
 
 
+def staged_workspace(n_rows, vocab_start, vocab_end, d, device):
+    nbytes = se_soft_embed_staged_workspace_bytes(n_rows, vocab_start, vocab_end, d)
+    return torch.empty((nbytes + 3) // 4, device=device, dtype=torch.float32) if nbytes else None
+
+
 def soft_embed(logits, row_lse, vocab_start, vocab_end, w_shard, gamma, *, fused=True,
-               out=None, ws=None, stream=None):
-    """gamma * softmax(logits)[:, s:e] @ w_shard[: e - s]: one rank's partial, fp32 [L, d]."""
+               out=None, ws=None, stream=None, staged=False):
+    """gamma * softmax(logits)[:, s:e] @ w_shard[: e - s]: one rank's partial, fp32 [L, d].
+    ``staged=True`` runs se_soft_embed_staged (same result as the fused call)."""
     n, d = logits.shape[0], w_shard.shape[1]
     if out is None:
         out = torch.empty((n, d), device=logits.device, dtype=torch.float32)
+    if staged:
+        if ws is None:
+            ws = staged_workspace(n, vocab_start, vocab_end, d, logits.device)
+        se_soft_embed_staged(logits, row_lse, vocab_start, vocab_end, w_shard, gamma, out, ws,
+                             stream=stream)
+        return out
     if ws is None:
         ws = workspace(n, vocab_start, vocab_end, d, logits.device)
     if fused:

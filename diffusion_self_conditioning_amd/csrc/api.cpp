@@ -31,19 +31,35 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   return g;
 }
 
-// Workspace of the one-pass call: bf16 probabilities [n_rows, ldp] of the slice, the
-// split partials (kept even for one split), and per-(split, row) statistics.
+namespace {
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+// bf16 probabilities of K slice positions in the super-step-tiled layout
+size_t tiled_probs_bytes(int64_t n_rows, int64_t K) {
+  return (size_t)((K + kSuperStep - 1) / kSuperStep) * (size_t)n_rows * kSuperStep * 2;
+}
+}  // namespace
+
+// Workspace of the one-pass call: tiled bf16 probabilities of the slice, the split
+// partials (kept even for one split), and per-(split, row) statistics.
 OnepassLayout onepass_layout(int64_t n_rows, int64_t K, int64_t d) {
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  auto up = up256;
   OnepassLayout o{};
   o.g = plan_gemm(n_rows, d, K);
-  o.ldp = (K + 7) / 8 * 8;
   o.rows_pad = o.g.tiles_m * kBM;
   o.off_probs = 0;
-  o.off_parts = up((size_t)(n_rows * o.ldp) * 2);
+  o.off_parts = up(tiled_probs_bytes(n_rows, K));
   o.off_stats = o.off_parts + up((size_t)(o.g.splits * o.g.tiles * kTileFloats) * 4);
   o.off_arg = o.off_stats + up((size_t)(o.g.splits * o.rows_pad) * 16);
   o.total = o.off_arg + up((size_t)(o.g.splits * o.rows_pad) * 4);
+  return o;
+}
+
+StagedLayout staged_layout(int64_t n_rows, int64_t K, int64_t d) {
+  StagedLayout o{};
+  o.g = plan_gemm(n_rows, d, K);
+  o.off_probs = 0;
+  o.off_parts = up256(tiled_probs_bytes(n_rows, K));
+  o.total = o.off_parts + o.g.ws_bytes;
   return o;
 }
 
@@ -112,6 +128,7 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
   se::GemmParams p{};
   p.a = a;
   p.lda = lda;
+  p.a_ss = (int64_t)se::kSuperStep * esz;
   p.lse = lse;
   p.col0 = s;
   p.w = w;
@@ -150,7 +167,7 @@ const char* se_status_string(se_status s) {
 }
 
 const char* se_version(void) {
-  return "libsoftembed 0.3 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table, one-pass)";
+  return "libsoftembed 0.3 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table, one-pass, staged)";
 }
 
 se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
@@ -230,6 +247,65 @@ se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const floa
   if (!aligned16(logits) || (ld_logits % 4) != 0 || !aligned4(row_lse)) return SE_ERR_ALIGN;
   return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start, vocab_end, w_shard,
                         nullptr, ld_w, d, gamma, out, ld_out, workspace, workspace_bytes, stream);
+}
+
+size_t se_soft_embed_staged_workspace_bytes(int64_t n_rows, int64_t vocab_start,
+                                            int64_t vocab_end, int64_t d) {
+  if (n_rows < 1 || d < 1 || vocab_start < 0 || vocab_end <= vocab_start) return 0;
+  if (n_rows > INT32_MAX || d > INT32_MAX || vocab_end > INT32_MAX) return 0;
+  return se::staged_layout(n_rows, vocab_end - vocab_start, d).total;
+}
+
+se_status se_soft_embed_staged(const float* logits, int64_t ld_logits, const float* row_lse,
+                               int64_t n_rows, int64_t vocab, int64_t vocab_start,
+                               int64_t vocab_end, const uint16_t* w_shard, int64_t w_rows,
+                               int64_t ld_w, int64_t d, float gamma, float* out, int64_t ld_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
+  if (rc != SE_OK) return rc;
+  if (ld_logits < vocab) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  if (!logits || !row_lse || !w_shard || !out) return SE_ERR_NULL;
+  rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_shard, out);
+  if (rc != SE_OK) return rc;
+  if (!aligned16(logits) || (ld_logits % 4) != 0 || !aligned4(row_lse)) return SE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t K = vocab_end - vocab_start;
+  if (K == 0) return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start,
+                                    vocab_end, w_shard, nullptr, ld_w, d, gamma, out, ld_out,
+                                    workspace, workspace_bytes, stream);   // writes zeros
+  const se::StagedLayout o = se::staged_layout(n_rows, K, d);
+  if (o.g.grid > INT32_MAX) return SE_ERR_SHAPE;
+  if ((int64_t)se::tiled_probs_bytes(n_rows, K) > (int64_t)UINT32_MAX ||
+      K * ld_w * 2 > (int64_t)UINT32_MAX)
+    return SE_ERR_SHAPE;
+  if (workspace_bytes < o.total) return SE_ERR_WORKSPACE;
+  if (!workspace) return SE_ERR_NULL;
+  if (!aligned16(workspace)) return SE_ERR_ALIGN;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t* probs = reinterpret_cast<uint16_t*>(ws + o.off_probs);
+  rc = from_hip(se::launch_probs_bf16_tiled(logits, ld_logits, row_lse, n_rows, vocab_start, K,
+                                            probs, st));
+  if (rc != SE_OK) return rc;
+  se::GemmParams p{};
+  p.a = probs;                       // super-step-tiled: [K / 128][n_rows][128]
+  p.lda = se::kSuperStep;
+  p.a_ss = n_rows * se::kSuperStep * 2;
+  p.col0 = 0;
+  p.w = w_shard;
+  p.ldw = ld_w;
+  p.M = n_rows;
+  p.N = d;
+  p.K = K;
+  p.gamma = gamma;
+  p.out = out;
+  p.ldo = ld_out;
+  p.ws = reinterpret_cast<float*>(ws + o.off_parts);
+  p.tiles_n = (int)o.g.tiles_n;
+  p.tiles = (int)o.g.tiles;
+  p.splits = (int)o.g.splits;
+  p.kblocks = (int)o.g.kblocks;
+  return from_hip(se::launch_soft_embed(p, false, false, st));
 }
 
 se_status se_quantize_table_fp8(const uint16_t* w, int64_t ld_w, int64_t rows, int64_t d,
@@ -314,7 +390,7 @@ se_status se_soft_embed_onepass(const float* logits, int64_t ld_logits, int64_t 
   if (o.g.grid > INT32_MAX || n_rows * o.g.splits > INT32_MAX) return SE_ERR_SHAPE;
   // 32-bit byte offsets: a tile's rows of the probabilities, a split's table rows, and a
   // row's range of logits in the sweep
-  if ((int64_t)(se::kBM - 1) * o.ldp * 2 + K * 2 > (int64_t)UINT32_MAX ||
+  if ((int64_t)se::tiled_probs_bytes(n_rows, K) > (int64_t)UINT32_MAX ||
       K * ld_w * 2 > (int64_t)UINT32_MAX || K * 4 > (int64_t)UINT32_MAX)
     return SE_ERR_SHAPE;
   if (workspace_bytes < o.total) return SE_ERR_WORKSPACE;
@@ -326,12 +402,13 @@ se_status se_soft_embed_onepass(const float* logits, int64_t ld_logits, int64_t 
   int32_t* stat_arg = reinterpret_cast<int32_t*>(ws + o.off_arg);
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = from_hip(se::launch_split_sweep(logits, ld_logits, vocab_start, K, n_rows,
-                                       (int)o.g.splits, (int)o.g.kblocks, probs, o.ldp, stats,
-                                       stat_arg, o.rows_pad, st));
+                                       (int)o.g.splits, (int)o.g.kblocks, probs, stats, stat_arg,
+                                       o.rows_pad, st));
   if (rc != SE_OK) return rc;
   se::GemmParams p{};
-  p.a = probs;
-  p.lda = o.ldp;
+  p.a = probs;                       // super-step-tiled: [K / 128][n_rows][128]
+  p.lda = se::kSuperStep;
+  p.a_ss = n_rows * se::kSuperStep * 2;
   p.col0 = 0;
   p.w = w_shard;
   p.ldw = ld_w;

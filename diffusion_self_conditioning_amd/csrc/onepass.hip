@@ -53,7 +53,7 @@ template <bool KEEP>
 __global__ void __launch_bounds__(kSweepThreads)
 split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, int64_t K,
                    int64_t n_rows, int splits, int kblocks, uint16_t* __restrict__ probs,
-                   int64_t ldp, float4* __restrict__ stats, int32_t* __restrict__ stat_arg,
+                   float4* __restrict__ stats, int32_t* __restrict__ stat_arg,
                    int64_t rows_pad) {
   extern __shared__ float4 keep[];                    // the range (KEEP only)
   __shared__ float red_v[kSweepWaves], red_w[kSweepWaves];
@@ -67,7 +67,13 @@ split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, i
   const int n = (int)(k_hi - k_lo);
   const int n4 = n / 4;                               // whole 16-byte groups
   const float* __restrict__ x = logits + row * ld + col0 + k_lo;
-  uint16_t* __restrict__ p = probs + row * ldp + k_lo;
+  // probabilities in the super-step-tiled layout: range position j (k_lo + j, k_lo a
+  // multiple of kSuperStep) of this row at blk[(j / kSuperStep) * n_rows * kSuperStep +
+  // j % kSuperStep]
+  uint16_t* __restrict__ blk = probs + (k_lo / kSuperStep) * n_rows * kSuperStep + row * kSuperStep;
+  auto pidx = [&](int j) -> int64_t {
+    return (int64_t)(j / kSuperStep) * n_rows * kSuperStep + j % kSuperStep;
+  };
 
   // pass 1
   float mv = -INFINITY;
@@ -118,14 +124,14 @@ split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, i
     uint2 o;
     o.x = pack_bf16x2(q0, q1);
     o.y = pack_bf16x2(q2, q3);
-    reinterpret_cast<uint2*>(p)[g] = o;
+    *reinterpret_cast<uint2*>(blk + pidx(4 * g)) = o;
   }
   for (int j = 4 * n4 + tid; j < n; j += kSweepThreads) {
     const float t = __builtin_fmaf(x[j], kLog2e, nl);
     const float q = exp2_hw(t);
     z += q;
     s1 = __builtin_fmaf(q, t, s1);
-    p[j] = __builtin_bit_cast(uint16_t, (__bf16)q);
+    blk[pidx(j)] = __builtin_bit_cast(uint16_t, (__bf16)q);
   }
   z = wave_sum(z);
   s1 = wave_sum(s1);
@@ -209,7 +215,7 @@ hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_
 
 hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int64_t K,
                               int64_t n_rows, int splits, int kblocks, uint16_t* probs,
-                              int64_t ldp, float* stats, int32_t* stat_arg, int64_t rows_pad,
+                              float* stats, int32_t* stat_arg, int64_t rows_pad,
                               hipStream_t stream) {
   // the longest split range: kSplitQuantum-position blocks dealt as evenly as possible
   const int64_t longest = min((int64_t)((kblocks + splits - 1) / splits) * kSplitQuantum, K);
@@ -217,11 +223,11 @@ hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int
   const dim3 grid((unsigned)(n_rows * splits));
   if (lds <= (size_t)kSweepLdsMax)
     hipLaunchKernelGGL(split_sweep_kernel<true>, grid, dim3(kSweepThreads), lds, stream, logits,
-                       ld, col0, K, n_rows, splits, kblocks, probs, ldp,
+                       ld, col0, K, n_rows, splits, kblocks, probs,
                        reinterpret_cast<float4*>(stats), stat_arg, rows_pad);
   else
     hipLaunchKernelGGL(split_sweep_kernel<false>, grid, dim3(kSweepThreads), 0, stream, logits,
-                       ld, col0, K, n_rows, splits, kblocks, probs, ldp,
+                       ld, col0, K, n_rows, splits, kblocks, probs,
                        reinterpret_cast<float4*>(stats), stat_arg, rows_pad);
   return hipGetLastError();
 }

@@ -24,6 +24,7 @@ constexpr int kBN = 256;
 #endif
 constexpr int kGemmThreads = 64 * SE_WAVES;
 constexpr int kSplitQuantum = 128;        // vocab positions per split block
+constexpr int kSuperStep = 128;           // vocab positions per super-step of the contraction
 constexpr int kMinBlocksPerSplit = 2;     // at least 256 vocab positions per split
 constexpr int kTargetCUs = 256;           // MI355X compute units: sizes the split count
 constexpr int64_t kTileFloats = (int64_t)kBM * kBN;
@@ -37,15 +38,26 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 
 struct OnepassLayout {
   GemmPlan g;
-  int64_t ldp, rows_pad;
+  int64_t rows_pad;
   size_t off_probs, off_parts, off_stats, off_arg, total;
 };
 
 OnepassLayout onepass_layout(int64_t n_rows, int64_t K, int64_t d);
 
+// workspace of the staged call: tiled bf16 probabilities, then the split partials
+struct StagedLayout {
+  GemmPlan g;
+  size_t off_probs, off_parts, total;
+};
+
+StagedLayout staged_layout(int64_t n_rows, int64_t K, int64_t d);
+
 struct GemmParams {
   const void* a;          // fused: fp32 logits; unfused: bf16 probabilities
   int64_t lda;            // elements
+  int64_t a_ss;           // bytes from one super-step of a row to the next: kSuperStep *
+                          // element size (row-major), or rows * kSuperStep * 2 for the
+                          // super-step-tiled bf16 layout [super-step][row][kSuperStep]
   const float* lse;       // fused only: per-row log-sum-exp
   int64_t col0;           // vocab_start: column of `a` holding slice position 0
   const void* w;          // shard, row 0 = slice position 0: bf16, or e4m3 codes
@@ -75,16 +87,22 @@ hipError_t launch_probs_bf16(const float* logits, int64_t ld, const float* row_l
                              int64_t n_rows, int64_t col0, int64_t K, uint16_t* probs,
                              int64_t ldp, hipStream_t stream);
 
+// the same probabilities of slice positions [0, K) in the super-step-tiled layout:
+// position k of row i at probs[(k / kSuperStep) * n_rows * kSuperStep + i * kSuperStep +
+// k % kSuperStep]
+hipError_t launch_probs_bf16_tiled(const float* logits, int64_t ld, const float* row_lse,
+                                   int64_t n_rows, int64_t col0, int64_t K, uint16_t* probs,
+                                   hipStream_t stream);
+
 // fused: `a` holds fp32 logits (else bf16 probabilities); w8: `w` holds e4m3 codes
 // with per-row scales (else bf16)
 hipError_t launch_soft_embed(const GemmParams& p, bool fused, bool w8, hipStream_t stream);
 
 // one-pass sweep: per (row, split range) maximum, Z, S1 and argmax, and the bf16
-// probabilities against the range maximum (probs [n_rows, ldp], slice position 0 at
-// column 0)
+// probabilities against the range maximum, in the super-step-tiled layout
 hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int64_t K,
                               int64_t n_rows, int splits, int kblocks, uint16_t* probs,
-                              int64_t ldp, float* stats, int32_t* stat_arg, int64_t rows_pad,
+                              float* stats, int32_t* stat_arg, int64_t rows_pad,
                               hipStream_t stream);
 
 hipError_t launch_onepass_reduce(const GemmParams& p, float* row_max, float* row_lse,

@@ -82,6 +82,7 @@ __device__ __forceinline__ int xcd_local_order(int b, int g) {
 constexpr int kBK = 32;                          // vocab positions per step
 constexpr int kQ = 4;                            // steps per super-step
 constexpr int kSS = kBK * kQ;                    // vocab positions per super-step
+static_assert(kSS == kSuperStep, "the host's view of a super-step");
 constexpr int kPBuf = kBM * kSS * 2;             // bf16 probability tile of a super-step
 constexpr int kWBuf = kBK * kBN * 2;             // bf16 table tile of a step
 constexpr int kWBase = 2 * kPBuf;                // LDS: [P0][P1][W0][W1]
@@ -191,10 +192,16 @@ soft_embed_kernel(const GemmParams p) {
   const int tile_rows = min(kBM, M - m0);
 
   // ---- probability producer: buffer resource at (row m0, column col0) -----------------
+  // Super-step S of a row starts p.a_ss bytes after super-step S - 1: 128 positions for
+  // a row-major matrix, or a whole [rows][128] block for the super-step-tiled layout
+  // of the staged probabilities (then every 4-row load is one contiguous 1 KB run).
   const int64_t a_ld = p.lda * kEsz;
+  const bool a_rowmajor = p.a_ss == (int64_t)kSS * kEsz;
+  const int64_t a_span = a_rowmajor ? p.K * kEsz
+                                    : ((p.K + kSS - 1) / kSS - 1) * p.a_ss + (int64_t)kSS * kEsz;
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(
       static_cast<const unsigned char*>(p.a) + ((int64_t)m0 * p.lda + p.col0) * kEsz,
-      (uint32_t)min((int64_t)(tile_rows - 1) * a_ld + p.K * kEsz, (int64_t)UINT32_MAX));
+      (uint32_t)min((int64_t)(tile_rows - 1) * a_ld + a_span, (int64_t)UINT32_MAX));
   const int a_row0 = kArows * wave;
   const uint32_t a_lo = (uint32_t)((a_row0 + G::row(0, lane)) * a_ld) + kEsz * G::pos(lane);
   // -(lse log2e) of row kArows wave + lane; load i fetches its rows' values with a
@@ -215,7 +222,7 @@ soft_embed_kernel(const GemmParams p) {
 
   // load i of super-step S (clamped by the caller)
   auto load_a = [&](int S, int i) -> AReg {
-    uint32_t voff, soff = (uint32_t)S * (kSS * kEsz);
+    uint32_t voff, soff = (uint32_t)S * (uint32_t)p.a_ss;
     if constexpr (FULL) {
       voff = a_lo;
       soff += (uint32_t)(i * G::kRowsPerLoad * a_ld);
@@ -446,7 +453,7 @@ soft_embed_kernel(const GemmParams p) {
   if (4 * Sf < ks_end) {
     const int64_t kb = (int64_t)Sf * kSS;
     const unsigned char* abase = static_cast<const unsigned char*>(p.a) +
-                                 ((int64_t)m0 * p.lda + p.col0 + kb) * kEsz;
+                                 ((int64_t)m0 * p.lda + p.col0) * kEsz + (int64_t)Sf * p.a_ss;
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int row = min(a_row0 + G::row(i, lane), tile_rows - 1);

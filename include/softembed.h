@@ -153,6 +153,25 @@ se_status se_soft_embed_fused(const float* logits, int64_t ld_logits, const floa
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * se_soft_embed_staged -- the result of se_soft_embed_fused, bit for bit, computed by
+ * staging the bf16 probabilities of the slice in the workspace in a layout the
+ * contraction streams in 1 KB runs ([super-step of 128 positions][row][128]).  On
+ * MI355X at the pages' shapes the extra 2 * n_rows * (e - s) bytes written and read
+ * back cost less than re-reading fp32 logits once per 256-column tile of the fused
+ * kernel.  Arguments and errors as se_soft_embed_fused, with a workspace of
+ * se_soft_embed_staged_workspace_bytes() bytes (16-byte aligned); an empty slice
+ * writes zeros and needs no workspace.
+ */
+size_t se_soft_embed_staged_workspace_bytes(int64_t n_rows, int64_t vocab_start,
+                                            int64_t vocab_end, int64_t d);
+
+se_status se_soft_embed_staged(const float* logits, int64_t ld_logits, const float* row_lse,
+                               int64_t n_rows, int64_t vocab, int64_t vocab_start,
+                               int64_t vocab_end, const uint16_t* w_shard, int64_t w_rows,
+                               int64_t ld_w, int64_t d, float gamma, float* out, int64_t ld_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * se_quantize_table_fp8 -- the e4m3 form of a bf16 embedding table (the pages serve
  * the model with FP8 weights: agentlenshq overview of DiffusionGemma in vLLM,
  * section on performance and quantization, quantized checkpoints).

@@ -295,14 +295,14 @@ def test_onepass_errors(kw, code):
 
 
 def test_onepass_workspace_plan():
-    """bf16 probabilities of the slice (rows padded to 8 positions), partials of every split
+    """bf16 probabilities of the slice in super-steps of 128 positions, partials of every split
     (kept even for one split) and 20 bytes of statistics per (split, row)."""
     ws = b.se_soft_embed_onepass_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
     tile = 256 * 256 * 4
     assert ws(256, 0, 262144, 2816) == up(256 * 262144 * 2) + up(23 * 11 * tile) + \
         up(23 * 256 * 16) + up(23 * 256 * 4)
-    assert ws(5, 16, 17, 16) == up(5 * 8 * 2) + up(tile) + up(256 * 16) + up(256 * 4)
+    assert ws(5, 16, 17, 16) == up(5 * 128 * 2) + up(tile) + up(256 * 16) + up(256 * 4)
     assert ws(5, 16, 16, 16) == 0 and ws(0, 0, 64, 16) == 0
 
 
@@ -327,3 +327,30 @@ def test_merge_slices_errors():
     assert call(out=P3 + 8) == b.SE_ERR_ALIGN
     assert call(ent=P2 + 130) == b.SE_ERR_ALIGN
     assert call(n=0, outs=None, out=None) == b.SE_OK
+
+
+def test_staged_workspace_plan_and_errors():
+    """Tiled bf16 probabilities (super-steps of 128 positions) plus the split partials."""
+    ws = b.se_soft_embed_staged_workspace_bytes
+    up = lambda x: (x + 255) // 256 * 256
+    assert ws(256, 65536, 131072, 2816) == up(256 * 65536 * 2) + 23 * 11 * 256 * 256 * 4
+    assert ws(16, 0, 64, 256) == up(16 * 128 * 2)                     # one split: no partials
+    assert ws(16, 8, 8, 256) == 0
+    st = lib.se_soft_embed_staged
+
+    def call(**kw):
+        a = dict(x=P1, ld=262144, lse=P2, n=256, vocab=262144, s=65536, e=131072, w=P3,
+                 w_rows=65536, ldw=2816, d=2816, gamma=53.0, out=P4, ldo=2816, ws=P5,
+                 ws_bytes=1 << 40)
+        a.update(kw)
+        return st(a["x"], a["ld"], a["lse"], a["n"], a["vocab"], a["s"], a["e"], a["w"],
+                  a["w_rows"], a["ldw"], a["d"], a["gamma"], a["out"], a["ldo"], a["ws"],
+                  a["ws_bytes"], None)
+    assert call(s=0, e=262144) == b.SE_ERR_SLICE          # the pages' failure, as an error code
+    assert call(lse=None) == b.SE_ERR_NULL
+    assert call(ws=None) == b.SE_ERR_NULL
+    assert call(ws_bytes=1024) == b.SE_ERR_WORKSPACE
+    assert call(ws=P5 + 8) == b.SE_ERR_ALIGN
+    assert call(x=P1 + 4) == b.SE_ERR_ALIGN
+    assert call(d=2812, ldw=2816, ldo=2816) == b.SE_ERR_ALIGN
+    assert call(n=0, x=None, lse=None, w=None, out=None, ws=None, ws_bytes=0) == b.SE_OK
