@@ -4,9 +4,12 @@
 A step is one pass of the whole hot path over one canvas batch: se_row_stats over
 the full-width fp32 logits, then the rank's slice contraction, both on one stream.
 The contraction path is chosen with --path:
-  unfused  se_probs_bf16 + se_soft_embed (default: the fastest exact path at these
-           shapes; its output is bitwise the fused call's)
-  fused    se_soft_embed_fused (probabilities rebuilt in the GEMM prologue)
+  step     se_soft_embed_step (default): statistics and the slice embedding in one
+           call, outputs bitwise those of se_row_stats + se_soft_embed_fused
+  unfused  se_row_stats, then se_probs_bf16 + se_soft_embed (bitwise the fused call)
+  staged   se_row_stats, then se_soft_embed_staged (bitwise the fused call)
+  fused    se_row_stats, then se_soft_embed_fused (probabilities rebuilt in the GEMM
+           prologue)
   onepass  se_soft_embed_onepass, which forms the row statistics from the same read
            of the logits (whole-vocabulary workloads only; no se_row_stats call)
 Inputs are seeded synthetic data already resident in HBM when the timed region starts.
@@ -35,8 +38,8 @@ sys.path.insert(0, ROOT)
 METRIC = "soft-embed GFLOP/s + steps/s at L_c=256,V=262144,d=2816; % of roofline"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-KERNEL_SOURCES = ["soft_embed.hip", "probs.hip", "onepass.hip", "se_device.h", "se_launch.h",
-                  "api.cpp"]
+KERNEL_SOURCES = ["soft_embed.hip", "row_stats.hip", "probs.hip", "onepass.hip", "se_device.h",
+                  "se_launch.h", "api.cpp"]
 
 
 def kernel_hash() -> str:
@@ -124,11 +127,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="rank", choices=["rank", "full", "conv", "batch", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", default="unfused", choices=["unfused", "fused", "staged", "onepass"],
-                    help="the step's contraction: se_probs_bf16 + se_soft_embed (default, the "
-                         "fastest exact path at these shapes), se_soft_embed_fused, or "
-                         "se_soft_embed_onepass (whole-vocabulary workloads; it forms the row "
-                         "statistics itself, so the step has no se_row_stats call)")
+    ap.add_argument("--path", default="step",
+                    choices=["unfused", "fused", "staged", "step", "onepass"],
+                    help="how the step runs: se_soft_embed_step (default, one call, the fastest "
+                         "exact path at these shapes), or se_row_stats followed by the unfused, "
+                         "staged or fused contraction, or se_soft_embed_onepass (whole-vocabulary "
+                         "workloads; softmax statistics from the same read of the logits)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference for scaling the HBM byte counters), then exit")
@@ -197,16 +201,22 @@ def main():
     def call_staged(o):
         B.se_soft_embed_staged(x, lse, w.vocab_start, w.vocab_end, shard, w.gamma, o, wss)
 
+    def call_step(o):
+        B.se_soft_embed_step(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse, ent, am,
+                             wss)
+
     def call_onepass(o):
         B.se_soft_embed_onepass(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse, ent,
                                 am, wso)
 
     calls = {"unfused": call_unfused, "fused": call_fused, "staged": call_staged,
-             "onepass": call_onepass}
+             "step": call_step, "onepass": call_onepass}
     call_names = {"unfused": "se_probs_bf16 + se_soft_embed", "fused": "se_soft_embed_fused",
-                  "staged": "se_soft_embed_staged", "onepass": "se_soft_embed_onepass"}
+                  "staged": "se_soft_embed_staged", "step": "se_soft_embed_step",
+                  "onepass": "se_soft_embed_onepass"}
     embed = calls[args.path]
-    with_stats = args.path != "onepass"       # the one-pass call forms the statistics itself
+    # the one-pass and whole-step calls form the statistics themselves
+    with_stats = args.path not in ("onepass", "step")
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -242,7 +252,11 @@ def main():
     flops = w.flops()
     gflops_step = flops / (ms_step * 1e-3) / 1e9
     gflops_call = flops / (us_embed_avg * 1e-6) / 1e9
-    call_bytes = fused_call_bytes(w) + (16 * L if args.path == "onepass" else 0)
+    call_bytes = fused_call_bytes(w)
+    if args.path == "onepass":          # plus the statistics it writes
+        call_bytes += 16 * L
+    elif args.path == "step":           # the whole step: every logit once, table, outputs
+        call_bytes = row_stats_bytes(w) + 2 * w.k * w.d + 4 * L * w.d
     achieved_gbs = call_bytes / (us_embed_avg * 1e-6) / 1e9
     t_roof_call_us = max(flops / (PEAK_BF16_TFLOPS * 1e12), call_bytes / (PEAK_HBM_GBS * 1e9)) * 1e6
     stats_bytes = row_stats_bytes(w) if with_stats else 0

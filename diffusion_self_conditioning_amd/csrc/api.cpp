@@ -149,6 +149,33 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
   return from_hip(se::launch_soft_embed(p, fused, w_scale != nullptr, st));
 }
 
+// The contraction of super-step-tiled bf16 probabilities ([K / 128][n_rows][128], slice
+// position 0 first) in the workspace of a staged call.
+se_status run_staged_gemm(const se::StagedLayout& o, const uint16_t* probs, int64_t n_rows,
+                          int64_t K, const uint16_t* w_shard, int64_t ld_w, int64_t d,
+                          float gamma, float* out, int64_t ld_out, unsigned char* ws,
+                          hipStream_t st) {
+  se::GemmParams p{};
+  p.a = probs;
+  p.lda = se::kSuperStep;
+  p.a_ss = n_rows * se::kSuperStep * 2;
+  p.col0 = 0;
+  p.w = w_shard;
+  p.ldw = ld_w;
+  p.M = n_rows;
+  p.N = d;
+  p.K = K;
+  p.gamma = gamma;
+  p.out = out;
+  p.ldo = ld_out;
+  p.ws = reinterpret_cast<float*>(ws + o.off_parts);
+  p.tiles_n = (int)o.g.tiles_n;
+  p.tiles = (int)o.g.tiles;
+  p.splits = (int)o.g.splits;
+  p.kblocks = (int)o.g.kblocks;
+  return from_hip(se::launch_soft_embed(p, false, false, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,7 +194,7 @@ const char* se_status_string(se_status s) {
 }
 
 const char* se_version(void) {
-  return "libsoftembed 0.3 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table, one-pass, staged)";
+  return "libsoftembed 0.3 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table, one-pass, staged, step)";
 }
 
 se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
@@ -287,25 +314,51 @@ se_status se_soft_embed_staged(const float* logits, int64_t ld_logits, const flo
   rc = from_hip(se::launch_probs_bf16_tiled(logits, ld_logits, row_lse, n_rows, vocab_start, K,
                                             probs, st));
   if (rc != SE_OK) return rc;
-  se::GemmParams p{};
-  p.a = probs;                       // super-step-tiled: [K / 128][n_rows][128]
-  p.lda = se::kSuperStep;
-  p.a_ss = n_rows * se::kSuperStep * 2;
-  p.col0 = 0;
-  p.w = w_shard;
-  p.ldw = ld_w;
-  p.M = n_rows;
-  p.N = d;
-  p.K = K;
-  p.gamma = gamma;
-  p.out = out;
-  p.ldo = ld_out;
-  p.ws = reinterpret_cast<float*>(ws + o.off_parts);
-  p.tiles_n = (int)o.g.tiles_n;
-  p.tiles = (int)o.g.tiles;
-  p.splits = (int)o.g.splits;
-  p.kblocks = (int)o.g.kblocks;
-  return from_hip(se::launch_soft_embed(p, false, false, st));
+  return run_staged_gemm(o, probs, n_rows, K, w_shard, ld_w, d, gamma, out, ld_out, ws, st);
+}
+
+se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_rows,
+                             int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                             const uint16_t* w_shard, int64_t w_rows, int64_t ld_w, int64_t d,
+                             float gamma, float* out, int64_t ld_out, float* row_max,
+                             float* row_lse, float* row_entropy, int32_t* row_argmax,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
+  if (rc != SE_OK) return rc;
+  if (ld_logits < vocab) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  if (!logits || !w_shard || !out || !row_max || !row_lse || !row_entropy || !row_argmax)
+    return SE_ERR_NULL;
+  rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_shard, out);
+  if (rc != SE_OK) return rc;
+  if (!aligned16(logits) || (ld_logits % 4) != 0) return SE_ERR_ALIGN;
+  if (!aligned4(row_max) || !aligned4(row_lse) || !aligned4(row_entropy) || !aligned4(row_argmax))
+    return SE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t K = vocab_end - vocab_start;
+  if (K == 0) {                       // statistics, and zeros for the empty slice
+    rc = from_hip(se::launch_row_stats(logits, ld_logits, n_rows, (int)vocab, row_max, row_lse,
+                                       row_entropy, row_argmax, st));
+    if (rc != SE_OK) return rc;
+    return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start, vocab_end,
+                          w_shard, nullptr, ld_w, d, gamma, out, ld_out, workspace,
+                          workspace_bytes, stream);
+  }
+  const se::StagedLayout o = se::staged_layout(n_rows, K, d);
+  if (o.g.grid > INT32_MAX) return SE_ERR_SHAPE;
+  if ((int64_t)se::tiled_probs_bytes(n_rows, K) > (int64_t)UINT32_MAX ||
+      K * ld_w * 2 > (int64_t)UINT32_MAX)
+    return SE_ERR_SHAPE;
+  if (workspace_bytes < o.total) return SE_ERR_WORKSPACE;
+  if (!workspace) return SE_ERR_NULL;
+  if (!aligned16(workspace)) return SE_ERR_ALIGN;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t* probs = reinterpret_cast<uint16_t*>(ws + o.off_probs);
+  rc = from_hip(se::launch_row_stats_probs(logits, ld_logits, n_rows, (int)vocab, row_max,
+                                           row_lse, row_entropy, row_argmax, vocab_start, K,
+                                           probs, st));
+  if (rc != SE_OK) return rc;
+  return run_staged_gemm(o, probs, n_rows, K, w_shard, ld_w, d, gamma, out, ld_out, ws, st);
 }
 
 se_status se_quantize_table_fp8(const uint16_t* w, int64_t ld_w, int64_t rows, int64_t d,

@@ -15,6 +15,13 @@
 // carry S1 and the argmax.  One workgroup of 1024 threads owns one row; each
 // thread streams 16-byte loads, 4 in flight, then wavefront shuffles and LDS
 // combine the 16 wave states in a fixed order.
+//
+// PROBS (the whole-step entry point): once the row's lse is known, the same
+// workgroup reads the vocabulary slice [col0, col0 + K) of its row again -- moments
+// after streaming it, so mostly from cache -- and writes the slice's bf16
+// probabilities, exactly as probs.hip forms them, in the super-step-tiled layout the
+// contraction streams: position k of row i at
+// probs[(k / kSuperStep) * n_rows * kSuperStep + i * kSuperStep + k % kSuperStep].
 #include "se_device.h"
 #include "se_launch.h"
 
@@ -79,10 +86,12 @@ __device__ __forceinline__ RowState shfl_xor_state(const RowState& s, int mask) 
   return o;
 }
 
+template <bool PROBS>
 __global__ void __launch_bounds__(kRowThreads)
 row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
                  float* __restrict__ row_max, float* __restrict__ row_lse,
-                 float* __restrict__ row_entropy, int32_t* __restrict__ row_argmax) {
+                 float* __restrict__ row_entropy, int32_t* __restrict__ row_argmax,
+                 int64_t col0, int64_t K, uint16_t* __restrict__ probs, int64_t n_rows) {
   const int64_t row = blockIdx.x;
   const float* __restrict__ x = logits + row * ld;
   const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x);
@@ -150,6 +159,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
   for (int mask = 32; mask >= 1; mask >>= 1) merge(st, shfl_xor_state(st, mask));
 
   __shared__ RowState partial[kRowThreads / 64];
+  __shared__ float row_lse_s;
   const int wave = tid >> 6, lane = tid & 63;
   if (lane == 0) partial[wave] = st;
   __syncthreads();
@@ -164,6 +174,43 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
       row_argmax[row] = r.idx;
       row_lse[row] = r.m + lnz;
       row_entropy[row] = lnz - (r.s1 * kLn2) / r.z;
+      row_lse_s = r.m + lnz;
+    }
+  }
+  if constexpr (PROBS) {
+    __syncthreads();
+    const float nl = neg_lse_log2(row_lse_s);
+    const float* __restrict__ xs = x + col0;
+    uint16_t* __restrict__ prow = probs + row * kSuperStep;
+    auto put8 = [&](int64_t k, const float4& a, const float4& b) {
+      uint4 o;
+      o.x = pack_bf16x2(prob_from_logit(a.x, nl), prob_from_logit(a.y, nl));
+      o.y = pack_bf16x2(prob_from_logit(a.z, nl), prob_from_logit(a.w, nl));
+      o.z = pack_bf16x2(prob_from_logit(b.x, nl), prob_from_logit(b.y, nl));
+      o.w = pack_bf16x2(prob_from_logit(b.z, nl), prob_from_logit(b.w, nl));
+      *reinterpret_cast<uint4*>(prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep) = o;
+    };
+    // four 8-position groups per thread in flight, then the remaining groups one by one
+    constexpr int64_t kStride = 8 * (int64_t)kRowThreads;
+    int64_t k = 8 * (int64_t)tid;
+    for (; k + 3 * kStride + 8 <= K; k += 4 * kStride) {
+      float4 a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = reinterpret_cast<const float4*>(xs + k + u * kStride)[0];
+        b[u] = reinterpret_cast<const float4*>(xs + k + u * kStride)[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) put8(k + u * kStride, a[u], b[u]);
+    }
+    for (; k < K; k += kStride) {
+      if (k + 8 <= K) {
+        put8(k, reinterpret_cast<const float4*>(xs + k)[0], reinterpret_cast<const float4*>(xs + k)[1]);
+      } else {
+        uint16_t* __restrict__ p = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
+        for (int64_t j = 0; j < K - k; ++j)
+          p[j] = __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(xs[k + j], nl));
+      }
     }
   }
 }
@@ -173,8 +220,19 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
 hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int vocab,
                             float* row_max, float* row_lse, float* row_entropy,
                             int32_t* row_argmax, hipStream_t stream) {
-  hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)n_rows), dim3(kRowThreads), 0, stream,
-                     logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax);
+  hipLaunchKernelGGL(row_stats_kernel<false>, dim3((unsigned)n_rows), dim3(kRowThreads), 0,
+                     stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax,
+                     (int64_t)0, (int64_t)0, nullptr, n_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats_probs(const float* logits, int64_t ld, int64_t n_rows, int vocab,
+                                  float* row_max, float* row_lse, float* row_entropy,
+                                  int32_t* row_argmax, int64_t col0, int64_t K,
+                                  uint16_t* probs, hipStream_t stream) {
+  hipLaunchKernelGGL(row_stats_kernel<true>, dim3((unsigned)n_rows), dim3(kRowThreads), 0,
+                     stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax, col0,
+                     K, probs, n_rows);
   return hipGetLastError();
 }
 

@@ -172,6 +172,25 @@ se_status se_soft_embed_staged(const float* logits, int64_t ld_logits, const flo
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * se_soft_embed_step -- one whole sampler step for a rank in one call: se_row_stats
+ * over the full width [0, vocab) followed by se_soft_embed_fused on [s, e), with
+ * outputs bit for bit those of the two calls.  The statistics kernel writes the
+ * slice's bf16 probabilities (staged, as se_soft_embed_staged) right after each
+ * row's statistics, while that row's logits are still in cache, so the slice is not
+ * read from memory a second time and one launch boundary disappears.
+ * Arguments: those of se_row_stats and se_soft_embed_fused together (row_max,
+ * row_lse, row_entropy and row_argmax are outputs here); workspace of
+ * se_soft_embed_staged_workspace_bytes() bytes (16-byte aligned; none for an empty
+ * slice).  Errors as those calls.
+ */
+se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_rows,
+                             int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                             const uint16_t* w_shard, int64_t w_rows, int64_t ld_w, int64_t d,
+                             float gamma, float* out, int64_t ld_out, float* row_max,
+                             float* row_lse, float* row_entropy, int32_t* row_argmax,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * se_quantize_table_fp8 -- the e4m3 form of a bf16 embedding table (the pages serve
  * the model with FP8 weights: agentlenshq overview of DiffusionGemma in vLLM,
  * section on performance and quantization, quantized checkpoints).

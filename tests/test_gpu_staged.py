@@ -1,4 +1,4 @@
-"""GPU parity of se_soft_embed_staged (MI355X), through the C ABI.
+"""GPU parity of se_soft_embed_staged and se_soft_embed_step (MI355X), through the C ABI.
 
 The staged call must return se_soft_embed_fused's output bit for bit: the same bf16
 probabilities (same rounding), contracted in the same order; only their trip through
@@ -7,6 +7,8 @@ test_gpu_parity.py; here the staged output is also gated directly on the small c
 Cases: whole and partial 256-row tiles, slices of 1 / 63 / 4097 positions and ragged
 hidden sizes, slices that start mid-vocabulary, shard rows past the slice holding NaN
 (never read), one split and many splits, and the one-rank workload at full size.
+se_soft_embed_step must return se_row_stats' statistics and the fused call's
+embedding bit for bit, on the same kinds of cases plus an empty slice.
 """
 import sys
 
@@ -100,3 +102,58 @@ def test_staged_full_size_rank():
     ref = oracle.soft_embed(x[rows], w.vocab_start, w.vocab_end,
                             bits[w.vocab_start:w.vocab_end], w.gamma)
     assert rel_fro(staged.cpu().numpy()[rows], ref) <= 5e-3
+
+
+STEP_CASES = {
+    # name: (L, V, s, e, d, seed)
+    "tiny": (16, 4096, 0, 4096, 256, 21),
+    "ragged": (17, 20008, 8, 20008, 48, 22),
+    "slice-63": (33, 1003, 64, 127, 2816, 23),        # V not a multiple of 4
+    "two-row-tiles": (300, 2048, 1024, 2048, 512, 24),
+    "empty-slice": (8, 512, 16, 16, 16, 25),
+}
+
+
+@pytest.mark.parametrize("case", sorted(STEP_CASES))
+def test_step_equals_row_stats_then_fused(case):
+    """se_soft_embed_step: statistics bitwise se_row_stats', embedding bitwise the fused call's."""
+    L, V, s, e, d, seed = STEP_CASES[case]
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    x[np.arange(L), rng.integers(0, V, L)] += 8.0
+    tab = wl.fp32_to_bf16_bits((rng.standard_normal((e - s + 24, d)) * 0.02).astype(np.float32))
+    tab[e - s:] = 0x7FC0
+    ld = ((V + 3) // 4) * 4
+    buf = np.full((L, ld), np.float32(1e30), np.float32)
+    buf[:, :V] = x
+    say("step", case, (L, V, s, e, d))
+    x_t, w_t = dev(buf)[:, :V], dev(tab)
+    out, mx, lse, ent, am = api.soft_embed_step(x_t, s, e, w_t, 5.0)
+    mx2, lse2, ent2, am2 = api.row_stats(x_t)
+    ref = api.soft_embed(x_t, lse2, s, e, w_t, 5.0, fused=True)
+    torch.cuda.synchronize()
+    for a, b in ((mx, mx2), (lse, lse2), (ent, ent2), (am, am2), (out, ref)):
+        assert torch.equal(a, b)
+    st = oracle.row_stats(x)
+    np.testing.assert_array_equal(am.cpu().numpy(), st["argmax"])
+    if e > s:
+        assert rel_fro(out.cpu().numpy(), oracle.soft_embed(x, s, e, tab[:e - s], 5.0)) <= 5e-3
+    else:
+        assert torch.count_nonzero(out) == 0
+
+
+def test_step_full_size_rank():
+    w = wl.get("rank")
+    say("step full-size rank: inputs")
+    x = wl.make_logits(w)
+    bits, _ = wl.make_table(w)
+    x_t, tab_t = dev(x), dev(bits)
+    shard = tab_t[w.vocab_start:]
+    say("step full-size rank: gpu")
+    out, mx, lse, ent, am = api.soft_embed_step(x_t, w.vocab_start, w.vocab_end, shard, w.gamma)
+    mx2, lse2, ent2, am2 = api.row_stats(x_t)
+    ref = api.soft_embed(x_t, lse2, w.vocab_start, w.vocab_end, shard, w.gamma, fused=True)
+    torch.cuda.synchronize()
+    for a, b in ((mx, mx2), (lse, lse2), (ent, ent2), (am, am2), (out, ref)):
+        assert torch.equal(a, b)
+    np.testing.assert_array_equal(am.cpu().numpy(), wl.planted_index(w))
