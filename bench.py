@@ -112,10 +112,18 @@ def cpu_baseline(w, x_np, bits, budget_s: float = 12.0):
         oracle.soft_embed(x_np[:rows], w.vocab_start, w.vocab_end, shard, w.gamma)
         dt = time.perf_counter() - t0
     flops = 2 * rows * w.k * w.d
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{rows} of {w.rows} rows of the {w.name} workload (row stats over "
-                      f"V={w.vocab} + fp64 contraction over the {w.k}-row slice), {dt:.2f} s"}
+                      f"V={w.vocab} + fp64 contraction over the {w.k}-row slice), {dt:.2f} s "
+                      f"on {model}"}
 
 
 def main():
@@ -248,6 +256,7 @@ def main():
     us_embed = [ev[k][1].elapsed_time(ev[k][2]) * 1e3 for k in range(K)]
     us_stats_avg = sum(us_stats) / K
     us_embed_avg = sum(us_embed) / K
+    us_step_sorted = sorted(a + b for a, b in zip(us_stats, us_embed))
 
     flops = w.flops()
     gflops_step = flops / (ms_step * 1e-3) / 1e9
@@ -367,6 +376,26 @@ def main():
                     "merge_4_slices_us": round(us_m, 2)}
     del oo, so, ao, outs4, st4, am4
 
+    # cold step: a 1 GiB write between steps evicts L2 and the 256 MB MALL first; and the
+    # achievable HBM rate of a plain 1 GiB device-to-device copy, beside the 8 TB/s peak
+    scrub = torch.empty(1 << 28, device=dev)
+    cold = []
+    for k in range(5):
+        scrub.fill_(float(k))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if with_stats:
+            stats()
+        embed(out)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    src = torch.ones(1 << 28, device=dev)
+    copy_us = event_time_us(lambda: scrub.copy_(src), 10, 3)
+    ceilings = {"cold_step_us_median": round(sorted(cold)[len(cold) // 2], 2),
+                "hbm_copy_gbs": round(2 * src.numel() * 4 / (copy_us * 1e-6) / 1e9, 1)}
+    del scrub, src
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
@@ -384,9 +413,12 @@ def main():
                    "rows": L, "vocab": w.vocab, "vocab_start": w.vocab_start,
                    "vocab_end": w.vocab_end, "d": d, "seed": w.seed},
         "steps_per_s": round(1e3 / ms_step, 2),
+        "canvas_steps_per_s": round(1e3 / ms_step * (L / 256), 2),
         "gflops_call": round(gflops_call, 2),
         "kernel_us": {"se_row_stats": round(us_stats_avg, 2) if with_stats else None,
                       call_names[args.path]: round(us_embed_avg, 2)},
+        "step_us_median": round(us_step_sorted[K // 2], 2),
+        "step_us_min": round(us_step_sorted[0], 2),
         "roofline": roof,
         "roofline_step": {"t_roof_us": round(t_roof_step_us, 2),
                           "frac": round(t_roof_step_us / (ms_step * 1e3), 4),
@@ -398,6 +430,7 @@ def main():
         "reduce_partials": red_side,
         "fp8_table": fp8_side,
         "onepass": onepass_side,
+        "cold_and_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -10,8 +10,37 @@
 #include <hip/hip_runtime_api.h>
 
 #include <climits>
+#include <mutex>
 
 namespace se {
+
+namespace {
+constexpr int kMaxCachedDevices = 64;
+std::once_flag cu_once[kMaxCachedDevices];
+int cu_count[kMaxCachedDevices];
+
+int query_cu_count(int dev) {
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1)
+    return kTargetCUs;
+  return n;
+}
+}  // namespace
+
+// Compute units of the calling thread's current device, read once per device and
+// kept for the life of the process (the library's only global state).  Without a
+// usable device (a host with no GPU asking for a workspace size) the MI355X count.
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return kTargetCUs;
+  }
+  if (dev >= kMaxCachedDevices) return query_cu_count(dev);
+  std::call_once(cu_once[dev], [dev] { cu_count[dev] = query_cu_count(dev); });
+  return cu_count[dev];
+}
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan g{};
@@ -20,8 +49,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   g.tiles = g.tiles_m * g.tiles_n;
   g.kblocks = (K + kSplitQuantum - 1) / kSplitQuantum;
   g.splits = 1;
-  if (g.tiles > 0 && g.tiles < kTargetCUs) {
-    int64_t s = kTargetCUs / g.tiles;
+  const int64_t cus = device_cu_count();
+  if (g.tiles > 0 && g.tiles < cus) {
+    int64_t s = cus / g.tiles;
     const int64_t cap = g.kblocks / kMinBlocksPerSplit;
     if (s > cap) s = cap;
     g.splits = s < 1 ? 1 : s;

@@ -26,7 +26,7 @@ constexpr int kGemmThreads = 64 * SE_WAVES;
 constexpr int kSplitQuantum = 128;        // vocab positions per split block
 constexpr int kSuperStep = 128;           // vocab positions per super-step of the contraction
 constexpr int kMinBlocksPerSplit = 2;     // at least 256 vocab positions per split
-constexpr int kTargetCUs = 256;           // MI355X compute units: sizes the split count
+constexpr int kTargetCUs = 256;           // MI355X compute units: the count used without a device
 constexpr int64_t kTileFloats = (int64_t)kBM * kBN;
 
 struct GemmPlan {
@@ -34,6 +34,8 @@ struct GemmPlan {
   size_t ws_bytes;
 };
 
+// Splits fill the current device's compute units: tiles x splits ~ CU count.
+int device_cu_count();
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 
 struct OnepassLayout {

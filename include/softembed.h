@@ -29,9 +29,14 @@
  *  - Outputs must not alias inputs or the workspace.
  *  - Every argument check happens synchronously on the host BEFORE anything is
  *    enqueued; on any error nothing is launched and the outputs are untouched.
- *  - Results are bitwise reproducible for the same inputs and shapes: the work
- *    decomposition depends only on the shapes, and every reduction runs in a
+ *  - Results are bitwise reproducible for the same inputs and shapes on the same
+ *    kind of device: the work decomposition depends only on the shapes and the
+ *    current device's compute-unit count (the contraction is split over the
+ *    vocabulary until tiles x splits fill the CUs), and every reduction runs in a
  *    fixed order.
+ *  - The only global state is a per-device cache of that CU count, read once per
+ *    device (std::call_once) from the HIP runtime; without a usable device the
+ *    MI355X count, 256, is used.
  *  - Logits must be finite (not checked on the device).
  *  - n_rows == 0 is a no-op that checks only sizes; its pointers may be NULL.
  *  - Calls are thread-safe and capture-safe (no allocation, no sync, no host
@@ -106,7 +111,9 @@ se_status se_probs_bf16(const float* logits, int64_t ld_logits, const float* row
 /*
  * se_soft_embed_workspace_bytes -- device workspace the two soft-embed entry
  * points need for this shape (0 when the contraction is not split).  It
- * depends only on the shape.  Returns 0 for shapes the calls would reject.
+ * depends on the shape and the current device's CU count, so query it with the
+ * device current that the calls will run on.  Returns 0 for shapes the calls
+ * would reject.
  */
 size_t se_soft_embed_workspace_bytes(int64_t n_rows, int64_t vocab_start, int64_t vocab_end,
                                      int64_t d);
