@@ -136,11 +136,12 @@ def main():
     ap.add_argument("--workload", default="rank", choices=["rank", "full", "conv", "batch", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="step",
-                    choices=["unfused", "fused", "staged", "step", "onepass"],
-                    help="how the step runs: se_soft_embed_step (default, one call, the fastest "
-                         "exact path at these shapes), or se_row_stats followed by the unfused, "
-                         "staged or fused contraction, or se_soft_embed_onepass (whole-vocabulary "
-                         "workloads; softmax statistics from the same read of the logits)")
+                    choices=["unfused", "fused", "staged", "step", "step_onepass", "onepass"],
+                    help="how the step runs: se_soft_embed_step (default, one call, bitwise the "
+                         "separate calls), se_soft_embed_step_onepass (one call, one read of the "
+                         "logits), or se_row_stats followed by the unfused, staged or fused "
+                         "contraction, or se_soft_embed_onepass (whole-vocabulary workloads; "
+                         "softmax statistics from the same read of the logits)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference for scaling the HBM byte counters), then exit")
@@ -195,6 +196,7 @@ def main():
     probs = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16)
     wso = api.onepass_workspace(L, w.vocab_start, w.vocab_end, d, dev)
     wss = api.staged_workspace(L, w.vocab_start, w.vocab_end, d, dev)
+    ws1 = api.step_onepass_workspace(L, w.vocab, w.vocab_start, w.vocab_end, d, dev)
 
     def stats():
         B.se_row_stats(x, mx, lse, ent, am)
@@ -213,18 +215,23 @@ def main():
         B.se_soft_embed_step(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse, ent, am,
                              wss)
 
+    def call_step_onepass(o):
+        B.se_soft_embed_step_onepass(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse,
+                                     ent, am, ws1)
+
     def call_onepass(o):
         B.se_soft_embed_onepass(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse, ent,
                                 am, wso)
 
     calls = {"unfused": call_unfused, "fused": call_fused, "staged": call_staged,
-             "step": call_step, "onepass": call_onepass}
+             "step": call_step, "step_onepass": call_step_onepass, "onepass": call_onepass}
     call_names = {"unfused": "se_probs_bf16 + se_soft_embed", "fused": "se_soft_embed_fused",
                   "staged": "se_soft_embed_staged", "step": "se_soft_embed_step",
+                  "step_onepass": "se_soft_embed_step_onepass",
                   "onepass": "se_soft_embed_onepass"}
     embed = calls[args.path]
     # the one-pass and whole-step calls form the statistics themselves
-    with_stats = args.path not in ("onepass", "step")
+    with_stats = args.path not in ("onepass", "step", "step_onepass")
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -264,7 +271,7 @@ def main():
     call_bytes = fused_call_bytes(w)
     if args.path == "onepass":          # plus the statistics it writes
         call_bytes += 16 * L
-    elif args.path == "step":           # the whole step: every logit once, table, outputs
+    elif args.path in ("step", "step_onepass"):   # the whole step: every logit once, table, outputs
         call_bytes = row_stats_bytes(w) + 2 * w.k * w.d + 4 * L * w.d
     achieved_gbs = call_bytes / (us_embed_avg * 1e-6) / 1e9
     t_roof_call_us = max(flops / (PEAK_BF16_TFLOPS * 1e12), call_bytes / (PEAK_HBM_GBS * 1e9)) * 1e6
@@ -286,12 +293,21 @@ def main():
     # each event-timed as one call; the unfused and fused outputs are compared bitwise
     side = {}
     ref_out = out.clone()
+    exact = args.path in ("unfused", "fused", "staged", "step")
     for name in ("unfused", "fused", "staged"):
         o = torch.empty_like(out)
         side[name + "_call_us"] = round(event_time_us(lambda: calls[name](o), K, args.warmup), 2)
-        if args.path != "onepass":
+        if exact:
             side[name + "_equals_step_output"] = bool(torch.equal(o, ref_out))
         del o
+    # the two whole-step calls (statistics included), and how far apart their outputs are
+    o1, o2 = torch.empty_like(out), torch.empty_like(out)
+    side["step_call_us"] = round(event_time_us(lambda: call_step(o1), K, args.warmup), 2)
+    side["step_onepass_call_us"] = round(event_time_us(lambda: call_step_onepass(o2), K,
+                                                       args.warmup), 2)
+    side["step_onepass_rel_diff_vs_step"] = float(
+        (o2.double() - o1.double()).norm() / o1.double().norm())
+    del o1, o2
     side["gflops_unfused_call"] = round(flops / (side["unfused_call_us"] * 1e-6) / 1e9, 2)
     side["gflops_fused_call"] = round(flops / (side["fused_call_us"] * 1e-6) / 1e9, 2)
     side["gflops_staged_call"] = round(flops / (side["staged_call_us"] * 1e-6) / 1e9, 2)

@@ -12,7 +12,8 @@ from ._binding import (SoftEmbedError, se_merge_slices, se_probs_bf16,  # noqa: 
                        se_quantize_table_fp8, se_row_stats, se_soft_embed, se_soft_embed_fp8,
                        se_soft_embed_fp8_fused, se_soft_embed_fused, se_soft_embed_onepass,
                        se_soft_embed_onepass_workspace_bytes, se_soft_embed_staged,
-                       se_soft_embed_step,
+                       se_soft_embed_step, se_soft_embed_step_onepass,
+                       se_soft_embed_step_onepass_workspace_bytes,
                        se_soft_embed_staged_workspace_bytes, se_soft_embed_workspace_bytes,
                        se_status_string, se_version)
 
@@ -114,14 +115,28 @@ def soft_embed_onepass(logits, vocab_start, vocab_end, w_shard, gamma, *, ws=Non
     return out, mx, lse, ent, am
 
 
-def soft_embed_step(logits, vocab_start, vocab_end, w_shard, gamma, *, ws=None, stream=None):
+def step_onepass_workspace(n_rows, vocab, vocab_start, vocab_end, d, device):
+    nbytes = se_soft_embed_step_onepass_workspace_bytes(n_rows, vocab, vocab_start, vocab_end, d)
+    return torch.empty((nbytes + 3) // 4, device=device, dtype=torch.float32) if nbytes else None
+
+
+def soft_embed_step(logits, vocab_start, vocab_end, w_shard, gamma, *, ws=None, stream=None,
+                    onepass=False):
     """(out, row_max, row_lse, row_entropy, row_argmax): full-width statistics and the slice's
-    soft embedding in one call."""
+    soft embedding in one call.  ``onepass=True`` runs se_soft_embed_step_onepass (one read
+    of the logits; equal to the two-pass step up to rounding)."""
     n, d = logits.shape[0], w_shard.shape[1]
     f = dict(device=logits.device, dtype=torch.float32)
     out = torch.empty((n, d), **f)
     mx, lse, ent = torch.empty(n, **f), torch.empty(n, **f), torch.empty(n, **f)
     am = torch.empty(n, device=logits.device, dtype=torch.int32)
+    if onepass:
+        if ws is None:
+            ws = step_onepass_workspace(n, logits.shape[1], vocab_start, vocab_end, d,
+                                        logits.device)
+        se_soft_embed_step_onepass(logits, vocab_start, vocab_end, w_shard, gamma, out, mx, lse,
+                                   ent, am, ws, stream=stream)
+        return out, mx, lse, ent, am
     if ws is None:
         ws = staged_workspace(n, vocab_start, vocab_end, d, logits.device)
     se_soft_embed_step(logits, vocab_start, vocab_end, w_shard, gamma, out, mx, lse, ent, am, ws,

@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <climits>
 #include <mutex>
 
@@ -69,18 +70,72 @@ size_t tiled_probs_bytes(int64_t n_rows, int64_t K) {
 }
 }  // namespace
 
+int sweep_waves(const GemmPlan& g, int64_t K) {
+  if (K <= 0) return 0;
+  const int64_t longest = std::min(((g.kblocks + g.splits - 1) / g.splits) * kSplitQuantum, K);
+  for (int w : {1, 2, 4})
+    if (longest <= kSweepPiece * (int64_t)w) return w;
+  return 0;
+}
+
 // Workspace of the one-pass call: tiled bf16 probabilities of the slice, the split
-// partials (kept even for one split), and per-(split, row) statistics.
+// partials (kept even for one split), per-(split, row) statistics, and per-(split, row)
+// factors.
 OnepassLayout onepass_layout(int64_t n_rows, int64_t K, int64_t d) {
   auto up = up256;
   OnepassLayout o{};
   o.g = plan_gemm(n_rows, d, K);
   o.rows_pad = o.g.tiles_m * kBM;
+  o.sweep_waves = sweep_waves(o.g, K);
   o.off_probs = 0;
   o.off_parts = up(tiled_probs_bytes(n_rows, K));
   o.off_stats = o.off_parts + up((size_t)(o.g.splits * o.g.tiles * kTileFloats) * 4);
   o.off_arg = o.off_stats + up((size_t)(o.g.splits * o.rows_pad) * 16);
-  o.total = o.off_arg + up((size_t)(o.g.splits * o.rows_pad) * 4);
+  o.off_fac = o.off_arg + up((size_t)(o.g.splits * o.rows_pad) * 4);
+  o.total = o.off_fac + up((size_t)(o.g.splits * o.rows_pad) * 4);
+  return o;
+}
+
+// Workspace of the one-read step: tiled bf16 probabilities of the slice, the split
+// partials (kept even for one split), per-(range, row) statistics and argmax, and the
+// per-(split, row) factors.  sweep_waves = 0 when the slice is empty or a split range
+// is longer than 4 waves hold in registers (4 * kSweepPiece positions); the call is then
+// the two-pass step and the workspace is that call's.
+struct StepOnepassLayout {
+  GemmPlan g;
+  StepRanges rg;
+  int sweep_waves, n_ranges;
+  size_t off_probs, off_parts, off_stats, off_arg, off_fac, total;
+};
+
+StagedLayout staged_layout(int64_t n_rows, int64_t K, int64_t d);
+
+StepOnepassLayout step_onepass_layout(int64_t n_rows, int64_t vocab, int64_t s, int64_t e,
+                                      int64_t d) {
+  StepOnepassLayout o{};
+  const int64_t K = e - s;
+  o.g = plan_gemm(n_rows, d, K);
+  o.sweep_waves = sweep_waves(o.g, K);
+  if (o.sweep_waves == 0) {
+    o.total = staged_layout(n_rows, K, d).total;
+    return o;
+  }
+  StepRanges& r = o.rg;
+  r.s = s;
+  r.e = e;
+  r.vocab = vocab;
+  r.chunk = kSweepPiece * (int64_t)o.sweep_waves;
+  r.n_pre = (int)((s + r.chunk - 1) / r.chunk);
+  r.splits = (int)o.g.splits;
+  r.kblocks = (int)o.g.kblocks;
+  r.n_post = e < vocab ? (int)((vocab - (e & ~(int64_t)3) + r.chunk - 1) / r.chunk) : 0;
+  o.n_ranges = r.n_pre + r.splits + r.n_post;
+  o.off_probs = 0;
+  o.off_parts = up256(tiled_probs_bytes(n_rows, K));
+  o.off_stats = o.off_parts + up256((size_t)(o.g.splits * o.g.tiles * kTileFloats) * 4);
+  o.off_arg = o.off_stats + up256((size_t)o.n_ranges * (size_t)n_rows * 16);
+  o.off_fac = o.off_arg + up256((size_t)o.n_ranges * (size_t)n_rows * 4);
+  o.total = o.off_fac + up256((size_t)o.g.splits * (size_t)n_rows * 4);
   return o;
 }
 
@@ -224,7 +279,7 @@ const char* se_status_string(se_status s) {
 }
 
 const char* se_version(void) {
-  return "libsoftembed 0.3 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table, one-pass, staged, step)";
+  return "libsoftembed 0.4 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table, one-pass, staged, step, one-read step)";
 }
 
 se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
@@ -391,6 +446,86 @@ se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_r
   return run_staged_gemm(o, probs, n_rows, K, w_shard, ld_w, d, gamma, out, ld_out, ws, st);
 }
 
+size_t se_soft_embed_step_onepass_workspace_bytes(int64_t n_rows, int64_t vocab,
+                                                  int64_t vocab_start, int64_t vocab_end,
+                                                  int64_t d) {
+  if (n_rows < 0 || d < 1 || vocab_start < 0 || vocab_end < vocab_start || vocab < vocab_end)
+    return 0;
+  if (n_rows > INT32_MAX || d > INT32_MAX || vocab > INT32_MAX) return 0;
+  if (n_rows == 0) return 0;
+  return se::step_onepass_layout(n_rows, vocab, vocab_start, vocab_end, d).total;
+}
+
+se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int64_t n_rows,
+                                     int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                                     const uint16_t* w_shard, int64_t w_rows, int64_t ld_w,
+                                     int64_t d, float gamma, float* out, int64_t ld_out,
+                                     float* row_max, float* row_lse, float* row_entropy,
+                                     int32_t* row_argmax, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
+  if (rc != SE_OK) return rc;
+  if (ld_logits < vocab) return SE_ERR_SHAPE;
+  if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  const se::StepOnepassLayout o =
+      se::step_onepass_layout(n_rows, vocab, vocab_start, vocab_end, d);
+  if (o.sweep_waves == 0)                  // empty slice, or split ranges too long: two passes
+    return se_soft_embed_step(logits, ld_logits, n_rows, vocab, vocab_start, vocab_end, w_shard,
+                              w_rows, ld_w, d, gamma, out, ld_out, row_max, row_lse,
+                              row_entropy, row_argmax, workspace, workspace_bytes, stream);
+  if (!logits || !w_shard || !out || !row_max || !row_lse || !row_entropy || !row_argmax)
+    return SE_ERR_NULL;
+  rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_shard, out);
+  if (rc != SE_OK) return rc;
+  if (!aligned16(logits) || (ld_logits % 4) != 0) return SE_ERR_ALIGN;
+  if (!aligned4(row_max) || !aligned4(row_lse) || !aligned4(row_entropy) || !aligned4(row_argmax))
+    return SE_ERR_ALIGN;
+  const int64_t K = vocab_end - vocab_start;
+  if (o.g.grid > INT32_MAX || n_rows * o.n_ranges > INT32_MAX) return SE_ERR_SHAPE;
+  if ((int64_t)se::tiled_probs_bytes(n_rows, K) > (int64_t)UINT32_MAX ||
+      K * ld_w * 2 > (int64_t)UINT32_MAX)
+    return SE_ERR_SHAPE;
+  if (workspace_bytes < o.total) return SE_ERR_WORKSPACE;
+  if (!workspace) return SE_ERR_NULL;
+  if (!aligned16(workspace)) return SE_ERR_ALIGN;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t* probs = reinterpret_cast<uint16_t*>(ws + o.off_probs);
+  float* stats = reinterpret_cast<float*>(ws + o.off_stats);
+  int32_t* stat_arg = reinterpret_cast<int32_t*>(ws + o.off_arg);
+  float* factors = reinterpret_cast<float*>(ws + o.off_fac);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = from_hip(se::launch_step_sweep(logits, ld_logits, n_rows, o.rg, o.sweep_waves, probs, stats,
+                                      stat_arg, st));
+  if (rc != SE_OK) return rc;
+  se::GemmParams p{};
+  p.a = probs;                       // super-step-tiled: [K / 128][n_rows][128]
+  p.lda = se::kSuperStep;
+  p.a_ss = n_rows * se::kSuperStep * 2;
+  p.col0 = 0;
+  p.w = w_shard;
+  p.ldw = ld_w;
+  p.M = n_rows;
+  p.N = d;
+  p.K = K;
+  p.gamma = gamma;
+  p.out = out;
+  p.ldo = ld_out;
+  p.ws = reinterpret_cast<float*>(ws + o.off_parts);
+  p.tiles_n = (int)o.g.tiles_n;
+  p.tiles = (int)o.g.tiles;
+  p.splits = (int)o.g.splits;
+  p.kblocks = (int)o.g.kblocks;
+  p.keep_partials = true;
+  p.rows_pad = n_rows;
+  rc = from_hip(se::launch_soft_embed(p, false, false, st));
+  if (rc != SE_OK) return rc;
+  rc = from_hip(se::launch_merge_ranges(stats, stat_arg, n_rows, o.n_ranges, o.rg.n_pre,
+                                        (int)o.g.splits, gamma, factors, row_max, row_lse,
+                                        row_entropy, row_argmax, st));
+  if (rc != SE_OK) return rc;
+  return from_hip(se::launch_scaled_reduce(p, factors, st));
+}
+
 se_status se_quantize_table_fp8(const uint16_t* w, int64_t ld_w, int64_t rows, int64_t d,
                                 uint8_t* codes, int64_t ld_codes, float* row_scale,
                                 void* stream) {
@@ -483,10 +618,25 @@ se_status se_soft_embed_onepass(const float* logits, int64_t ld_logits, int64_t 
   uint16_t* probs = reinterpret_cast<uint16_t*>(ws + o.off_probs);
   float* stats = reinterpret_cast<float*>(ws + o.off_stats);
   int32_t* stat_arg = reinterpret_cast<int32_t*>(ws + o.off_arg);
+  float* factors = reinterpret_cast<float*>(ws + o.off_fac);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = from_hip(se::launch_split_sweep(logits, ld_logits, vocab_start, K, n_rows,
-                                       (int)o.g.splits, (int)o.g.kblocks, probs, stats, stat_arg,
-                                       o.rows_pad, st));
+  // split ranges that fit the wave-per-range sweep: that sweep (its ranges are exactly
+  // the splits), the range merge and the factor-scaled split reduction; longer ranges:
+  // the workgroup-per-range sweep and the one-pass reduction
+  se::StepRanges rg{};
+  rg.s = vocab_start;
+  rg.e = vocab_end;
+  rg.vocab = vocab_end;
+  rg.chunk = se::kSweepPiece * (int64_t)o.sweep_waves;
+  rg.splits = (int)o.g.splits;
+  rg.kblocks = (int)o.g.kblocks;
+  if (o.sweep_waves > 0)
+    rc = from_hip(se::launch_step_sweep(logits, ld_logits, n_rows, rg, o.sweep_waves, probs, stats,
+                                        stat_arg, st));
+  else
+    rc = from_hip(se::launch_split_sweep(logits, ld_logits, vocab_start, K, n_rows,
+                                         (int)o.g.splits, (int)o.g.kblocks, probs, stats,
+                                         stat_arg, o.rows_pad, st));
   if (rc != SE_OK) return rc;
   se::GemmParams p{};
   p.a = probs;                       // super-step-tiled: [K / 128][n_rows][128]
@@ -512,8 +662,16 @@ se_status se_soft_embed_onepass(const float* logits, int64_t ld_logits, int64_t 
   p.rows_pad = o.rows_pad;
   rc = from_hip(se::launch_soft_embed(p, false, false, st));
   if (rc != SE_OK) return rc;
-  return from_hip(se::launch_onepass_reduce(p, row_max, row_lse, row_entropy, row_argmax,
-                                            vocab_start, st));
+  if (o.sweep_waves == 0)
+    return from_hip(se::launch_onepass_reduce(p, row_max, row_lse, row_entropy, row_argmax,
+                                              vocab_start, st));
+  // the sweep wrote statistics and factors with row stride n_rows
+  p.rows_pad = n_rows;
+  rc = from_hip(se::launch_merge_ranges(stats, stat_arg, n_rows, (int)o.g.splits, 0,
+                                        (int)o.g.splits, gamma, factors, row_max, row_lse,
+                                        row_entropy, row_argmax, st));
+  if (rc != SE_OK) return rc;
+  return from_hip(se::launch_scaled_reduce(p, factors, st));
 }
 
 se_status se_merge_slices(const float* outs, int64_t n_parts, int64_t part_stride,

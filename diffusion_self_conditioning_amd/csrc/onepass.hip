@@ -146,6 +146,203 @@ split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, i
   }
 }
 
+// ---- the whole step in one read -------------------------------------------------------
+// The statistics of a row need every logit of it; the probabilities of the slice need
+// the row's lse.  Cutting the whole row into ranges and normalising each slice range
+// against its own maximum (as in the one-pass call) lets one sweep produce both: the
+// range statistics merge into the row's, and the split reduction rescales split r by
+// e^(m_r - lse).  One wavefront owns one (row, range): its values stay in registers
+// between the maximum and the sums, and its reductions are the fixed DPP butterflies of
+// a single wave, so no workgroup barrier is involved.
+
+constexpr int kStepSweepThreads = 256;              // four (row, range) items per workgroup
+#ifndef SE_SWEEP_LOAD
+#define SE_SWEEP_LOAD buffer_load_f4_nt               // the logits are read once
+#endif
+
+__device__ __forceinline__ void step_range(const StepRanges& g, int r, int64_t& c0,
+                                           int64_t& c1) {
+  if (r < g.n_pre) {
+    c0 = (int64_t)r * g.chunk;
+    c1 = min(c0 + g.chunk, g.s);
+    return;
+  }
+  r -= g.n_pre;
+  if (r < g.splits) {
+    const int64_t K = g.e - g.s;
+    c0 = g.s + (((int64_t)r * g.kblocks) / g.splits) * kSplitQuantum;
+    c1 = g.s + min((((int64_t)(r + 1) * g.kblocks) / g.splits) * kSplitQuantum, K);
+    return;
+  }
+  r -= g.splits;
+  const int64_t e0 = g.e & ~(int64_t)3;
+  c0 = max(g.e, e0 + (int64_t)r * g.chunk);
+  c1 = min(g.vocab, e0 + (int64_t)(r + 1) * g.chunk);
+}
+
+// W wavefronts (1, 2 or 4) of a workgroup share one (row, range); wave k of the group
+// takes the k-th of W near-equal, 4-aligned pieces, at most 3072 positions (12 16-byte
+// groups per lane, held in registers between the maximum and the sums).  The group
+// combines its maxima and then its sums through LDS in wave order.
+constexpr int kSweepNF4 = 12;
+static_assert(kSweepPiece == 64 * 4 * kSweepNF4, "a wave holds 12 groups of 4 per lane");
+
+template <int W>
+__global__ void __launch_bounds__(kStepSweepThreads)
+step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, StepRanges g,
+                  int n_ranges, uint16_t* __restrict__ probs, float4* __restrict__ stats,
+                  int32_t* __restrict__ stat_arg) {
+  constexpr int kWaves = kStepSweepThreads / 64;
+  constexpr int NF4 = kSweepNF4;
+  __shared__ float grp_v[kWaves], grp_z[kWaves], grp_s[kWaves];
+  __shared__ int grp_i[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int k = wave % W;
+  const int64_t item = (int64_t)blockIdx.x * (kWaves / W) + wave / W;
+  const bool active = item < n_rows * n_ranges;
+  if (W == 1 && !active) return;                      // whole wavefronts; no barrier below
+  const int64_t row = active ? item / n_ranges : 0;
+  const int r = active ? (int)(item % n_ranges) : 0;
+  int64_t c0 = 0, c1 = 0;
+  if (active) step_range(g, r, c0, c1);
+  const bool in_slice = r >= g.n_pre && r < g.n_pre + g.splits;
+  // this wave's piece [p0, p1) of the range
+  const int64_t piece = (((c1 - c0) + W - 1) / W + 3) & ~(int64_t)3;
+  const int64_t p0 = min(c0 + k * piece, c1), p1 = min(p0 + piece, c1);
+  const float* __restrict__ x = logits + row * ld;
+  // 16-byte groups [a0, a1) (row starts are 16-byte aligned); at most 3 positions
+  // before a0 and 3 after a1, one per lane (lanes 0-2 and 4-6)
+  const int64_t a0 = min((p0 + 3) & ~(int64_t)3, p1);
+  const int64_t a1 = max(p1 & ~(int64_t)3, a0);
+  const int ng = (int)((a1 - a0) >> 2);
+  const int base = (int)(a0 - c0);                      // range position of group 0
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + a0, (uint32_t)ng * 16u);
+  float4 v[NF4];
+#pragma unroll
+  for (int u = 0; u < NF4; ++u) v[u] = SE_SWEEP_LOAD(xr, (uint32_t)(u * 64 + lane) * 16u, 0u);
+  int rs = -1;                                          // range position of the scalar
+  if (lane < (int)(a0 - p0)) rs = (int)(p0 - c0) + lane;
+  else if (lane >= 4 && lane < 4 + (int)(p1 - a1)) rs = (int)(a1 - c0) + lane - 4;
+  const float xs = rs >= 0 ? x[c0 + rs] : 0.f;
+
+  float mv = -INFINITY;
+  int mi = INT_MAX;
+#pragma unroll
+  for (int u = 0; u < NF4; ++u) {
+    const int gi = u * 64 + lane;
+    if (gi < ng) {
+      const int kk = base + 4 * gi;
+      argmax_step(mv, mi, v[u].x, kk);
+      argmax_step(mv, mi, v[u].y, kk + 1);
+      argmax_step(mv, mi, v[u].z, kk + 2);
+      argmax_step(mv, mi, v[u].w, kk + 3);
+    }
+  }
+  if (rs >= 0) argmax_step(mv, mi, xs, rs);
+  wave_argmax(mv, mi);
+  if constexpr (W > 1) {
+    if (lane == 0) { grp_v[wave] = mv; grp_i[wave] = mi; }
+    __syncthreads();
+    const int w0 = wave - k;
+    mv = grp_v[w0];
+    mi = grp_i[w0];
+    for (int q = 1; q < W; ++q) argmax_step(mv, mi, grp_v[w0 + q], grp_i[w0 + q]);
+  }
+  const float nl = neg_lse_log2(mv);
+
+  // probabilities of slice position j of this row at
+  // probs[(j / kSuperStep) * n_rows * kSuperStep + row * kSuperStep + j % kSuperStep]
+  uint16_t* __restrict__ prow = probs + row * kSuperStep;
+  const int64_t js = c0 - g.s;                          // slice position of range position 0
+  auto tiled = [&](int64_t j) -> int64_t {
+    return (j / kSuperStep) * n_rows * kSuperStep + j % kSuperStep;
+  };
+  float z = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int u = 0; u < NF4; ++u) {
+    const int gi = u * 64 + lane;
+    if (gi < ng) {
+      const float t0 = __builtin_fmaf(v[u].x, kLog2e, nl), t1 = __builtin_fmaf(v[u].y, kLog2e, nl);
+      const float t2 = __builtin_fmaf(v[u].z, kLog2e, nl), t3 = __builtin_fmaf(v[u].w, kLog2e, nl);
+      const float q0 = exp2_hw(t0), q1 = exp2_hw(t1), q2 = exp2_hw(t2), q3 = exp2_hw(t3);
+      z += (q0 + q1) + (q2 + q3);
+      s1 = __builtin_fmaf(q0, t0, __builtin_fmaf(q1, t1, __builtin_fmaf(q2, t2, __builtin_fmaf(q3, t3, s1))));
+      if (active && in_slice) {                         // 4 positions in one super-step
+        uint2 o;
+        o.x = pack_bf16x2(q0, q1);
+        o.y = pack_bf16x2(q2, q3);
+        *reinterpret_cast<uint2*>(prow + tiled(js + base + 4 * gi)) = o;
+      }
+    }
+  }
+  if (rs >= 0) {
+    const float t = __builtin_fmaf(xs, kLog2e, nl);
+    const float q = exp2_hw(t);
+    z += q;
+    s1 = __builtin_fmaf(q, t, s1);
+    if (active && in_slice) prow[tiled(js + rs)] = __builtin_bit_cast(uint16_t, (__bf16)q);
+  }
+  z = wave_sum(z);
+  s1 = wave_sum(s1);
+  if constexpr (W > 1) {
+    if (lane == 0) { grp_z[wave] = z; grp_s[wave] = s1; }
+    __syncthreads();
+    const int w0 = wave - k;
+    z = grp_z[w0];
+    s1 = grp_s[w0];
+    for (int q = 1; q < W; ++q) { z += grp_z[w0 + q]; s1 += grp_s[w0 + q]; }
+  }
+  if (active && k == 0 && lane == 0) {
+    stats[(int64_t)r * n_rows + row] = make_float4(mv, z, s1 * kLn2, mv);
+    stat_arg[(int64_t)r * n_rows + row] = (int32_t)(c0 + mi);
+  }
+}
+
+// One wavefront per row: the ranges merge at the overall maximum M,
+//   Z = sum_r e^(m_r - M) Z_r,  S1 = sum_r e^(m_r - M) (S1_r + (m_r - M) Z_r),
+//   lse = M + ln Z,  H = ln Z - S1 / Z,  argmax = the smallest position reaching M,
+// and split range r0 + j gets the factor gamma e^(m - M) / Z.  Lane l takes ranges
+// l, l + 64, ... in order; the lanes then combine in the fixed butterfly order, so the
+// result is bitwise repeatable.
+constexpr int kMergeRangesThreads = 256;
+
+__global__ void __launch_bounds__(kMergeRangesThreads)
+merge_ranges_kernel(const float4* __restrict__ stats, const int32_t* __restrict__ stat_arg,
+                    int64_t n_rows, int n_ranges, int r0, int splits, float gamma,
+                    float* __restrict__ factors, float* __restrict__ row_max,
+                    float* __restrict__ row_lse, float* __restrict__ row_entropy,
+                    int32_t* __restrict__ row_argmax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kMergeRangesThreads / 64) + (threadIdx.x >> 6);
+  if (row >= n_rows) return;                           // whole wavefronts only
+  float mx = -INFINITY;
+  int arg = INT_MAX;
+  for (int r = lane; r < n_ranges; r += 64)
+    argmax_step(mx, arg, stats[(int64_t)r * n_rows + row].x, stat_arg[(int64_t)r * n_rows + row]);
+  wave_argmax(mx, arg);
+  float z = 0.f, s1 = 0.f;
+  for (int r = lane; r < n_ranges; r += 64) {
+    const float4 st = stats[(int64_t)r * n_rows + row];
+    const float d = st.x - mx;
+    const float f = exp2_hw(d * kLog2e);
+    z = __builtin_fmaf(f, st.y, z);
+    s1 = __builtin_fmaf(f, __builtin_fmaf(d, st.y, st.z), s1);
+  }
+  z = wave_sum(z);
+  s1 = wave_sum(s1);
+  const float lz = logf(z);
+  if (lane == 0) {
+    row_max[row] = mx;
+    row_lse[row] = mx + lz;
+    row_entropy[row] = lz - s1 / z;
+    row_argmax[row] = arg;
+  }
+  const float gz = gamma / z;
+  for (int j = lane; j < splits; j += 64)
+    factors[(int64_t)j * n_rows + row] =
+        gz * exp2_hw((stats[(int64_t)(r0 + j) * n_rows + row].x - mx) * kLog2e);
+}
+
 // Merge of T slice results (one-pass calls on disjoint vocabulary slices, in vocabulary
 // order) into the result over their union.  With lse = ln sum_r e^(lse_r), slice r
 // carries probability mass pi_r = e^(lse_r - lse):
@@ -210,6 +407,41 @@ hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_
                      (int)n_parts, part_stride, n_rows, d, ld_part, part_max, part_lse,
                      part_entropy, part_argmax, out, ld_out, row_max, row_lse, row_entropy,
                      row_argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
+                             const StepRanges& g, int waves, uint16_t* probs, float* stats,
+                             int32_t* stat_arg, hipStream_t stream) {
+  if (waves != 1 && waves != 2 && waves != 4) return hipErrorInvalidValue;
+  const int n_ranges = g.n_pre + g.splits + g.n_post;
+  const int per_block = (kStepSweepThreads / 64) / waves;    // (row, range) items
+  const dim3 grid((unsigned)((n_rows * n_ranges + per_block - 1) / per_block));
+  const dim3 block(kStepSweepThreads);
+  float4* st = reinterpret_cast<float4*>(stats);
+  if (waves == 1)
+    hipLaunchKernelGGL(step_sweep_kernel<1>, grid, block, 0, stream, logits, ld, n_rows, g,
+                       n_ranges, probs, st, stat_arg);
+  else if (waves == 2)
+    hipLaunchKernelGGL(step_sweep_kernel<2>, grid, block, 0, stream, logits, ld, n_rows, g,
+                       n_ranges, probs, st, stat_arg);
+  else if (waves == 4)
+    hipLaunchKernelGGL(step_sweep_kernel<4>, grid, block, 0, stream, logits, ld, n_rows, g,
+                       n_ranges, probs, st, stat_arg);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_ranges(const float* stats, const int32_t* stat_arg, int64_t n_rows,
+                               int n_ranges, int r0, int splits, float gamma, float* factors,
+                               float* row_max, float* row_lse, float* row_entropy,
+                               int32_t* row_argmax, hipStream_t stream) {
+  const int per_block = kMergeRangesThreads / 64;
+  const dim3 grid((unsigned)((n_rows + per_block - 1) / per_block));
+  hipLaunchKernelGGL(merge_ranges_kernel, grid, dim3(kMergeRangesThreads), 0, stream,
+                     reinterpret_cast<const float4*>(stats), stat_arg, n_rows, n_ranges, r0,
+                     splits, gamma, factors, row_max, row_lse, row_entropy, row_argmax);
   return hipGetLastError();
 }
 

@@ -56,6 +56,11 @@ __device__ __forceinline__ float4 buffer_load_f4(__amdgpu_buffer_rsrc_t r, uint3
   const f32x4_t v = se_raw_buffer_load_f4(r, (int)voff, (int)soff, 0);
   return make_float4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ float4 buffer_load_f4_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                    uint32_t soff) {
+  const f32x4_t v = se_raw_buffer_load_f4(r, (int)voff, (int)soff, 2);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 __device__ float se_raw_buffer_load_f1(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
                                       int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.f32");
 __device__ __forceinline__ float buffer_load_f1(__amdgpu_buffer_rsrc_t r, uint32_t voff,

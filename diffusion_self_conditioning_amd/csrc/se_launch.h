@@ -41,8 +41,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 struct OnepassLayout {
   GemmPlan g;
   int64_t rows_pad;
-  size_t off_probs, off_parts, off_stats, off_arg, total;
+  int sweep_waves;        // waves per range of the register sweep (0: ranges too long)
+  size_t off_probs, off_parts, off_stats, off_arg, off_fac, total;
 };
+
+// Positions one wave of the sweep holds in registers (12 16-byte groups per lane).
+constexpr int kSweepPiece = 64 * 4 * 12;
+
+// Waves per range (1, 2 or 4) that hold the longest split range of `g`, or 0.
+int sweep_waves(const GemmPlan& g, int64_t K);
 
 OnepassLayout onepass_layout(int64_t n_rows, int64_t K, int64_t d);
 
@@ -117,6 +124,34 @@ hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int
 hipError_t launch_onepass_reduce(const GemmParams& p, float* row_max, float* row_lse,
                                  float* row_entropy, int32_t* row_argmax, int64_t col0,
                                  hipStream_t stream);
+
+// Whole-step sweep.  The ranges of one row, in column order (r = 0 .. n_ranges - 1):
+// [0, s) cut every `chunk` positions; the contraction's split ranges of the slice
+// [s, e); then [e, vocab) cut at e0 + j chunk, e0 = e rounded down to a multiple of 4.
+struct StepRanges {
+  int64_t s, e, vocab, chunk;
+  int n_pre, splits, n_post, kblocks;
+};
+
+// One read of every logit: per (row, range) maximum, first argmax (a vocabulary id),
+// Z and S1 against the range maximum (stats[r * n_rows + row] = {m, Z, S1 nats, m},
+// stat_arg likewise), and for the slice's split ranges the bf16 probabilities against
+// the range maximum in the super-step-tiled layout.  `waves` (1, 2 or 4) wavefronts
+// share a range of at most waves * kSweepPiece positions.
+hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
+                             const StepRanges& g, int waves, uint16_t* probs, float* stats,
+                             int32_t* stat_arg, hipStream_t stream);
+
+// Merge of each row's range statistics: row max / lse / entropy / argmax, and the
+// factor gamma e^(m_r - lse) of every split range r0 + j (factors[j * n_rows + row]).
+hipError_t launch_merge_ranges(const float* stats, const int32_t* stat_arg, int64_t n_rows,
+                               int n_ranges, int r0, int splits, float gamma, float* factors,
+                               float* row_max, float* row_lse, float* row_entropy,
+                               int32_t* row_argmax, hipStream_t stream);
+
+// out = sum_s factors[s * p.rows_pad + row] * partial_s, splits in order (partials as
+// the contraction left them with keep_partials).
+hipError_t launch_scaled_reduce(const GemmParams& p, const float* factors, hipStream_t stream);
 
 hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_stride,
                                int64_t n_rows, int64_t d, int64_t ld_part,

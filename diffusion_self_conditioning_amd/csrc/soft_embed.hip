@@ -57,6 +57,9 @@
 #include "se_device.h"
 #include "se_launch.h"
 
+#ifndef SE_APRE
+#define SE_APRE 0           // probability fragments of the next step read before the barrier: 0, 1 or 2 substeps
+#endif
 #ifndef SE_SCHED
 #define SE_SCHED 0            // VALU instructions placed after each MFMA (0: compiler's order)
 #endif
@@ -325,6 +328,21 @@ soft_embed_kernel(const GemmParams p) {
                                        __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
+  auto frag_read_a = [&](int pbuf, int u, bf16x8 (&af)[kMI]) {
+    const unsigned char* pa = lds + pbuf * kPBuf + rd_row + (rd_chk ^ (uint32_t)(32 * u));
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi) af[mi] = *reinterpret_cast<const bf16x8*>(pa + 8192 * mi);
+  };
+  auto frag_read_b = [&](int wbuf, int q, bf16x8 (&bf)[kNI]) {
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const unsigned char* wp = lds + wbuf * kWBuf + b_rd[ni] + 8192 * q;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp + 2048));
+      bf[ni] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
+                                       __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
   auto mfmas = [&](const bf16x8 (&af)[kMI], const bf16x8 (&bf)[kNI]) {
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
@@ -372,8 +390,40 @@ soft_embed_kernel(const GemmParams p) {
 #endif
     __builtin_amdgcn_sched_barrier(0);
   };
+  // The same step for the main loop.  The probability tile of a super-step is complete
+  // from its first step on, so the first SE_APRE substeps' A fragments of step qstep + 1
+  // are read at the end of step qstep, before the barrier (`next`), and taken from
+  // `apre` at the start of that step (`have`).  Table fragments come after the barrier.
+  constexpr int kApre = SE_APRE;
+  auto compute_pre = [&](int pbuf, int wbuf, int qstep, bf16x8 (&apre)[2][kMI], bool have,
+                         bool next, auto&& side) {
+    bf16x8 a0[kMI], b0[kNI], a1[kMI], b1[kNI];
+    if (kApre >= 1 && have) {
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi) a0[mi] = apre[0][mi];
+    } else {
+      frag_read_a(pbuf, 2 * qstep, a0);
+    }
+    frag_read_b(wbuf, 0, b0);
+    if (kApre >= 2 && have) {
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi) a1[mi] = apre[1][mi];
+    } else {
+      frag_read_a(pbuf, 2 * qstep + 1, a1);
+    }
+    frag_read_b(wbuf, 1, b1);
+    mfmas(a0, b0);
+    side(0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a1, b1);
+    side(1);
+    if (kApre >= 1 && next) frag_read_a(pbuf, 2 * qstep + 2, apre[0]);
+    if (kApre >= 2 && next) frag_read_a(pbuf, 2 * qstep + 3, apre[1]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // ---- main loop over the full super-steps [S0, Sf) ------------------------------------
+  bf16x8 apre[2][kMI];               // A fragments read ahead (SE_APRE)
   AReg ra[2][kPerQ];                 // quarter registers: set q % 2
   uint4 rw[2][kWJ];                  // table register stages
   float rs[2][kWJ];                  // e4m3 row scales of those stages
@@ -427,7 +477,7 @@ soft_embed_kernel(const GemmParams p) {
           for (int i = 0; i < kPerQ; ++i) nlq[i] = nl_of(q * kPerQ + i);
         }
         __builtin_amdgcn_sched_barrier(0);
-        compute(S & 1, q & 1, q, [&](int h) {
+        auto side = [&](int h) {
           // table loads j in [ceil(h kWJ / 2), ceil((h + 1) kWJ / 2)): a single load
           // goes with the first half
 #pragma unroll
@@ -443,7 +493,9 @@ soft_embed_kernel(const GemmParams p) {
           }
 #pragma unroll
           for (int i = h * kPerQ / 2; i < (h + 1) * kPerQ / 2; ++i) rq[i] = load_a(Sr, qr * kPerQ + i);
-        });
+        };
+        if constexpr (kApre > 0) compute_pre(S & 1, q & 1, q, apre, q > 0, q < kQ - 1, side);
+        else compute(S & 1, q & 1, q, side);
         __syncthreads();
       }
     }
@@ -563,6 +615,39 @@ splitk_reduce_kernel(const float* __restrict__ ws, int tiles, int tiles_n, int s
       make_float4(gamma * a.x, gamma * a.y, gamma * a.z, gamma * a.w);
 }
 
+// Split reduction with a factor per (split, row): out = sum_s f[s][row] U_s in split
+// order (the whole-step sweep's rescaling, f = gamma e^(m_s - lse)).
+__global__ void __launch_bounds__(kReduceThreads)
+scaled_reduce_kernel(const float* __restrict__ ws, const float* __restrict__ factors,
+                     int64_t rows_pad, int tiles, int tiles_n, int splits, int64_t M, int64_t N,
+                     float* __restrict__ out, int64_t ldo) {
+  constexpr int kBlocksPerTile = (int)(kTileFloats / (4 * kReduceThreads));
+  const int t = blockIdx.x / kBlocksPerTile;
+  const int e0 = ((blockIdx.x % kBlocksPerTile) * kReduceThreads + threadIdx.x) * 4;
+  const int l0 = e0 & 63;
+  const int r = (e0 >> 6) & 15;
+  const int blk = e0 >> 10;
+  const int wave = blk / (kMI * kNI), mi = (blk / kNI) % kMI, ni = blk % kNI;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int64_t row = (int64_t)(t / tiles_n) * kBM + 128 * wm + 32 * mi + 8 * (r >> 2) +
+                      4 * (l0 >> 5) + (r & 3);
+  const int64_t col = (int64_t)(t % tiles_n) * kBN + kTN * wn + 32 * ni + (l0 & 31);
+  if (row >= M || col >= N) return;
+  const float* src = ws + (int64_t)t * kTileFloats + e0;
+  float f = factors[row];
+  float4 v = *reinterpret_cast<const float4*>(src);
+  float4 a = make_float4(f * v.x, f * v.y, f * v.z, f * v.w);
+  for (int s = 1; s < splits; ++s) {
+    f = factors[(int64_t)s * rows_pad + row];
+    v = *reinterpret_cast<const float4*>(src + (int64_t)s * tiles * kTileFloats);
+    a.x = __builtin_fmaf(f, v.x, a.x);
+    a.y = __builtin_fmaf(f, v.y, a.y);
+    a.z = __builtin_fmaf(f, v.z, a.z);
+    a.w = __builtin_fmaf(f, v.w, a.w);
+  }
+  *reinterpret_cast<float4*>(out + row * ldo + col) = a;
+}
+
 // One-pass reduction.  Split s holds the partial U_s of probabilities taken against a
 // reference m_s, with Z_s and S1_s against the same reference and its maximum M_s
 // (stats[s][row] = {m_s, Z_s, S1_s, M_s}).  At the overall maximum M = max_s M_s:
@@ -663,6 +748,13 @@ hipError_t launch_onepass_reduce(const GemmParams& p, float* row_max, float* row
                      reinterpret_cast<const float4*>(p.stats), p.stat_arg, p.rows_pad, p.tiles,
                      p.tiles_n, p.splits, p.M, p.N, p.gamma, col0, p.out, p.ldo, row_max,
                      row_lse, row_entropy, row_argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_scaled_reduce(const GemmParams& p, const float* factors, hipStream_t stream) {
+  const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));
+  hipLaunchKernelGGL(scaled_reduce_kernel, dim3(blocks), dim3(kReduceThreads), 0, stream, p.ws,
+                     factors, p.rows_pad, p.tiles, p.tiles_n, p.splits, p.M, p.N, p.out, p.ldo);
   return hipGetLastError();
 }
 

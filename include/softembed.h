@@ -183,8 +183,9 @@ se_status se_soft_embed_staged(const float* logits, int64_t ld_logits, const flo
  * over the full width [0, vocab) followed by se_soft_embed_fused on [s, e), with
  * outputs bit for bit those of the two calls.  The statistics kernel writes the
  * slice's bf16 probabilities (staged, as se_soft_embed_staged) right after each
- * row's statistics, while that row's logits are still in cache, so the slice is not
- * read from memory a second time and one launch boundary disappears.
+ * row's statistics, reading the row's slice again (from whatever cache level still
+ * holds it; at the pages' shapes that second read misses the L2), and one launch
+ * boundary disappears.
  * Arguments: those of se_row_stats and se_soft_embed_fused together (row_max,
  * row_lse, row_entropy and row_argmax are outputs here); workspace of
  * se_soft_embed_staged_workspace_bytes() bytes (16-byte aligned; none for an empty
@@ -196,6 +197,39 @@ se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_r
                              float gamma, float* out, int64_t ld_out, float* row_max,
                              float* row_lse, float* row_entropy, int32_t* row_argmax,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * se_soft_embed_step_onepass -- the same step as se_soft_embed_step (row statistics
+ * over the full width [0, vocab), the slice's soft embedding against them) from ONE
+ * read of the logits.  The row is cut into ranges: [0, s) and [e, vocab) in chunks,
+ * and the slice in the contraction's split ranges.  Each range yields its maximum,
+ * first argmax, Z_r = sum e^(l - m_r) and S1_r = sum e^(l - m_r)(l - m_r); each slice
+ * range also writes its bf16 probabilities against its own maximum,
+ * bf16_rne(e^(l - m_r)).  The ranges merge at the row maximum M,
+ *     Z = sum_r e^(m_r - M) Z_r,  lse = M + ln Z,
+ *     H = ln Z - sum_r e^(m_r - M) (S1_r + (m_r - M) Z_r) / Z,
+ * and the contraction of split r is scaled by gamma e^(m_r - lse) before the splits are
+ * summed in order: the partition identity of calvarado04.com, "The fix" (a sum over
+ * disjoint vocabulary pieces), applied to softmax numerators.  Results agree with
+ * se_soft_embed_step to rounding (argmax and row max exactly), are bitwise repeatable,
+ * but are not bitwise those of the two-pass calls.
+ * When the slice is empty, or one split range is longer than 12,288 positions (the
+ * sweep holds a range in registers), the call is se_soft_embed_step itself.
+ * Arguments and errors as se_soft_embed_step, with a workspace of
+ * se_soft_embed_step_onepass_workspace_bytes() bytes (16-byte aligned): the bf16
+ * slice, the split partials and per-(range, row) statistics.
+ */
+size_t se_soft_embed_step_onepass_workspace_bytes(int64_t n_rows, int64_t vocab,
+                                                  int64_t vocab_start, int64_t vocab_end,
+                                                  int64_t d);
+
+se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int64_t n_rows,
+                                     int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                                     const uint16_t* w_shard, int64_t w_rows, int64_t ld_w,
+                                     int64_t d, float gamma, float* out, int64_t ld_out,
+                                     float* row_max, float* row_lse, float* row_entropy,
+                                     int32_t* row_argmax, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /*
  * se_quantize_table_fp8 -- the e4m3 form of a bf16 embedding table (the pages serve

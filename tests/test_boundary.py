@@ -296,13 +296,14 @@ def test_onepass_errors(kw, code):
 
 def test_onepass_workspace_plan():
     """bf16 probabilities of the slice in super-steps of 128 positions, partials of every split
-    (kept even for one split) and 20 bytes of statistics per (split, row)."""
+    (kept even for one split), 20 bytes of statistics and a 4-byte factor per (split, row)."""
     ws = b.se_soft_embed_onepass_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
     tile = 256 * 256 * 4
     assert ws(256, 0, 262144, 2816) == up(256 * 262144 * 2) + up(23 * 11 * tile) + \
-        up(23 * 256 * 16) + up(23 * 256 * 4)
-    assert ws(5, 16, 17, 16) == up(5 * 128 * 2) + up(tile) + up(256 * 16) + up(256 * 4)
+        up(23 * 256 * 16) + up(23 * 256 * 4) + up(23 * 256 * 4)
+    assert ws(5, 16, 17, 16) == up(5 * 128 * 2) + up(tile) + up(256 * 16) + up(256 * 4) + \
+        up(256 * 4)
     assert ws(5, 16, 16, 16) == 0 and ws(0, 0, 64, 16) == 0
 
 
@@ -354,3 +355,46 @@ def test_staged_workspace_plan_and_errors():
     assert call(x=P1 + 4) == b.SE_ERR_ALIGN
     assert call(d=2812, ldw=2816, ldo=2816) == b.SE_ERR_ALIGN
     assert call(n=0, x=None, lse=None, w=None, out=None, ws=None, ws_bytes=0) == b.SE_OK
+
+
+def test_step_onepass_workspace_plan_and_errors():
+    """Tiled bf16 slice, partials of every split (kept even for one split), 20 bytes of
+    statistics per (range, row) and a factor per (split, row).  At the one-rank shape the
+    row is 22 chunks of 3072 positions before the slice, 23 split ranges, 43 chunks after.
+    An empty slice or split ranges too long for the sweep take the two-pass step and its
+    workspace."""
+    ws = b.se_soft_embed_step_onepass_workspace_bytes
+    staged = b.se_soft_embed_staged_workspace_bytes
+    up = lambda x: (x + 255) // 256 * 256
+    tile = 256 * 256 * 4
+    n_r = 22 + 23 + 43
+    assert ws(256, 262144, 65536, 131072, 2816) == up(256 * 65536 * 2) + up(23 * 11 * tile) + \
+        up(n_r * 256 * 16) + up(n_r * 256 * 4) + up(23 * 256 * 4)
+    # slice [16, 17) of 1000 columns, one split: 1 chunk before, 1 range, 1 chunk after
+    assert ws(5, 1000, 16, 17, 16) == up(5 * 128 * 2) + up(tile) + up(3 * 5 * 16) + \
+        up(3 * 5 * 4) + up(5 * 4)
+    assert ws(8, 512, 16, 16, 16) == staged(8, 16, 16, 16) == 0
+    assert ws(2048, 30000, 0, 26000, 2816) == staged(2048, 0, 26000, 2816) > 0
+    assert ws(0, 1000, 0, 64, 16) == 0 and ws(4, 100, 0, 200, 16) == 0
+    st = lib.se_soft_embed_step_onepass
+
+    def call(**kw):
+        a = dict(x=P1, ld=262144, n=256, vocab=262144, s=65536, e=131072, w=P3, w_rows=65536,
+                 ldw=2816, d=2816, gamma=53.0, out=P4, ldo=2816, mx=P2, lse=P2 + 1024,
+                 ent=P2 + 2048, am=P2 + 3072, ws=P5, ws_bytes=1 << 40)
+        a.update(kw)
+        return st(a["x"], a["ld"], a["n"], a["vocab"], a["s"], a["e"], a["w"], a["w_rows"],
+                  a["ldw"], a["d"], a["gamma"], a["out"], a["ldo"], a["mx"], a["lse"], a["ent"],
+                  a["am"], a["ws"], a["ws_bytes"], None)
+    assert call(w_rows=1000) == b.SE_ERR_SLICE
+    assert call(ld=1000) == b.SE_ERR_SHAPE
+    assert call(x=None) == b.SE_ERR_NULL
+    assert call(am=None) == b.SE_ERR_NULL
+    assert call(ws=None) == b.SE_ERR_NULL
+    assert call(ws_bytes=1024) == b.SE_ERR_WORKSPACE
+    assert call(ws=P5 + 8) == b.SE_ERR_ALIGN
+    assert call(x=P1 + 4) == b.SE_ERR_ALIGN
+    assert call(ent=P2 + 2050) == b.SE_ERR_ALIGN
+    assert call(s=65540) == b.SE_ERR_ALIGN
+    assert call(n=0, x=None, w=None, out=None, mx=None, lse=None, ent=None, am=None, ws=None,
+                ws_bytes=0) == b.SE_OK
