@@ -43,6 +43,17 @@ int device_cu_count() {
   return cu_count[dev];
 }
 
+// The split count minimises a makespan model of the contraction:
+//   waves(s) * (ceil(kblocks / s) * t_block + t_start) + s * M * N * 8 bytes / partial_rate,
+// where waves(s) = ceil(tiles * s / CUs).  Each workgroup streams one 128-position block of
+// its tile per t_block, a launch with more workgroups than CUs runs in waves, each wave
+// pays a start-up (its first probability tile and table stages), and every split writes
+// and reads back an fp32 partial of the output (the last term, only for s > 1).  The
+// constants are MI355X measurements: about 4 us per block at the one-rank shape, 2 us of
+// start-up, and 5 TB/s for the partials' round trip (a plain copy's rate).
+constexpr double kBlockUs = 4.0, kStartUs = 2.0, kPartialBytesPerUs = 5.0e6;
+constexpr int64_t kMaxSplits = 64;
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan g{};
   g.tiles_m = (M + kBM - 1) / kBM;
@@ -51,11 +62,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   g.kblocks = (K + kSplitQuantum - 1) / kSplitQuantum;
   g.splits = 1;
   const int64_t cus = device_cu_count();
-  if (g.tiles > 0 && g.tiles < cus) {
-    int64_t s = cus / g.tiles;
-    const int64_t cap = g.kblocks / kMinBlocksPerSplit;
-    if (s > cap) s = cap;
-    g.splits = s < 1 ? 1 : s;
+  if (g.tiles > 0 && g.kblocks > 0) {
+    const int64_t cap = std::max<int64_t>(1, std::min(kMaxSplits, g.kblocks / kMinBlocksPerSplit));
+    double best = 0.0;
+    for (int64_t sp = 1; sp <= cap; ++sp) {
+      const double waves = (double)((g.tiles * sp + cus - 1) / cus);
+      const double blocks = (double)((g.kblocks + sp - 1) / sp);
+      double t = waves * (blocks * kBlockUs + kStartUs);
+      if (sp > 1) t += (double)sp * (double)M * (double)N * 8.0 / kPartialBytesPerUs;
+      if (sp == 1 || t < best) { best = t; g.splits = sp; }
+    }
   }
   g.grid = g.tiles * g.splits;
   g.ws_bytes = g.splits > 1 ? (size_t)(g.splits * g.tiles * kTileFloats) * sizeof(float) : 0;

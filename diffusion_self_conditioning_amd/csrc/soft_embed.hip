@@ -57,9 +57,6 @@
 #include "se_device.h"
 #include "se_launch.h"
 
-#ifndef SE_APRE
-#define SE_APRE 0           // probability fragments of the next step read before the barrier: 0, 1 or 2 substeps
-#endif
 #ifndef SE_SCHED
 #define SE_SCHED 0            // VALU instructions placed after each MFMA (0: compiler's order)
 #endif
@@ -328,21 +325,6 @@ soft_embed_kernel(const GemmParams p) {
                                        __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
-  auto frag_read_a = [&](int pbuf, int u, bf16x8 (&af)[kMI]) {
-    const unsigned char* pa = lds + pbuf * kPBuf + rd_row + (rd_chk ^ (uint32_t)(32 * u));
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) af[mi] = *reinterpret_cast<const bf16x8*>(pa + 8192 * mi);
-  };
-  auto frag_read_b = [&](int wbuf, int q, bf16x8 (&bf)[kNI]) {
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const unsigned char* wp = lds + wbuf * kWBuf + b_rd[ni] + 8192 * q;
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp + 2048));
-      bf[ni] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
-                                       __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  };
   auto mfmas = [&](const bf16x8 (&af)[kMI], const bf16x8 (&bf)[kNI]) {
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
@@ -390,40 +372,8 @@ soft_embed_kernel(const GemmParams p) {
 #endif
     __builtin_amdgcn_sched_barrier(0);
   };
-  // The same step for the main loop.  The probability tile of a super-step is complete
-  // from its first step on, so the first SE_APRE substeps' A fragments of step qstep + 1
-  // are read at the end of step qstep, before the barrier (`next`), and taken from
-  // `apre` at the start of that step (`have`).  Table fragments come after the barrier.
-  constexpr int kApre = SE_APRE;
-  auto compute_pre = [&](int pbuf, int wbuf, int qstep, bf16x8 (&apre)[2][kMI], bool have,
-                         bool next, auto&& side) {
-    bf16x8 a0[kMI], b0[kNI], a1[kMI], b1[kNI];
-    if (kApre >= 1 && have) {
-#pragma unroll
-      for (int mi = 0; mi < kMI; ++mi) a0[mi] = apre[0][mi];
-    } else {
-      frag_read_a(pbuf, 2 * qstep, a0);
-    }
-    frag_read_b(wbuf, 0, b0);
-    if (kApre >= 2 && have) {
-#pragma unroll
-      for (int mi = 0; mi < kMI; ++mi) a1[mi] = apre[1][mi];
-    } else {
-      frag_read_a(pbuf, 2 * qstep + 1, a1);
-    }
-    frag_read_b(wbuf, 1, b1);
-    mfmas(a0, b0);
-    side(0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(a1, b1);
-    side(1);
-    if (kApre >= 1 && next) frag_read_a(pbuf, 2 * qstep + 2, apre[0]);
-    if (kApre >= 2 && next) frag_read_a(pbuf, 2 * qstep + 3, apre[1]);
-    __builtin_amdgcn_sched_barrier(0);
-  };
 
   // ---- main loop over the full super-steps [S0, Sf) ------------------------------------
-  bf16x8 apre[2][kMI];               // A fragments read ahead (SE_APRE)
   AReg ra[2][kPerQ];                 // quarter registers: set q % 2
   uint4 rw[2][kWJ];                  // table register stages
   float rs[2][kWJ];                  // e4m3 row scales of those stages
@@ -494,8 +444,7 @@ soft_embed_kernel(const GemmParams p) {
 #pragma unroll
           for (int i = h * kPerQ / 2; i < (h + 1) * kPerQ / 2; ++i) rq[i] = load_a(Sr, qr * kPerQ + i);
         };
-        if constexpr (kApre > 0) compute_pre(S & 1, q & 1, q, apre, q > 0, q < kQ - 1, side);
-        else compute(S & 1, q & 1, q, side);
+        compute(S & 1, q & 1, q, side);
         __syncthreads();
       }
     }

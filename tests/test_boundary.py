@@ -147,13 +147,15 @@ def test_probs_errors():
 
 
 def test_workspace_plan():
-    """256 x 256 output tiles, vocab split in blocks of 128 positions, split count =
-    floor(256 / tiles) capped so every split has at least 2 blocks; partial tiles are fp32."""
+    """256 x 256 output tiles, vocab split in blocks of 128 positions; the split count
+    minimises the library's makespan model (waves of workgroups x blocks per workgroup,
+    plus the fp32 partials' round trip), at least 2 blocks per split, and is the same on
+    a host without a GPU (the MI355X count of 256 CUs).  Partial tiles are fp32."""
     tile = 256 * 256 * 4
     ws = b.se_soft_embed_workspace_bytes
     assert ws(256, 65536, 131072, 2816) == 23 * 11 * tile        # one rank: 11 tiles x 23 splits
     assert ws(256, 0, 262144, 2816) == 23 * 11 * tile
-    assert ws(2048, 0, 262144, 2816) == 2 * 88 * tile            # 88 tiles x 2 splits
+    assert ws(1024, 0, 65536, 2816) == 11 * 44 * tile            # 44 tiles x 11 splits
     assert ws(16, 0, 4096, 256) == 16 * 1 * tile                 # 32 blocks -> 16 splits
     assert ws(16, 0, 64, 256) == 0                               # one block: no split
     assert ws(16, 8, 8, 256) == 0                                # empty slice
@@ -161,9 +163,12 @@ def test_workspace_plan():
 
 
 def test_workspace_plan_large_m():
-    # 16 x 11 = 176 tiles: floor(256 / 176) = 1 split, no workspace
-    assert b.se_soft_embed_workspace_bytes(4096, 0, 262144, 2816) == 0
-    assert b.se_soft_embed_workspace_bytes(8192, 0, 262144, 2816) == 0
+    """Many row tiles: more splits than fit one wave of workgroups can still win, because
+    every CU then works (88 tiles x 2 splits would leave 80 of 256 CUs idle)."""
+    tile = 256 * 256 * 4
+    assert b.se_soft_embed_workspace_bytes(2048, 0, 262144, 2816) == 17 * 88 * tile
+    assert b.se_soft_embed_workspace_bytes(4096, 0, 262144, 2816) == 10 * 176 * tile
+    assert b.se_soft_embed_workspace_bytes(8192, 0, 262144, 2816) == 8 * 352 * tile
 
 
 def accept(**kw):
@@ -374,7 +379,7 @@ def test_step_onepass_workspace_plan_and_errors():
     assert ws(5, 1000, 16, 17, 16) == up(5 * 128 * 2) + up(tile) + up(3 * 5 * 16) + \
         up(3 * 5 * 4) + up(5 * 4)
     assert ws(8, 512, 16, 16, 16) == staged(8, 16, 16, 16) == 0
-    assert ws(2048, 30000, 0, 26000, 2816) == staged(2048, 0, 26000, 2816) > 0
+    assert ws(4096, 50000, 0, 50000, 1024) == staged(4096, 0, 50000, 1024) > 0
     assert ws(0, 1000, 0, 64, 16) == 0 and ws(4, 100, 0, 200, 16) == 0
     st = lib.se_soft_embed_step_onepass
 

@@ -128,15 +128,19 @@ def test_onepass_special_rows(kind):
     check_slice(x, 0, V, table(V, d, 12), 3.0)
 
 
-def test_onepass_long_ranges_read_twice():
-    """Split ranges longer than the sweep keeps in LDS (300 rows x 11 n-tiles -> 11 splits of
-    about 18,000 positions): the second pass reads the logits from memory again."""
-    L, V, d = 300, 200000, 2816
+@pytest.mark.parametrize("shape", [(768, 100000, 2816), (4096, 65536, 1024)],
+                         ids=["lds-keep", "read-twice"])
+def test_onepass_long_split_ranges(shape):
+    """Split ranges longer than the register sweep holds (12,288 positions) take the
+    workgroup-per-range sweep: 768 rows x 11 n-tiles -> 7 splits of 14,336 positions (kept
+    in LDS between its passes); 4096 rows x 4 n-tiles -> 4 splits of 16,384 (longer than
+    LDS holds: the second pass reads the logits from memory again)."""
+    L, V, d = shape
     rng = np.random.default_rng(17)
     x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
     x[np.arange(L), rng.integers(0, V, L)] += 9.0
-    say("onepass long ranges")
-    check_slice(x, 0, V, table(V, d, 18), 2.5, rows=np.array([0, 1, 150, 299]))
+    say("onepass long ranges", shape)
+    check_slice(x, 0, V, table(V, d, 18), 2.5, rows=np.array([0, 1, L // 2, L - 1]))
 
 
 def test_onepass_agrees_with_the_two_pass_path():
