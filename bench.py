@@ -408,9 +408,16 @@ def main():
         cold.append(e0.elapsed_time(e1) * 1e3)
     src = torch.ones(1 << 28, device=dev)
     copy_us = event_time_us(lambda: scrub.copy_(src), 10, 3)
-    ceilings = {"cold_step_us_median": round(sorted(cold)[len(cold) // 2], 2),
-                "hbm_copy_gbs": round(2 * src.numel() * 4 / (copy_us * 1e-6) / 1e9, 1)}
     del scrub, src
+    # achievable dense bf16 matrix-core rate on this machine: the vendor GEMM (torch.mm, contiguous
+    # operands) on an 8192-cube, beside the 2.5 PFLOP/s peak
+    ga = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
+    gb = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
+    mm_us = event_time_us(lambda: torch.mm(ga, gb), 10, 5)
+    del ga, gb
+    ceilings = {"cold_step_us_median": round(sorted(cold)[len(cold) // 2], 2),
+                "hbm_copy_gbs": round(2 * (1 << 28) * 4 / (copy_us * 1e-6) / 1e9, 1),
+                "bf16_gemm_8192_tflops": round(2 * 8192 ** 3 / (mm_us * 1e-6) / 1e12, 1)}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -403,3 +403,27 @@ def test_step_onepass_workspace_plan_and_errors():
     assert call(s=65540) == b.SE_ERR_ALIGN
     assert call(n=0, x=None, w=None, out=None, mx=None, lse=None, ent=None, am=None, ws=None,
                 ws_bytes=0) == b.SE_OK
+
+
+def test_workspace_queries_are_thread_safe():
+    """The plan reads the per-device compute-unit count once (std::call_once) and is
+    otherwise pure: concurrent queries from many threads agree with a serial one."""
+    import threading
+    shapes = [(256, 65536, 131072, 2816), (2048, 0, 262144, 2816), (16, 0, 4096, 256),
+              (1024, 0, 65536, 2816)]
+    want = [b.se_soft_embed_workspace_bytes(*sh) for sh in shapes]
+    want1 = b.se_soft_embed_step_onepass_workspace_bytes(256, 262144, 65536, 131072, 2816)
+    bad = []
+
+    def worker():
+        for _ in range(200):
+            got = [b.se_soft_embed_workspace_bytes(*sh) for sh in shapes]
+            got1 = b.se_soft_embed_step_onepass_workspace_bytes(256, 262144, 65536, 131072, 2816)
+            if got != want or got1 != want1:
+                bad.append((got, got1))
+    ts = [threading.Thread(target=worker) for _ in range(16)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not bad

@@ -157,3 +157,43 @@ def test_step_full_size_rank():
     for a, b in ((mx, mx2), (lse, lse2), (ent, ent2), (am, am2), (out, ref)):
         assert torch.equal(a, b)
     np.testing.assert_array_equal(am.cpu().numpy(), wl.planted_index(w))
+
+
+def test_step_from_two_threads_on_two_streams():
+    """Calls are reentrant: two host threads, each with its own stream, buffers and
+    workspace, run the whole step concurrently and get the serial call's result bit for
+    bit (the library keeps no per-call state of its own)."""
+    import threading
+    L, V, s, e, d = 64, 20000, 4000, 12000, 256
+    rng = np.random.default_rng(31)
+    xs = [(rng.standard_normal((L, V)) * 3).astype(np.float32) for _ in range(2)]
+    tab = wl.fp32_to_bf16_bits((rng.standard_normal((e - s, d)) * 0.02).astype(np.float32))
+    w_t = dev(tab)
+    x_ts = [dev(x) for x in xs]
+    ref = [api.soft_embed_step(x_t, s, e, w_t, 2.0) for x_t in x_ts]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None, None]
+    errs = []
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                outs = None
+                for _ in range(20):
+                    outs = api.soft_embed_step(x_ts[i], s, e, w_t, 2.0,
+                                               stream=streams[i].cuda_stream)
+                streams[i].synchronize()
+                got[i] = outs
+        except Exception as ex:          # reported after join
+            errs.append(ex)
+    say("step from two threads")
+    ts = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errs, errs
+    for i in range(2):
+        for a, b in zip(got[i], ref[i]):
+            assert torch.equal(a, b)
