@@ -354,6 +354,13 @@ def main():
         x, lse, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, ws), K, args.warmup)
     us_u8 = event_time_us(lambda: B.se_soft_embed_fp8(
         pr8, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, ws), K, args.warmup)
+    # the whole step against the e4m3 table (statistics + staged probabilities + contraction)
+    mx8, lse8, ent8 = torch.empty(L, device=dev), torch.empty(L, device=dev), torch.empty(L, device=dev)
+    am8 = torch.empty(L, device=dev, dtype=torch.int32)
+    us_s8 = event_time_us(lambda: B.se_soft_embed_step_fp8(
+        x, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, mx8, lse8, ent8, am8, wss),
+        K, args.warmup)
+    s8_bytes = row_stats_bytes(w) + w.k * d + 4 * w.k + 4 * L * d
     us_q = event_time_us(lambda: B.se_quantize_table_fp8(shard, codes, wscale), 3, 1)
     f8_bytes = fp8_call_bytes(w)
     fp8_side = {"fused_call_us": round(us_f8, 2),
@@ -364,8 +371,14 @@ def main():
                                         "peak": PEAK_HBM_GBS,
                                         "frac": round(f8_bytes / (us_f8 * 1e-6) / 1e9
                                                       / PEAK_HBM_GBS, 4)},
+                "step_us": round(us_s8, 2),
+                "gflops_step": round(flops / (us_s8 * 1e-6) / 1e9, 2),
+                "roofline_step": {"bound": "hbm", "algorithmic_bytes": s8_bytes,
+                                  "achieved": round(s8_bytes / (us_s8 * 1e-6) / 1e9, 2),
+                                  "peak": PEAK_HBM_GBS,
+                                  "frac": round(s8_bytes / (us_s8 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
                 "quantize_shard_us": round(us_q, 2)}
-    del codes, wscale, out8, pr8
+    del codes, wscale, out8, pr8, mx8, lse8, ent8, am8
 
     # side measurement: the one-pass call over the same slice (softmax over the slice, row
     # statistics from the same read of the logits), and the merge of 4 slice results.  For

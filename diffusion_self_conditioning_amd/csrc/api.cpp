@@ -253,8 +253,8 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
 // The contraction of super-step-tiled bf16 probabilities ([K / 128][n_rows][128], slice
 // position 0 first) in the workspace of a staged call.
 se_status run_staged_gemm(const se::StagedLayout& o, const uint16_t* probs, int64_t n_rows,
-                          int64_t K, const uint16_t* w_shard, int64_t ld_w, int64_t d,
-                          float gamma, float* out, int64_t ld_out, unsigned char* ws,
+                          int64_t K, const void* w_shard, const float* w_scale, int64_t ld_w,
+                          int64_t d, float gamma, float* out, int64_t ld_out, unsigned char* ws,
                           hipStream_t st) {
   se::GemmParams p{};
   p.a = probs;
@@ -262,6 +262,7 @@ se_status run_staged_gemm(const se::StagedLayout& o, const uint16_t* probs, int6
   p.a_ss = n_rows * se::kSuperStep * 2;
   p.col0 = 0;
   p.w = w_shard;
+  p.wscale = w_scale;
   p.ldw = ld_w;
   p.M = n_rows;
   p.N = d;
@@ -274,7 +275,7 @@ se_status run_staged_gemm(const se::StagedLayout& o, const uint16_t* probs, int6
   p.tiles = (int)o.g.tiles;
   p.splits = (int)o.g.splits;
   p.kblocks = (int)o.g.kblocks;
-  return from_hip(se::launch_soft_embed(p, false, false, st));
+  return from_hip(se::launch_soft_embed(p, false, w_scale != nullptr, st));
 }
 
 }  // namespace
@@ -415,15 +416,21 @@ se_status se_soft_embed_staged(const float* logits, int64_t ld_logits, const flo
   rc = from_hip(se::launch_probs_bf16_tiled(logits, ld_logits, row_lse, n_rows, vocab_start, K,
                                             probs, st));
   if (rc != SE_OK) return rc;
-  return run_staged_gemm(o, probs, n_rows, K, w_shard, ld_w, d, gamma, out, ld_out, ws, st);
+  return run_staged_gemm(o, probs, n_rows, K, w_shard, nullptr, ld_w, d, gamma, out, ld_out, ws, st);
 }
 
-se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_rows,
-                             int64_t vocab, int64_t vocab_start, int64_t vocab_end,
-                             const uint16_t* w_shard, int64_t w_rows, int64_t ld_w, int64_t d,
-                             float gamma, float* out, int64_t ld_out, float* row_max,
-                             float* row_lse, float* row_entropy, int32_t* row_argmax,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The whole step: statistics (with the slice's staged probabilities), then the
+// contraction of the staged probabilities against a bf16 table, or an e4m3 table with
+// per-row scales when w_scale is given.
+se_status run_step(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
+                   int64_t vocab_start, int64_t vocab_end, const void* w_shard,
+                   const float* w_scale, int64_t w_rows, int64_t ld_w, int64_t d, float gamma,
+                   float* out, int64_t ld_out, float* row_max, float* row_lse,
+                   float* row_entropy, int32_t* row_argmax, void* workspace,
+                   size_t workspace_bytes, void* stream, bool w8) {
   se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
   if (rc != SE_OK) return rc;
   if (ld_logits < vocab) return SE_ERR_SHAPE;
@@ -432,6 +439,10 @@ se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_r
     return SE_ERR_NULL;
   rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_shard, out);
   if (rc != SE_OK) return rc;
+  if (w8) {
+    rc = check_fp8_layout(d, ld_w, w_scale);
+    if (rc != SE_OK) return rc;
+  }
   if (!aligned16(logits) || (ld_logits % 4) != 0) return SE_ERR_ALIGN;
   if (!aligned4(row_max) || !aligned4(row_lse) || !aligned4(row_entropy) || !aligned4(row_argmax))
     return SE_ERR_ALIGN;
@@ -442,13 +453,13 @@ se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_r
                                        row_entropy, row_argmax, st));
     if (rc != SE_OK) return rc;
     return run_soft_embed(true, logits, ld_logits, row_lse, n_rows, vocab_start, vocab_end,
-                          w_shard, nullptr, ld_w, d, gamma, out, ld_out, workspace,
-                          workspace_bytes, stream);
+                          w_shard, w8 ? w_scale : nullptr, ld_w, d, gamma, out, ld_out,
+                          workspace, workspace_bytes, stream);
   }
   const se::StagedLayout o = se::staged_layout(n_rows, K, d);
   if (o.g.grid > INT32_MAX) return SE_ERR_SHAPE;
   if ((int64_t)se::tiled_probs_bytes(n_rows, K) > (int64_t)UINT32_MAX ||
-      K * ld_w * 2 > (int64_t)UINT32_MAX)
+      K * ld_w * (w8 ? 1 : 2) > (int64_t)UINT32_MAX)
     return SE_ERR_SHAPE;
   if (workspace_bytes < o.total) return SE_ERR_WORKSPACE;
   if (!workspace) return SE_ERR_NULL;
@@ -459,7 +470,34 @@ se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_r
                                            row_lse, row_entropy, row_argmax, vocab_start, K,
                                            probs, st));
   if (rc != SE_OK) return rc;
-  return run_staged_gemm(o, probs, n_rows, K, w_shard, ld_w, d, gamma, out, ld_out, ws, st);
+  return run_staged_gemm(o, probs, n_rows, K, w_shard, w8 ? w_scale : nullptr, ld_w, d, gamma,
+                         out, ld_out, ws, st);
+}
+}  // namespace
+
+extern "C" {
+
+se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_rows,
+                             int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                             const uint16_t* w_shard, int64_t w_rows, int64_t ld_w, int64_t d,
+                             float gamma, float* out, int64_t ld_out, float* row_max,
+                             float* row_lse, float* row_entropy, int32_t* row_argmax,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return run_step(logits, ld_logits, n_rows, vocab, vocab_start, vocab_end, w_shard, nullptr,
+                  w_rows, ld_w, d, gamma, out, ld_out, row_max, row_lse, row_entropy,
+                  row_argmax, workspace, workspace_bytes, stream, false);
+}
+
+se_status se_soft_embed_step_fp8(const float* logits, int64_t ld_logits, int64_t n_rows,
+                                 int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                                 const uint8_t* w_codes, const float* w_scale, int64_t w_rows,
+                                 int64_t ld_w, int64_t d, float gamma, float* out,
+                                 int64_t ld_out, float* row_max, float* row_lse,
+                                 float* row_entropy, int32_t* row_argmax, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return run_step(logits, ld_logits, n_rows, vocab, vocab_start, vocab_end, w_codes, w_scale,
+                  w_rows, ld_w, d, gamma, out, ld_out, row_max, row_lse, row_entropy,
+                  row_argmax, workspace, workspace_bytes, stream, true);
 }
 
 size_t se_soft_embed_step_onepass_workspace_bytes(int64_t n_rows, int64_t vocab,

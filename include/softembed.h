@@ -199,6 +199,24 @@ se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_r
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * se_soft_embed_step_fp8 -- se_soft_embed_step against an e4m3 table with per-row
+ * power-of-two scales (as se_quantize_table_fp8 writes them; the pages serve FP8
+ * weights: agentlenshq overview of DiffusionGemma in vLLM, performance and
+ * quantization).  Outputs are bit for bit those of se_row_stats followed by
+ * se_soft_embed_fp8_fused.  Arguments: those of se_soft_embed_step with the table given
+ * as w_codes (uint8 [w_rows, ld_w]) and w_scale (fp32 [w_rows]) as in se_soft_embed_fp8;
+ * workspace of se_soft_embed_staged_workspace_bytes() bytes.  Errors as
+ * se_soft_embed_step, and those of se_soft_embed_fp8's table checks.
+ */
+se_status se_soft_embed_step_fp8(const float* logits, int64_t ld_logits, int64_t n_rows,
+                                 int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                                 const uint8_t* w_codes, const float* w_scale, int64_t w_rows,
+                                 int64_t ld_w, int64_t d, float gamma, float* out,
+                                 int64_t ld_out, float* row_max, float* row_lse,
+                                 float* row_entropy, int32_t* row_argmax, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * se_soft_embed_step_onepass -- the same step as se_soft_embed_step (row statistics
  * over the full width [0, vocab), the slice's soft embedding against them) from ONE
  * read of the logits.  The row is cut into ranges: [0, s) and [e, vocab) in chunks,

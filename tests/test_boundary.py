@@ -427,3 +427,25 @@ def test_workspace_queries_are_thread_safe():
     for t in ts:
         t.join()
     assert not bad
+
+
+def test_step_fp8_errors():
+    st = lib.se_soft_embed_step_fp8
+
+    def call(**kw):
+        a = dict(x=P1, ld=262144, n=256, vocab=262144, s=65536, e=131072, w=P3, sc=P2 + 4096,
+                 w_rows=65536, ldw=2816, d=2816, gamma=53.0, out=P4, ldo=2816, mx=P2, lse=P2 + 1024,
+                 ent=P2 + 2048, am=P2 + 3072, ws=P5, ws_bytes=1 << 40)
+        a.update(kw)
+        return st(a["x"], a["ld"], a["n"], a["vocab"], a["s"], a["e"], a["w"], a["sc"],
+                  a["w_rows"], a["ldw"], a["d"], a["gamma"], a["out"], a["ldo"], a["mx"], a["lse"],
+                  a["ent"], a["am"], a["ws"], a["ws_bytes"], None)
+    assert call(w_rows=1000) == b.SE_ERR_SLICE
+    assert call(sc=None) == b.SE_ERR_NULL
+    assert call(x=None) == b.SE_ERR_NULL
+    assert call(d=2808, ldw=2816, ldo=2816) == b.SE_ERR_ALIGN     # d % 16 != 0
+    assert call(ldw=2824) == b.SE_ERR_ALIGN                      # ld_w % 16 != 0
+    assert call(sc=P2 + 4098) == b.SE_ERR_ALIGN
+    assert call(ws_bytes=1024) == b.SE_ERR_WORKSPACE
+    assert call(n=0, x=None, w=None, sc=None, out=None, mx=None, lse=None, ent=None, am=None,
+                ws=None, ws_bytes=0) == b.SE_OK

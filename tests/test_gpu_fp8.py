@@ -247,3 +247,67 @@ def test_fp8_rank_full_size():
     r = rel_fro(f8f.cpu().numpy()[rows], ref)
     say("rel_fro", f"{r:.3e}")
     assert r <= GATE
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_fp8_step_equals_row_stats_then_fp8_fused(case):
+    """se_soft_embed_step_fp8: statistics bitwise se_row_stats', embedding bitwise
+    se_soft_embed_fp8_fused's on the oracle's codes (NaN codes and scales past the slice,
+    never read), and within the gate of the fp64 oracle on the dequantized table."""
+    L, V, s, e, d, seed = CASES[case]
+    rng = np.random.default_rng(seed + 50)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    x[np.arange(L), rng.integers(0, V, L)] += 8.0
+    tab = (rng.standard_normal((e - s, d)) * 0.02).astype(np.float32)
+    bits = (tab.view(np.uint32) >> 16).astype(np.uint16)
+    codes, scale = fp8.quantize_table(bits)
+    c_t = dev(np.concatenate([codes, np.full((24, d), 0x7F, np.uint8)]))
+    s_t = dev(np.concatenate([scale, np.full(24, np.nan, np.float32)]))
+    x_t = dev(x)
+    say("fp8 step", case, (L, V, s, e, d))
+    out, mx, lse, ent, am = api.soft_embed_step_fp8(x_t, s, e, c_t, s_t, 7.5)
+    mx2, lse2, ent2, am2 = api.row_stats(x_t)
+    ref = torch.full((L, d), float("nan"), device=DEV)
+    B.se_soft_embed_fp8_fused(x_t, lse2, s, e, c_t, s_t, 7.5, ref, api.workspace(L, s, e, d, DEV))
+    torch.cuda.synchronize()
+    for a, b in ((mx, mx2), (lse, lse2), (ent, ent2), (am, am2), (out, ref)):
+        assert torch.equal(a, b)
+    r = rel_fro(out.cpu().numpy(),
+                oracle.soft_embed(x, s, e, fp8.dequantize(codes, scale).astype(np.float32), 7.5))
+    say("rel_fro", f"{r:.3e}")
+    assert r <= GATE
+
+
+def test_fp8_step_empty_slice():
+    x_t = dev(np.random.default_rng(3).standard_normal((4, 64)).astype(np.float32))
+    out, mx, lse, ent, am = api.soft_embed_step_fp8(
+        x_t, 16, 16, dev(np.zeros((8, 16), np.uint8)), dev(np.ones(8, np.float32)), 1.0)
+    mx2, lse2, ent2, am2 = api.row_stats(x_t)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
+    for a, b in ((mx, mx2), (lse, lse2), (ent, ent2), (am, am2)):
+        assert torch.equal(a, b)
+
+
+def test_fp8_step_rank_full_size():
+    """The one-rank shape: the e4m3 step equals se_row_stats + se_soft_embed_fp8_fused bit for
+    bit, and its argmax is the planted index."""
+    w = wl.get("rank")
+    bits, _ = wl.make_table(w)
+    shard = np.ascontiguousarray(bits[w.vocab_start:w.vocab_end])
+    del bits
+    say("fp8 step rank: gpu quantize")
+    c_t, s_t = gpu_quantize(shard)
+    x = wl.make_logits(w)
+    x_t = dev(x)
+    say("fp8 step rank: gpu calls")
+    out, mx, lse, ent, am = api.soft_embed_step_fp8(x_t, w.vocab_start, w.vocab_end, c_t, s_t,
+                                                    w.gamma)
+    mx2, lse2, ent2, am2 = api.row_stats(x_t)
+    ref = torch.empty_like(out)
+    B.se_soft_embed_fp8_fused(x_t, lse2, w.vocab_start, w.vocab_end, c_t, s_t, w.gamma, ref,
+                              api.workspace(w.rows, w.vocab_start, w.vocab_end, w.d, DEV))
+    torch.cuda.synchronize()
+    for a, b in ((mx, mx2), (lse, lse2), (ent, ent2), (am, am2), (out, ref)):
+        assert torch.equal(a, b)
+    np.testing.assert_array_equal(am.cpu().numpy(), wl.planted_index(w))
