@@ -197,3 +197,31 @@ def test_step_from_two_threads_on_two_streams():
     for i in range(2):
         for a, b in zip(got[i], ref[i]):
             assert torch.equal(a, b)
+
+
+def test_more_rows_than_one_grid_dimension_holds():
+    """70,000 rows: the launches that put rows in a grid dimension of at most 65,535 go in
+    chunks (staged probabilities, the empty slice's zero fill).  The staged call equals the
+    fused call and the step equals the separate calls, bit for bit; the one-read step agrees
+    on argmax and max; the argmax matches the oracle."""
+    L, V, s, e, d = 70000, 64, 8, 56, 16
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    x[np.arange(L), rng.integers(0, V, L)] += 8.0
+    tab = wl.fp32_to_bf16_bits((rng.standard_normal((e - s, d)) * 0.02).astype(np.float32))
+    x_t, w_t = dev(x), dev(tab)
+    say("70000 rows")
+    mx, lse, ent, am = api.row_stats(x_t)
+    fused = api.soft_embed(x_t, lse, s, e, w_t, 3.0, fused=True)
+    staged = api.soft_embed(x_t, lse, s, e, w_t, 3.0, staged=True)
+    step = api.soft_embed_step(x_t, s, e, w_t, 3.0)
+    one = api.soft_embed_step(x_t, s, e, w_t, 3.0, onepass=True)
+    empty = api.soft_embed_step(x_t, 16, 16, w_t, 3.0)
+    torch.cuda.synchronize()
+    assert torch.equal(staged, fused)
+    for a, b in zip(step, (fused, mx, lse, ent, am)):
+        assert torch.equal(a, b)
+    assert torch.equal(one[1], mx) and torch.equal(one[4], am)
+    assert rel_fro(one[0].cpu().numpy(), fused.cpu().numpy()) <= 5e-3
+    assert torch.count_nonzero(empty[0]) == 0
+    np.testing.assert_array_equal(am.cpu().numpy(), oracle.row_stats(x)["argmax"])
