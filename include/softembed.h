@@ -32,15 +32,16 @@
  *  - Results are bitwise reproducible for the same inputs and shapes on the same
  *    kind of device: the work decomposition depends only on the shapes and the
  *    current device's compute-unit count (the contraction is split over the
- *    vocabulary until tiles x splits fill the CUs), and every reduction runs in a
- *    fixed order.
+ *    vocabulary into the number of pieces that minimises a makespan model of the
+ *    shape on that many CUs), and every reduction runs in a fixed order.
  *  - The only global state is a per-device cache of that CU count, read once per
  *    device (std::call_once) from the HIP runtime; without a usable device the
  *    MI355X count, 256, is used.
  *  - Logits must be finite (not checked on the device).
  *  - n_rows == 0 is a no-op that checks only sizes; its pointers may be NULL.
  *  - Calls are thread-safe and capture-safe (no allocation, no sync, no host
- *    read of device data).
+ *    read of device data): a caller may issue them from several threads on
+ *    several streams, or capture them into a HIP graph and replay it.
  */
 #ifndef SOFTEMBED_H
 #define SOFTEMBED_H
