@@ -428,9 +428,24 @@ def main():
     gb = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
     mm_us = event_time_us(lambda: torch.mm(ga, gb), 10, 5)
     del ga, gb
+    # the vendor GEMM at this call's own shape: the slice's bf16 probabilities [rows, K]
+    # (row-major, contiguous) times the bf16 shard [K, d], fp32 output, beside the library's
+    # contraction of the same operands (se_soft_embed on the probabilities se_probs_bf16 wrote)
+    B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, probs)
+    pa = probs[:, w.vocab_start:w.vocab_end].contiguous()
+    pb = shard.view(torch.bfloat16)
+    og = torch.empty_like(out)
+    vend_us = event_time_us(lambda: torch.mm(pa, pb, out_dtype=torch.float32), 10, 5)
+    ours_us = event_time_us(lambda: B.se_soft_embed(probs, w.vocab_start, w.vocab_end, shard,
+                                                    w.gamma, og, ws), 10, 5)
+    del pa, pb, og
     ceilings = {"cold_step_us_median": round(sorted(cold)[len(cold) // 2], 2),
                 "hbm_copy_gbs": round(2 * (1 << 28) * 4 / (copy_us * 1e-6) / 1e9, 1),
-                "bf16_gemm_8192_tflops": round(2 * 8192 ** 3 / (mm_us * 1e-6) / 1e12, 1)}
+                "bf16_gemm_8192_tflops": round(2 * 8192 ** 3 / (mm_us * 1e-6) / 1e12, 1),
+                "vendor_gemm_same_shape_us": round(vend_us, 2),
+                "vendor_gemm_same_shape_tflops": round(flops / (vend_us * 1e-6) / 1e12, 1),
+                "library_contraction_same_shape_us": round(ours_us, 2),
+                "library_contraction_same_shape_tflops": round(flops / (ours_us * 1e-6) / 1e12, 1)}
 
     cpu = None
     if not args.no_cpu_baseline:
