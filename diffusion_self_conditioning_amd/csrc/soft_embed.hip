@@ -637,9 +637,318 @@ __global__ void zero_rows_kernel(float* __restrict__ out, int64_t ldo, int64_t N
 
 namespace {
 
+// ---- contraction of staged probabilities: ping-pong waves, operands straight into LDS ---
+// For probabilities in the super-step-tiled layout (the staged, whole-step and one-pass
+// calls), the bf16 table and whole 256-row tiles.  Same 8 waves, wave tiles, MFMAs, k order
+// and partial layout as soft_embed_kernel, so the results are bit for bit the same; the
+// schedule differs:
+//   - Waves 0-3 (group 0) and 4-7 (group 1), one of each per SIMD, run a phase apart.  A
+//     32-position step is two phases per wave: M (the step's fragments read from LDS, loads
+//     for later steps issued) and C (its 16 MFMAs, at raised wave priority).  While one
+//     group is in C the other is in M, so each SIMD's matrix core has a wave to feed it
+//     while the other wave waits on LDS and memory.  Every phase ends with a workgroup
+//     barrier; group 1 takes one extra barrier before its loop and group 0 one after it.
+//   - Operands go from memory to LDS with buffer_load ... lds: no staging registers and no
+//     LDS writes in the loop.  Group 0 loads the probability stages (64 positions, 32 KB,
+//     two buffers, a whole stage in the M phase of every other step); group 1 the table
+//     steps (32 positions, 16 KB, ring of four, three steps ahead, nontemporal).
+//   - Every buffer is its own LDS array and the barriers are plain s_barrier with the wait
+//     counts written out (empty asm memory clobbers keep LDS accesses on their side), so a
+//     wave waits only for the loads the next phases read.
+// When a step's data lands, for step s (group 0's M(s) follows barrier 2 s, group 1's one
+// barrier later):
+//   - group 0 loads stage t + 1 in M(2 t) into the buffer stage t - 1 held (released by
+//     group 1's M(2 t - 1)) and waits for it at the end of C(2 t + 1);
+//   - group 1 loads table step s + 3 in M(s) into the buffer of step s - 1 (released by its
+//     own M(s - 1)) and, keeping its last 8 loads in flight, has step s + 1 in LDS at the
+//     end of M(s).
+constexpr int kPPStage = 64;                      // positions per probability stage
+constexpr int kPPStageBytes = kBM * kPPStage * 2; // [256 rows][64 positions] bf16
+constexpr int kPPStepBytes = kBK * kBN * 2;       // [32 rows][256 columns] bf16
+static_assert(2 * kPPStageBytes + 4 * kPPStepBytes <= 160 * 1024, "LDS budget of one CU");
+// probability stage: row m at 128 m bytes, 16-byte chunk c (8 positions) at c ^ pp_swz(m).
+// A fragment read takes one chunk of 32 consecutive rows; the swizzle gives every 8 (and
+// every 16) consecutive rows distinct 16-byte slots of a 128-byte (256-byte) bank line.
+__device__ __forceinline__ int pp_swz(int m) { return ((m >> 1) ^ ((m & 1) << 2)) & 7; }
+__device__ __forceinline__ int pp_off(int m, int c) { return m * 128 + 16 * (c ^ pp_swz(m)); }
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// s_waitcnt with vmcnt(n) and lgkmcnt(0) (expcnt not waited on)
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | ((n >> 4) << 14));
+}
+// Workgroup barrier once this wave's LDS reads are complete and all but its n most recent
+// memory loads have landed.  The scheduling barriers keep every instruction on its side of
+// the phase boundary; the asm clobbers keep memory accesses there (s_barrier is no fence).
+template <int n>
+__device__ __forceinline__ void phase_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  wait_vm_lgkm0<n>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+constexpr int kNoVmWait = 63;
+
+__global__ void __launch_bounds__(kGemmThreads)
+__attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+soft_embed_pp_kernel(const GemmParams p) {
+  static_assert(kWaves == 8 && kMI == 4 && kNI == 2 && kWN == 4, "the 8-wave layout");
+  __shared__ __attribute__((aligned(16))) unsigned char P0[kPPStageBytes], P1[kPPStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char W0[kPPStepBytes], W1[kPPStepBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char W2[kPPStepBytes], W3[kPPStepBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, q = wave & 3;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int b = xcd_local_order((int)blockIdx.x, (int)gridDim.x);
+  const int t = b % p.tiles;
+  const int s = b / p.tiles;
+  const int m0 = (t / p.tiles_n) * kBM;
+  const int n0 = (t % p.tiles_n) * kBN;
+  const int N = (int)p.N;
+  // this split's vocab range [k_lo, k_hi): nq whole super-steps, then (last split only)
+  // the remaining positions
+  const int64_t k_lo = (((int64_t)s * p.kblocks) / p.splits) * kSplitQuantum;
+  const int64_t k_hi = min((((int64_t)(s + 1) * p.kblocks) / p.splits) * kSplitQuantum, p.K);
+  const int nq = (int)((min(k_hi, (p.K / kSS) * kSS) - k_lo) / kSS);
+  const int nsteps = kQ * nq;
+
+  // probabilities: position k of row m at (k / 128) a_blk + 256 m + 2 (k % 128) bytes
+  const int64_t a_blk = p.M * (int64_t)kSuperStep * 2;
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(
+      static_cast<const unsigned char*>(p.a) + (int64_t)m0 * kSuperStep * 2,
+      (uint32_t)min(((p.K + kSuperStep - 1) / kSuperStep - 1) * a_blk + (int64_t)kBM * kSuperStep * 2,
+                    (int64_t)UINT32_MAX));
+  const int64_t w_ld = p.ldw * 2;
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      make_rsrc(static_cast<const unsigned char*>(p.w) + k_lo * w_ld,
+                (uint32_t)min((k_hi - k_lo) * w_ld, (int64_t)UINT32_MAX));
+  // Each load moves 64 lanes x 16 bytes into 1 KB of LDS, lane l at byte 16 l.
+  //   group 0, wave q: stage rows 64 q .. + 63, 8 rows per load; lane l of load i writes row
+  //     64 q + 8 i + l / 8, stored chunk l % 8, which holds logical chunk (l % 8) ^ pp_swz(row)
+  //   group 1, wave q: step rows 8 q .. + 7, 2 rows per load; lane l of load i writes row
+  //     8 q + 2 i + l / 32, stored chunk l % 32, which holds column chunk (l % 32) ^ 4 (row % 4)
+  uint32_t voff[8];
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 64 * q + 8 * i + (lane >> 3);
+      voff[i] = (uint32_t)(r * 256 + 16 * ((lane & 7) ^ pp_swz(r)));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = 8 * q + 2 * i + (lane >> 5);
+      const int col = n0 + 8 * ((lane & 31) ^ (4 * (k & 3)));
+      voff[i] = (uint32_t)(k * w_ld) + 2u * (uint32_t)min(col, N - 8);
+    }
+#pragma unroll
+    for (int i = 4; i < 8; ++i) voff[i] = 0u;
+  }
+  // loads past the last stage or step repeat the last one (into a buffer no later phase reads)
+  auto load_stage = [&](unsigned char* buf, int ps) {
+    const int64_t k0 = k_lo + (int64_t)kPPStage * min(ps, 2 * nq - 1);
+    const uint32_t soff = (uint32_t)((k0 / kSuperStep) * a_blk + 2 * (k0 % kSuperStep));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(buf + 1024 * (8 * q + i)),
+                                               16, voff[i], soff, 0, 0);
+  };
+  auto load_step = [&](unsigned char* buf, int st) {
+    const uint32_t soff = (uint32_t)((int64_t)kBK * min(st, nsteps - 1) * w_ld);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(buf + 1024 * (4 * q + i)),
+                                               16, voff[i], soff, 0, 2);
+  };
+
+  f32x16 acc[kMI][kNI];
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  // fragments of substep u (16 positions) of a step held in half h of a stage: A row
+  // 128 wm + 32 mi + lane % 32, positions 32 h + 16 u + 8 (lane / 32) .. +7; B as in
+  // soft_embed_kernel
+  const int a_row = 128 * wm + (lane & 31);
+  uint32_t b_rd[kNI];
+  {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+      b_rd[ni] = (uint32_t)w_off(8 * (g >> 1) + (i >> 2), kTN * wn + 32 * ni + 16 * (g & 1) + 4 * (i & 3));
+  }
+  bf16x8 a0[kMI], b0[kNI], a1[kMI], b1[kNI];
+  auto frag = [&](const unsigned char* pb, const unsigned char* wb, int h, int u, bf16x8 (&af)[kMI],
+                  bf16x8 (&bf)[kNI]) {
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+      af[mi] = *reinterpret_cast<const bf16x8*>(pb + pp_off(a_row + 32 * mi, 4 * h + 2 * u + (lane >> 5)));
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const unsigned char* wp = wb + b_rd[ni] + 8192 * u;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp + 2048));
+      bf[ni] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
+                                       __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto mfmas = [&](const bf16x8 (&af)[kMI], const bf16x8 (&bf)[kNI]) {
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+  };
+  auto m_phase = [&](const unsigned char* pb, const unsigned char* wb, int h) {
+    frag(pb, wb, h, 0, a0, b0);
+    frag(pb, wb, h, 1, a1, b1);
+  };
+  auto c_phase = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+    mfmas(a0, b0);
+    mfmas(a1, b1);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (nq > 0) {
+    if (grp == 0) {
+      load_stage(P0, 0);
+    } else {
+      load_step(W0, 0);
+      load_step(W1, 1);
+      load_step(W2, 2);
+    }
+    phase_end<0>();
+    if (grp == 0) {
+      for (int qd = 0; qd < nq; ++qd) {         // steps 4 qd .. 4 qd + 3: stages 2 qd, 2 qd + 1
+        load_stage(P1, 2 * qd + 1);
+        m_phase(P0, W0, 0);
+        phase_end<kNoVmWait>();
+        c_phase();
+        phase_end<kNoVmWait>();
+        m_phase(P0, W1, 1);
+        phase_end<kNoVmWait>();
+        c_phase();
+        phase_end<0>();                         // stage 2 qd + 1 in LDS
+        load_stage(P0, 2 * qd + 2);
+        m_phase(P1, W2, 0);
+        phase_end<kNoVmWait>();
+        c_phase();
+        phase_end<kNoVmWait>();
+        m_phase(P1, W3, 1);
+        phase_end<kNoVmWait>();
+        c_phase();
+        phase_end<0>();                         // stage 2 qd + 2 in LDS
+      }
+      phase_end<kNoVmWait>();                   // pairs with group 1's first barrier
+    } else {
+      phase_end<kNoVmWait>();                   // one phase behind group 0
+      for (int qd = 0; qd < nq; ++qd) {
+        const int s0 = kQ * qd;
+        load_step(W3, s0 + 3);
+        m_phase(P0, W0, 0);
+        phase_end<8>();                         // table step s0 + 1 in LDS
+        c_phase();
+        phase_end<kNoVmWait>();
+        load_step(W0, s0 + 4);
+        m_phase(P0, W1, 1);
+        phase_end<8>();
+        c_phase();
+        phase_end<kNoVmWait>();
+        load_step(W1, s0 + 5);
+        m_phase(P1, W2, 0);
+        phase_end<8>();
+        c_phase();
+        phase_end<kNoVmWait>();
+        load_step(W2, s0 + 6);
+        m_phase(P1, W3, 1);
+        phase_end<8>();
+        c_phase();
+        phase_end<kNoVmWait>();
+      }
+    }
+  }
+  // no load may still be writing LDS when the tail reuses the buffers or the waves end
+  phase_end<0>();
+
+  // ---- the last split's remaining positions, 32 at a time, with guarded loads ---------
+  for (int64_t k0 = k_lo + (int64_t)kSS * nq; k0 < k_hi; k0 += kBK) {
+    // probabilities: 256 rows x 4 chunks of 8 positions, 2 per thread
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = tid + kGemmThreads * j;
+      const int row = e >> 2, c = e & 3;
+      const int64_t kk = k0 + 8 * c;
+      const uint16_t* hp = reinterpret_cast<const uint16_t*>(
+          static_cast<const unsigned char*>(p.a) + (kk / kSuperStep) * a_blk +
+          ((int64_t)(m0 + row) * kSuperStep + kk % kSuperStep) * 2);
+      uint32_t v[8];
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) v[e8] = (kk + e8 < p.K) ? (uint32_t)hp[e8] : 0u;
+      *reinterpret_cast<uint4*>(P0 + pp_off(row, c)) =
+          make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+    }
+    // table: 32 rows x 32 chunks of 8 columns, 2 per thread
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = tid + kGemmThreads * j;
+      const int k = e >> 5, c = e & 31;
+      const int64_t kr = k0 + k;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (kr < p.K)
+        v = *reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(p.w) + kr * w_ld +
+                                            2 * (int64_t)min(n0 + 8 * c, N - 8));
+      *reinterpret_cast<uint4*>(W0 + w_off(k, 8 * c)) = v;
+    }
+    __syncthreads();
+    m_phase(P0, W0, 0);
+    mfmas(a0, b0);
+    mfmas(a1, b1);
+    __syncthreads();
+  }
+
+  // ---- epilogue, as soft_embed_kernel's ------------------------------------------------
+  if (p.splits == 1 && !p.keep_partials) {
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int col = n0 + kTN * wn + 32 * ni + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (col < N) p.out[(int64_t)row * p.ldo + col] = p.gamma * acc[mi][ni][r];
+        }
+      }
+  } else {
+    float* dst = p.ws + ((int64_t)s * p.tiles + t) * kTileFloats;
+    constexpr int kMF = kMI * kNI;
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dst[((wave * kMF + mi * kNI + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
+  }
+}
+
 template <bool FUSED, bool W8>
 void launch_contraction(const GemmParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles * p.splits));
+  // staged (super-step-tiled) probabilities in whole 256-row tiles, bf16 table: the
+  // ping-pong kernel (bit for bit the same result)
+  if (!FUSED && !W8 && p.M % kBM == 0 && p.a_ss == p.M * (int64_t)kSuperStep * 2) {
+    hipLaunchKernelGGL(soft_embed_pp_kernel, grid, dim3(kGemmThreads), 0, stream, p);
+    return;
+  }
   // whole 256-row tiles take the path with per-lane addresses fixed for the kernel
   if (p.M % kBM == 0)
     hipLaunchKernelGGL((soft_embed_kernel<FUSED, true, W8>), grid, dim3(kGemmThreads), 0, stream, p);

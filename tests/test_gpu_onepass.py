@@ -94,6 +94,8 @@ CASES = {
     "slice-4097": (255, 8200, 8, 4105, 272, 5),
     "two-row-tiles": (300, 2048, 0, 2048, 512, 6),
     "256-splits": (16, 65536, 0, 65536, 256, 7),
+    "whole-tile-ragged": (256, 20008, 8, 12353, 264, 8),  # ping-pong contraction, tail
+    "two-whole-tiles": (512, 4104, 0, 4104, 128, 9),
 }
 
 

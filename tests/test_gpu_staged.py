@@ -4,9 +4,10 @@ The staged call must return se_soft_embed_fused's output bit for bit: the same b
 probabilities (same rounding), contracted in the same order; only their trip through
 memory differs.  The fused call is itself gated against the fp64 oracle in
 test_gpu_parity.py; here the staged output is also gated directly on the small cases.
-Cases: whole and partial 256-row tiles, slices of 1 / 63 / 4097 positions and ragged
-hidden sizes, slices that start mid-vocabulary, shard rows past the slice holding NaN
-(never read), one split and many splits, and the one-rank workload at full size.
+Cases: whole and partial 256-row tiles (the two contraction kernels), slices of 1 / 63 /
+4097 positions and ragged hidden sizes, slices that start mid-vocabulary, shard rows past
+the slice holding NaN (never read), one split and many splits, tails of the last split,
+and the one-rank workload at full size.
 se_soft_embed_step must return se_row_stats' statistics and the fused call's
 embedding bit for bit, on the same kinds of cases plus an empty slice.
 """
@@ -74,6 +75,43 @@ def test_staged_equals_fused(case):
         assert rel_fro(staged.cpu().numpy(), ref) <= 5e-3
 
 
+# Whole 256-row tiles of staged probabilities take the ping-pong contraction (the shapes
+# above, with partial row tiles, take the register-staged one): the tail of the last split
+# alone (slices of 1 and 63 positions), one super-step with and without a tail, two row
+# tiles, many splits with a tail, hidden sizes that are not a multiple of 256, long splits.
+TILE_CASES = {
+    # name: (L, V, s, e, d, seed)
+    "k1": (256, 1000, 8, 9, 64, 61),
+    "k63": (256, 1004, 64, 127, 272, 62),
+    "k128": (256, 4096, 0, 128, 128, 63),
+    "k200-two-tiles": (512, 5000, 40, 240, 256, 64),
+    "k4097": (256, 8200, 8, 4105, 2816, 65),
+    "k12345": (512, 50000, 12344, 24689, 520, 66),
+    "k65553": (256, 70000, 0, 65553, 256, 67),
+}
+
+
+@pytest.mark.parametrize("case", sorted(TILE_CASES))
+def test_staged_whole_tiles_equals_fused(case):
+    L, V, s, e, d, seed = TILE_CASES[case]
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    x[np.arange(L), rng.integers(0, V, L)] += 8.0
+    tab = wl.fp32_to_bf16_bits((rng.standard_normal((e - s + 40, d)) * 0.02).astype(np.float32))
+    tab[e - s:] = 0x7FC0                                  # rows past the slice: NaN, never read
+    say("staged whole tiles", case, (L, V, s, e, d))
+    x_t, w_t = dev(x), dev(tab)
+    _, lse, _, _ = api.row_stats(x_t)
+    fused = api.soft_embed(x_t, lse, s, e, w_t, 5.0, fused=True)
+    staged = api.soft_embed(x_t, lse, s, e, w_t, 5.0, staged=True)
+    again = api.soft_embed(x_t, lse, s, e, w_t, 5.0, staged=True)
+    torch.cuda.synchronize()
+    assert torch.equal(staged, fused)
+    assert torch.equal(again, staged)
+    ref = oracle.soft_embed(x, s, e, tab[:e - s], 5.0)
+    assert rel_fro(staged.cpu().numpy(), ref) <= 5e-3
+
+
 def test_staged_empty_slice_writes_zeros():
     x_t = dev(np.zeros((4, 64), np.float32))
     _, lse, _, _ = api.row_stats(x_t)
@@ -111,6 +149,7 @@ STEP_CASES = {
     "slice-63": (33, 1003, 64, 127, 2816, 23),        # V not a multiple of 4
     "two-row-tiles": (300, 2048, 1024, 2048, 512, 24),
     "empty-slice": (8, 512, 16, 16, 16, 25),
+    "whole-tile": (256, 20003, 4000, 8097, 512, 26),   # the ping-pong contraction
 }
 
 

@@ -106,6 +106,7 @@ CASES = {
     "slice-in-middle": (64, 50000, 12344, 37001, 128, 6),
     "two-row-tiles": (300, 2048, 1024, 2048, 512, 7),
     "many-pre-chunks": (8, 120000, 96000, 100003, 32, 8),
+    "whole-tile": (256, 30003, 1000, 13337, 272, 10),   # ping-pong contraction, tail
 }
 
 
