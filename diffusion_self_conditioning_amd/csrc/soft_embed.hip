@@ -651,7 +651,7 @@ namespace {
 //   - Operands go from memory to LDS with buffer_load ... lds: no staging registers and no
 //     LDS writes in the loop.  Group 0 loads the probability stages (64 positions, 32 KB,
 //     two buffers, a whole stage in the M phase of every other step); group 1 the table
-//     steps (32 positions, 16 KB, ring of four, three steps ahead, nontemporal).
+//     steps (32 positions, 16 KB, ring of four, three steps ahead).
 //   - Every buffer is its own LDS array and the barriers are plain s_barrier with the wait
 //     counts written out (empty asm memory clobbers keep LDS accesses on their side), so a
 //     wave waits only for the loads the next phases read.
@@ -693,6 +693,10 @@ __device__ __forceinline__ void phase_end() {
 }
 constexpr int kNoVmWait = 63;
 
+// TABLE_NT: the table loads carry the nontemporal hint.  Right when one row tile reads each
+// table row once; with several row tiles the others re-read it, and cached loads let them
+// find it in L2.
+template <bool TABLE_NT>
 __global__ void __launch_bounds__(kGemmThreads)
 __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 soft_embed_pp_kernel(const GemmParams p) {
@@ -762,7 +766,7 @@ soft_embed_pp_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(buf + 1024 * (4 * q + i)),
-                                               16, voff[i], soff, 0, 2);
+                                               16, voff[i], soff, 0, TABLE_NT ? 2 : 0);
   };
 
   f32x16 acc[kMI][kNI];
@@ -946,7 +950,10 @@ void launch_contraction(const GemmParams& p, hipStream_t stream) {
   // staged (super-step-tiled) probabilities in whole 256-row tiles, bf16 table: the
   // ping-pong kernel (bit for bit the same result)
   if (!FUSED && !W8 && p.M % kBM == 0 && p.a_ss == p.M * (int64_t)kSuperStep * 2) {
-    hipLaunchKernelGGL(soft_embed_pp_kernel, grid, dim3(kGemmThreads), 0, stream, p);
+    if (p.tiles == p.tiles_n)                   // one row tile
+      hipLaunchKernelGGL(soft_embed_pp_kernel<true>, grid, dim3(kGemmThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(soft_embed_pp_kernel<false>, grid, dim3(kGemmThreads), 0, stream, p);
     return;
   }
   // whole 256-row tiles take the path with per-lane addresses fixed for the kernel
