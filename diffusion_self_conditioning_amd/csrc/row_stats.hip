@@ -86,7 +86,15 @@ __device__ __forceinline__ RowState shfl_xor_state(const RowState& s, int mask) 
   return o;
 }
 
-template <bool PROBS>
+// A group: the kUnroll chunks c, c + kRowThreads, ... of every thread, kUnroll * kRowThreads
+// float4s (16,384 positions) of the row; the main loop takes one group per iteration.
+constexpr int kGroupF4 = kUnroll * kRowThreads;
+// HOLD (with PROBS): the slice is whole groups [hg0, hg0 + hn), hn <= HOLD, inside the main
+// loop's range; they are met in the same order as always and kept in registers, and the
+// probabilities are written from there once the row's lse is known (no second read).
+constexpr int kHoldGroups = 4;
+
+template <bool PROBS, int HOLD>
 __global__ void __launch_bounds__(kRowThreads)
 row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
                  float* __restrict__ row_max, float* __restrict__ row_lse,
@@ -102,10 +110,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
   int c = tid;
   // Each thread visits its chunks in increasing index order, so a strict ">"
   // keeps the first occurrence of the maximum.
-  for (; c + (kUnroll - 1) * kRowThreads < n4; c += kUnroll * kRowThreads) {
-    float4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = load_stream_f4(x4 + c + u * kRowThreads);
+  auto group = [&](int c, const float4 (&v)[kUnroll]) {
     float cm = v[0].x;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
@@ -130,6 +135,33 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
       accum(st, v[u].z, nml);
       accum(st, v[u].w, nml);
     }
+  };
+  float4 held[HOLD > 0 ? HOLD : 1][kUnroll];
+  int hg0 = 0, hn = 0;
+  if constexpr (HOLD > 0) {
+    hg0 = (int)(col0 / (4 * kGroupF4));
+    hn = (int)(K / (4 * kGroupF4));
+    for (; c < tid + hg0 * kGroupF4; c += kGroupF4) {
+      float4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = load_stream_f4(x4 + c + u * kRowThreads);
+      group(c, v);
+    }
+#pragma unroll
+    for (int h = 0; h < HOLD; ++h) {
+      if (h < hn) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) held[h][u] = load_stream_f4(x4 + c + u * kRowThreads);
+        group(c, held[h]);
+        c += kGroupF4;
+      }
+    }
+  }
+  for (; c + (kUnroll - 1) * kRowThreads < n4; c += kGroupF4) {
+    float4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load_stream_f4(x4 + c + u * kRowThreads);
+    group(c, v);
   }
   for (; c < n4; c += kRowThreads) {
     const float4 v = load_stream_f4(x4 + c);
@@ -177,7 +209,25 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
       row_lse_s = r.m + lnz;
     }
   }
-  if constexpr (PROBS) {
+  if constexpr (PROBS && HOLD > 0) {
+    __syncthreads();
+    const float nl = neg_lse_log2(row_lse_s);
+    uint16_t* __restrict__ prow = probs + row * kSuperStep;
+    // chunk c of the row holds positions 4 c .. 4 c + 3 (one super-step, as 4 c % 128 <= 124)
+#pragma unroll
+    for (int h = 0; h < HOLD; ++h) {
+      if (h < hn) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int64_t k = 4 * (int64_t)(tid + (hg0 + h) * kGroupF4 + u * kRowThreads) - col0;
+          uint2 o;
+          o.x = pack_bf16x2(prob_from_logit(held[h][u].x, nl), prob_from_logit(held[h][u].y, nl));
+          o.y = pack_bf16x2(prob_from_logit(held[h][u].z, nl), prob_from_logit(held[h][u].w, nl));
+          *reinterpret_cast<uint2*>(prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep) = o;
+        }
+      }
+    }
+  } else if constexpr (PROBS) {
     __syncthreads();
     const float nl = neg_lse_log2(row_lse_s);
     const float* __restrict__ xs = x + col0;
@@ -220,7 +270,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
 hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int vocab,
                             float* row_max, float* row_lse, float* row_entropy,
                             int32_t* row_argmax, hipStream_t stream) {
-  hipLaunchKernelGGL(row_stats_kernel<false>, dim3((unsigned)n_rows), dim3(kRowThreads), 0,
+  hipLaunchKernelGGL((row_stats_kernel<false, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
                      stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax,
                      (int64_t)0, (int64_t)0, nullptr, n_rows);
   return hipGetLastError();
@@ -230,9 +280,19 @@ hipError_t launch_row_stats_probs(const float* logits, int64_t ld, int64_t n_row
                                   float* row_max, float* row_lse, float* row_entropy,
                                   int32_t* row_argmax, int64_t col0, int64_t K,
                                   uint16_t* probs, hipStream_t stream) {
-  hipLaunchKernelGGL(row_stats_kernel<true>, dim3((unsigned)n_rows), dim3(kRowThreads), 0,
-                     stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax, col0,
-                     K, probs, n_rows);
+  // a slice of at most kHoldGroups whole groups inside the main loop's range: kept in
+  // registers; otherwise read again after the statistics
+  const int64_t gpos = 4 * (int64_t)kGroupF4;
+  const bool hold = K > 0 && col0 % gpos == 0 && K % gpos == 0 && K / gpos <= kHoldGroups &&
+                    (col0 + K) / gpos <= (vocab / 4) / kGroupF4;
+  if (hold)
+    hipLaunchKernelGGL((row_stats_kernel<true, kHoldGroups>), dim3((unsigned)n_rows),
+                       dim3(kRowThreads), 0, stream, logits, ld, vocab, row_max, row_lse,
+                       row_entropy, row_argmax, col0, K, probs, n_rows);
+  else
+    hipLaunchKernelGGL((row_stats_kernel<true, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
+                       stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax, col0,
+                       K, probs, n_rows);
   return hipGetLastError();
 }
 

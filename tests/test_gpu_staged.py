@@ -150,6 +150,12 @@ STEP_CASES = {
     "two-row-tiles": (300, 2048, 1024, 2048, 512, 24),
     "empty-slice": (8, 512, 16, 16, 16, 25),
     "whole-tile": (256, 20003, 4000, 8097, 512, 26),   # the ping-pong contraction
+    # slices of whole 16,384-position groups: the statistics kernel keeps 1 to 4 of them in
+    # registers instead of reading them twice; 5 groups take the second read
+    "held-1-group": (16, 65536, 16384, 32768, 64, 27),
+    "held-4-groups": (16, 65536, 0, 65536, 64, 28),
+    "held-2-groups-at-end": (8, 81920, 49152, 81920, 128, 29),
+    "five-groups-read-twice": (8, 81920, 0, 81920, 64, 30),
 }
 
 
