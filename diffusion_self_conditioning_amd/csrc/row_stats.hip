@@ -87,12 +87,14 @@ __device__ __forceinline__ RowState shfl_xor_state(const RowState& s, int mask) 
 }
 
 // A group: the kUnroll chunks c, c + kRowThreads, ... of every thread, kUnroll * kRowThreads
-// float4s (16,384 positions) of the row; the main loop takes one group per iteration.
+// float4s (16,384 positions at 1024 threads and 4 chunks) of the row; the main loop takes
+// one group per iteration.
 constexpr int kGroupF4 = kUnroll * kRowThreads;
 // HOLD (with PROBS): the slice is whole groups [hg0, hg0 + hn), hn <= HOLD, inside the main
 // loop's range; they are met in the same order as always and kept in registers, and the
 // probabilities are written from there once the row's lse is known (no second read).
-constexpr int kHoldGroups = 4;
+constexpr int kHoldGroups = 16 / kUnroll;        // 16 float4 (64 VGPRs) per thread
+static_assert(kHoldGroups >= 1, "at most 16 chunks per group");
 
 template <bool PROBS, int HOLD>
 __global__ void __launch_bounds__(kRowThreads)

@@ -28,9 +28,11 @@ def say(*a):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("which", ["step", "step_onepass", "staged"])
+@pytest.mark.parametrize("which", ["step", "step_onepass", "staged", "step_held_slice"])
 def test_captured_step_replays_match_eager_calls(which):
     L, V, s, e, d = 256, 30000, 8000, 20000, 512
+    if which == "step_held_slice":          # two whole 16,384-position groups: kept in registers
+        V, s, e = 65536, 16384, 49152
     rng = np.random.default_rng(51)
     tab = wl.fp32_to_bf16_bits((rng.standard_normal((e - s, d)) * 0.02).astype(np.float32))
     w_t = torch.from_numpy(tab).to(DEV)
@@ -45,7 +47,7 @@ def test_captured_step_replays_match_eager_calls(which):
         ws = api.staged_workspace(L, s, e, d, DEV)
 
     def call():
-        if which == "step":
+        if which in ("step", "step_held_slice"):
             B.se_soft_embed_step(x_t, s, e, w_t, 2.0, out, mx, lse, ent, am, ws)
         elif which == "step_onepass":
             B.se_soft_embed_step_onepass(x_t, s, e, w_t, 2.0, out, mx, lse, ent, am, ws)
