@@ -112,6 +112,47 @@ def test_staged_whole_tiles_equals_fused(case):
     assert rel_fro(staged.cpu().numpy(), ref) <= 5e-3
 
 
+def test_whole_tiles_with_row_pitches():
+    """Whole 256-row tiles with every row pitch wider than its row: logits (V + 8), table
+    (d + 72, so the table loads skip columns), output (d + 4, columns past d untouched).
+    Staged equals fused and the step equals the separate calls, bit for bit; both meet the
+    oracle."""
+    L, V, s, e, d = 256, 20000, 8, 12353, 264
+    rng = np.random.default_rng(71)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    x[np.arange(L), rng.integers(0, V, L)] += 8.0
+    xb = np.full((L, V + 8), np.float32(1e30), np.float32)
+    xb[:, :V] = x
+    tab = wl.fp32_to_bf16_bits((rng.standard_normal((e - s, d)) * 0.02).astype(np.float32))
+    tb = np.full((e - s, d + 72), 0x7FC0, np.uint16)          # padding columns: NaN, never read
+    tb[:, :d] = tab
+    x_t, w_t = dev(xb)[:, :V], dev(tb)[:, :d]
+    assert x_t.stride(0) == V + 8 and w_t.stride(0) == d + 72
+    say("whole tiles with row pitches")
+    mx, lse, ent, am = api.row_stats(x_t)
+    outs = {}
+    for name in ("fused", "staged", "step"):
+        buf = torch.full((L, d + 4), -7.0, device=DEV)
+        o = buf[:, :d]
+        if name == "fused":
+            api.se_soft_embed_fused(x_t, lse, s, e, w_t, 5.0, o, api.workspace(L, s, e, d, DEV))
+        elif name == "staged":
+            api.se_soft_embed_staged(x_t, lse, s, e, w_t, 5.0, o, api.staged_workspace(L, s, e, d, DEV))
+        else:
+            st = [torch.empty(L, device=DEV) for _ in range(3)] + [torch.empty(L, device=DEV, dtype=torch.int32)]
+            api.se_soft_embed_step(x_t, s, e, w_t, 5.0, o, *st, api.staged_workspace(L, s, e, d, DEV))
+            for a, b in zip(st, (mx, lse, ent, am)):
+                outs.setdefault("stats_equal", True)
+                outs["stats_equal"] &= bool(torch.equal(a, b))
+        outs[name] = buf
+    torch.cuda.synchronize()
+    assert outs["stats_equal"]
+    assert torch.equal(outs["staged"], outs["fused"]) and torch.equal(outs["step"], outs["fused"])
+    assert bool((outs["staged"][:, d:] == -7.0).all())
+    ref = oracle.soft_embed(x, s, e, tab, 5.0)
+    assert rel_fro(outs["staged"][:, :d].cpu().numpy(), ref) <= 5e-3
+
+
 def test_staged_empty_slice_writes_zeros():
     x_t = dev(np.zeros((4, 64), np.float32))
     _, lse, _, _ = api.row_stats(x_t)
