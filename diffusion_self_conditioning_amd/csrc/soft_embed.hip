@@ -639,9 +639,9 @@ namespace {
 
 // ---- contraction of staged probabilities: ping-pong waves, operands straight into LDS ---
 // For probabilities in the super-step-tiled layout (the staged, whole-step and one-pass
-// calls), the bf16 table and whole 256-row tiles.  Same 8 waves, wave tiles, MFMAs, k order
-// and partial layout as soft_embed_kernel, so the results are bit for bit the same; the
-// schedule differs:
+// calls) and whole 256-row tiles; bf16 table, or e4m3 table (W8) with one row tile.  Same
+// 8 waves, wave tiles, MFMAs, k order and partial layout as soft_embed_kernel, so the
+// results are bit for bit the same; the schedule differs:
 //   - Waves 0-3 (group 0) and 4-7 (group 1), one of each per SIMD, run a phase apart.  A
 //     32-position step is two phases per wave: M (the step's fragments read from LDS, loads
 //     for later steps issued) and C (its 16 MFMAs, at raised wave priority).  While one
@@ -692,11 +692,24 @@ __device__ __forceinline__ void phase_end() {
   __builtin_amdgcn_sched_barrier(0);
 }
 constexpr int kNoVmWait = 63;
+constexpr int kPP8RawBytes = kBK * kBN;           // [32 rows][256 columns] e4m3 codes
+static_assert(2 * kPPStageBytes + 4 * kPPStepBytes + 4 * kPP8RawBytes <= 160 * 1024, "LDS budget");
+// s_waitcnt with vmcnt(n) only
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
 
 // TABLE_NT: the table loads carry the nontemporal hint.  Right when one row tile reads each
 // table row once; with several row tiles the others re-read it, and cached loads let them
 // find it in L2.
-template <bool TABLE_NT>
+// W8: the table is e4m3 codes with a power-of-two scale per row.  Group 1 loads a step's
+// codes into a raw buffer (ring of four, three steps ahead) and the scales of its rows into
+// registers; two M phases later each wave converts the rows it loaded itself (so a wait on
+// its own loads suffices) to bf16, exactly as soft_embed_kernel's e4m3 producer does, into
+// the step's table buffer, one step before anyone reads it.
+template <bool TABLE_NT, bool W8>
 __global__ void __launch_bounds__(kGemmThreads)
 __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 soft_embed_pp_kernel(const GemmParams p) {
@@ -704,6 +717,9 @@ soft_embed_pp_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char P0[kPPStageBytes], P1[kPPStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char W0[kPPStepBytes], W1[kPPStepBytes];
   __shared__ __attribute__((aligned(16))) unsigned char W2[kPPStepBytes], W3[kPPStepBytes];
+  // e4m3 table: the codes of four steps as loaded ([32 rows][256 codes], row r at 256 r)
+  __shared__ __attribute__((aligned(16))) unsigned char R0[W8 ? kPP8RawBytes : 16], R1[W8 ? kPP8RawBytes : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char R2[W8 ? kPP8RawBytes : 16], R3[W8 ? kPP8RawBytes : 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave >> 2, q = wave & 3;
   const int wm = wave / kWN, wn = wave % kWN;
@@ -726,10 +742,14 @@ soft_embed_pp_kernel(const GemmParams p) {
       static_cast<const unsigned char*>(p.a) + (int64_t)m0 * kSuperStep * 2,
       (uint32_t)min(((p.K + kSuperStep - 1) / kSuperStep - 1) * a_blk + (int64_t)kBM * kSuperStep * 2,
                     (int64_t)UINT32_MAX));
-  const int64_t w_ld = p.ldw * 2;
+  const int64_t w_ld = p.ldw * (W8 ? 1 : 2);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       make_rsrc(static_cast<const unsigned char*>(p.w) + k_lo * w_ld,
                 (uint32_t)min((k_hi - k_lo) * w_ld, (int64_t)UINT32_MAX));
+  // e4m3 table: one fp32 (power-of-two) scale per shard row
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      make_rsrc(W8 ? static_cast<const void*>(p.wscale + k_lo) : p.w,
+                W8 ? (uint32_t)min((k_hi - k_lo) * 4, (int64_t)UINT32_MAX) : 0u);
   // Each load moves 64 lanes x 16 bytes into 1 KB of LDS, lane l at byte 16 l.
   //   group 0, wave q: stage rows 64 q .. + 63, 8 rows per load; lane l of load i writes row
   //     64 q + 8 i + l / 8, stored chunk l % 8, which holds logical chunk (l % 8) ^ pp_swz(row)
@@ -742,12 +762,23 @@ soft_embed_pp_kernel(const GemmParams p) {
       const int r = 64 * q + 8 * i + (lane >> 3);
       voff[i] = (uint32_t)(r * 256 + 16 * ((lane & 7) ^ pp_swz(r)));
     }
-  } else {
+  } else if constexpr (!W8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = 8 * q + 2 * i + (lane >> 5);
       const int col = n0 + 8 * ((lane & 31) ^ (4 * (k & 3)));
       voff[i] = (uint32_t)(k * w_ld) + 2u * (uint32_t)min(col, N - 8);
+    }
+#pragma unroll
+    for (int i = 4; i < 8; ++i) voff[i] = 0u;
+  } else {
+    // e4m3: wave q loads step rows 8 q .. + 7 as codes, 4 rows per load (lane l of load i:
+    // row 8 q + 4 i + l / 16, columns 16 (l % 16) .. + 15), and the scales of its rows
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k = 8 * q + 4 * i + (lane >> 4);
+      voff[i] = (uint32_t)(k * w_ld) + (uint32_t)min(n0 + 16 * (lane & 15), N - 16);
+      voff[2 + i] = 4u * (uint32_t)k;
     }
 #pragma unroll
     for (int i = 4; i < 8; ++i) voff[i] = 0u;
@@ -768,6 +799,30 @@ soft_embed_pp_kernel(const GemmParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(buf + 1024 * (4 * q + i)),
                                                16, voff[i], soff, 0, TABLE_NT ? 2 : 0);
   };
+  // e4m3: codes of step st into a raw buffer, the scales of the wave's rows into sc
+  auto load_step8 = [&](unsigned char* raw, int st, float (&sc)[2]) {
+    const int64_t k0 = (int64_t)kBK * min(st, nsteps - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(raw + 1024 * (2 * q + i)), 16,
+                                               voff[i], (uint32_t)(k0 * w_ld), 0, TABLE_NT ? 2 : 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sc[i] = buffer_load_f1(s_rsrc, voff[2 + i], (uint32_t)(4 * k0));
+  };
+  // e4m3: the wave's own rows of a raw step, times their scales, as bf16 into a table buffer
+  // (the layout soft_embed_kernel's e4m3 producer writes)
+  auto convert8 = [&](const unsigned char* raw, unsigned char* wb, const float (&sc)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 c = *reinterpret_cast<const uint4*>(raw + 1024 * (2 * q + i) + 16 * lane);
+      const int k = 8 * q + 4 * i + (lane >> 4), col = 16 * (lane & 15);
+      uint4 lo, hi;
+      fp8x16_to_bf16(c, sc[i], lo, hi);
+      *reinterpret_cast<uint4*>(wb + w_off(k, col)) = lo;
+      *reinterpret_cast<uint4*>(wb + w_off(k, col + 8)) = hi;
+    }
+  };
+  float sc0[2], sc1[2], sc2[2], sc3[2];
 
   f32x16 acc[kMI][kNI];
 #pragma unroll
@@ -824,12 +879,20 @@ soft_embed_pp_kernel(const GemmParams p) {
   if (nq > 0) {
     if (grp == 0) {
       load_stage(P0, 0);
-    } else {
+    } else if constexpr (!W8) {
       load_step(W0, 0);
       load_step(W1, 1);
       load_step(W2, 2);
+    } else {
+      load_step8(R0, 0, sc0);
+      load_step8(R1, 1, sc1);
+      load_step8(R2, 2, sc2);
     }
     phase_end<0>();
+    if constexpr (W8) {                         // table step 0 as bf16 before anyone reads it
+      if (grp == 1) convert8(R0, W0, sc0);
+      phase_end<0>();
+    }
     if (grp == 0) {
       for (int qd = 0; qd < nq; ++qd) {         // steps 4 qd .. 4 qd + 3: stages 2 qd, 2 qd + 1
         load_stage(P1, 2 * qd + 1);
@@ -856,26 +919,59 @@ soft_embed_pp_kernel(const GemmParams p) {
       phase_end<kNoVmWait>();                   // one phase behind group 0
       for (int qd = 0; qd < nq; ++qd) {
         const int s0 = kQ * qd;
-        load_step(W3, s0 + 3);
-        m_phase(P0, W0, 0);
-        phase_end<8>();                         // table step s0 + 1 in LDS
-        c_phase();
-        phase_end<kNoVmWait>();
-        load_step(W0, s0 + 4);
-        m_phase(P0, W1, 1);
-        phase_end<8>();
-        c_phase();
-        phase_end<kNoVmWait>();
-        load_step(W1, s0 + 5);
-        m_phase(P1, W2, 0);
-        phase_end<8>();
-        c_phase();
-        phase_end<kNoVmWait>();
-        load_step(W2, s0 + 6);
-        m_phase(P1, W3, 1);
-        phase_end<8>();
-        c_phase();
-        phase_end<kNoVmWait>();
+        if constexpr (!W8) {
+          load_step(W3, s0 + 3);
+          m_phase(P0, W0, 0);
+          phase_end<8>();                       // table step s0 + 1 in LDS
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step(W0, s0 + 4);
+          m_phase(P0, W1, 1);
+          phase_end<8>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step(W1, s0 + 5);
+          m_phase(P1, W2, 0);
+          phase_end<8>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step(W2, s0 + 6);
+          m_phase(P1, W3, 1);
+          phase_end<8>();
+          c_phase();
+          phase_end<kNoVmWait>();
+        } else {
+          // step s: codes of step s + 3 requested; step s + 1's (requested two M phases
+          // ago: at most the 8 later loads may be in flight) converted into its buffer
+          load_step8(R3, s0 + 3, sc3);
+          m_phase(P0, W0, 0);
+          wait_vm<8>();
+          convert8(R1, W1, sc1);
+          phase_end<kNoVmWait>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step8(R0, s0 + 4, sc0);
+          m_phase(P0, W1, 1);
+          wait_vm<8>();
+          convert8(R2, W2, sc2);
+          phase_end<kNoVmWait>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step8(R1, s0 + 5, sc1);
+          m_phase(P1, W2, 0);
+          wait_vm<8>();
+          convert8(R3, W3, sc3);
+          phase_end<kNoVmWait>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step8(R2, s0 + 6, sc2);
+          m_phase(P1, W3, 1);
+          wait_vm<8>();
+          convert8(R0, W0, sc0);
+          phase_end<kNoVmWait>();
+          c_phase();
+          phase_end<kNoVmWait>();
+        }
       }
     }
   }
@@ -899,17 +995,32 @@ soft_embed_pp_kernel(const GemmParams p) {
       *reinterpret_cast<uint4*>(P0 + pp_off(row, c)) =
           make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
     }
-    // table: 32 rows x 32 chunks of 8 columns, 2 per thread
+    if constexpr (!W8) {
+      // table: 32 rows x 32 chunks of 8 columns, 2 per thread
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = tid + kGemmThreads * j;
-      const int k = e >> 5, c = e & 31;
+      for (int j = 0; j < 2; ++j) {
+        const int e = tid + kGemmThreads * j;
+        const int k = e >> 5, c = e & 31;
+        const int64_t kr = k0 + k;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (kr < p.K)
+          v = *reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(p.w) + kr * w_ld +
+                                              2 * (int64_t)min(n0 + 8 * c, N - 8));
+        *reinterpret_cast<uint4*>(W0 + w_off(k, 8 * c)) = v;
+      }
+    } else {
+      // e4m3 table: 32 rows x 16 pieces of 16 codes, one per thread, converted with the
+      // row's scale (rows past the slice: zeros)
+      const int k = tid >> 4, col = 16 * (tid & 15);
       const int64_t kr = k0 + k;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (kr < p.K)
-        v = *reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(p.w) + kr * w_ld +
-                                            2 * (int64_t)min(n0 + 8 * c, N - 8));
-      *reinterpret_cast<uint4*>(W0 + w_off(k, 8 * c)) = v;
+      uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
+      if (kr < p.K) {
+        const uint4 c = *reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(p.w) +
+                                                        kr * w_ld + min(n0 + col, N - 16));
+        fp8x16_to_bf16(c, p.wscale[kr], lo, hi);
+      }
+      *reinterpret_cast<uint4*>(W0 + w_off(k, col)) = lo;
+      *reinterpret_cast<uint4*>(W0 + w_off(k, col + 8)) = hi;
     }
     __syncthreads();
     m_phase(P0, W0, 0);
@@ -949,11 +1060,14 @@ void launch_contraction(const GemmParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles * p.splits));
   // staged (super-step-tiled) probabilities in whole 256-row tiles, bf16 table: the
   // ping-pong kernel (bit for bit the same result)
-  if (!FUSED && !W8 && p.M % kBM == 0 && p.a_ss == p.M * (int64_t)kSuperStep * 2) {
+  // (e4m3 table: one row tile only; with several, the conversion, all in group 1's M
+  // phase, outlasts the other group's MFMAs and the register-staged kernel is faster)
+  if (!FUSED && p.M % kBM == 0 && p.a_ss == p.M * (int64_t)kSuperStep * 2 &&
+      (!W8 || p.tiles == p.tiles_n)) {
     if (p.tiles == p.tiles_n)                   // one row tile
-      hipLaunchKernelGGL(soft_embed_pp_kernel<true>, grid, dim3(kGemmThreads), 0, stream, p);
+      hipLaunchKernelGGL((soft_embed_pp_kernel<true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL(soft_embed_pp_kernel<false>, grid, dim3(kGemmThreads), 0, stream, p);
+      hipLaunchKernelGGL((soft_embed_pp_kernel<false, W8>), grid, dim3(kGemmThreads), 0, stream, p);
     return;
   }
   // whole 256-row tiles take the path with per-lane addresses fixed for the kernel

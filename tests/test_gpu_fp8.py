@@ -182,6 +182,12 @@ CASES = {
     "slice-63": (33, 1000, 64, 127, 2816, 4),
     "slice-4097": (255, 8200, 8, 4105, 272, 5),
     "two-tiles-rows": (300, 2048, 0, 2048, 512, 6),
+    # whole 256-row tiles (staged probabilities take the ping-pong contraction): a tail of
+    # one position, two row tiles with a 72-position tail, a tail alone, a held slice
+    "whole-tile-tail": (256, 8200, 8, 4105, 272, 7),
+    "two-whole-tiles": (512, 5000, 40, 240, 256, 8),
+    "whole-tile-k63": (256, 1004, 64, 127, 2816, 9),
+    "whole-tile-held-slice": (256, 65536, 16384, 49152, 512, 10),
 }
 
 
