@@ -188,6 +188,7 @@ CASES = {
     "two-whole-tiles": (512, 5000, 40, 240, 256, 8),
     "whole-tile-k63": (256, 1004, 64, 127, 2816, 9),
     "whole-tile-held-slice": (256, 65536, 16384, 49152, 512, 10),
+    "whole-tile-d16": (256, 5000, 0, 4097, 16, 11),
 }
 
 

@@ -88,6 +88,7 @@ TILE_CASES = {
     "k4097": (256, 8200, 8, 4105, 2816, 65),
     "k12345": (512, 50000, 12344, 24689, 520, 66),
     "k65553": (256, 70000, 0, 65553, 256, 67),
+    "d16": (256, 5000, 0, 4097, 16, 68),          # one n-tile of 16 columns: clamped loads
 }
 
 
