@@ -637,11 +637,11 @@ __global__ void zero_rows_kernel(float* __restrict__ out, int64_t ldo, int64_t N
 
 namespace {
 
-// ---- contraction of staged probabilities: ping-pong waves, operands straight into LDS ---
-// For probabilities in the super-step-tiled layout (the staged, whole-step and one-pass
-// calls) and whole 256-row tiles; bf16 table, or e4m3 table (W8) with one row tile.  Same
-// 8 waves, wave tiles, MFMAs, k order and partial layout as soft_embed_kernel, so the
-// results are bit for bit the same; the schedule differs:
+// ---- contraction of bf16 probabilities: ping-pong waves, operands straight into LDS -----
+// For bf16 probabilities, super-step-tiled (the staged, whole-step and one-pass calls) or
+// row-major (se_soft_embed), in whole 256-row tiles; bf16 table, or e4m3 table (W8) with one
+// row tile.  Same 8 waves, wave tiles, MFMAs, k order and partial layout as
+// soft_embed_kernel, so the results are bit for bit the same; the schedule differs:
 //   - Waves 0-3 (group 0) and 4-7 (group 1), one of each per SIMD, run a phase apart.  A
 //     32-position step is two phases per wave: M (the step's fragments read from LDS, loads
 //     for later steps issued) and C (its 16 MFMAs, at raised wave priority).  While one
@@ -736,12 +736,21 @@ soft_embed_pp_kernel(const GemmParams p) {
   const int nq = (int)((min(k_hi, (p.K / kSS) * kSS) - k_lo) / kSS);
   const int nsteps = kQ * nq;
 
-  // probabilities: position k of row m at (k / 128) a_blk + 256 m + 2 (k % 128) bytes
-  const int64_t a_blk = p.M * (int64_t)kSuperStep * 2;
+  // probabilities: position k of the tile's row m at (k / 128) a_blk + m a_rs + 2 (k % 128)
+  // bytes from a_base; super-step-tiled (a_blk = rows * 256, a_rs = 256) or row-major
+  // (a_blk = 256, a_rs = 2 lda, a_base at column col0).  The main loop reads whole
+  // super-steps only, so no load reaches past the slice.
+  const bool a_tiled = p.a_ss != (int64_t)kSuperStep * 2;
+  const int64_t a_blk = a_tiled ? p.M * (int64_t)kSuperStep * 2 : (int64_t)kSuperStep * 2;
+  const int64_t a_rs = a_tiled ? (int64_t)kSuperStep * 2 : p.lda * 2;
+  const unsigned char* a_base =
+      static_cast<const unsigned char*>(p.a) +
+      (a_tiled ? (int64_t)m0 * kSuperStep * 2 : ((int64_t)m0 * p.lda + p.col0) * 2);
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(
-      static_cast<const unsigned char*>(p.a) + (int64_t)m0 * kSuperStep * 2,
-      (uint32_t)min(((p.K + kSuperStep - 1) / kSuperStep - 1) * a_blk + (int64_t)kBM * kSuperStep * 2,
-                    (int64_t)UINT32_MAX));
+      a_base, (uint32_t)min(a_tiled ? ((p.K + kSuperStep - 1) / kSuperStep - 1) * a_blk +
+                                          (int64_t)kBM * kSuperStep * 2
+                                    : (kBM - 1) * a_rs + p.K * 2,
+                            (int64_t)UINT32_MAX));
   const int64_t w_ld = p.ldw * (W8 ? 1 : 2);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       make_rsrc(static_cast<const unsigned char*>(p.w) + k_lo * w_ld,
@@ -760,7 +769,7 @@ soft_embed_pp_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 64 * q + 8 * i + (lane >> 3);
-      voff[i] = (uint32_t)(r * 256 + 16 * ((lane & 7) ^ pp_swz(r)));
+      voff[i] = (uint32_t)(r * a_rs) + 16u * (uint32_t)((lane & 7) ^ pp_swz(r));
     }
   } else if constexpr (!W8) {
 #pragma unroll
@@ -987,8 +996,7 @@ soft_embed_pp_kernel(const GemmParams p) {
       const int row = e >> 2, c = e & 3;
       const int64_t kk = k0 + 8 * c;
       const uint16_t* hp = reinterpret_cast<const uint16_t*>(
-          static_cast<const unsigned char*>(p.a) + (kk / kSuperStep) * a_blk +
-          ((int64_t)(m0 + row) * kSuperStep + kk % kSuperStep) * 2);
+          a_base + (kk / kSuperStep) * a_blk + row * a_rs + 2 * (kk % kSuperStep));
       uint32_t v[8];
 #pragma unroll
       for (int e8 = 0; e8 < 8; ++e8) v[e8] = (kk + e8 < p.K) ? (uint32_t)hp[e8] : 0u;
@@ -1058,11 +1066,12 @@ soft_embed_pp_kernel(const GemmParams p) {
 template <bool FUSED, bool W8>
 void launch_contraction(const GemmParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles * p.splits));
-  // staged (super-step-tiled) probabilities in whole 256-row tiles, bf16 table: the
-  // ping-pong kernel (bit for bit the same result)
+  // bf16 probabilities (staged super-step-tiled, or row-major) in whole 256-row tiles:
+  // the ping-pong kernel (bit for bit the same result)
   // (e4m3 table: one row tile only; with several, the conversion, all in group 1's M
   // phase, outlasts the other group's MFMAs and the register-staged kernel is faster)
-  if (!FUSED && p.M % kBM == 0 && p.a_ss == p.M * (int64_t)kSuperStep * 2 &&
+  if (!FUSED && p.M % kBM == 0 &&
+      (p.a_ss == p.M * (int64_t)kSuperStep * 2 || p.a_ss == (int64_t)kSuperStep * 2) &&
       (!W8 || p.tiles == p.tiles_n)) {
     if (p.tiles == p.tiles_n)                   // one row tile
       hipLaunchKernelGGL((soft_embed_pp_kernel<true, W8>), grid, dim3(kGemmThreads), 0, stream, p);

@@ -106,18 +106,24 @@ def test_staged_whole_tiles_equals_fused(case):
     fused = api.soft_embed(x_t, lse, s, e, w_t, 5.0, fused=True)
     staged = api.soft_embed(x_t, lse, s, e, w_t, 5.0, staged=True)
     again = api.soft_embed(x_t, lse, s, e, w_t, 5.0, staged=True)
+    # row-major bf16 probabilities (pitch rounded up to 8 elements) through se_soft_embed
+    probs = torch.empty((L, (V + 7) // 8 * 8), device=DEV, dtype=torch.bfloat16)[:, :V]
+    api.se_probs_bf16(x_t, lse, s, e, probs)
+    unfused = torch.empty((L, d), device=DEV)
+    api.se_soft_embed(probs, s, e, w_t, 5.0, unfused, api.workspace(L, s, e, d, DEV))
     torch.cuda.synchronize()
     assert torch.equal(staged, fused)
     assert torch.equal(again, staged)
+    assert torch.equal(unfused, fused)
     ref = oracle.soft_embed(x, s, e, tab[:e - s], 5.0)
     assert rel_fro(staged.cpu().numpy(), ref) <= 5e-3
 
 
 def test_whole_tiles_with_row_pitches():
-    """Whole 256-row tiles with every row pitch wider than its row: logits (V + 8), table
-    (d + 72, so the table loads skip columns), output (d + 4, columns past d untouched).
-    Staged equals fused and the step equals the separate calls, bit for bit; both meet the
-    oracle."""
+    """Whole 256-row tiles with every row pitch wider than its row: logits and row-major
+    probabilities (V + 8), table (d + 72, so the table loads skip columns), output (d + 4,
+    columns past d untouched).  Staged and unfused equal fused and the step equals the
+    separate calls, bit for bit; all meet the oracle."""
     L, V, s, e, d = 256, 20000, 8, 12353, 264
     rng = np.random.default_rng(71)
     x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
@@ -132,13 +138,17 @@ def test_whole_tiles_with_row_pitches():
     say("whole tiles with row pitches")
     mx, lse, ent, am = api.row_stats(x_t)
     outs = {}
-    for name in ("fused", "staged", "step"):
+    probs = torch.empty((L, V + 8), device=DEV, dtype=torch.bfloat16)[:, :V]   # pitch V + 8
+    api.se_probs_bf16(x_t, lse, s, e, probs)
+    for name in ("fused", "staged", "step", "unfused"):
         buf = torch.full((L, d + 4), -7.0, device=DEV)
         o = buf[:, :d]
         if name == "fused":
             api.se_soft_embed_fused(x_t, lse, s, e, w_t, 5.0, o, api.workspace(L, s, e, d, DEV))
         elif name == "staged":
             api.se_soft_embed_staged(x_t, lse, s, e, w_t, 5.0, o, api.staged_workspace(L, s, e, d, DEV))
+        elif name == "unfused":
+            api.se_soft_embed(probs, s, e, w_t, 5.0, o, api.workspace(L, s, e, d, DEV))
         else:
             st = [torch.empty(L, device=DEV) for _ in range(3)] + [torch.empty(L, device=DEV, dtype=torch.int32)]
             api.se_soft_embed_step(x_t, s, e, w_t, 5.0, o, *st, api.staged_workspace(L, s, e, d, DEV))
@@ -149,6 +159,7 @@ def test_whole_tiles_with_row_pitches():
     torch.cuda.synchronize()
     assert outs["stats_equal"]
     assert torch.equal(outs["staged"], outs["fused"]) and torch.equal(outs["step"], outs["fused"])
+    assert torch.equal(outs["unfused"], outs["fused"])
     assert bool((outs["staged"][:, d:] == -7.0).all())
     ref = oracle.soft_embed(x, s, e, tab, 5.0)
     assert rel_fro(outs["staged"][:, :d].cpu().numpy(), ref) <= 5e-3
