@@ -639,9 +639,9 @@ namespace {
 
 // ---- contraction of bf16 probabilities: ping-pong waves, operands straight into LDS -----
 // For bf16 probabilities, super-step-tiled (the staged, whole-step and one-pass calls) or
-// row-major (se_soft_embed), in whole 256-row tiles; bf16 table, or e4m3 table (W8) with one
-// row tile.  Same 8 waves, wave tiles, MFMAs, k order and partial layout as
-// soft_embed_kernel, so the results are bit for bit the same; the schedule differs:
+// row-major (se_soft_embed); bf16 table, or e4m3 table (W8) with one row tile.  Same 8
+// waves, wave tiles, MFMAs, k order and partial layout as soft_embed_kernel, so the results
+// are bit for bit the same; the schedule differs:
 //   - Waves 0-3 (group 0) and 4-7 (group 1), one of each per SIMD, run a phase apart.  A
 //     32-position step is two phases per wave: M (the step's fragments read from LDS, loads
 //     for later steps issued) and C (its 16 MFMAs, at raised wave priority).  While one
@@ -735,6 +735,9 @@ soft_embed_pp_kernel(const GemmParams p) {
   const int64_t k_hi = min((((int64_t)(s + 1) * p.kblocks) / p.splits) * kSplitQuantum, p.K);
   const int nq = (int)((min(k_hi, (p.K / kSS) * kSS) - k_lo) / kSS);
   const int nsteps = kQ * nq;
+  // rows of this tile that exist; rows past them load row tile_rows - 1 again (finite data,
+  // every load in bounds) and are never written out
+  const int tile_rows = min(kBM, (int)p.M - m0);
 
   // probabilities: position k of the tile's row m at (k / 128) a_blk + m a_rs + 2 (k % 128)
   // bytes from a_base; super-step-tiled (a_blk = rows * 256, a_rs = 256) or row-major
@@ -769,7 +772,7 @@ soft_embed_pp_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 64 * q + 8 * i + (lane >> 3);
-      voff[i] = (uint32_t)(r * a_rs) + 16u * (uint32_t)((lane & 7) ^ pp_swz(r));
+      voff[i] = (uint32_t)(min(r, tile_rows - 1) * a_rs) + 16u * (uint32_t)((lane & 7) ^ pp_swz(r));
     }
   } else if constexpr (!W8) {
 #pragma unroll
@@ -996,7 +999,7 @@ soft_embed_pp_kernel(const GemmParams p) {
       const int row = e >> 2, c = e & 3;
       const int64_t kk = k0 + 8 * c;
       const uint16_t* hp = reinterpret_cast<const uint16_t*>(
-          a_base + (kk / kSuperStep) * a_blk + row * a_rs + 2 * (kk % kSuperStep));
+          a_base + (kk / kSuperStep) * a_blk + min(row, tile_rows - 1) * a_rs + 2 * (kk % kSuperStep));
       uint32_t v[8];
 #pragma unroll
       for (int e8 = 0; e8 < 8; ++e8) v[e8] = (kk + e8 < p.K) ? (uint32_t)hp[e8] : 0u;
@@ -1047,7 +1050,7 @@ soft_embed_pp_kernel(const GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (col < N) p.out[(int64_t)row * p.ldo + col] = p.gamma * acc[mi][ni][r];
+          if (col < N && row < (int)p.M) p.out[(int64_t)row * p.ldo + col] = p.gamma * acc[mi][ni][r];
         }
       }
   } else {
@@ -1066,12 +1069,11 @@ soft_embed_pp_kernel(const GemmParams p) {
 template <bool FUSED, bool W8>
 void launch_contraction(const GemmParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles * p.splits));
-  // bf16 probabilities (staged super-step-tiled, or row-major) in whole 256-row tiles:
-  // the ping-pong kernel (bit for bit the same result)
+  // bf16 probabilities (staged super-step-tiled, or row-major): the ping-pong kernel (bit
+  // for bit the same result)
   // (e4m3 table: one row tile only; with several, the conversion, all in group 1's M
   // phase, outlasts the other group's MFMAs and the register-staged kernel is faster)
-  if (!FUSED && p.M % kBM == 0 &&
-      (p.a_ss == p.M * (int64_t)kSuperStep * 2 || p.a_ss == (int64_t)kSuperStep * 2) &&
+  if (!FUSED && (p.a_ss == p.M * (int64_t)kSuperStep * 2 || p.a_ss == (int64_t)kSuperStep * 2) &&
       (!W8 || p.tiles == p.tiles_n)) {
     if (p.tiles == p.tiles_n)                   // one row tile
       hipLaunchKernelGGL((soft_embed_pp_kernel<true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
