@@ -165,6 +165,28 @@ def test_whole_tiles_with_row_pitches():
     assert rel_fro(outs["staged"][:, :d].cpu().numpy(), ref) <= 5e-3
 
 
+@pytest.mark.parametrize("shape", [(256, 262144, 65536, 131072, 2816), (2048, 20480, 0, 16384, 2816)],
+                         ids=["rank-shape", "eight-row-tiles"])
+def test_staged_repeated_calls_stay_bitwise(shape):
+    """The ping-pong contraction's hand-written wait counts and barriers, exercised back to
+    back: 60 staged calls on one stream, each output equal to the fused call's bit for bit."""
+    L, V, s, e, d = shape
+    rng = np.random.default_rng(81)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    x[np.arange(L), rng.integers(0, V, L)] += 8.0
+    tab = wl.fp32_to_bf16_bits((rng.standard_normal((e - s, d)) * 0.02).astype(np.float32))
+    x_t, w_t = dev(x), dev(tab)
+    say("repeated staged calls", shape)
+    _, lse, _, _ = api.row_stats(x_t)
+    ref = api.soft_embed(x_t, lse, s, e, w_t, 3.0, fused=True)
+    ws = api.staged_workspace(L, s, e, d, DEV)
+    outs = [torch.empty_like(ref) for _ in range(60)]
+    for o in outs:
+        api.soft_embed(x_t, lse, s, e, w_t, 3.0, staged=True, out=o, ws=ws)
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, ref) for o in outs)
+
+
 def test_staged_empty_slice_writes_zeros():
     x_t = dev(np.zeros((4, 64), np.float32))
     _, lse, _, _ = api.row_stats(x_t)
