@@ -90,9 +90,9 @@ __device__ __forceinline__ RowState shfl_xor_state(const RowState& s, int mask) 
 // float4s (16,384 positions at 1024 threads and 4 chunks) of the row; the main loop takes
 // one group per iteration.
 constexpr int kGroupF4 = kUnroll * kRowThreads;
-// HOLD (with PROBS): the slice is whole groups [hg0, hg0 + hn), hn <= HOLD, inside the main
+// HOLD (with PROBS): the slice lies in groups [hg0, hg0 + hn), hn <= HOLD, inside the main
 // loop's range; they are met in the same order as always and kept in registers, and the
-// probabilities are written from there once the row's lse is known (no second read).
+// slice's probabilities are written from there once the row's lse is known (no second read).
 constexpr int kHoldGroups = 16 / kUnroll;        // 16 float4 (64 VGPRs) per thread
 static_assert(kHoldGroups >= 1, "at most 16 chunks per group");
 
@@ -142,7 +142,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
   int hg0 = 0, hn = 0;
   if constexpr (HOLD > 0) {
     hg0 = (int)(col0 / (4 * kGroupF4));
-    hn = (int)(K / (4 * kGroupF4));
+    hn = (int)((col0 + K + 4 * kGroupF4 - 1) / (4 * kGroupF4)) - hg0;
     for (; c < tid + hg0 * kGroupF4; c += kGroupF4) {
       float4 v[kUnroll];
 #pragma unroll
@@ -215,17 +215,28 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
     __syncthreads();
     const float nl = neg_lse_log2(row_lse_s);
     uint16_t* __restrict__ prow = probs + row * kSuperStep;
-    // chunk c of the row holds positions 4 c .. 4 c + 3 (one super-step, as 4 c % 128 <= 124)
+    // chunk c of the row holds positions 4 c .. 4 c + 3 (one super-step, as 4 c % 128 <= 124);
+    // slice position k = 4 c - col0.  col0 is a multiple of 8, so no chunk straddles it; a
+    // chunk straddling the slice's end is written element by element.
 #pragma unroll
     for (int h = 0; h < HOLD; ++h) {
       if (h < hn) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           const int64_t k = 4 * (int64_t)(tid + (hg0 + h) * kGroupF4 + u * kRowThreads) - col0;
-          uint2 o;
-          o.x = pack_bf16x2(prob_from_logit(held[h][u].x, nl), prob_from_logit(held[h][u].y, nl));
-          o.y = pack_bf16x2(prob_from_logit(held[h][u].z, nl), prob_from_logit(held[h][u].w, nl));
-          *reinterpret_cast<uint2*>(prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep) = o;
+          if (k < 0 || k >= K) continue;
+          uint16_t* dst = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
+          const float4 v = held[h][u];
+          if (k + 4 <= K) {
+            uint2 o;
+            o.x = pack_bf16x2(prob_from_logit(v.x, nl), prob_from_logit(v.y, nl));
+            o.y = pack_bf16x2(prob_from_logit(v.z, nl), prob_from_logit(v.w, nl));
+            *reinterpret_cast<uint2*>(dst) = o;
+          } else {
+            const float e4[4] = {v.x, v.y, v.z, v.w};
+            for (int j = 0; j < (int)(K - k); ++j)
+              dst[j] = __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(e4[j], nl));
+          }
         }
       }
     }
@@ -282,11 +293,12 @@ hipError_t launch_row_stats_probs(const float* logits, int64_t ld, int64_t n_row
                                   float* row_max, float* row_lse, float* row_entropy,
                                   int32_t* row_argmax, int64_t col0, int64_t K,
                                   uint16_t* probs, hipStream_t stream) {
-  // a slice of at most kHoldGroups whole groups inside the main loop's range: kept in
+  // a slice within at most kHoldGroups groups inside the main loop's range: kept in
   // registers; otherwise read again after the statistics
   const int64_t gpos = 4 * (int64_t)kGroupF4;
-  const bool hold = K > 0 && col0 % gpos == 0 && K % gpos == 0 && K / gpos <= kHoldGroups &&
-                    (col0 + K) / gpos <= (vocab / 4) / kGroupF4;
+  const int64_t g_end = (col0 + K + gpos - 1) / gpos;
+  const bool hold = K > 0 && g_end - col0 / gpos <= kHoldGroups &&
+                    g_end <= (vocab / 4) / kGroupF4;
   if (hold)
     hipLaunchKernelGGL((row_stats_kernel<true, kHoldGroups>), dim3((unsigned)n_rows),
                        dim3(kRowThreads), 0, stream, logits, ld, vocab, row_max, row_lse,
