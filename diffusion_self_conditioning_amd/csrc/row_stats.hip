@@ -90,9 +90,11 @@ __device__ __forceinline__ RowState shfl_xor_state(const RowState& s, int mask) 
 // float4s (16,384 positions at 1024 threads and 4 chunks) of the row; the main loop takes
 // one group per iteration.
 constexpr int kGroupF4 = kUnroll * kRowThreads;
-// HOLD (with PROBS): the slice lies in groups [hg0, hg0 + hn), hn <= HOLD, inside the main
-// loop's range; they are met in the same order as always and kept in registers, and the
-// slice's probabilities are written from there once the row's lse is known (no second read).
+// HOLD (with PROBS): the slice's first groups [hg0, hg0 + hn), hn <= HOLD, inside the main
+// loop's range, are met in the same order as always and kept in registers; the slice's
+// probabilities there are written from registers once the row's lse is known, and the rest
+// of the slice (if it is longer) is read again.  The groups read earliest are the ones held:
+// they are the likeliest to have left the caches.
 constexpr int kHoldGroups = 16 / kUnroll;        // 16 float4 (64 VGPRs) per thread
 static_assert(kHoldGroups >= 1, "at most 16 chunks per group");
 
@@ -142,7 +144,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
   int hg0 = 0, hn = 0;
   if constexpr (HOLD > 0) {
     hg0 = (int)(col0 / (4 * kGroupF4));
-    hn = (int)((col0 + K + 4 * kGroupF4 - 1) / (4 * kGroupF4)) - hg0;
+    hn = min((int)((col0 + K + 4 * kGroupF4 - 1) / (4 * kGroupF4)) - hg0, HOLD);
     for (; c < tid + hg0 * kGroupF4; c += kGroupF4) {
       float4 v[kUnroll];
 #pragma unroll
@@ -211,69 +213,75 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
       row_lse_s = r.m + lnz;
     }
   }
-  if constexpr (PROBS && HOLD > 0) {
-    __syncthreads();
-    const float nl = neg_lse_log2(row_lse_s);
-    uint16_t* __restrict__ prow = probs + row * kSuperStep;
-    // chunk c of the row holds positions 4 c .. 4 c + 3 (one super-step, as 4 c % 128 <= 124);
-    // slice position k = 4 c - col0.  col0 is a multiple of 8, so no chunk straddles it; a
-    // chunk straddling the slice's end is written element by element.
-#pragma unroll
-    for (int h = 0; h < HOLD; ++h) {
-      if (h < hn) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int64_t k = 4 * (int64_t)(tid + (hg0 + h) * kGroupF4 + u * kRowThreads) - col0;
-          if (k < 0 || k >= K) continue;
-          uint16_t* dst = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
-          const float4 v = held[h][u];
-          if (k + 4 <= K) {
-            uint2 o;
-            o.x = pack_bf16x2(prob_from_logit(v.x, nl), prob_from_logit(v.y, nl));
-            o.y = pack_bf16x2(prob_from_logit(v.z, nl), prob_from_logit(v.w, nl));
-            *reinterpret_cast<uint2*>(dst) = o;
-          } else {
-            const float e4[4] = {v.x, v.y, v.z, v.w};
-            for (int j = 0; j < (int)(K - k); ++j)
-              dst[j] = __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(e4[j], nl));
-          }
-        }
-      }
-    }
-  } else if constexpr (PROBS) {
+  if constexpr (PROBS) {
     __syncthreads();
     const float nl = neg_lse_log2(row_lse_s);
     const float* __restrict__ xs = x + col0;
     uint16_t* __restrict__ prow = probs + row * kSuperStep;
-    auto put8 = [&](int64_t k, const float4& a, const float4& b) {
-      uint4 o;
-      o.x = pack_bf16x2(prob_from_logit(a.x, nl), prob_from_logit(a.y, nl));
-      o.y = pack_bf16x2(prob_from_logit(a.z, nl), prob_from_logit(a.w, nl));
-      o.z = pack_bf16x2(prob_from_logit(b.x, nl), prob_from_logit(b.y, nl));
-      o.w = pack_bf16x2(prob_from_logit(b.z, nl), prob_from_logit(b.w, nl));
-      *reinterpret_cast<uint4*>(prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep) = o;
+    // the slice's positions [k_begin, K) read again (k_begin a multiple of 8)
+    auto reread = [&](int64_t k_begin) {
+      auto put8 = [&](int64_t k, const float4& a, const float4& b) {
+        uint4 o;
+        o.x = pack_bf16x2(prob_from_logit(a.x, nl), prob_from_logit(a.y, nl));
+        o.y = pack_bf16x2(prob_from_logit(a.z, nl), prob_from_logit(a.w, nl));
+        o.z = pack_bf16x2(prob_from_logit(b.x, nl), prob_from_logit(b.y, nl));
+        o.w = pack_bf16x2(prob_from_logit(b.z, nl), prob_from_logit(b.w, nl));
+        *reinterpret_cast<uint4*>(prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep) = o;
+      };
+      // four 8-position groups per thread in flight, then the remaining groups one by one
+      constexpr int64_t kStride = 8 * (int64_t)kRowThreads;
+      int64_t k = k_begin + 8 * (int64_t)tid;
+      for (; k + 3 * kStride + 8 <= K; k += 4 * kStride) {
+        float4 a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[u] = reinterpret_cast<const float4*>(xs + k + u * kStride)[0];
+          b[u] = reinterpret_cast<const float4*>(xs + k + u * kStride)[1];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) put8(k + u * kStride, a[u], b[u]);
+      }
+      for (; k < K; k += kStride) {
+        if (k + 8 <= K) {
+          put8(k, reinterpret_cast<const float4*>(xs + k)[0], reinterpret_cast<const float4*>(xs + k)[1]);
+        } else {
+          uint16_t* __restrict__ pp = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
+          for (int64_t j = 0; j < K - k; ++j)
+            pp[j] = __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(xs[k + j], nl));
+        }
+      }
     };
-    // four 8-position groups per thread in flight, then the remaining groups one by one
-    constexpr int64_t kStride = 8 * (int64_t)kRowThreads;
-    int64_t k = 8 * (int64_t)tid;
-    for (; k + 3 * kStride + 8 <= K; k += 4 * kStride) {
-      float4 a[4], b[4];
+    if constexpr (HOLD > 0) {
+      // chunk c of the row holds positions 4 c .. 4 c + 3 (one super-step, as 4 c % 128 <=
+      // 124); slice position k = 4 c - col0.  col0 is a multiple of 8, so no chunk straddles
+      // it; a chunk straddling the slice's end is written element by element.
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = reinterpret_cast<const float4*>(xs + k + u * kStride)[0];
-        b[u] = reinterpret_cast<const float4*>(xs + k + u * kStride)[1];
-      }
+      for (int h = 0; h < HOLD; ++h) {
+        if (h < hn) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) put8(k + u * kStride, a[u], b[u]);
-    }
-    for (; k < K; k += kStride) {
-      if (k + 8 <= K) {
-        put8(k, reinterpret_cast<const float4*>(xs + k)[0], reinterpret_cast<const float4*>(xs + k)[1]);
-      } else {
-        uint16_t* __restrict__ p = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
-        for (int64_t j = 0; j < K - k; ++j)
-          p[j] = __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(xs[k + j], nl));
+          for (int u = 0; u < kUnroll; ++u) {
+            const int64_t k = 4 * (int64_t)(tid + (hg0 + h) * kGroupF4 + u * kRowThreads) - col0;
+            if (k < 0 || k >= K) continue;
+            uint16_t* dst = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
+            const float4 v = held[h][u];
+            if (k + 4 <= K) {
+              uint2 o;
+              o.x = pack_bf16x2(prob_from_logit(v.x, nl), prob_from_logit(v.y, nl));
+              o.y = pack_bf16x2(prob_from_logit(v.z, nl), prob_from_logit(v.w, nl));
+              *reinterpret_cast<uint2*>(dst) = o;
+            } else {
+              const float e4[4] = {v.x, v.y, v.z, v.w};
+              for (int j = 0; j < (int)(K - k); ++j)
+                dst[j] = __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(e4[j], nl));
+            }
+          }
+        }
       }
+      // a slice longer than the held groups: the rest is read again
+      const int64_t k_rest = (int64_t)(hg0 + hn) * 4 * kGroupF4 - col0;
+      if (k_rest < K) reread(k_rest);
+    } else {
+      reread(0);
     }
   }
 }
@@ -293,12 +301,12 @@ hipError_t launch_row_stats_probs(const float* logits, int64_t ld, int64_t n_row
                                   float* row_max, float* row_lse, float* row_entropy,
                                   int32_t* row_argmax, int64_t col0, int64_t K,
                                   uint16_t* probs, hipStream_t stream) {
-  // a slice within at most kHoldGroups groups inside the main loop's range: kept in
-  // registers; otherwise read again after the statistics
+  // the slice's first kHoldGroups groups, when they lie inside the main loop's range: kept
+  // in registers (the rest of a longer slice is read again); otherwise all read again
   const int64_t gpos = 4 * (int64_t)kGroupF4;
-  const int64_t g_end = (col0 + K + gpos - 1) / gpos;
-  const bool hold = K > 0 && g_end - col0 / gpos <= kHoldGroups &&
-                    g_end <= (vocab / 4) / kGroupF4;
+  const int64_t g0 = col0 / gpos;
+  const int64_t g_held = min((col0 + K + gpos - 1) / gpos, g0 + kHoldGroups);
+  const bool hold = K > 0 && g_held <= (vocab / 4) / kGroupF4;
   if (hold)
     hipLaunchKernelGGL((row_stats_kernel<true, kHoldGroups>), dim3((unsigned)n_rows),
                        dim3(kRowThreads), 0, stream, logits, ld, vocab, row_max, row_lse,

@@ -184,12 +184,12 @@ se_status se_soft_embed_staged(const float* logits, int64_t ld_logits, const flo
  * over the full width [0, vocab) followed by se_soft_embed_fused on [s, e), with
  * outputs bit for bit those of the two calls.  The statistics kernel writes the
  * slice's bf16 probabilities (staged, as se_soft_embed_staged) right after each
- * row's statistics, and one launch boundary disappears.  When the slice lies within at
- * most 4 of the row's whole groups of 16,384 positions (a tensor-parallel rank's share
- * of a large vocabulary at 4 or more ranks), the kernel keeps those groups in registers
- * as they stream past and reads nothing twice; otherwise it reads the row's slice again
- * (from whatever cache level still holds it; at the pages' shapes that second read
- * misses the L2).
+ * row's statistics, and one launch boundary disappears.  The kernel keeps the slice's
+ * first (up to) 4 groups of 16,384 positions in registers as they stream past, when they
+ * are whole groups of the row; a slice within them (a tensor-parallel rank's share of a
+ * large vocabulary at 4 or more ranks) is read only once, and the rest of a longer slice
+ * is read again (from whatever cache level still holds it; at the pages' shapes that
+ * second read misses the L2).
  * Arguments: those of se_row_stats and se_soft_embed_fused together (row_max,
  * row_lse, row_entropy and row_argmax are outputs here); workspace of
  * se_soft_embed_staged_workspace_bytes() bytes (16-byte aligned; none for an empty

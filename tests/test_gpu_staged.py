@@ -226,11 +226,12 @@ STEP_CASES = {
     "empty-slice": (8, 512, 16, 16, 16, 25),
     "whole-tile": (256, 20003, 4000, 8097, 512, 26),   # the ping-pong contraction
     # slices within 1 to 4 groups of 16,384 positions: the statistics kernel keeps those
-    # groups in registers instead of reading the slice twice; 5 groups take the second read
+    # groups in registers instead of reading the slice twice; a longer slice keeps its first
+    # 4 groups and reads the rest again
     "held-1-group": (16, 65536, 16384, 32768, 64, 27),
     "held-4-groups": (16, 65536, 0, 65536, 64, 28),
     "held-2-groups-at-end": (8, 81920, 49152, 81920, 128, 29),
-    "five-groups-read-twice": (8, 81920, 0, 81920, 64, 30),
+    "five-groups-four-held": (8, 81920, 0, 81920, 64, 30),     # the fifth is read again
     # unaligned slices within at most 4 groups are held too (only [s, e) is written)
     "held-unaligned-4-groups": (16, 65536, 8, 50001, 64, 31),
     "held-unaligned-2-groups": (8, 81920, 20008, 45011, 128, 32),
