@@ -10,6 +10,8 @@ The contraction path is chosen with --path:
   staged   se_row_stats, then se_soft_embed_staged (bitwise the fused call)
   fused    se_row_stats, then se_soft_embed_fused (probabilities rebuilt in the GEMM
            prologue)
+  step_onepass  se_soft_embed_step_onepass: the whole step from one read of the
+           logits (equal to the step up to rounding)
   onepass  se_soft_embed_onepass, which forms the row statistics from the same read
            of the logits (whole-vocabulary workloads only; no se_row_stats call)
 Inputs are seeded synthetic data already resident in HBM when the timed region starts.
@@ -20,8 +22,10 @@ bf16 table padded to 262,400 rows, d = 2,816, gamma = sqrt(2816)).
 
 Prints ONE JSON line.  ``value`` is soft-embed GFLOP/s over the whole step
 (2 L (e - s) d FLOP per step / step time); the same line carries steps/s, per-call
-times, the roofline of the step's contraction call, every other path timed on the
-same inputs, and the fp64 oracle timed on this host as a CPU baseline.
+times, the roofline of the timed call (the whole step for step, step_onepass and
+onepass; the contraction call otherwise), every other path timed on the same inputs,
+the vendor GEMM at the same shape, and the fp64 oracle timed on this host as a CPU
+baseline.
 """
 from __future__ import annotations
 
