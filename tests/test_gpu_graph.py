@@ -28,7 +28,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("which", ["step", "step_onepass", "staged", "step_held_slice"])
+@pytest.mark.parametrize("which", ["step", "step_onepass", "staged", "step_held_slice", "step_fp8"])
 def test_captured_step_replays_match_eager_calls(which):
     L, V, s, e, d = 256, 30000, 8000, 20000, 512
     if which == "step_held_slice":          # two whole 16,384-position groups: kept in registers
@@ -45,12 +45,17 @@ def test_captured_step_replays_match_eager_calls(which):
         ws = api.step_onepass_workspace(L, V, s, e, d, DEV)
     else:
         ws = api.staged_workspace(L, s, e, d, DEV)
+    if which == "step_fp8":                 # e4m3 table, quantized once before the capture
+        codes, wscale = api.quantize_table_fp8(w_t)
+        torch.cuda.synchronize()
 
     def call():
         if which in ("step", "step_held_slice"):
             B.se_soft_embed_step(x_t, s, e, w_t, 2.0, out, mx, lse, ent, am, ws)
         elif which == "step_onepass":
             B.se_soft_embed_step_onepass(x_t, s, e, w_t, 2.0, out, mx, lse, ent, am, ws)
+        elif which == "step_fp8":
+            B.se_soft_embed_step_fp8(x_t, s, e, codes, wscale, 2.0, out, mx, lse, ent, am, ws)
         else:                                   # statistics call, then the staged contraction
             B.se_row_stats(x_t, mx, lse, ent, am)
             B.se_soft_embed_staged(x_t, lse, s, e, w_t, 2.0, out, ws)
