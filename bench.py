@@ -1,31 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the self-conditioning soft embedding on one MI355X.
 
-A step is one pass of the whole hot path over one canvas batch: se_row_stats over
-the full-width fp32 logits, then the rank's slice contraction, both on one stream.
-The contraction path is chosen with --path:
-  step     se_soft_embed_step (default): statistics and the slice embedding in one
-           call, outputs bitwise those of se_row_stats + se_soft_embed_fused
-  unfused  se_row_stats, then se_probs_bf16 + se_soft_embed (bitwise the fused call)
-  staged   se_row_stats, then se_soft_embed_staged (bitwise the fused call)
-  fused    se_row_stats, then se_soft_embed_fused (probabilities rebuilt in the GEMM
-           prologue)
-  step_onepass  se_soft_embed_step_onepass: the whole step from one read of the
-           logits (equal to the step up to rounding)
-  onepass  se_soft_embed_onepass, which forms the row statistics from the same read
-           of the logits (whole-vocabulary workloads only; no se_row_stats call)
-Inputs are seeded synthetic data already resident in HBM when the timed region starts.
+A step is one pass of the whole hot path over one canvas batch: the softmax
+statistics of the full-width fp32 logits (max, log-sum-exp, entropy, argmax) and the
+soft embedding gamma * P[:, s:e] W_shard of the step's vocabulary slice.
 
-Default workload: one tensor-parallel rank's share at its real shape (L_c = 256
-canvas positions, full-width logits over V = 262,144, slice [65536, 131072) of a
-bf16 table padded to 262,400 rows, d = 2,816, gamma = sqrt(2816)).
+Default workload: the whole vocabulary, one canvas (L_c = 256 positions, V = 262,144,
+slice [0, 262144), d = 2,816, gamma = sqrt(2816); 378 GFLOP of soft embedding per step),
+timed on its fastest whole-step path, se_soft_embed_step_onepass (statistics and
+embedding from one read of the logits).  --path picks another way to run the step:
+  step          se_soft_embed_step: statistics then the slice embedding, one call, bitwise
+                se_row_stats + se_soft_embed_fused
+  step_onepass  se_soft_embed_step_onepass (one read of the logits; equal to step up to
+                rounding)
+  onepass       se_soft_embed_onepass (whole-vocabulary workloads: the slice statistics are
+                the row statistics)
+  unfused       se_row_stats, then se_probs_bf16 + se_soft_embed
+  staged        se_row_stats, then se_soft_embed_staged
+  fused         se_row_stats, then se_soft_embed_fused
+Inputs are seeded synthetic data, resident in HBM before the timed region starts.
 
-Prints ONE JSON line.  ``value`` is soft-embed GFLOP/s over the whole step
-(2 L (e - s) d FLOP per step / step time); the same line carries steps/s, per-call
-times, the roofline of the timed call (the whole step for step, step_onepass and
-onepass; the contraction call otherwise), every other path timed on the same inputs,
-the vendor GEMM at the same shape, and the fp64 oracle timed on this host as a CPU
-baseline.
+Prints ONE JSON line.  ``value`` is soft-embed GFLOP/s over whole steps (2 L (e - s) d
+FLOP per step / ms_per_step).  The line also carries: steps/s; the per-kernel times of
+one step from HIP events recorded between the library's own launches
+(se_set_launch_events); ``roofline`` of the dominant kernel (the contraction) and
+``roofline_step`` of the whole step, both on measured times; ``parity`` of the timed
+step's outputs against the fp64 oracle on every row (the rows the CPU baseline
+computes); ``cpu_baseline`` (that oracle's time on this host's cores); every other path
+on the same inputs; and ``workloads``: the one-rank shard (65,536-position slice), the
+near-converged canvas and the 2,048-row batch, each timed on its fastest path with its
+own rooflines and sampled oracle parity.
 """
 from __future__ import annotations
 
@@ -44,6 +48,24 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 KERNEL_SOURCES = ["soft_embed.hip", "row_stats.hip", "probs.hip", "onepass.hip", "se_device.h",
                   "se_launch.h", "api.cpp"]
+# fastest whole-step path of each workload (measured on MI355X)
+BEST_PATH = {"tiny": "step", "rank": "step", "full": "step_onepass", "conv": "step_onepass",
+             "batch": "step_onepass"}
+# kernel launches of one call, in order
+LAUNCHES = {
+    "step": ["row_stats_kernel<stats + staged slice>", "soft_embed_pp_kernel",
+             "splitk_reduce_kernel"],
+    "step_onepass": ["step_sweep_kernel", "soft_embed_pp_kernel", "merge_ranges_kernel",
+                     "scaled_reduce_kernel"],
+    "onepass": ["step_sweep_kernel", "soft_embed_pp_kernel", "merge_ranges_kernel",
+                "scaled_reduce_kernel"],
+    "staged": ["row_stats_kernel", "probs_bf16_kernel<tiled>", "soft_embed_pp_kernel",
+               "splitk_reduce_kernel"],
+    "fused": ["row_stats_kernel", "soft_embed_kernel<fused>", "splitk_reduce_kernel"],
+    "unfused": ["row_stats_kernel", "probs_bf16_kernel", "soft_embed_pp_kernel",
+                "splitk_reduce_kernel"],
+}
+GATE_REL_FRO, ENTROPY_TOL, LSE_REL_TOL = 5e-3, 1e-4, 2e-6
 
 
 def kernel_hash() -> str:
@@ -52,18 +74,6 @@ def kernel_hash() -> str:
         with open(os.path.join(ROOT, "diffusion_self_conditioning_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
-
-
-def fused_call_bytes(w) -> int:
-    """Algorithmic HBM bytes of one fused call: the bf16 shard slice once, the fp32 logits
-    slice once, the fp32 output once."""
-    return 2 * w.k * w.d + 4 * w.rows * w.k + 4 * w.rows * w.d
-
-
-def fp8_call_bytes(w) -> int:
-    """Algorithmic HBM bytes of one fused call on the e4m3 table: the codes and row scales of
-    the slice once, the fp32 logits slice once, the fp32 output once."""
-    return w.k * w.d + 4 * w.k + 4 * w.rows * w.k + 4 * w.rows * w.d
 
 
 def event_time_us(fn, K: int, warmup: int) -> float:
@@ -81,71 +91,309 @@ def event_time_us(fn, K: int, warmup: int) -> float:
     return sum(ev[k].elapsed_time(ev[k + 1]) for k in range(K)) * 1e3 / K
 
 
-def row_stats_bytes(w) -> int:
-    return 4 * w.rows * w.vocab + 16 * w.rows
+def step_bytes_logits_once(w) -> int:
+    """Algorithmic HBM bytes of a whole step that reads every logit once: the full-width
+    fp32 logits, the bf16 table slice, the fp32 output and the four statistics per row."""
+    return 4 * w.rows * w.vocab + 2 * w.k * w.d + 4 * w.rows * w.d + 16 * w.rows
 
 
-def measured_traffic(path: str, workload: str):
-    """HBM bytes per call of the step's contraction path from the committed rocprofv3 counter
-    summary of this workload, if it was taken on the current kernel sources; else None."""
+def step_bytes_two_pass(w) -> int:
+    """The step's bytes as the two-pass design counts them: statistics over the full width
+    (4 L V + 16 L) plus the fused call (table slice, logits slice, output)."""
+    return (4 * w.rows * w.vocab + 16 * w.rows) + (2 * w.k * w.d + 4 * w.rows * w.k
+                                                   + 4 * w.rows * w.d)
+
+
+def contraction_bytes(w, fused: bool) -> int:
+    """Algorithmic HBM bytes of one contraction launch: the bf16 table slice once and the
+    probability operand once (staged bf16, or fp32 logits for the fused kernel).  The
+    split partials are implementation traffic, not counted."""
+    return 2 * w.k * w.d + (4 if fused else 2) * w.rows * w.k
+
+
+def roofline(flops: int, nbytes: int, us: float, traffic=None) -> dict:
+    mfma = flops / (PEAK_BF16_TFLOPS * 1e12) > nbytes / (PEAK_HBM_GBS * 1e9)
+    achieved = flops / (us * 1e-6) / 1e12 if mfma else nbytes / (us * 1e-6) / 1e9
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS
+    return {"bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s" if mfma else "GB/s", "frac": round(achieved / peak, 4),
+            "traffic": traffic}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary of this
+    workload, if it was taken on the current kernel sources; else (None, reason)."""
+    name = f"profiles/traffic_{kernel}_{workload}.json"
     try:
-        with open(os.path.join(ROOT, "profiles", f"traffic_soft_embed_{path}_{workload}.json")) as fh:
+        with open(os.path.join(ROOT, name)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
-        return None
+        return None, f"no counter summary {name}"
     if t.get("kernel_hash") != kernel_hash():
-        return None
-    return t.get("bytes_per_call")
+        return None, f"{name} was taken on kernel sources {t.get('kernel_hash')}, not these"
+    return t.get("bytes_per_launch"), f"{t.get('source', name)} (kernel sources {t['kernel_hash']})"
 
 
-def cpu_baseline(w, x_np, bits, budget_s: float = 12.0):
-    """The fp64 oracle (row stats + slice contraction) on a bounded row sample of the same
-    workload, on this host's cores; scaled to GFLOP/s of the soft embedding."""
+class Step:
+    """Device buffers of one workload and the calls that run its step."""
+
+    def __init__(self, w, x_np, bits, dev):
+        import torch
+        from diffusion_self_conditioning_amd import api
+        self.w, self.dev = w, dev
+        self.x = torch.from_numpy(x_np).to(dev)
+        self.table = torch.from_numpy(bits).to(dev)
+        self.shard = self.table[w.vocab_start:w.vocab_end]
+        L, d = w.rows, w.d
+        f = dict(device=dev, dtype=torch.float32)
+        self.mx, self.lse, self.ent = torch.empty(L, **f), torch.empty(L, **f), torch.empty(L, **f)
+        self.am = torch.empty(L, device=dev, dtype=torch.int32)
+        self.out = torch.empty((L, d), **f)
+        self.ws = api.workspace(L, w.vocab_start, w.vocab_end, d, dev)
+        self.wss = api.staged_workspace(L, w.vocab_start, w.vocab_end, d, dev)
+        self.ws1 = api.step_onepass_workspace(L, w.vocab, w.vocab_start, w.vocab_end, d, dev)
+        self.wso = None
+        self.probs = None
+
+    def call(self, path: str, out=None):
+        from diffusion_self_conditioning_amd import _binding as B
+        from diffusion_self_conditioning_amd import api
+        w, o = self.w, (self.out if out is None else out)
+        s, e = w.vocab_start, w.vocab_end
+        stats = (self.mx, self.lse, self.ent, self.am)
+        if path == "step":
+            B.se_soft_embed_step(self.x, s, e, self.shard, w.gamma, o, *stats, self.wss)
+        elif path == "step_onepass":
+            B.se_soft_embed_step_onepass(self.x, s, e, self.shard, w.gamma, o, *stats, self.ws1)
+        elif path == "onepass":
+            if self.wso is None:
+                self.wso = api.onepass_workspace(w.rows, s, e, w.d, self.dev)
+            B.se_soft_embed_onepass(self.x, s, e, self.shard, w.gamma, o, *stats, self.wso)
+        else:
+            B.se_row_stats(self.x, *stats)
+            if path == "unfused":
+                if self.probs is None:
+                    import torch
+                    self.probs = torch.empty((w.rows, w.vocab), device=self.dev,
+                                             dtype=torch.bfloat16)
+                B.se_probs_bf16(self.x, self.lse, s, e, self.probs)
+                B.se_soft_embed(self.probs, s, e, self.shard, w.gamma, o, self.ws)
+            elif path == "staged":
+                B.se_soft_embed_staged(self.x, self.lse, s, e, self.shard, w.gamma, o, self.wss)
+            elif path == "fused":
+                B.se_soft_embed_fused(self.x, self.lse, s, e, self.shard, w.gamma, o, self.ws)
+            else:
+                raise ValueError(path)
+
+
+def timed_steps(st: Step, path: str, K: int, W: int):
+    """W warmup steps, then K timed steps bracketed by synchronisations, each with events
+    on the launch stream.  Returns (ms_per_step, per-step µs list, wall seconds)."""
+    import torch
+    for _ in range(W):
+        st.call(path)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for k in range(K):
+        st.call(path)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(K)]
+    return ev[0].elapsed_time(ev[K]) / K, per, wall
+
+
+def kernel_times(st: Step, path: str, K: int):
+    """Per-launch times of one step, averaged over K steps: an event recorded before the
+    call, then one marker after each of the library's launches (se_set_launch_events)."""
+    import torch
+    from diffusion_self_conditioning_amd import _binding as B
+    n_max = 8
+    sums, n_used = None, None
+    for _ in range(K):
+        start = torch.cuda.Event(enable_timing=True)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_max)]
+        for m in marks:                     # create the underlying HIP events
+            m.record()
+        start.record()
+        B.se_set_launch_events([m.cuda_event for m in marks])
+        st.call(path)
+        used = B.se_launch_events_used()
+        B.se_set_launch_events([])
+        torch.cuda.synchronize()
+        t = [start.elapsed_time(marks[0]) * 1e3] + [
+            marks[j - 1].elapsed_time(marks[j]) * 1e3 for j in range(1, used)]
+        if sums is None:
+            sums, n_used = [0.0] * used, used
+        if used != n_used:
+            raise RuntimeError("launch count changed between steps")
+        sums = [a + b for a, b in zip(sums, t)]
+    names = LAUNCHES.get(path, [])
+    if len(names) != n_used and path in ("step_onepass", "onepass") and n_used == 3:
+        names = LAUNCHES["step"]            # the one-read call ran the two-pass step
+    if len(names) != n_used:
+        names = [f"launch_{j}" for j in range(n_used)]
+    return [(names[j], sums[j] / K) for j in range(n_used)]
+
+
+def step_report(st: Step, path: str, K: int, W: int) -> dict:
+    """Timed steps, per-kernel times and rooflines of one workload on one path."""
+    w = st.w
+    ms, per, wall = timed_steps(st, path, K, W)
+    kt = kernel_times(st, path, K)
+    flops = w.flops()
+    dom_i = max(range(len(kt)), key=lambda j: kt[j][1] if "soft_embed" in kt[j][0] else -1)
+    dom_name, dom_us = kt[dom_i]
+    fused = "fused" in dom_name
+    traffic, source = measured_traffic("soft_embed_pp_kernel" if not fused else
+                                       "soft_embed_kernel_fused", w.name)
+    roof = roofline(flops, contraction_bytes(w, fused), dom_us, traffic)
+    roof.update({"kernel": dom_name, "kernel_us": round(dom_us, 2),
+                 "algorithmic_bytes": contraction_bytes(w, fused),
+                 "algorithmic_flops": flops, "traffic_source": source,
+                 "basis": "algorithmic bytes (bf16 table slice + staged bf16 probabilities) "
+                          "or FLOP of one launch / its event-timed duration"})
+    once, two = step_bytes_logits_once(w), step_bytes_two_pass(w)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12) * 1e6
+
+    def step_roof(nbytes):
+        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9) * 1e6
+        # the statistics pass is HBM work that cannot hide under an MFMA-bound contraction
+        stats_us = (4 * w.rows * w.vocab + 16 * w.rows) / (PEAK_HBM_GBS * 1e9) * 1e6
+        t_roof = max(t_hbm, stats_us + t_mfma)
+        return {"algorithmic_bytes": nbytes, "t_roof_us": round(t_roof, 2),
+                "frac": round(t_roof / (ms * 1e3), 4)}
+
+    srt = sorted(per)
+    return {
+        "path": path, "ms_per_step": round(ms, 5), "steps_per_s": round(1e3 / ms, 2),
+        "canvas_steps_per_s": round(1e3 / ms * (w.rows / 256), 2),
+        "gflops": round(flops / (ms * 1e-3) / 1e9, 2),
+        "step_us_median": round(srt[len(srt) // 2], 2), "step_us_min": round(srt[0], 2),
+        "wall_s_timed": round(wall, 4),
+        "kernel_us": {name: round(us, 2) for name, us in kt},
+        "roofline": roof,
+        "roofline_step": {
+            "basis": "whole-step algorithmic bytes (or the statistics pass plus the MFMA "
+                     "time, if longer) / ms_per_step",
+            "logits_once": step_roof(once),
+            "two_pass_design": step_roof(two)},
+    }
+
+
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            return next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
+                        "unknown CPU")
+    except OSError:
+        return "unknown CPU"
+
+
+def parity(w, got: dict, ref_stats: dict, ref_out, rows) -> dict:
+    """The GPU step's outputs against the fp64 oracle on `rows`: argmax and row max exact,
+    lse within 2e-6 relative, entropy within 1e-4 nats, the soft embedding within 5e-3
+    relative Frobenius (the oracle takes exact p)."""
+    import numpy as np
+    r = np.asarray(rows)
+    am_bad = int(np.sum(got["argmax"][r] != ref_stats["argmax"][r]))
+    d_max = float(np.max(np.abs(got["max"][r].astype(np.float64) - ref_stats["max"][r])))
+    lse_rel = float(np.max(np.abs(got["lse"][r] - ref_stats["lse"][r])
+                           / np.maximum(1.0, np.abs(ref_stats["lse"][r]))))
+    d_h = float(np.max(np.abs(got["entropy"][r] - ref_stats["entropy"][r])))
+    o = got["out"][r].astype(np.float64)
+    rel = float(np.linalg.norm(o - ref_out) / max(np.linalg.norm(ref_out), 1e-300))
+    row_rel = np.linalg.norm(o - ref_out, axis=1) / np.maximum(
+        np.linalg.norm(ref_out, axis=1), 1e-300)
+    ok = am_bad == 0 and d_max == 0.0 and lse_rel <= LSE_REL_TOL and d_h <= ENTROPY_TOL \
+        and rel <= GATE_REL_FRO
+    return {"rows_checked": int(r.size), "rows_total": w.rows,
+            "argmax_mismatches": am_bad, "max_abs_d_row_max": d_max,
+            "max_rel_d_lse": lse_rel, "max_abs_d_entropy_nats": d_h,
+            "rel_fro": rel, "max_row_rel_fro": float(np.max(row_rel)),
+            "tolerances": {"argmax": "exact", "row_max": "exact", "lse_rel": LSE_REL_TOL,
+                           "entropy_nats": ENTROPY_TOL, "rel_fro": GATE_REL_FRO},
+            "pass": bool(ok)}
+
+
+def fetch(st: Step) -> dict:
+    return {"out": st.out.cpu().numpy(), "max": st.mx.cpu().numpy(),
+            "lse": st.lse.cpu().numpy(), "entropy": st.ent.cpu().numpy(),
+            "argmax": st.am.cpu().numpy()}
+
+
+def cpu_baseline_and_parity(w, x_np, bits, got, budget_s: float = 30.0):
+    """The fp64 oracle (statistics over the full width + slice contraction) on this host's
+    cores: every row when it fits the time budget, else an even sample; its time is the
+    CPU baseline, its results the parity reference."""
+    import numpy as np
     import oracle
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     shard = bits[w.vocab_start:w.vocab_end]
-    rows = max(1, cores)
+    probe = min(w.rows, max(1, cores))
     t0 = time.perf_counter()
-    oracle.row_stats(x_np[:rows])
-    oracle.soft_embed(x_np[:rows], w.vocab_start, w.vocab_end, shard, w.gamma)
+    oracle.soft_embed(x_np[:probe], w.vocab_start, w.vocab_end, shard, w.gamma)
+    per_row = (time.perf_counter() - t0) / probe
+    n = w.rows if per_row * w.rows <= budget_s else max(probe, int(budget_s / per_row))
+    rows = np.unique(np.linspace(0, w.rows - 1, n).round().astype(np.int64))
+    xs = np.ascontiguousarray(x_np[rows])
+    t0 = time.perf_counter()
+    ref_stats_s = oracle.row_stats(xs)
+    ref_out = oracle.soft_embed(xs, w.vocab_start, w.vocab_end, shard, w.gamma)
     dt = time.perf_counter() - t0
-    if dt < budget_s / 3:
-        rows = min(w.rows, max(rows, int(rows * budget_s / max(dt, 1e-3))) // cores * cores or cores)
-        t0 = time.perf_counter()
-        oracle.row_stats(x_np[:rows])
-        oracle.soft_embed(x_np[:rows], w.vocab_start, w.vocab_end, shard, w.gamma)
-        dt = time.perf_counter() - t0
-    flops = 2 * rows * w.k * w.d
-    model = "unknown CPU"
-    try:
-        with open("/proc/cpuinfo") as fh:
-            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
-                         model)
-    except OSError:
-        pass
-    return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{rows} of {w.rows} rows of the {w.name} workload (row stats over "
-                      f"V={w.vocab} + fp64 contraction over the {w.k}-row slice), {dt:.2f} s "
-                      f"on {model}"}
+    ref_stats = {k: np.zeros(w.rows, v.dtype) for k, v in ref_stats_s.items()}
+    for k, v in ref_stats_s.items():
+        ref_stats[k][rows] = v
+    par = parity(w, got, ref_stats, ref_out, rows)
+    base = {"value": round(2 * rows.size * w.k * w.d / dt / 1e9, 4), "unit": "GFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{rows.size} of {w.rows} rows of the {w.name} workload (statistics over "
+                      f"V={w.vocab} + fp64 contraction over the {w.k}-position slice), "
+                      f"{dt:.2f} s on {host_cpu()}"}
+    return base, par
+
+
+def sampled_parity(w, x_np, bits, got, seed: int = 11):
+    """Oracle parity on two seeded rows of every 256-row tile plus the first and last row;
+    statistics on every row."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(seed)
+    rows = {0, w.rows - 1}
+    for t0 in range(0, w.rows, 256):
+        n = min(256, w.rows - t0)
+        rows.update(int(t0 + v) for v in rng.choice(n, size=min(2, n), replace=False))
+    rows = np.array(sorted(rows))
+    ref_stats = oracle.row_stats(x_np)
+    ref_out = oracle.soft_embed(np.ascontiguousarray(x_np[rows]), w.vocab_start, w.vocab_end,
+                                bits[w.vocab_start:w.vocab_end], w.gamma)
+    par = parity(w, got, ref_stats, ref_out, rows)
+    # statistics of every row
+    am_bad = int(np.sum(got["argmax"] != ref_stats["argmax"]))
+    d_h = float(np.max(np.abs(got["entropy"] - ref_stats["entropy"])))
+    par["stats_all_rows"] = {"argmax_mismatches": am_bad, "max_abs_d_entropy_nats": d_h,
+                             "max_abs_d_row_max": float(np.max(np.abs(
+                                 got["max"].astype(np.float64) - ref_stats["max"])))}
+    par["pass"] = bool(par["pass"] and am_bad == 0 and d_h <= ENTROPY_TOL)
+    return par
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the GPU needs tens of milliseconds of this work before its kernels run at their
-    # steady-state speed (measured: 5 warmup steps leave the rank step about 6% slow)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="rank", choices=["rank", "full", "conv", "batch", "tiny"])
+    ap.add_argument("--workload", default="full", choices=["full", "rank", "conv", "batch", "tiny"])
+    ap.add_argument("--path", default="auto",
+                    choices=["auto", "step", "step_onepass", "onepass", "unfused", "staged",
+                             "fused"],
+                    help="how the step runs (auto: the workload's fastest whole-step path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", default="step",
-                    choices=["unfused", "fused", "staged", "step", "step_onepass", "onepass"],
-                    help="how the step runs: se_soft_embed_step (default, one call, bitwise the "
-                         "separate calls), se_soft_embed_step_onepass (one call, one read of the "
-                         "logits), or se_row_stats followed by the unfused, staged or fused "
-                         "contraction, or se_soft_embed_onepass (whole-vocabulary workloads; "
-                         "softmax statistics from the same read of the logits)")
+    ap.add_argument("--side-workloads", default="rank,conv,batch",
+                    help="comma-separated workloads timed beside the main one on their fastest "
+                         "paths ('' for none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference for scaling the HBM byte counters), then exit")
@@ -174,319 +422,183 @@ def main():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         sys.exit(1)
     from diffusion_self_conditioning_amd import _binding as B
-    from diffusion_self_conditioning_amd import api
     from diffusion_self_conditioning_amd import workloads as wl
 
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     w = wl.get(args.workload)
+    path = BEST_PATH[w.name] if args.path == "auto" else args.path
     whole = w.vocab_start == 0 and w.vocab_end == w.vocab
-    if args.path == "onepass" and not whole:
+    if path == "onepass" and not whole:
         print("--path onepass needs a workload whose slice is the whole vocabulary (its row "
               "statistics are those of the slice)", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
-    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    K, W = args.steps, args.warmup
+    say(f"generating {w.name} inputs")
     x_np = wl.make_logits(w)
     bits, _ = wl.make_table(w)
-    x = torch.from_numpy(x_np).to(dev)
-    table = torch.from_numpy(bits).to(dev)
-    shard = table[w.vocab_start:w.vocab_end]
+    st = Step(w, x_np, bits, dev)
     L, d = w.rows, w.d
-    mx = torch.empty(L, device=dev)
-    lse = torch.empty(L, device=dev)
-    ent = torch.empty(L, device=dev)
-    am = torch.empty(L, device=dev, dtype=torch.int32)
-    out = torch.empty((L, d), device=dev)
-    ws = api.workspace(L, w.vocab_start, w.vocab_end, d, dev)
-    probs = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16)
-    wso = api.onepass_workspace(L, w.vocab_start, w.vocab_end, d, dev)
-    wss = api.staged_workspace(L, w.vocab_start, w.vocab_end, d, dev)
-    ws1 = api.step_onepass_workspace(L, w.vocab, w.vocab_start, w.vocab_end, d, dev)
-
-    def stats():
-        B.se_row_stats(x, mx, lse, ent, am)
-
-    def call_unfused(o):
-        B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, probs)
-        B.se_soft_embed(probs, w.vocab_start, w.vocab_end, shard, w.gamma, o, ws)
-
-    def call_fused(o):
-        B.se_soft_embed_fused(x, lse, w.vocab_start, w.vocab_end, shard, w.gamma, o, ws)
-
-    def call_staged(o):
-        B.se_soft_embed_staged(x, lse, w.vocab_start, w.vocab_end, shard, w.gamma, o, wss)
-
-    def call_step(o):
-        B.se_soft_embed_step(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse, ent, am,
-                             wss)
-
-    def call_step_onepass(o):
-        B.se_soft_embed_step_onepass(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse,
-                                     ent, am, ws1)
-
-    def call_onepass(o):
-        B.se_soft_embed_onepass(x, w.vocab_start, w.vocab_end, shard, w.gamma, o, mx, lse, ent,
-                                am, wso)
-
-    calls = {"unfused": call_unfused, "fused": call_fused, "staged": call_staged,
-             "step": call_step, "step_onepass": call_step_onepass, "onepass": call_onepass}
-    call_names = {"unfused": "se_probs_bf16 + se_soft_embed", "fused": "se_soft_embed_fused",
-                  "staged": "se_soft_embed_staged", "step": "se_soft_embed_step",
-                  "step_onepass": "se_soft_embed_step_onepass",
-                  "onepass": "se_soft_embed_onepass"}
-    embed = calls[args.path]
-    # the one-pass and whole-step calls form the statistics themselves
-    with_stats = args.path not in ("onepass", "step", "step_onepass")
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        if with_stats:
-            stats()
-        embed(out)
-    torch.cuda.synchronize()
-
-    # timed region: K whole steps, events around each call on the launch stream
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    t_start.record()
-    for k in range(K):
-        ev[k][0].record()
-        if with_stats:
-            stats()
-        ev[k][1].record()
-        embed(out)
-        ev[k][2].record()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / K
-    us_stats = [ev[k][0].elapsed_time(ev[k][1]) * 1e3 for k in range(K)]
-    us_embed = [ev[k][1].elapsed_time(ev[k][2]) * 1e3 for k in range(K)]
-    us_stats_avg = sum(us_stats) / K
-    us_embed_avg = sum(us_embed) / K
-    us_step_sorted = sorted(a + b for a, b in zip(us_stats, us_embed))
-
     flops = w.flops()
-    gflops_step = flops / (ms_step * 1e-3) / 1e9
-    gflops_call = flops / (us_embed_avg * 1e-6) / 1e9
-    call_bytes = fused_call_bytes(w)
-    if args.path == "onepass":          # plus the statistics it writes
-        call_bytes += 16 * L
-    elif args.path in ("step", "step_onepass"):   # the whole step: every logit once, table, outputs
-        call_bytes = row_stats_bytes(w) + 2 * w.k * w.d + 4 * L * w.d
-    achieved_gbs = call_bytes / (us_embed_avg * 1e-6) / 1e9
-    t_roof_call_us = max(flops / (PEAK_BF16_TFLOPS * 1e12), call_bytes / (PEAK_HBM_GBS * 1e9)) * 1e6
-    stats_bytes = row_stats_bytes(w) if with_stats else 0
-    step_bytes = call_bytes + stats_bytes
-    t_roof_step_us = (stats_bytes / (PEAK_HBM_GBS * 1e9) + t_roof_call_us * 1e-6) * 1e6
-    mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > call_bytes / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(args.path, w.name)
-    roof = {"bound": "mfma" if mfma_bound else "hbm",
-            "achieved": round(gflops_call / 1e3 if mfma_bound else achieved_gbs, 2),
-            "peak": PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS,
-            "unit": "TFLOP/s" if mfma_bound else "GB/s",
-            "traffic": traffic}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = call_names[args.path] + " call"
-    roof["algorithmic_bytes"] = call_bytes
 
-    # side measurements (not part of `value`): every contraction path on the same inputs,
-    # each event-timed as one call; the unfused and fused outputs are compared bitwise
+    # every path once on the same inputs, event-timed as whole steps (these run before the
+    # headline's warmup, so the timed steps below see a GPU that has been under load)
+    say("paths")
     side = {}
-    ref_out = out.clone()
-    exact = args.path in ("unfused", "fused", "staged", "step")
-    for name in ("unfused", "fused", "staged"):
-        o = torch.empty_like(out)
-        side[name + "_call_us"] = round(event_time_us(lambda: calls[name](o), K, args.warmup), 2)
-        if exact:
-            side[name + "_equals_step_output"] = bool(torch.equal(o, ref_out))
-        del o
-    # the two whole-step calls (statistics included), and how far apart their outputs are
-    o1, o2 = torch.empty_like(out), torch.empty_like(out)
-    side["step_call_us"] = round(event_time_us(lambda: call_step(o1), K, args.warmup), 2)
-    side["step_onepass_call_us"] = round(event_time_us(lambda: call_step_onepass(o2), K,
-                                                       args.warmup), 2)
+    outs = {}
+    for p in ("step", "step_onepass", "unfused", "staged", "fused") + (("onepass",) if whole
+                                                                       else ()):
+        o = torch.empty_like(st.out)
+        side[p + "_step_us"] = round(event_time_us(lambda: st.call(p, o), K, W), 2)
+        outs[p] = o
+    ref = outs["step"]
+    for p in ("unfused", "staged", "fused"):
+        side[p + "_equals_step_output"] = bool(torch.equal(outs[p], ref))
     side["step_onepass_rel_diff_vs_step"] = float(
-        (o2.double() - o1.double()).norm() / o1.double().norm())
-    del o1, o2
-    side["gflops_unfused_call"] = round(flops / (side["unfused_call_us"] * 1e-6) / 1e9, 2)
-    side["gflops_fused_call"] = round(flops / (side["fused_call_us"] * 1e-6) / 1e9, 2)
-    side["gflops_staged_call"] = round(flops / (side["staged_call_us"] * 1e-6) / 1e9, 2)
+        (outs["step_onepass"].double() - ref.double()).norm() / ref.double().norm())
+    del outs, o
 
-    # side measurement: the sampler's acceptance / convergence step on this step's row
-    # statistics (canvases of 256 positions)
+    # the headline: W warmup steps, K timed steps of the chosen path
+    say(f"warmup {W}, {K} timed steps ({path})")
+    main_rep = step_report(st, path, K, W)
+    got = fetch(st)           # the last timed step's outputs (the marker pass repeats it)
+
+    # side measurements on the same inputs
+    say("side measurements")
     acc_side = None
     if L % 256 == 0:
         nc = L // 256
-        st = {"acc": torch.zeros(L, dtype=torch.uint8, device=dev),
-              "prev": torch.full((L,), -1, dtype=torch.int32, device=dev),
-              "sc": torch.zeros(nc, dtype=torch.int32, device=dev),
-              "stc": torch.zeros(nc, dtype=torch.int32, device=dev),
-              "new": torch.empty(L, dtype=torch.uint8, device=dev),
-              "conv": torch.empty(nc, dtype=torch.uint8, device=dev)}
+        acc = {"acc": torch.zeros(L, dtype=torch.uint8, device=dev),
+               "prev": torch.full((L,), -1, dtype=torch.int32, device=dev),
+               "sc": torch.zeros(nc, dtype=torch.int32, device=dev),
+               "stc": torch.zeros(nc, dtype=torch.int32, device=dev),
+               "new": torch.empty(L, dtype=torch.uint8, device=dev),
+               "conv": torch.empty(nc, dtype=torch.uint8, device=dev)}
 
         def accept_step():
-            B.se_accept_converge(ent, am, 256, 8.0, 3, 0.05, 64, st["acc"], st["prev"], st["sc"],
-                                 st["stc"], st["new"], st["conv"])
+            B.se_accept_converge(st.ent, st.am, 256, 8.0, 3, 0.05, 64, acc["acc"], acc["prev"],
+                                 acc["sc"], acc["stc"], acc["new"], acc["conv"])
 
-        acc_side = {"accept_converge_us": round(event_time_us(accept_step, K, args.warmup), 2),
-                    "canvases": nc, "accepted_last_step": int(st["new"].sum().item())}
-
-    # side measurement: the on-device sum of 4 per-rank partials of this output shape,
-    # written as fp32 and bf16
+        acc_side = {"accept_converge_us": round(event_time_us(accept_step, K, W), 2),
+                    "canvases": nc, "accepted_last_step": int(acc["new"].sum().item())}
+        del acc
     parts4 = torch.randn((4, L, d), device=dev)
     red_f = torch.empty((L, d), device=dev)
     red_b = torch.empty((L, d), dtype=torch.bfloat16, device=dev)
-    red_us = event_time_us(lambda: B.se_reduce_partials(parts4, out=red_f, out_bf16=red_b), K,
-                           args.warmup)
+    red_us = event_time_us(lambda: B.se_reduce_partials(parts4, out=red_f, out_bf16=red_b), K, W)
     red_side = {"reduce_partials_us": round(red_us, 2), "parts": 4,
                 "gbs": round((4 * 4 + 4 + 2) * L * d / (red_us * 1e-6) / 1e9, 1)}
     del parts4, red_f, red_b
 
-    # side measurement: the same calls on the e4m3 form of the shard (quantized once on the
-    # GPU, untimed), fused and unfused, with the fused call's HBM roofline
+    # the e4m3 form of the shard (quantized once, untimed): the whole step against it
     codes = torch.empty((w.k, d), dtype=torch.uint8, device=dev)
     wscale = torch.empty(w.k, device=dev)
-    B.se_quantize_table_fp8(shard, codes, wscale)
-    out8 = torch.empty_like(out)
-    pr8 = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16)
-    B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, pr8)
-    us_f8 = event_time_us(lambda: B.se_soft_embed_fp8_fused(
-        x, lse, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, ws), K, args.warmup)
-    us_u8 = event_time_us(lambda: B.se_soft_embed_fp8(
-        pr8, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, ws), K, args.warmup)
-    # the whole step against the e4m3 table (statistics + staged probabilities + contraction)
-    mx8, lse8, ent8 = torch.empty(L, device=dev), torch.empty(L, device=dev), torch.empty(L, device=dev)
-    am8 = torch.empty(L, device=dev, dtype=torch.int32)
+    B.se_quantize_table_fp8(st.shard, codes, wscale)
+    out8 = torch.empty_like(st.out)
+    s8 = [torch.empty(L, device=dev) for _ in range(3)] + [
+        torch.empty(L, device=dev, dtype=torch.int32)]
     us_s8 = event_time_us(lambda: B.se_soft_embed_step_fp8(
-        x, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, mx8, lse8, ent8, am8, wss),
-        K, args.warmup)
-    s8_bytes = row_stats_bytes(w) + w.k * d + 4 * w.k + 4 * L * d
-    us_q = event_time_us(lambda: B.se_quantize_table_fp8(shard, codes, wscale), 3, 1)
-    f8_bytes = fp8_call_bytes(w)
-    fp8_side = {"fused_call_us": round(us_f8, 2),
-                "gflops_fused_call": round(flops / (us_f8 * 1e-6) / 1e9, 2),
-                "unfused_gemm_only_us": round(us_u8, 2),
-                "roofline_fused_call": {"bound": "hbm", "algorithmic_bytes": f8_bytes,
-                                        "achieved": round(f8_bytes / (us_f8 * 1e-6) / 1e9, 2),
-                                        "peak": PEAK_HBM_GBS,
-                                        "frac": round(f8_bytes / (us_f8 * 1e-6) / 1e9
-                                                      / PEAK_HBM_GBS, 4)},
-                "step_us": round(us_s8, 2),
-                "gflops_step": round(flops / (us_s8 * 1e-6) / 1e9, 2),
+        st.x, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, *s8, st.wss), K, W)
+    s8_bytes = 4 * L * w.vocab + w.k * d + 4 * w.k + 4 * L * d + 16 * L
+    us_q = event_time_us(lambda: B.se_quantize_table_fp8(st.shard, codes, wscale), 3, 1)
+    fp8_side = {"step_us": round(us_s8, 2), "gflops_step": round(flops / (us_s8 * 1e-6) / 1e9, 2),
                 "roofline_step": {"bound": "hbm", "algorithmic_bytes": s8_bytes,
                                   "achieved": round(s8_bytes / (us_s8 * 1e-6) / 1e9, 2),
                                   "peak": PEAK_HBM_GBS,
-                                  "frac": round(s8_bytes / (us_s8 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
-                "quantize_shard_us": round(us_q, 2)}
-    del codes, wscale, out8, pr8, mx8, lse8, ent8, am8
+                                  "frac": round(s8_bytes / (us_s8 * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                                4)},
+                "quantize_shard_us": round(us_q, 2),
+                "note": "a different numerical contract (the dequantized e4m3 table); not value"}
+    del codes, wscale, out8, s8
 
-    # side measurement: the one-pass call over the same slice (softmax over the slice, row
-    # statistics from the same read of the logits), and the merge of 4 slice results.  For
-    # a slice that is the whole vocabulary the one-pass call is a whole step.
-    oo = torch.empty((L, d), device=dev)
-    so = [torch.empty(L, device=dev) for _ in range(3)]
-    ao = torch.empty(L, device=dev, dtype=torch.int32)
-    us_o = event_time_us(lambda: B.se_soft_embed_onepass(
-        x, w.vocab_start, w.vocab_end, shard, w.gamma, oo, so[0], so[1], so[2], ao, wso), K,
-        args.warmup)
-    outs4 = torch.randn((4, L, d), device=dev)
-    st4 = [torch.randn((4, L), device=dev) for _ in range(3)]
-    am4 = torch.zeros((4, L), device=dev, dtype=torch.int32)
-    us_m = event_time_us(lambda: B.se_merge_slices(outs4, st4[0], st4[1], st4[2], am4, oo, so[0],
-                                                   so[1], so[2], ao), K, args.warmup)
-    o_bytes = fused_call_bytes(w) + 16 * L
-    onepass_side = {"call_us": round(us_o, 2),
-                    "gflops_call": round(flops / (us_o * 1e-6) / 1e9, 2),
-                    "roofline_call": {"bound": "hbm", "algorithmic_bytes": o_bytes,
-                                      "achieved": round(o_bytes / (us_o * 1e-6) / 1e9, 2),
-                                      "peak": PEAK_HBM_GBS,
-                                      "frac": round(o_bytes / (us_o * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                                                    4)},
-                    "merge_4_slices_us": round(us_m, 2)}
-    del oo, so, ao, outs4, st4, am4
-
-    # cold step: a 1 GiB write between steps evicts L2 and the 256 MB MALL first; and the
-    # achievable HBM rate of a plain 1 GiB device-to-device copy, beside the 8 TB/s peak
+    # cold step, and the box's achievable ceilings beside the peaks
     scrub = torch.empty(1 << 28, device=dev)
     cold = []
     for k in range(5):
         scrub.fill_(float(k))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        if with_stats:
-            stats()
-        embed(out)
+        st.call(path)
         e1.record()
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e3)
     src = torch.ones(1 << 28, device=dev)
     copy_us = event_time_us(lambda: scrub.copy_(src), 10, 3)
     del scrub, src
-    # achievable dense bf16 matrix-core rate on this machine: the vendor GEMM (torch.mm, contiguous
-    # operands) on an 8192-cube, beside the 2.5 PFLOP/s peak
     ga = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
     gb = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
     mm_us = event_time_us(lambda: torch.mm(ga, gb), 10, 5)
     del ga, gb
-    # the vendor GEMM at this call's own shape: the slice's bf16 probabilities [rows, K]
-    # (row-major, contiguous) times the bf16 shard [K, d], fp32 output, beside the library's
-    # contraction of the same operands (se_soft_embed on the probabilities se_probs_bf16 wrote)
-    B.se_probs_bf16(x, lse, w.vocab_start, w.vocab_end, probs)
-    pa = probs[:, w.vocab_start:w.vocab_end].contiguous()
-    pb = shard.view(torch.bfloat16)
-    og = torch.empty_like(out)
+    # the vendor GEMM at the contraction's own shape: the slice's bf16 probabilities
+    # [rows, K] (contiguous) times the bf16 shard [K, d], fp32 output
+    B.se_row_stats(st.x, st.mx, st.lse, st.ent, st.am)
+    pr = torch.empty((L, w.vocab), device=dev, dtype=torch.bfloat16)
+    B.se_probs_bf16(st.x, st.lse, w.vocab_start, w.vocab_end, pr)
+    pa = pr[:, w.vocab_start:w.vocab_end].contiguous()
+    del pr
+    pb = st.shard.view(torch.bfloat16)
     vend_us = event_time_us(lambda: torch.mm(pa, pb, out_dtype=torch.float32), 10, 5)
-    ours_us = event_time_us(lambda: B.se_soft_embed(probs, w.vocab_start, w.vocab_end, shard,
-                                                    w.gamma, og, ws), 10, 5)
-    del pa, pb, og
+    del pa, pb
     ceilings = {"cold_step_us_median": round(sorted(cold)[len(cold) // 2], 2),
                 "hbm_copy_gbs": round(2 * (1 << 28) * 4 / (copy_us * 1e-6) / 1e9, 1),
                 "bf16_gemm_8192_tflops": round(2 * 8192 ** 3 / (mm_us * 1e-6) / 1e12, 1),
                 "vendor_gemm_same_shape_us": round(vend_us, 2),
-                "vendor_gemm_same_shape_tflops": round(flops / (vend_us * 1e-6) / 1e12, 1),
-                "library_contraction_same_shape_us": round(ours_us, 2),
-                "library_contraction_same_shape_tflops": round(flops / (ours_us * 1e-6) / 1e12, 1)}
+                "vendor_gemm_same_shape_tflops": round(flops / (vend_us * 1e-6) / 1e12, 1)}
 
-    cpu = None
+    cpu, par = None, None
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, x_np, bits)
+        say("cpu baseline and parity (fp64 oracle)")
+        cpu, par = cpu_baseline_and_parity(w, x_np, bits, got)
+    del st
+    torch.cuda.empty_cache()
+
+    # the other workloads, each on its fastest path, with sampled oracle parity
+    others = {}
+    for name in [n for n in args.side_workloads.split(",") if n and n != w.name]:
+        ow = wl.get(name)
+        say(f"side workload {name}")
+        ox = wl.make_logits(ow)
+        ob, _ = wl.make_table(ow)
+        ost = Step(ow, ox, ob, dev)
+        op = BEST_PATH[name]
+        rep = step_report(ost, op, K, W)
+        rep["config"] = (f"{name}: L_c={ow.rows}, V={ow.vocab}, slice [{ow.vocab_start},"
+                         f"{ow.vocab_end}), d={ow.d}, seed {ow.seed}")
+        if not args.no_cpu_baseline:
+            rep["parity"] = sampled_parity(ow, ox, ob, fetch(ost))
+        others[name] = rep
+        del ost, ox, ob
+        torch.cuda.empty_cache()
 
     line = {
-        "metric": METRIC, "value": round(gflops_step, 2), "unit": "GFLOP/s", "n_gpus": 1,
-        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "metric": METRIC, "value": main_rep["gflops"], "unit": "GFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": main_rep["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: L_c={L} rows, full-width fp32 logits V={w.vocab}, "
                                f"slice [{w.vocab_start},{w.vocab_end}) of a bf16 table "
-                               f"[{w.table_rows}, {d}], gamma={w.gamma:.6g}"
-                               + f" ({args.path})",
+                               f"[{w.table_rows}, {d}], gamma={w.gamma:.6g}; whole step on "
+                               f"{path}",
                    "rows": L, "vocab": w.vocab, "vocab_start": w.vocab_start,
-                   "vocab_end": w.vocab_end, "d": d, "seed": w.seed},
-        "steps_per_s": round(1e3 / ms_step, 2),
-        "canvas_steps_per_s": round(1e3 / ms_step * (L / 256), 2),
-        "gflops_call": round(gflops_call, 2),
-        "kernel_us": {"se_row_stats": round(us_stats_avg, 2) if with_stats else None,
-                      call_names[args.path]: round(us_embed_avg, 2)},
-        "step_us_median": round(us_step_sorted[K // 2], 2),
-        "step_us_min": round(us_step_sorted[0], 2),
-        "roofline": roof,
-        "roofline_step": {"t_roof_us": round(t_roof_step_us, 2),
-                          "frac": round(t_roof_step_us / (ms_step * 1e3), 4),
-                          "algorithmic_bytes": step_bytes},
-        "roofline_call_t_roof_us": round(t_roof_call_us, 2),
-        "wall_s_timed": round(wall, 4),
+                   "vocab_end": w.vocab_end, "d": d, "seed": w.seed, "path": path,
+                   "flops_per_step": flops},
+        "steps_per_s": main_rep["steps_per_s"],
+        "canvas_steps_per_s": main_rep["canvas_steps_per_s"],
+        "step_us_median": main_rep["step_us_median"], "step_us_min": main_rep["step_us_min"],
+        "kernel_us": main_rep["kernel_us"],
+        "roofline": main_rep["roofline"],
+        "roofline_step": main_rep["roofline_step"],
+        "parity": par,
+        "cpu_baseline": cpu,
+        "wall_s_timed": main_rep["wall_s_timed"],
         "paths": side,
+        "workloads": others,
         "accept_converge": acc_side,
         "reduce_partials": red_side,
         "fp8_table": fp8_side,
-        "onepass": onepass_side,
         "cold_and_ceilings": ceilings,
-        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -27,7 +27,8 @@ EXPORTS = ("se_status_string", "se_version", "se_row_stats", "se_probs_bf16",
            "se_soft_embed_onepass", "se_merge_slices", "se_soft_embed_staged_workspace_bytes",
            "se_soft_embed_staged", "se_soft_embed_step",
            "se_soft_embed_step_onepass_workspace_bytes", "se_soft_embed_step_onepass",
-           "se_soft_embed_step_fp8")
+           "se_soft_embed_step_fp8", "se_set_launch_events", "se_launch_events_used",
+           "se_soft_embed_splits")
 
 
 class SoftEmbedError(RuntimeError):
@@ -77,7 +78,12 @@ def _declare(lib):
     lib.se_soft_embed_step_onepass.argtypes = lib.se_soft_embed_step.argtypes
     lib.se_soft_embed_step_fp8.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, i64, i64, i64, f32,
                                            vp, i64, vp, vp, vp, vp, vp, sz, vp]
-    for fn in ("se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
+    lib.se_soft_embed_splits.argtypes = [i64, i64, i64, i64]
+    lib.se_soft_embed_splits.restype = i64
+    lib.se_set_launch_events.argtypes = [vp, i32]
+    lib.se_launch_events_used.argtypes = []
+    lib.se_launch_events_used.restype = i32
+    for fn in ("se_set_launch_events", "se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
                "se_accept_converge", "se_reduce_partials", "se_quantize_table_fp8",
                "se_soft_embed_fp8", "se_soft_embed_fp8_fused", "se_soft_embed_onepass",
                "se_merge_slices", "se_soft_embed_staged", "se_soft_embed_step",
@@ -156,6 +162,19 @@ def se_probs_bf16(logits, row_lse, vocab_start, vocab_end, probs, *, vocab=None,
 
 def se_soft_embed_workspace_bytes(n_rows: int, vocab_start: int, vocab_end: int, d: int) -> int:
     return int(lib.se_soft_embed_workspace_bytes(n_rows, vocab_start, vocab_end, d))
+
+
+def se_soft_embed_splits(n_rows: int, vocab_start: int, vocab_end: int, d: int) -> int:
+    return int(lib.se_soft_embed_splits(n_rows, vocab_start, vocab_end, d))
+
+
+def se_soft_embed_ranges(n_rows: int, vocab_start: int, vocab_end: int, d: int) -> list:
+    """The vocabulary ids [s, b_1, ..., e] bounding the contraction's split ranges (the
+    rule stated in include/softembed.h under se_soft_embed_splits)."""
+    S = se_soft_embed_splits(n_rows, vocab_start, vocab_end, d)
+    K = vocab_end - vocab_start
+    nb = (K + 127) // 128
+    return [vocab_start + min(128 * ((r * nb) // S), K) for r in range(S)] + [vocab_end]
 
 
 def se_soft_embed(probs, vocab_start, vocab_end, w_shard, gamma, out, workspace=None, *,
@@ -368,3 +387,21 @@ def se_soft_embed_step(logits, vocab_start, vocab_end, w_shard, gamma, out, row_
         _ptr(logits), _ld(logits), n, vocab, vocab_start, vocab_end, _ptr(w_shard), w_rows,
         _ld(w_shard), d, float(gamma), _ptr(out), _ld(out), _ptr(row_max), _ptr(row_lse),
         _ptr(row_entropy), _ptr(row_argmax), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def se_set_launch_events(events) -> None:
+    """Arm the calling thread's per-launch timing markers with HIP event handles (ints, e.g.
+    ``torch.cuda.Event.cuda_event`` after a first record); an empty list disarms them.  The
+    handle array is kept alive here until the next call."""
+    global _armed
+    handles = [int(e) for e in events]
+    _armed = (ctypes.c_void_p * max(1, len(handles)))(*handles)
+    _check("se_set_launch_events",
+           lib.se_set_launch_events(_armed if handles else None, len(handles)))
+
+
+def se_launch_events_used() -> int:
+    return int(lib.se_launch_events_used())
+
+
+_armed = None

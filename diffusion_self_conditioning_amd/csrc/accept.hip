@@ -148,7 +148,7 @@ hipError_t launch_accept_converge(const float* row_entropy, const int32_t* row_a
   hipLaunchKernelGGL(accept_converge_kernel, dim3((unsigned)n_canvas), dim3(nt), 0,
                      stream, row_entropy, row_argmax, len, budget, stable_steps, tau, step_limit,
                      accepted, prev_argmax, stable_count, step_count, newly, converged);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 }  // namespace se

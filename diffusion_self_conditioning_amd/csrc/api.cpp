@@ -43,6 +43,27 @@ int device_cu_count() {
   return cu_count[dev];
 }
 
+// ---- launch markers ------------------------------------------------------------------
+// Per-thread list of caller-created HIP events armed by se_set_launch_events; each kernel
+// launch the thread makes afterwards records the next one on the launch's stream.
+namespace {
+struct LaunchMarkers {
+  void* const* events = nullptr;
+  int32_t n = 0;
+  int32_t used = 0;
+};
+thread_local LaunchMarkers t_markers;
+}  // namespace
+
+void mark_launch(hipStream_t stream) {
+  LaunchMarkers& m = t_markers;
+  if (m.events == nullptr || m.used >= m.n) return;
+  if (hipEventRecord(static_cast<hipEvent_t>(m.events[m.used]), stream) == hipSuccess)
+    ++m.used;
+  else
+    (void)hipGetLastError();
+}
+
 // The split count minimises a makespan model of the contraction:
 //   waves(s) * (ceil(kblocks / s) * t_block + t_start) + s * M * N * 8 bytes / partial_rate,
 // where waves(s) = ceil(tiles * s / CUs).  Each workgroup streams one 128-position block of
@@ -299,6 +320,18 @@ const char* se_version(void) {
   return "libsoftembed 0.4 gfx950 (row_stats, probs_bf16, soft_embed bf16-mfma split-K, fused, accept_converge, reduce_partials, e4m3 table, one-pass, staged, step, one-read step)";
 }
 
+se_status se_set_launch_events(void* const* events, int32_t n_events) {
+  if (n_events < 0) return SE_ERR_SHAPE;
+  if (n_events > 0 && events == nullptr) return SE_ERR_NULL;
+  se::LaunchMarkers& m = se::t_markers;
+  m.events = n_events > 0 ? events : nullptr;
+  m.n = n_events;
+  m.used = 0;
+  return SE_OK;
+}
+
+int32_t se_launch_events_used(void) { return se::t_markers.used; }
+
 se_status se_row_stats(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
                        float* row_max, float* row_lse, float* row_entropy, int32_t* row_argmax,
                        void* stream) {
@@ -343,6 +376,12 @@ size_t se_soft_embed_workspace_bytes(int64_t n_rows, int64_t vocab_start, int64_
   if (n_rows > INT32_MAX || d > INT32_MAX || vocab_end > INT32_MAX) return 0;
   if (n_rows == 0 || vocab_end == vocab_start) return 0;
   return se::plan_gemm(n_rows, d, vocab_end - vocab_start).ws_bytes;
+}
+
+int64_t se_soft_embed_splits(int64_t n_rows, int64_t vocab_start, int64_t vocab_end, int64_t d) {
+  if (n_rows < 1 || d < 1 || vocab_start < 0 || vocab_end <= vocab_start) return 0;
+  if (n_rows > INT32_MAX || d > INT32_MAX || vocab_end > INT32_MAX) return 0;
+  return se::plan_gemm(n_rows, d, vocab_end - vocab_start).splits;
 }
 
 se_status se_soft_embed(const uint16_t* probs, int64_t ld_probs, int64_t n_rows, int64_t vocab,

@@ -407,7 +407,7 @@ hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_
                      (int)n_parts, part_stride, n_rows, d, ld_part, part_max, part_lse,
                      part_entropy, part_argmax, out, ld_out, row_max, row_lse, row_entropy,
                      row_argmax);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
@@ -430,7 +430,7 @@ hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
                        n_ranges, probs, st, stat_arg);
   else
     return hipErrorInvalidValue;
-  return hipGetLastError();
+  return launched(stream);
 }
 
 hipError_t launch_merge_ranges(const float* stats, const int32_t* stat_arg, int64_t n_rows,
@@ -442,7 +442,7 @@ hipError_t launch_merge_ranges(const float* stats, const int32_t* stat_arg, int6
   hipLaunchKernelGGL(merge_ranges_kernel, grid, dim3(kMergeRangesThreads), 0, stream,
                      reinterpret_cast<const float4*>(stats), stat_arg, n_rows, n_ranges, r0,
                      splits, gamma, factors, row_max, row_lse, row_entropy, row_argmax);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int64_t K,
@@ -461,7 +461,7 @@ hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int
     hipLaunchKernelGGL(split_sweep_kernel<false>, grid, dim3(kSweepThreads), 0, stream, logits,
                        ld, col0, K, n_rows, splits, kblocks, probs,
                        reinterpret_cast<float4*>(stats), stat_arg, rows_pad);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 }  // namespace se

@@ -51,7 +51,7 @@ hipError_t launch_probs_bf16(const float* logits, int64_t ld, const float* row_l
   const dim3 grid((unsigned)((groups + kProbThreads - 1) / kProbThreads), (unsigned)n_rows);
   hipLaunchKernelGGL(probs_bf16_kernel<false>, grid, dim3(kProbThreads), 0, stream, logits, ld,
                      row_lse, col0, K, probs, ldp, n_rows, (int64_t)0);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 hipError_t launch_probs_bf16_tiled(const float* logits, int64_t ld, const float* row_lse,
@@ -64,7 +64,7 @@ hipError_t launch_probs_bf16_tiled(const float* logits, int64_t ld, const float*
     const dim3 grid((unsigned)((groups + kProbThreads - 1) / kProbThreads), (unsigned)nr);
     hipLaunchKernelGGL(probs_bf16_kernel<true>, grid, dim3(kProbThreads), 0, stream, logits, ld,
                        row_lse, col0, K, probs, (int64_t)0, n_rows, r0);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launched(stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

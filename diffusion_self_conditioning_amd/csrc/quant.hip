@@ -84,7 +84,7 @@ hipError_t launch_quantize_fp8(const uint16_t* w, int64_t ldw, int64_t rows, int
   const int64_t blocks = (rows + kQuantRows - 1) / kQuantRows;
   hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
                      w, ldw, rows, (int)d, codes, ldq, row_scale);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 }  // namespace se

@@ -45,7 +45,7 @@ hipError_t launch_reduce_parts(const float* parts, int64_t n_parts, int64_t part
   const dim3 grid((unsigned)((d / 4 + kReduceThreads - 1) / kReduceThreads), (unsigned)n_rows);
   hipLaunchKernelGGL(reduce_parts_kernel, grid, dim3(kReduceThreads), 0, stream, parts, n_parts,
                      part_stride, d, ld_part, out, ld_out, out_bf16, ld_bf16);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 }  // namespace se

@@ -294,7 +294,7 @@ hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int
   hipLaunchKernelGGL((row_stats_kernel<false, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
                      stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax,
                      (int64_t)0, (int64_t)0, nullptr, n_rows);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 hipError_t launch_row_stats_probs(const float* logits, int64_t ld, int64_t n_rows, int vocab,
@@ -315,7 +315,7 @@ hipError_t launch_row_stats_probs(const float* logits, int64_t ld, int64_t n_row
     hipLaunchKernelGGL((row_stats_kernel<true, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
                        stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax, col0,
                        K, probs, n_rows);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 }  // namespace se

@@ -8,6 +8,17 @@
 
 namespace se {
 
+// ---- launch markers (se_set_launch_events) ----------------------------------------------
+// Records the calling thread's next armed event, if any, on `stream` (right after a kernel
+// launch on that stream).
+void mark_launch(hipStream_t stream);
+// The status of the launch just made; a successful launch is then marked.
+inline hipError_t launched(hipStream_t stream) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) mark_launch(stream);
+  return e;
+}
+
 // ---- work decomposition of the slice contraction (pure host logic) -------------
 // The output [M, N] is cut into BM x BN tiles; the contracted (vocab) axis into
 // blocks of kSplitQuantum positions, and the blocks of each tile into `splits`

@@ -1095,12 +1095,12 @@ hipError_t launch_soft_embed(const GemmParams& p, bool fused, bool w8, hipStream
   else if (fused) launch_contraction<true, false>(p, stream);
   else if (w8) launch_contraction<false, true>(p, stream);
   else launch_contraction<false, false>(p, stream);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launched(stream);
   if (e != hipSuccess || p.splits == 1 || p.keep_partials) return e;
   const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(kReduceThreads), 0, stream, p.ws,
                      p.tiles, p.tiles_n, p.splits, p.M, p.N, p.gamma, p.out, p.ldo);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 hipError_t launch_onepass_reduce(const GemmParams& p, float* row_max, float* row_lse,
@@ -1111,21 +1111,21 @@ hipError_t launch_onepass_reduce(const GemmParams& p, float* row_max, float* row
                      reinterpret_cast<const float4*>(p.stats), p.stat_arg, p.rows_pad, p.tiles,
                      p.tiles_n, p.splits, p.M, p.N, p.gamma, col0, p.out, p.ldo, row_max,
                      row_lse, row_entropy, row_argmax);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 hipError_t launch_scaled_reduce(const GemmParams& p, const float* factors, hipStream_t stream) {
   const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));
   hipLaunchKernelGGL(scaled_reduce_kernel, dim3(blocks), dim3(kReduceThreads), 0, stream, p.ws,
                      factors, p.rows_pad, p.tiles, p.tiles_n, p.splits, p.M, p.N, p.out, p.ldo);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 hipError_t launch_zero_rows(float* out, int64_t ldo, int64_t M, int64_t N, hipStream_t stream) {
   const int64_t groups = (N + 3) / 4;
   const dim3 grid((unsigned)((groups + 255) / 256), (unsigned)M);
   hipLaunchKernelGGL(zero_rows_kernel, grid, dim3(256), 0, stream, out, ldo, N);
-  return hipGetLastError();
+  return launched(stream);
 }
 
 }  // namespace se

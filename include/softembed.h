@@ -36,7 +36,8 @@
  *    shape on that many CUs), and every reduction runs in a fixed order.
  *  - The only global state is a per-device cache of that CU count, read once per
  *    device (std::call_once) from the HIP runtime; without a usable device the
- *    MI355X count, 256, is used.
+ *    MI355X count, 256, is used.  Besides it, each thread has its own list of
+ *    timing markers (se_set_launch_events), empty unless the thread arms it.
  *  - Logits must be finite (not checked on the device).
  *  - n_rows == 0 is a no-op that checks only sizes; its pointers may be NULL.
  *  - Calls are thread-safe and capture-safe (no allocation, no sync, no host
@@ -57,7 +58,19 @@ typedef enum {
     SE_OK = 0,
     SE_ERR_NULL = 1,      /* a required pointer is NULL                                  */
     SE_ERR_SHAPE = 2,     /* negative/zero size where one is required, ld too small,      */
-                          /* vocab or d above INT32_MAX                                   */
+                          /* vocab or d above INT32_MAX, or a buffer the kernels address  */
+                          /* with 32-bit byte offsets reaching 4 GiB (2^32 bytes):        */
+                          /*  - the staged bf16 probabilities of the staged, step and    */
+                          /*    one-pass calls, n_rows * ceil((e - s) / 128) * 256 bytes  */
+                          /*    (at e - s = 262,144: at most 8,191 rows per call);        */
+                          /*  - the shard slice, (e - s) * ld_w * element size (2 for     */
+                          /*    bf16, 1 for e4m3 codes);                                  */
+                          /*  - one 256-row tile of the probability operand of            */
+                          /*    se_soft_embed / se_soft_embed_fused and their e4m3 forms, */
+                          /*    255 * ld * element size + (e - s) * element size (fp32    */
+                          /*    logits: 4, bf16 probabilities: 2);                        */
+                          /*  - a one-pass slice of logits, (e - s) * 4 bytes.            */
+                          /* Larger work is split into several calls by rows or slices.   */
     SE_ERR_SLICE = 3,     /* not 0 <= vocab_start <= vocab_end <= vocab, or the slice is  */
                           /* longer than the shard (vocab_end - vocab_start > w_rows)     */
     SE_ERR_ALIGN = 4,     /* pointer not 16-byte aligned, a row pitch not a multiple of   */
@@ -71,6 +84,28 @@ const char* se_status_string(se_status s);
 
 /* Number of kernels / version, for diagnostics. */
 const char* se_version(void);
+
+/*
+ * se_set_launch_events -- per-kernel timing markers for the calling thread.
+ *
+ * events: n_events HIP events (hipEvent_t, passed as void*), created by the caller
+ * (with timing enabled, to read durations) and owned by it; they must stay valid until
+ * the markers are disarmed or exhausted.  After this call, every kernel launch the
+ * calling thread makes through this library records the next event of the list on the
+ * launch's stream, right after the launch, until n_events have been recorded; later
+ * launches record nothing.  An entry point that makes k launches thus records k events
+ * in launch order, and the time from the previous marker (or an event the caller
+ * recorded just before the call) to marker j is kernel j plus the gap before it.
+ * n_events == 0 (events may then be NULL) disarms the markers.  The markers are
+ * thread-local: other threads' calls are unaffected.  A failed record is skipped
+ * silently (the event is not counted).  Not for use under graph capture.
+ * Errors: SE_ERR_SHAPE if n_events < 0; SE_ERR_NULL if events is NULL with
+ * n_events > 0.
+ */
+se_status se_set_launch_events(void* const* events, int32_t n_events);
+
+/* Markers recorded since the calling thread last armed them with se_set_launch_events. */
+int32_t se_launch_events_used(void);
 
 /*
  * se_row_stats -- softmax statistics of each logits row over the full width.
@@ -118,6 +153,19 @@ se_status se_probs_bf16(const float* logits, int64_t ld_logits, const float* row
  */
 size_t se_soft_embed_workspace_bytes(int64_t n_rows, int64_t vocab_start, int64_t vocab_end,
                                      int64_t d);
+
+/*
+ * se_soft_embed_splits -- the number S of vocabulary ranges the contraction cuts the
+ * slice [s, e) into for this shape on the current device (split-K; 0 for shapes the
+ * calls would reject or that have nothing to contract).  With nb = ceil((e - s) / 128)
+ * blocks of 128 positions, range r holds the slice positions
+ *     [128 floor(r nb / S), min(128 floor((r + 1) nb / S), e - s)),   r = 0 .. S-1.
+ * Every contraction adds its ranges' partial products in the order r = 0 .. S-1; the
+ * one-read calls (se_soft_embed_onepass, se_soft_embed_step_onepass) also normalise each
+ * range's probabilities against that range's own maximum, so their roundings follow these
+ * ranges.
+ */
+int64_t se_soft_embed_splits(int64_t n_rows, int64_t vocab_start, int64_t vocab_end, int64_t d);
 
 /*
  * se_soft_embed -- gamma * P[:, s:e] W_shard[0:e-s, :] from materialised bf16

@@ -9,6 +9,7 @@ Functions
 ---------
 row_stats(logits)                      -> dict(max, argmax, lse, entropy)  (fp64 / int32)
 soft_embed(logits, s, e, w, gamma, ..) -> ndarray [rows, d] fp64
+soft_embed_ranges(logits, bounds, w, gamma, ..) -> the same, range by range (one-read form)
 round_bf16(x)                          -> fp64 values rounded to bfloat16 (RNE)
 """
 from __future__ import annotations
@@ -45,6 +46,9 @@ def _load():
         lib.oracle_soft_embed.argtypes = [p, i64, i64, i64, i64, i64, p, p, i64, i64,
                                           ctypes.c_double, ctypes.c_int, p, i64]
         lib.oracle_soft_embed.restype = ctypes.c_int
+        lib.oracle_soft_embed_ranges.argtypes = [p, i64, i64, i64, i64, i64, p, i64, p, p, i64,
+                                                 i64, ctypes.c_double, ctypes.c_int, p, i64]
+        lib.oracle_soft_embed_ranges.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16.restype = ctypes.c_double
         _lib = lib
@@ -106,6 +110,37 @@ def soft_embed(logits: np.ndarray, vocab_start: int, vocab_end: int, w: np.ndarr
                                    wf, wb, ldw, d, g, int(bool(round_p_bf16)), _ptr(out), d)
     if rc:
         raise ValueError(f"oracle_soft_embed failed ({rc})")
+    return out
+
+
+def soft_embed_ranges(logits: np.ndarray, bounds, w: np.ndarray, gamma: float,
+                      round_q_bf16: bool = False) -> np.ndarray:
+    """gamma * softmax(logits)[:, s:e] @ w[: e - s] formed range by range: ``bounds`` =
+    [s, b_1, ..., e] (vocab ids); range r's probabilities are e^(l - m_r) against the
+    range's own maximum m_r (optionally rounded to bf16), rescaled by e^(m_r - lse)."""
+    x = _rows(logits)
+    n, v = x.shape
+    b = np.ascontiguousarray(np.asarray(bounds, dtype=np.int64))
+    s, e = int(b[0]), int(b[-1])
+    w = np.asarray(w)
+    if w.ndim != 2 or w.strides[1] != w.itemsize:
+        w = np.ascontiguousarray(w)
+    if w.shape[0] < e - s:
+        raise ValueError("table shard shorter than the slice")
+    d = w.shape[1]
+    out = np.empty((n, d))
+    g = float(np.float32(gamma))
+    if w.dtype == np.float32:
+        wf, wb = _ptr(w), None
+    elif w.dtype == np.uint16:
+        wf, wb = None, _ptr(w)
+    else:
+        raise TypeError("table must be float32 or uint16 (bf16 bits)")
+    rc = _load().oracle_soft_embed_ranges(_ptr(x), x.strides[0] // 4, n, v, s, e, _ptr(b),
+                                          b.size - 1, wf, wb, w.strides[0] // w.itemsize, d, g,
+                                          int(bool(round_q_bf16)), _ptr(out), d)
+    if rc:
+        raise ValueError(f"oracle_soft_embed_ranges failed ({rc})")
     return out
 
 

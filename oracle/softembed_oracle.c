@@ -135,3 +135,73 @@ int oracle_soft_embed(const float* logits, int64_t ld, int64_t n_rows, int64_t v
     }
     return bad;
 }
+
+/* Soft embedding of rows of `logits` over the slice [s, e), computed range by range as
+ * the one-read step forms it (each range's probabilities taken against the range's own
+ * maximum, the ranges rescaled to the full row's log-sum-exp; calvarado04.com, "The
+ * fix": the product split over disjoint vocabulary pieces and summed):
+ *
+ *   lse        = log-sum-exp of the FULL row
+ *   m_r        = max of l over range r = [bounds[r], bounds[r+1])
+ *   q_v        = exp(l_v - m_r)            (rounded to bf16 if round_q_bf16)
+ *   out_i,:    = gamma * sum_r exp(m_r - lse) * sum_{v in range r} q_v W[v - s, :]
+ *
+ * bounds holds n_ranges + 1 increasing vocab ids with bounds[0] = s and
+ * bounds[n_ranges] = e.  Without rounding this is oracle_soft_embed's result up to the
+ * order of fp64 roundings.  With rounding it is a diagnostic of a kernel that rounds
+ * e^(l - m_r) to bf16 before an fp32 contraction.  Returns 0 on success. */
+int oracle_soft_embed_ranges(const float* logits, int64_t ld, int64_t n_rows, int64_t vocab,
+                             int64_t s, int64_t e, const int64_t* bounds, int64_t n_ranges,
+                             const float* w_f32, const uint16_t* w_bf16, int64_t ld_w,
+                             int64_t d, double gamma, int round_q_bf16, double* out,
+                             int64_t ld_out)
+{
+    if ((w_f32 == NULL) == (w_bf16 == NULL)) return 2;
+    if (s < 0 || e < s || e > vocab || n_ranges < 1) return 3;
+    if (bounds[0] != s || bounds[n_ranges] != e) return 4;
+    for (int64_t r = 0; r < n_ranges; ++r)
+        if (bounds[r + 1] <= bounds[r]) return 4;
+    int bad = 0;
+#pragma omp parallel reduction(|| : bad)
+    {
+        double* acc = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+        double* tot = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            const float* x = logits + i * ld;
+            double m = (double)x[0];
+            for (int64_t v = 0; v < vocab; ++v) {
+                if (!isfinite(x[v])) bad = 1;
+                if ((double)x[v] > m) m = (double)x[v];
+            }
+            double z = 0.0;
+            for (int64_t v = 0; v < vocab; ++v) z += exp((double)x[v] - m);
+            double lse = m + log(z);
+            for (int64_t j = 0; j < d; ++j) tot[j] = 0.0;
+            for (int64_t r = 0; r < n_ranges; ++r) {
+                double mr = (double)x[bounds[r]];
+                for (int64_t v = bounds[r]; v < bounds[r + 1]; ++v)
+                    if ((double)x[v] > mr) mr = (double)x[v];
+                for (int64_t j = 0; j < d; ++j) acc[j] = 0.0;
+                for (int64_t v = bounds[r]; v < bounds[r + 1]; ++v) {
+                    double q = exp((double)x[v] - mr);
+                    if (round_q_bf16) q = oracle_round_bf16(q);
+                    int64_t k = v - s;
+                    if (w_f32) {
+                        const float* wr = w_f32 + k * ld_w;
+                        for (int64_t j = 0; j < d; ++j) acc[j] += q * (double)wr[j];
+                    } else {
+                        const uint16_t* wr = w_bf16 + k * ld_w;
+                        for (int64_t j = 0; j < d; ++j) acc[j] += q * bf16_bits_value(wr[j]);
+                    }
+                }
+                double f = exp(mr - lse);
+                for (int64_t j = 0; j < d; ++j) tot[j] += f * acc[j];
+            }
+            for (int64_t j = 0; j < d; ++j) out[i * ld_out + j] = gamma * tot[j];
+        }
+        free(acc);
+        free(tot);
+    }
+    return bad;
+}

@@ -38,7 +38,7 @@ def test_every_entry_point_has_declared_argument_types():
     for n in b.EXPORTS:
         fn = getattr(lib, n)
         assert fn.argtypes is not None, n
-        decl = re.search(r"(?:se_status|size_t|const char\*)\s+" + n + r"\s*\(([^)]*)\)",
+        decl = re.search(r"(?:se_status|size_t|int32_t|int64_t|const char\*)\s+" + n + r"\s*\(([^)]*)\)",
                          open(HEADER).read())
         params = [x for x in decl.group(1).split(",") if x.strip() not in ("", "void")]
         assert len(fn.argtypes) == len(params), n
@@ -449,3 +449,49 @@ def test_step_fp8_errors():
     assert call(ws_bytes=1024) == b.SE_ERR_WORKSPACE
     assert call(n=0, x=None, w=None, sc=None, out=None, mx=None, lse=None, ent=None, am=None,
                 ws=None, ws_bytes=0) == b.SE_OK
+
+
+def test_32bit_offset_limits_both_sides():
+    """The kernels address staged probabilities, a split's shard rows and a 256-row tile of the
+    probability operand with 32-bit byte offsets, so each must stay below 4 GiB; at the limit the
+    calls return SE_ERR_SHAPE, just below it they pass the check and stop at the (empty)
+    workspace."""
+    step = lib.se_soft_embed_step
+
+    def call_step(n=256, s=0, e=262144, ldw=2816, d=2816):
+        return step(P1, 262144, n, 262144, s, e, P3, e - s, ldw, d, 53.0, P4, 2816, P2,
+                    P2 + 1024, P2 + 2048, P2 + 3072, P5, 0, None)
+    # staged bf16 probabilities: n_rows x 262144 positions x 2 bytes
+    assert call_step(n=8191) == b.SE_ERR_WORKSPACE           # 4 GiB - 512 KiB
+    assert call_step(n=8192) == b.SE_ERR_SHAPE               # 4 GiB exactly
+    # the shard slice: (e - s) x ld_w x 2 bytes
+    assert call_step(ldw=8184) == b.SE_ERR_WORKSPACE         # 262144 x 8184 x 2 < 2^32
+    assert call_step(ldw=8192) == b.SE_ERR_SHAPE             # = 2^32
+    fused = lib.se_soft_embed_fused
+
+    def call_fused(ld, ldw=2816, s=65536, e=131072):
+        return fused(P1, ld, P2, 256, 262144, s, e, P3, e - s, ldw, 2816, 53.0, P4, 2816, P5, 0,
+                     None)
+    # one 256-row tile of fp32 logits: 255 x ld x 4 + (e - s) x 4 bytes
+    assert call_fused(4210492) == b.SE_ERR_WORKSPACE
+    assert call_fused(4210496) == b.SE_ERR_SHAPE
+    assert call_fused(262144, ldw=32768) == b.SE_ERR_SHAPE   # 65536 x 32768 x 2 = 2^32
+    assert call_fused(262144, ldw=32760) == b.SE_ERR_WORKSPACE
+
+
+def test_launch_markers_and_split_query():
+    assert lib.se_set_launch_events(None, -1) == b.SE_ERR_SHAPE
+    assert lib.se_set_launch_events(None, 2) == b.SE_ERR_NULL
+    assert lib.se_set_launch_events(None, 0) == b.SE_OK
+    assert b.se_launch_events_used() == 0
+    b.se_set_launch_events([])
+    # the contraction's split ranges (the header's rule); without a device 256 CUs are assumed
+    S = b.se_soft_embed_splits(256, 65536, 131072, 2816)
+    assert S == 23
+    r = b.se_soft_embed_ranges(256, 65536, 131072, 2816)
+    assert len(r) == S + 1 and r[0] == 65536 and r[-1] == 131072
+    assert all(128 * 22 <= y - x <= 128 * 23 for x, y in zip(r, r[1:]))
+    assert all((x - 65536) % 128 == 0 for x in r[:-1])
+    assert b.se_soft_embed_splits(16, 0, 64, 256) == 1
+    assert b.se_soft_embed_ranges(16, 0, 100, 256) == [0, 100]
+    assert b.se_soft_embed_splits(0, 0, 64, 256) == 0 and b.se_soft_embed_splits(4, 8, 8, 16) == 0

@@ -292,3 +292,81 @@ def test_page_figures():
 def test_gamma_is_fp32_sqrt_d():
     assert wl.get("full").gamma == float(np.float32(math.sqrt(2816)))
     assert Fraction(wl.get("tiny").gamma) == 16
+
+
+# --- the range-wise form used to check the one-read calls --------------------------
+def _bf16_py(x: float) -> float:
+    """Nearest bf16 value (8 significant bits, ties to even) of a positive normal double,
+    written with Python's round-half-even on the exact scaled significand."""
+    if x == 0.0:
+        return 0.0
+    m, e = math.frexp(x)                 # x = m 2^e, m in [0.5, 1)
+    return math.ldexp(round(m * 256.0), e - 8)
+
+
+def _brute_ranges(xrow, table, bounds, gamma, d, rnd):
+    m = max(xrow)
+    lse = m + math.log(math.fsum(math.exp(v - m) for v in xrow))
+    s = bounds[0]
+    out = [0.0] * d
+    for a, b in zip(bounds, bounds[1:]):
+        mr = max(xrow[a:b])
+        qs = [math.exp(xrow[v] - mr) for v in range(a, b)]
+        if rnd:
+            qs = [_bf16_py(q) for q in qs]
+        f = math.exp(mr - lse)
+        for j in range(d):
+            out[j] += f * math.fsum(q * table[a + t - s][j] for t, q in enumerate(qs))
+    return [gamma * o for o in out]
+
+
+def test_ranges_brute_force_small():
+    """Each range's probabilities against its own maximum, rescaled by e^(m_r - lse): the
+    oracle's range-wise form against a pure-Python evaluation, with and without bf16
+    rounding of e^(l - m_r)."""
+    rng = np.random.default_rng(21)
+    for L in (1, 3):
+        for V in (5, 9, 16):
+            d = 3
+            x = (rng.standard_normal((L, V)) * 2).astype(np.float32)
+            table = rng.integers(-3, 4, size=(V, d)).astype(np.float32) / np.float32(4)
+            for bounds in ([0, V], [0, 2, V], [1, 3, V - 1], [2, 3, 4, V]):
+                s, e = bounds[0], bounds[-1]
+                for rnd in (False, True):
+                    out = oracle.soft_embed_ranges(x, bounds, table[s:], 1.5, round_q_bf16=rnd)
+                    for i in range(L):
+                        bo = _brute_ranges([float(t) for t in x[i]],
+                                           [[float(t) for t in r] for r in table[s:]],
+                                           bounds, 1.5, d, rnd)
+                        np.testing.assert_allclose(out[i], bo, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("bounds", [[0, 4096], [0, 128, 2048, 4096], [256, 1024, 1152, 3072]])
+def test_ranges_without_rounding_are_the_partition_identity(bounds):
+    """Page 1, 'The fix': the product over a slice is the sum of the products over any
+    partition of it; rescaling each piece's softmax numerators changes nothing exactly."""
+    w = wl.get("tiny")
+    x = wl.make_logits(w.diffuse())[:5]
+    bits, _ = wl.make_table(w)
+    s, e = bounds[0], bounds[-1]
+    got = oracle.soft_embed_ranges(x, bounds, bits[s:], w.gamma)
+    want = oracle.soft_embed(x, s, e, bits[s:], w.gamma)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_ranges_one_hot_and_uniform():
+    """A point mass in range r gives q = 1 there (exact in bf16) and gamma W_k; uniform logits
+    give q = 1 everywhere and gamma times the column mean, with or without rounding."""
+    V, d, gamma = 1024, 16, np.float32(53.065998)
+    table = _bf16_table(V, d)
+    bounds = [0, 256, 512, 896, 1024]
+    x = wl.one_hot_logits(2, V, [300, 1000])
+    for rnd in (False, True):
+        out = oracle.soft_embed_ranges(x, bounds, table, gamma, round_q_bf16=rnd)
+        for i, k in enumerate([300, 1000]):
+            np.testing.assert_allclose(out[i], float(gamma) * _table_values(table[k]),
+                                       rtol=1e-13, atol=1e-80)
+        u = oracle.soft_embed_ranges(wl.uniform_logits(1, V, 0.25), bounds, table, gamma,
+                                     round_q_bf16=rnd)
+        np.testing.assert_allclose(u[0], float(gamma) * _table_values(table).mean(axis=0),
+                                   rtol=1e-12, atol=1e-15)
