@@ -226,6 +226,15 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
                          int64_t s, int64_t e, const void* w, const float* w_scale, int64_t ldw,
                          int64_t d, float gamma, float* out, int64_t ld_out, void* ws,
                          size_t ws_bytes, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (e == s) {
+    for (int64_t r0 = 0; r0 < n_rows; r0 += kMaxGridY) {
+      const int64_t nr = (n_rows - r0) < kMaxGridY ? (n_rows - r0) : kMaxGridY;
+      se_status rc = from_hip(se::launch_zero_rows(out + r0 * ld_out, ld_out, nr, d, st));
+      if (rc != SE_OK) return rc;
+    }
+    return SE_OK;
+  }
   const se::GemmPlan g = se::plan_gemm(n_rows, d, e - s);
   if (g.grid > INT32_MAX) return SE_ERR_SHAPE;
   // the kernels address one tile's rows of `a` and a split's rows of the shard with
@@ -238,15 +247,6 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
   if (ws_bytes < g.ws_bytes) return SE_ERR_WORKSPACE;
   if (g.ws_bytes > 0 && (ws == nullptr)) return SE_ERR_NULL;
   if (g.ws_bytes > 0 && !aligned16(ws)) return SE_ERR_ALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (e == s) {
-    for (int64_t r0 = 0; r0 < n_rows; r0 += kMaxGridY) {
-      const int64_t nr = (n_rows - r0) < kMaxGridY ? (n_rows - r0) : kMaxGridY;
-      se_status rc = from_hip(se::launch_zero_rows(out + r0 * ld_out, ld_out, nr, d, st));
-      if (rc != SE_OK) return rc;
-    }
-    return SE_OK;
-  }
   se::GemmParams p{};
   p.a = a;
   p.lda = lda;
@@ -460,16 +460,16 @@ se_status se_soft_embed_staged(const float* logits, int64_t ld_logits, const flo
 
 }  // extern "C"
 
-namespace {
-// The whole step: statistics (with the slice's staged probabilities), then the
-// contraction of the staged probabilities against a bf16 table, or an e4m3 table with
-// per-row scales when w_scale is given.
-se_status run_step(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
-                   int64_t vocab_start, int64_t vocab_end, const void* w_shard,
-                   const float* w_scale, int64_t w_rows, int64_t ld_w, int64_t d, float gamma,
-                   float* out, int64_t ld_out, float* row_max, float* row_lse,
-                   float* row_entropy, int32_t* row_argmax, void* workspace,
-                   size_t workspace_bytes, void* stream, bool w8) {
+namespace se {
+// Every check of the whole step that needs neither the workspace nor the device: sizes,
+// the slice, pointers, alignment and the 32-bit offset limits.  SE_OK for n_rows == 0
+// once the sizes are valid.
+se_status check_step(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
+                     int64_t vocab_start, int64_t vocab_end, const void* w_shard,
+                     const float* w_scale, int64_t w_rows, int64_t ld_w, int64_t d,
+                     const float* out, int64_t ld_out, const float* row_max,
+                     const float* row_lse, const float* row_entropy, const int32_t* row_argmax,
+                     bool w8) {
   se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
   if (rc != SE_OK) return rc;
   if (ld_logits < vocab) return SE_ERR_SHAPE;
@@ -485,6 +485,31 @@ se_status run_step(const float* logits, int64_t ld_logits, int64_t n_rows, int64
   if (!aligned16(logits) || (ld_logits % 4) != 0) return SE_ERR_ALIGN;
   if (!aligned4(row_max) || !aligned4(row_lse) || !aligned4(row_entropy) || !aligned4(row_argmax))
     return SE_ERR_ALIGN;
+  const int64_t K = vocab_end - vocab_start;
+  if (K == 0) return SE_OK;
+  const se::StagedLayout o = se::staged_layout(n_rows, K, d);
+  if (o.g.grid > INT32_MAX) return SE_ERR_SHAPE;
+  if ((int64_t)se::tiled_probs_bytes(n_rows, K) > (int64_t)UINT32_MAX ||
+      K * ld_w * (w8 ? 1 : 2) > (int64_t)UINT32_MAX)
+    return SE_ERR_SHAPE;
+  return SE_OK;
+}
+}  // namespace se
+
+namespace {
+// The whole step: statistics (with the slice's staged probabilities), then the
+// contraction of the staged probabilities against a bf16 table, or an e4m3 table with
+// per-row scales when w_scale is given.
+se_status run_step(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
+                   int64_t vocab_start, int64_t vocab_end, const void* w_shard,
+                   const float* w_scale, int64_t w_rows, int64_t ld_w, int64_t d, float gamma,
+                   float* out, int64_t ld_out, float* row_max, float* row_lse,
+                   float* row_entropy, int32_t* row_argmax, void* workspace,
+                   size_t workspace_bytes, void* stream, bool w8) {
+  se_status rc = se::check_step(logits, ld_logits, n_rows, vocab, vocab_start, vocab_end,
+                                w_shard, w_scale, w_rows, ld_w, d, out, ld_out, row_max, row_lse,
+                                row_entropy, row_argmax, w8);
+  if (rc != SE_OK || n_rows == 0) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t K = vocab_end - vocab_start;
   if (K == 0) {                       // statistics, and zeros for the empty slice
@@ -496,10 +521,6 @@ se_status run_step(const float* logits, int64_t ld_logits, int64_t n_rows, int64
                           workspace, workspace_bytes, stream);
   }
   const se::StagedLayout o = se::staged_layout(n_rows, K, d);
-  if (o.g.grid > INT32_MAX) return SE_ERR_SHAPE;
-  if ((int64_t)se::tiled_probs_bytes(n_rows, K) > (int64_t)UINT32_MAX ||
-      K * ld_w * (w8 ? 1 : 2) > (int64_t)UINT32_MAX)
-    return SE_ERR_SHAPE;
   if (workspace_bytes < o.total) return SE_ERR_WORKSPACE;
   if (!workspace) return SE_ERR_NULL;
   if (!aligned16(workspace)) return SE_ERR_ALIGN;

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/softembed.h"
+
 namespace se {
 
 // ---- launch markers (se_set_launch_events) ----------------------------------------------
@@ -98,6 +100,14 @@ struct GemmParams {
   const int32_t* stat_arg;
   int64_t rows_pad;
 };
+
+// The host-side checks of se_soft_embed_step (and its e4m3 form, w8) short of the workspace.
+se_status check_step(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,
+                     int64_t vocab_start, int64_t vocab_end, const void* w_shard,
+                     const float* w_scale, int64_t w_rows, int64_t ld_w, int64_t d,
+                     const float* out, int64_t ld_out, const float* row_max,
+                     const float* row_lse, const float* row_entropy, const int32_t* row_argmax,
+                     bool w8);
 
 hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int vocab,
                             float* row_max, float* row_lse, float* row_entropy,
