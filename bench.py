@@ -394,6 +394,9 @@ def main():
     ap.add_argument("--side-workloads", default="rank,conv,batch",
                     help="comma-separated workloads timed beside the main one on their fastest "
                          "paths ('' for none)")
+    ap.add_argument("--minimal", action="store_true",
+                    help="only the headline steps (warmup, timed steps, per-kernel times): for "
+                         "profiling runs; no side paths, side workloads or CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference for scaling the HBM byte counters), then exit")
@@ -442,6 +445,17 @@ def main():
     st = Step(w, x_np, bits, dev)
     L, d = w.rows, w.d
     flops = w.flops()
+
+    if args.minimal:
+        say(f"warmup {W}, {K} timed steps ({path})")
+        rep = step_report(st, path, K, W)
+        print(json.dumps({"metric": METRIC, "value": rep["gflops"], "unit": "GFLOP/s",
+                          "n_gpus": 1, "steps": K, "warmup": W,
+                          "ms_per_step": rep["ms_per_step"], "minimal": True,
+                          "config": {"workload": w.name, "path": path},
+                          "kernel_us": rep["kernel_us"], "roofline": rep["roofline"]}),
+              flush=True)
+        return
 
     # every path once on the same inputs, event-timed as whole steps (these run before the
     # headline's warmup, so the timed steps below see a GPU that has been under load)

@@ -110,7 +110,7 @@ size_t tiled_probs_bytes(int64_t n_rows, int64_t K) {
 int sweep_waves(const GemmPlan& g, int64_t K) {
   if (K <= 0) return 0;
   const int64_t longest = std::min(((g.kblocks + g.splits - 1) / g.splits) * kSplitQuantum, K);
-  for (int w : {1, 2, 4})
+  for (int w : {1, 2, 4, 8})
     if (longest <= kSweepPiece * (int64_t)w) return w;
   return 0;
 }
@@ -136,7 +136,7 @@ OnepassLayout onepass_layout(int64_t n_rows, int64_t K, int64_t d) {
 // Workspace of the one-read step: tiled bf16 probabilities of the slice, the split
 // partials (kept even for one split), per-(range, row) statistics and argmax, and the
 // per-(split, row) factors.  sweep_waves = 0 when the slice is empty or a split range
-// is longer than 4 waves hold in registers (4 * kSweepPiece positions); the call is then
+// is longer than 8 waves hold in registers (8 * kSweepPiece positions); the call is then
 // the two-pass step and the workspace is that call's.
 struct StepOnepassLayout {
   GemmPlan g;

@@ -13,9 +13,10 @@
 // split by e^(m_s - M), M = max_s m_s, and divides by Z = sum_s e^(m_s - M) Z_s: the
 // merge rule of the partition identity ("The fix") written for softmax numerators.
 //
-// One workgroup per (row, split range): a first pass reads the range once from memory
-// and finds its maximum and first position; a second pass over the same values, kept
-// in LDS, forms the probabilities, writes them as bf16 and sums Z_s and S1_s in fp32.
+// One workgroup per (row, split range), for split ranges longer than the register sweep
+// below holds: a first pass reads the range and finds its maximum and first position; a
+// second pass reads it again, forms the probabilities, writes them as bf16 and sums Z_s
+// and S1_s in fp32.
 #include "se_device.h"
 #include "se_launch.h"
 
@@ -24,10 +25,6 @@ namespace {
 
 constexpr int kSweepThreads = 512;                  // one workgroup per (row, split range)
 constexpr int kSweepWaves = kSweepThreads / 64;
-// The range is kept in LDS between the two passes when it fits (up to 60 KB of fp32,
-// 15,360 positions, within the 64 KB a launch gets by default); longer ranges read the
-// logits again in the second pass.
-constexpr int kSweepLdsMax = 61440;
 
 // whole-wave reductions (64 lanes) on top of the half-wave ones
 __device__ __forceinline__ float wave_sum(float v) {
@@ -44,18 +41,15 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   argmax_step(v, i, v1, i1);
 }
 
-// Pass 1 reads the range (16-byte buffer loads, eight in flight per lane), keeps it in
-// LDS when it fits, and finds the first maximum; pass 2
-// forms the probabilities against it from LDS (or from memory), writes them as bf16
-// and sums Z and S1.  Cross-wave reductions go through a small LDS array in wave
-// order, so the sums are independent of scheduling.
-template <bool KEEP>
+// Pass 1 reads the range (16-byte buffer loads, eight in flight per lane) and finds the
+// first maximum; pass 2 reads it again, forms the probabilities against that maximum,
+// writes them as bf16 and sums Z and S1.  Cross-wave reductions go through a small LDS
+// array in wave order, so the sums are independent of scheduling.
 __global__ void __launch_bounds__(kSweepThreads)
 split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, int64_t K,
                    int64_t n_rows, int splits, int kblocks, uint16_t* __restrict__ probs,
                    float4* __restrict__ stats, int32_t* __restrict__ stat_arg,
                    int64_t rows_pad) {
-  extern __shared__ float4 keep[];                    // the range (KEEP only)
   __shared__ float red_v[kSweepWaves], red_w[kSweepWaves];
   __shared__ int red_i[kSweepWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -95,10 +89,7 @@ split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, i
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int g = base + u * kSweepThreads + tid;
-      if (g < n4) {
-        if constexpr (KEEP) keep[g] = v[u];
-        max4(v[u], 4 * g);
-      }
+      if (g < n4) max4(v[u], 4 * g);
     }
   }
   for (int j = 4 * n4 + tid; j < n; j += kSweepThreads) argmax_step(mv, mi, x[j], j);
@@ -113,9 +104,7 @@ split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, i
   // pass 2
   float z = 0.f, s1 = 0.f;
   for (int g = tid; g < n4; g += kSweepThreads) {
-    float4 v;
-    if constexpr (KEEP) v = keep[g];
-    else v = reinterpret_cast<const float4*>(x)[g];
+    const float4 v = reinterpret_cast<const float4*>(x)[g];
     const float t0 = __builtin_fmaf(v.x, kLog2e, nl), t1 = __builtin_fmaf(v.y, kLog2e, nl);
     const float t2 = __builtin_fmaf(v.z, kLog2e, nl), t3 = __builtin_fmaf(v.w, kLog2e, nl);
     const float q0 = exp2_hw(t0), q1 = exp2_hw(t1), q2 = exp2_hw(t2), q3 = exp2_hw(t3);
@@ -155,7 +144,9 @@ split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, i
 // between the maximum and the sums, and its reductions are the fixed DPP butterflies of
 // a single wave, so no workgroup barrier is involved.
 
-constexpr int kStepSweepThreads = 256;              // four (row, range) items per workgroup
+// A workgroup holds 256 threads (four (row, range) items of 1 wave, two of 2 waves, one of
+// 4), or 512 threads for one item of 8 waves.
+constexpr int sweep_threads(int W) { return W <= 4 ? 256 : 64 * W; }
 #ifndef SE_SWEEP_LOAD
 #define SE_SWEEP_LOAD buffer_load_f4_nt               // the logits are read once
 #endif
@@ -180,7 +171,7 @@ __device__ __forceinline__ void step_range(const StepRanges& g, int r, int64_t& 
   c1 = min(g.vocab, e0 + (int64_t)(r + 1) * g.chunk);
 }
 
-// W wavefronts (1, 2 or 4) of a workgroup share one (row, range); wave k of the group
+// W wavefronts (1, 2, 4 or 8) of a workgroup share one (row, range); wave k of the group
 // takes the k-th of W near-equal, 4-aligned pieces, at most 3072 positions (12 16-byte
 // groups per lane, held in registers between the maximum and the sums).  The group
 // combines its maxima and then its sums through LDS in wave order.
@@ -188,11 +179,11 @@ constexpr int kSweepNF4 = 12;
 static_assert(kSweepPiece == 64 * 4 * kSweepNF4, "a wave holds 12 groups of 4 per lane");
 
 template <int W>
-__global__ void __launch_bounds__(kStepSweepThreads)
+__global__ void __launch_bounds__(sweep_threads(W))
 step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, StepRanges g,
                   int n_ranges, uint16_t* __restrict__ probs, float4* __restrict__ stats,
                   int32_t* __restrict__ stat_arg) {
-  constexpr int kWaves = kStepSweepThreads / 64;
+  constexpr int kWaves = sweep_threads(W) / 64;
   constexpr int NF4 = kSweepNF4;
   __shared__ float grp_v[kWaves], grp_z[kWaves], grp_s[kWaves];
   __shared__ int grp_i[kWaves];
@@ -413,24 +404,22 @@ hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_
 hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
                              const StepRanges& g, int waves, uint16_t* probs, float* stats,
                              int32_t* stat_arg, hipStream_t stream) {
-  if (waves != 1 && waves != 2 && waves != 4) return hipErrorInvalidValue;
   const int n_ranges = g.n_pre + g.splits + g.n_post;
-  const int per_block = (kStepSweepThreads / 64) / waves;    // (row, range) items
-  const dim3 grid((unsigned)((n_rows * n_ranges + per_block - 1) / per_block));
-  const dim3 block(kStepSweepThreads);
   float4* st = reinterpret_cast<float4*>(stats);
-  if (waves == 1)
-    hipLaunchKernelGGL(step_sweep_kernel<1>, grid, block, 0, stream, logits, ld, n_rows, g,
+  auto go = [&](auto kernel, int w) {
+    const int per_block = (sweep_threads(w) / 64) / w;          // (row, range) items
+    const dim3 grid((unsigned)((n_rows * n_ranges + per_block - 1) / per_block));
+    hipLaunchKernelGGL(kernel, grid, dim3(sweep_threads(w)), 0, stream, logits, ld, n_rows, g,
                        n_ranges, probs, st, stat_arg);
-  else if (waves == 2)
-    hipLaunchKernelGGL(step_sweep_kernel<2>, grid, block, 0, stream, logits, ld, n_rows, g,
-                       n_ranges, probs, st, stat_arg);
-  else if (waves == 4)
-    hipLaunchKernelGGL(step_sweep_kernel<4>, grid, block, 0, stream, logits, ld, n_rows, g,
-                       n_ranges, probs, st, stat_arg);
-  else
-    return hipErrorInvalidValue;
-  return launched(stream);
+    return launched(stream);
+  };
+  switch (waves) {
+    case 1: return go(step_sweep_kernel<1>, 1);
+    case 2: return go(step_sweep_kernel<2>, 2);
+    case 4: return go(step_sweep_kernel<4>, 4);
+    case 8: return go(step_sweep_kernel<8>, 8);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_merge_ranges(const float* stats, const int32_t* stat_arg, int64_t n_rows,
@@ -449,18 +438,10 @@ hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int
                               int64_t n_rows, int splits, int kblocks, uint16_t* probs,
                               float* stats, int32_t* stat_arg, int64_t rows_pad,
                               hipStream_t stream) {
-  // the longest split range: kSplitQuantum-position blocks dealt as evenly as possible
-  const int64_t longest = min((int64_t)((kblocks + splits - 1) / splits) * kSplitQuantum, K);
-  const size_t lds = (size_t)(longest / 4) * sizeof(float4);
   const dim3 grid((unsigned)(n_rows * splits));
-  if (lds <= (size_t)kSweepLdsMax)
-    hipLaunchKernelGGL(split_sweep_kernel<true>, grid, dim3(kSweepThreads), lds, stream, logits,
-                       ld, col0, K, n_rows, splits, kblocks, probs,
-                       reinterpret_cast<float4*>(stats), stat_arg, rows_pad);
-  else
-    hipLaunchKernelGGL(split_sweep_kernel<false>, grid, dim3(kSweepThreads), 0, stream, logits,
-                       ld, col0, K, n_rows, splits, kblocks, probs,
-                       reinterpret_cast<float4*>(stats), stat_arg, rows_pad);
+  hipLaunchKernelGGL(split_sweep_kernel, grid, dim3(kSweepThreads), 0, stream, logits, ld, col0,
+                     K, n_rows, splits, kblocks, probs, reinterpret_cast<float4*>(stats),
+                     stat_arg, rows_pad);
   return launched(stream);
 }
 

@@ -61,7 +61,7 @@ struct OnepassLayout {
 // Positions one wave of the sweep holds in registers (12 16-byte groups per lane).
 constexpr int kSweepPiece = 64 * 4 * 12;
 
-// Waves per range (1, 2 or 4) that hold the longest split range of `g`, or 0.
+// Waves per range (1, 2, 4 or 8) that hold the longest split range of `g`, or 0.
 int sweep_waves(const GemmPlan& g, int64_t K);
 
 OnepassLayout onepass_layout(int64_t n_rows, int64_t K, int64_t d);
@@ -157,7 +157,7 @@ struct StepRanges {
 // One read of every logit: per (row, range) maximum, first argmax (a vocabulary id),
 // Z and S1 against the range maximum (stats[r * n_rows + row] = {m, Z, S1 nats, m},
 // stat_arg likewise), and for the slice's split ranges the bf16 probabilities against
-// the range maximum in the super-step-tiled layout.  `waves` (1, 2 or 4) wavefronts
+// the range maximum in the super-step-tiled layout.  `waves` (1, 2, 4 or 8) wavefronts
 // share a range of at most waves * kSweepPiece positions.
 hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
                              const StepRanges& g, int waves, uint16_t* probs, float* stats,

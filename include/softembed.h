@@ -283,8 +283,9 @@ se_status se_soft_embed_step_fp8(const float* logits, int64_t ld_logits, int64_t
  * disjoint vocabulary pieces), applied to softmax numerators.  Results agree with
  * se_soft_embed_step to rounding (argmax and row max exactly), are bitwise repeatable,
  * but are not bitwise those of the two-pass calls.
- * When the slice is empty, or one split range is longer than 12,288 positions (the
- * sweep holds a range in registers), the call is se_soft_embed_step itself.
+ * When the slice is empty, or one split range is longer than 24,576 positions (the
+ * sweep holds a range in the registers of at most 8 wavefronts), the call is
+ * se_soft_embed_step itself.
  * Arguments and errors as se_soft_embed_step, with a workspace of
  * se_soft_embed_step_onepass_workspace_bytes() bytes (16-byte aligned): the bf16
  * slice, the split partials and per-(range, row) statistics.

@@ -61,7 +61,7 @@ hipError_t launch_onepass_reduce(const GemmParams&, float*, float*, float*, int3
                                  hipStream_t s) { return launched_stub(s); }
 hipError_t launch_step_sweep(const float*, int64_t, int64_t, const StepRanges&, int waves,
                              uint16_t*, float*, int32_t*, hipStream_t s) {
-  if (waves != 1 && waves != 2 && waves != 4) return hipErrorInvalidValue;
+  if (waves != 1 && waves != 2 && waves != 4 && waves != 8) return hipErrorInvalidValue;
   return launched_stub(s);
 }
 hipError_t launch_merge_ranges(const float*, const int32_t*, int64_t, int, int, int, float,

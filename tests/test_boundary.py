@@ -379,7 +379,8 @@ def test_step_onepass_workspace_plan_and_errors():
     assert ws(5, 1000, 16, 17, 16) == up(5 * 128 * 2) + up(tile) + up(3 * 5 * 16) + \
         up(3 * 5 * 4) + up(5 * 4)
     assert ws(8, 512, 16, 16, 16) == staged(8, 16, 16, 16) == 0
-    assert ws(4096, 50000, 0, 50000, 1024) == staged(4096, 0, 50000, 1024) > 0
+    assert ws(4096, 110000, 0, 110000, 1024) == staged(4096, 0, 110000, 1024) > 0
+    assert ws(4096, 50000, 0, 50000, 1024) != staged(4096, 0, 50000, 1024)   # 8-wave sweep
     assert ws(0, 1000, 0, 64, 16) == 0 and ws(4, 100, 0, 200, 16) == 0
     st = lib.se_soft_embed_step_onepass
 

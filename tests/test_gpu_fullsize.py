@@ -39,7 +39,7 @@ DEV = "cuda:0"
 GATE, DIAG = 5e-3, 1e-4
 # the one-read step sweeps a split range from registers when it holds at most this many
 # positions; otherwise the call is the two-pass step (include/softembed.h)
-ONE_READ_MAX_RANGE = 4 * 3072
+ONE_READ_MAX_RANGE = 8 * 3072
 
 
 def say(*a):

@@ -130,13 +130,14 @@ def test_onepass_special_rows(kind):
     check_slice(x, 0, V, table(V, d, 12), 3.0)
 
 
-@pytest.mark.parametrize("shape", [(768, 100000, 2816), (4096, 65536, 1024)],
-                         ids=["lds-keep", "read-twice"])
+@pytest.mark.parametrize("shape", [(768, 100000, 2816), (4096, 65536, 1024), (4096, 110000, 1024)],
+                         ids=["eight-waves-14336", "eight-waves-16384", "read-twice"])
 def test_onepass_long_split_ranges(shape):
-    """Split ranges longer than the register sweep holds (12,288 positions) take the
-    workgroup-per-range sweep: 768 rows x 11 n-tiles -> 7 splits of 14,336 positions (kept
-    in LDS between its passes); 4096 rows x 4 n-tiles -> 4 splits of 16,384 (longer than
-    LDS holds: the second pass reads the logits from memory again)."""
+    """Long split ranges: 768 rows x 11 n-tiles -> 7 splits of 14,336 positions and 4096
+    rows x 4 n-tiles -> 4 splits of 16,384 take the register sweep with 8 waves per range;
+    110,000 positions over 4096 rows x 4 n-tiles -> 4 splits of 27,520, longer than 8 waves
+    hold (24,576), take the workgroup-per-range sweep, whose second pass reads the logits
+    again."""
     L, V, d = shape
     rng = np.random.default_rng(17)
     x = (rng.standard_normal((L, V)) * 3).astype(np.float32)

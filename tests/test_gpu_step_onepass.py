@@ -172,11 +172,11 @@ def test_step_onepass_repeatable():
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("shape", [(8, 512, 16, 16, 16), (4096, 50000, 0, 50000, 1024)],
+@pytest.mark.parametrize("shape", [(8, 512, 16, 16, 16), (4096, 110000, 0, 110000, 1024)],
                          ids=["empty-slice", "long-split-ranges"])
 def test_step_onepass_falls_back_to_the_two_pass_step(shape):
-    """An empty slice, or split ranges longer than 12,288 positions (4096 rows x 4
-    n-tiles are 64 tiles; 4 splits of 12,544 positions): the call is se_soft_embed_step,
+    """An empty slice, or split ranges longer than 24,576 positions (4096 rows x 4
+    n-tiles are 64 tiles; 4 splits of 27,520 positions): the call is se_soft_embed_step,
     bit for bit."""
     L, V, s, e, d = shape
     rng = np.random.default_rng(27)
