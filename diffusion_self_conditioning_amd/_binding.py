@@ -28,7 +28,8 @@ EXPORTS = ("se_status_string", "se_version", "se_row_stats", "se_probs_bf16",
            "se_soft_embed_staged", "se_soft_embed_step",
            "se_soft_embed_step_onepass_workspace_bytes", "se_soft_embed_step_onepass",
            "se_soft_embed_step_fp8", "se_set_launch_events", "se_launch_events_used",
-           "se_soft_embed_splits")
+           "se_soft_embed_splits", "se_soft_embed_step_noalloc_max_bytes",
+           "se_soft_embed_step_noalloc")
 
 
 class SoftEmbedError(RuntimeError):
@@ -78,12 +79,16 @@ def _declare(lib):
     lib.se_soft_embed_step_onepass.argtypes = lib.se_soft_embed_step.argtypes
     lib.se_soft_embed_step_fp8.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, i64, i64, i64, f32,
                                            vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.se_soft_embed_step_noalloc_max_bytes.argtypes = []
+    lib.se_soft_embed_step_noalloc_max_bytes.restype = sz
+    lib.se_soft_embed_step_noalloc.argtypes = [vp, i64, i64, i64, i64, i64, vp, i64, i64, i64,
+                                               f32, vp, i64, vp, vp, vp, vp, vp]
     lib.se_soft_embed_splits.argtypes = [i64, i64, i64, i64]
     lib.se_soft_embed_splits.restype = i64
     lib.se_set_launch_events.argtypes = [vp, i32]
     lib.se_launch_events_used.argtypes = []
     lib.se_launch_events_used.restype = i32
-    for fn in ("se_set_launch_events", "se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
+    for fn in ("se_soft_embed_step_noalloc", "se_set_launch_events", "se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
                "se_accept_converge", "se_reduce_partials", "se_quantize_table_fp8",
                "se_soft_embed_fp8", "se_soft_embed_fp8_fused", "se_soft_embed_onepass",
                "se_merge_slices", "se_soft_embed_staged", "se_soft_embed_step",
@@ -405,3 +410,22 @@ def se_launch_events_used() -> int:
 
 
 _armed = None
+
+
+def se_soft_embed_step_noalloc(logits, vocab_start, vocab_end, w_shard, gamma, out, row_max,
+                               row_lse, row_entropy, row_argmax, *, vocab=None, d=None,
+                               w_rows=None, stream=None):
+    """se_soft_embed_step with the library's own device workspace (no allocation)."""
+    w_shard = _as_u16(w_shard)
+    n, v = logits.shape
+    vocab = v if vocab is None else vocab
+    d = w_shard.shape[1] if d is None else d
+    w_rows = w_shard.shape[0] if w_rows is None else w_rows
+    _check("se_soft_embed_step_noalloc", lib.se_soft_embed_step_noalloc(
+        _ptr(logits), _ld(logits), n, vocab, vocab_start, vocab_end, _ptr(w_shard), w_rows,
+        _ld(w_shard), d, float(gamma), _ptr(out), _ld(out), _ptr(row_max), _ptr(row_lse),
+        _ptr(row_entropy), _ptr(row_argmax), _stream(stream)))
+
+
+def se_soft_embed_step_noalloc_max_bytes() -> int:
+    return int(lib.se_soft_embed_step_noalloc_max_bytes())

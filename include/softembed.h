@@ -251,6 +251,33 @@ se_status se_soft_embed_step(const float* logits, int64_t ld_logits, int64_t n_r
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * se_soft_embed_step_noalloc -- se_soft_embed_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a device array owned by the library, of
+ * se_soft_embed_step_noalloc_max_bytes() bytes (128 MiB), one per GPU, held from the
+ * moment the library's code is loaded on that GPU until the process ends.  Its device
+ * address is looked up once per device on the first call there.  The call allocates
+ * nothing and returns exactly what se_soft_embed_step returns for the same arguments with
+ * that array as its workspace.
+ * Arguments: those of se_soft_embed_step without the workspace.
+ * Limit: shapes whose se_soft_embed_staged_workspace_bytes() exceeds the array return
+ * SE_ERR_WORKSPACE and launch nothing (the one-rank shape, 256 rows by a 65,536-position
+ * slice at d = 2,816, needs about 95 MiB; a whole 262,144-position vocabulary does not fit).
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one GPU (on
+ * different streams or threads) race: serialise them.  Nothing in the array needs to
+ * start at any value; it keeps the last call's contents.  SE_ERR_HIP if the array's
+ * address cannot be obtained.  Other errors as se_soft_embed_step.
+ */
+size_t se_soft_embed_step_noalloc_max_bytes(void);
+
+se_status se_soft_embed_step_noalloc(const float* logits, int64_t ld_logits, int64_t n_rows,
+                                     int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                                     const uint16_t* w_shard, int64_t w_rows, int64_t ld_w,
+                                     int64_t d, float gamma, float* out, int64_t ld_out,
+                                     float* row_max, float* row_lse, float* row_entropy,
+                                     int32_t* row_argmax, void* stream);
+
+/*
  * se_soft_embed_step_fp8 -- se_soft_embed_step against an e4m3 table with per-row
  * power-of-two scales (as se_quantize_table_fp8 writes them; the pages serve FP8
  * weights: agentlenshq overview of DiffusionGemma in vLLM, performance and
