@@ -110,17 +110,14 @@ split_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t col0, i
     const float q0 = exp2_hw(t0), q1 = exp2_hw(t1), q2 = exp2_hw(t2), q3 = exp2_hw(t3);
     z += (q0 + q1) + (q2 + q3);
     s1 = __builtin_fmaf(q0, t0, __builtin_fmaf(q1, t1, __builtin_fmaf(q2, t2, __builtin_fmaf(q3, t3, s1))));
-    uint2 o;
-    o.x = pack_bf16x2(q0, q1);
-    o.y = pack_bf16x2(q2, q3);
-    *reinterpret_cast<uint2*>(blk + pidx(4 * g)) = o;
+    store_stream_u2(blk + pidx(4 * g), pack_bf16x2(q0, q1), pack_bf16x2(q2, q3));
   }
   for (int j = 4 * n4 + tid; j < n; j += kSweepThreads) {
     const float t = __builtin_fmaf(x[j], kLog2e, nl);
     const float q = exp2_hw(t);
     z += q;
     s1 = __builtin_fmaf(q, t, s1);
-    blk[pidx(j)] = __builtin_bit_cast(uint16_t, (__bf16)q);
+    store_stream_u16(blk + pidx(j), __builtin_bit_cast(uint16_t, (__bf16)q));
   }
   z = wave_sum(z);
   s1 = wave_sum(s1);
@@ -259,10 +256,7 @@ step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, 
       z += (q0 + q1) + (q2 + q3);
       s1 = __builtin_fmaf(q0, t0, __builtin_fmaf(q1, t1, __builtin_fmaf(q2, t2, __builtin_fmaf(q3, t3, s1))));
       if (active && in_slice) {                         // 4 positions in one super-step
-        uint2 o;
-        o.x = pack_bf16x2(q0, q1);
-        o.y = pack_bf16x2(q2, q3);
-        *reinterpret_cast<uint2*>(prow + tiled(js + base + 4 * gi)) = o;
+        store_stream_u2(prow + tiled(js + base + 4 * gi), pack_bf16x2(q0, q1), pack_bf16x2(q2, q3));
       }
     }
   }
@@ -271,7 +265,7 @@ step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, 
     const float q = exp2_hw(t);
     z += q;
     s1 = __builtin_fmaf(q, t, s1);
-    if (active && in_slice) prow[tiled(js + rs)] = __builtin_bit_cast(uint16_t, (__bf16)q);
+    if (active && in_slice) store_stream_u16(prow + tiled(js + rs), __builtin_bit_cast(uint16_t, (__bf16)q));
   }
   z = wave_sum(z);
   s1 = wave_sum(s1);

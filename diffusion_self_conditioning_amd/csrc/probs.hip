@@ -35,10 +35,10 @@ probs_bf16_kernel(const float* __restrict__ logits, int64_t ld, const float* __r
     o.y = pack_bf16x2(prob_from_logit(a.z, nl), prob_from_logit(a.w, nl));
     o.z = pack_bf16x2(prob_from_logit(b.x, nl), prob_from_logit(b.y, nl));
     o.w = pack_bf16x2(prob_from_logit(b.z, nl), prob_from_logit(b.w, nl));
-    *reinterpret_cast<uint4*>(p) = o;
+    store_stream_u4(p, o);
   } else {
     for (int64_t j = 0; j < K - k; ++j)
-      p[j] = __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(x[j], nl));
+      store_stream_u16(p + j, __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(x[j], nl)));
   }
 }
 

@@ -226,7 +226,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
         o.y = pack_bf16x2(prob_from_logit(a.z, nl), prob_from_logit(a.w, nl));
         o.z = pack_bf16x2(prob_from_logit(b.x, nl), prob_from_logit(b.y, nl));
         o.w = pack_bf16x2(prob_from_logit(b.z, nl), prob_from_logit(b.w, nl));
-        *reinterpret_cast<uint4*>(prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep) = o;
+        store_stream_u4(prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep, o);
       };
       // four 8-position groups per thread in flight, then the remaining groups one by one
       constexpr int64_t kStride = 8 * (int64_t)kRowThreads;
@@ -247,7 +247,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
         } else {
           uint16_t* __restrict__ pp = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
           for (int64_t j = 0; j < K - k; ++j)
-            pp[j] = __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(xs[k + j], nl));
+            store_stream_u16(pp + j, __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(xs[k + j], nl)));
         }
       }
     };
@@ -265,14 +265,12 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
             uint16_t* dst = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
             const float4 v = held[h][u];
             if (k + 4 <= K) {
-              uint2 o;
-              o.x = pack_bf16x2(prob_from_logit(v.x, nl), prob_from_logit(v.y, nl));
-              o.y = pack_bf16x2(prob_from_logit(v.z, nl), prob_from_logit(v.w, nl));
-              *reinterpret_cast<uint2*>(dst) = o;
+              store_stream_u2(dst, pack_bf16x2(prob_from_logit(v.x, nl), prob_from_logit(v.y, nl)),
+                              pack_bf16x2(prob_from_logit(v.z, nl), prob_from_logit(v.w, nl)));
             } else {
               const float e4[4] = {v.x, v.y, v.z, v.w};
               for (int j = 0; j < (int)(K - k); ++j)
-                dst[j] = __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(e4[j], nl));
+                store_stream_u16(dst + j, __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(e4[j], nl)));
             }
           }
         }

@@ -27,6 +27,23 @@ __device__ __forceinline__ float4 load_stream_f4(const void* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// Streaming stores of bf16 probabilities (nontemporal hint): they are read back only by
+// the contraction that follows, so they are written past the caches instead of leaving
+// dirty lines in L2 that the contraction's table stream would then have to evict
+// (measured on MI355X: the whole-vocabulary step 4-5% faster).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_stream_u2(void* p, uint32_t lo, uint32_t hi) {
+  const u32x2_t v = {lo, hi};
+  __builtin_nontemporal_store(v, static_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void store_stream_u4(void* p, const uint4& o) {
+  const u32x4_t v = {o.x, o.y, o.z, o.w};
+  __builtin_nontemporal_store(v, static_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream_u16(uint16_t* p, uint16_t v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 // Buffer resource over [base, base + bytes) for raw (unstructured) buffer loads:
 // the base sits in scalar registers, each load adds a 32-bit per-lane offset and a
 // 32-bit wave-uniform offset.  Dword 3 selects 32-bit raw access on gfx950.
