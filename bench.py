@@ -76,9 +76,20 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def event_time_us(fn, K: int, warmup: int) -> float:
-    """Average time of fn() over K back-to-back calls, from events on the current stream."""
+def event_time_us(fn, K: int, warmup: int, settle_ms: float = 0.0) -> float:
+    """Average time of fn() over K back-to-back calls, from events on the current stream,
+    after `warmup` calls (and, with settle_ms, after running fn back to back for that long)."""
     import torch
+    if settle_ms > 0:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        spent = 0.0
+        while spent < settle_ms:
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            e1.synchronize()
+            spent += e0.elapsed_time(e1)
     for _ in range(warmup):
         fn()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
@@ -186,6 +197,26 @@ class Step:
                 raise ValueError(path)
 
 
+def condition(st: Step, path: str, min_ms: float = 60.0, min_calls: int = 20):
+    """Run the step back to back for at least `min_ms` of GPU time before anything is timed.
+    After an idle gap of a few milliseconds the GPU starts a burst at a high clock and then,
+    a few steps in, drops below its sustained clock for tens of milliseconds while its power
+    control settles (measured: the first 60 whole-vocabulary steps after a 10 ms gap average
+    467 us, against 430 us back to back); this brings every measurement that follows to the
+    sustained state a serving loop runs in."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n, spent = 0, 0.0
+    while n < min_calls or spent < min_ms:
+        e0.record()
+        for _ in range(10):
+            st.call(path)
+        e1.record()
+        e1.synchronize()
+        spent += e0.elapsed_time(e1)
+        n += 10
+
+
 def timed_steps(st: Step, path: str, K: int, W: int):
     """W warmup steps, then K timed steps bracketed by synchronisations, each with events
     on the launch stream.  Returns (ms_per_step, per-step µs list, wall seconds)."""
@@ -206,29 +237,37 @@ def timed_steps(st: Step, path: str, K: int, W: int):
 
 
 def kernel_times(st: Step, path: str, K: int):
-    """Per-launch times of one step, averaged over K steps: an event recorded before the
-    call, then one marker after each of the library's launches (se_set_launch_events)."""
+    """Per-launch times of one step, averaged over K back-to-back steps: an event recorded
+    before each call, then one marker after each of the library's launches
+    (se_set_launch_events); nothing synchronises between the steps, so the first kernel of
+    a step starts right after the last one of the step before."""
     import torch
     from diffusion_self_conditioning_amd import _binding as B
     n_max = 8
-    sums, n_used = None, None
+    steps = []
     for _ in range(K):
         start = torch.cuda.Event(enable_timing=True)
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_max)]
-        for m in marks:                     # create the underlying HIP events
+        steps.append((start, marks))
+    for _, marks in steps:                   # create the underlying HIP events
+        for m in marks:
             m.record()
+    torch.cuda.synchronize()
+    used = []
+    for start, marks in steps:
         start.record()
         B.se_set_launch_events([m.cuda_event for m in marks])
         st.call(path)
-        used = B.se_launch_events_used()
+        used.append(B.se_launch_events_used())
         B.se_set_launch_events([])
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    n_used = used[0]
+    if any(u != n_used for u in used):
+        raise RuntimeError("launch count changed between steps")
+    sums = [0.0] * n_used
+    for start, marks in steps:
         t = [start.elapsed_time(marks[0]) * 1e3] + [
-            marks[j - 1].elapsed_time(marks[j]) * 1e3 for j in range(1, used)]
-        if sums is None:
-            sums, n_used = [0.0] * used, used
-        if used != n_used:
-            raise RuntimeError("launch count changed between steps")
+            marks[j - 1].elapsed_time(marks[j]) * 1e3 for j in range(1, n_used)]
         sums = [a + b for a, b in zip(sums, t)]
     names = LAUNCHES.get(path, [])
     if len(names) != n_used and path in ("step_onepass", "onepass") and n_used == 3:
@@ -241,6 +280,7 @@ def kernel_times(st: Step, path: str, K: int):
 def step_report(st: Step, path: str, K: int, W: int) -> dict:
     """Timed steps, per-kernel times and rooflines of one workload on one path."""
     w = st.w
+    condition(st, path)
     ms, per, wall = timed_steps(st, path, K, W)
     kt = kernel_times(st, path, K)
     flops = w.flops()
@@ -457,9 +497,10 @@ def main():
               flush=True)
         return
 
-    # every path once on the same inputs, event-timed as whole steps (these run before the
-    # headline's warmup, so the timed steps below see a GPU that has been under load)
+    # every path on the same inputs, event-timed as whole steps, after the GPU has been
+    # brought to its sustained state under this load
     say("paths")
+    condition(st, path)
     side = {}
     outs = {}
     for p in ("step", "step_onepass", "unfused", "staged", "fused") + (("onepass",) if whole
@@ -514,7 +555,8 @@ def main():
     s8 = [torch.empty(L, device=dev) for _ in range(3)] + [
         torch.empty(L, device=dev, dtype=torch.int32)]
     us_s8 = event_time_us(lambda: B.se_soft_embed_step_fp8(
-        st.x, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, *s8, st.wss), K, W)
+        st.x, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, *s8, st.wss), K, W,
+        settle_ms=60.0)
     s8_bytes = 4 * L * w.vocab + w.k * d + 4 * w.k + 4 * L * d + 16 * L
     us_q = event_time_us(lambda: B.se_quantize_table_fp8(st.shard, codes, wscale), 3, 1)
     fp8_side = {"step_us": round(us_s8, 2), "gflops_step": round(flops / (us_s8 * 1e-6) / 1e9, 2),
