@@ -18,7 +18,11 @@ embedding from one read of the logits).  --path picks another way to run the ste
   unfused       se_row_stats, then se_probs_bf16 + se_soft_embed
   staged        se_row_stats, then se_soft_embed_staged
   fused         se_row_stats, then se_soft_embed_fused
-Inputs are seeded synthetic data, resident in HBM before the timed region starts.
+Inputs are seeded synthetic data, resident in HBM before the timed region starts.  Before
+anything is timed the step runs back to back for 60 ms: after an idle gap of a few
+milliseconds the GPU's power control drops below its sustained clock for tens of
+milliseconds, and a sampler runs its steps back to back.  Then --warmup W steps and
+--steps K timed steps.
 
 Prints ONE JSON line.  ``value`` is soft-embed GFLOP/s over whole steps (2 L (e - s) d
 FLOP per step / ms_per_step).  The line also carries: steps/s; the per-kernel times of
@@ -270,8 +274,15 @@ def kernel_times(st: Step, path: str, K: int):
             marks[j - 1].elapsed_time(marks[j]) * 1e3 for j in range(1, n_used)]
         sums = [a + b for a, b in zip(sums, t)]
     names = LAUNCHES.get(path, [])
-    if len(names) != n_used and path in ("step_onepass", "onepass") and n_used == 3:
-        names = LAUNCHES["step"]            # the one-read call ran the two-pass step
+    if path in ("step_onepass", "onepass") and n_used == 3:
+        from diffusion_self_conditioning_amd import _binding as B
+        w = st.w
+        two_pass = path == "step_onepass" and (
+            B.se_soft_embed_step_onepass_workspace_bytes(w.rows, w.vocab, w.vocab_start,
+                                                         w.vocab_end, w.d)
+            == B.se_soft_embed_staged_workspace_bytes(w.rows, w.vocab_start, w.vocab_end, w.d))
+        names = (LAUNCHES["step"] if two_pass       # the one-read call ran the two-pass step
+                 else ["step_sweep_kernel", "soft_embed_pp_kernel", "scaled_reduce_kernel"])
     if len(names) != n_used:
         names = [f"launch_{j}" for j in range(n_used)]
     return [(names[j], sums[j] / K) for j in range(n_used)]

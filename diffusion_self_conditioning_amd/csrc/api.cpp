@@ -107,6 +107,15 @@ size_t tiled_probs_bytes(int64_t n_rows, int64_t K) {
 }
 }  // namespace
 
+bool contraction_can_merge(const GemmPlan& g, int64_t m_rows) {
+  if (g.grid > device_cu_count() || g.splits < 2) return false;
+  const int64_t longest = (g.kblocks + g.splits - 1) / g.splits;
+  int64_t short_splits = 0;
+  for (int64_t s = 0; s < g.splits; ++s)
+    short_splits += (((s + 1) * g.kblocks) / g.splits - (s * g.kblocks) / g.splits) < longest;
+  return short_splits * g.tiles * (kGemmThreads / 64) >= m_rows;
+}
+
 int sweep_waves(const GemmPlan& g, int64_t K) {
   if (K <= 0) return 0;
   const int64_t longest = std::min(((g.kblocks + g.splits - 1) / g.splits) * kSplitQuantum, K);
@@ -631,12 +640,25 @@ se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int
   p.kblocks = (int)o.g.kblocks;
   p.keep_partials = true;
   p.rows_pad = n_rows;
+  // the range merge rides in the contraction's short-split workgroups when it can
+  p.merge_rows = se::contraction_can_merge(o.g, n_rows);
+  p.stats = stats;
+  p.stat_arg = stat_arg;
+  p.merge_ranges = o.n_ranges;
+  p.merge_r0 = o.rg.n_pre;
+  p.factors = factors;
+  p.row_max = row_max;
+  p.row_lse = row_lse;
+  p.row_entropy = row_entropy;
+  p.row_argmax = row_argmax;
   rc = from_hip(se::launch_soft_embed(p, false, false, st));
   if (rc != SE_OK) return rc;
-  rc = from_hip(se::launch_merge_ranges(stats, stat_arg, n_rows, o.n_ranges, o.rg.n_pre,
-                                        (int)o.g.splits, gamma, factors, row_max, row_lse,
-                                        row_entropy, row_argmax, st));
-  if (rc != SE_OK) return rc;
+  if (!p.merge_rows) {
+    rc = from_hip(se::launch_merge_ranges(stats, stat_arg, n_rows, o.n_ranges, o.rg.n_pre,
+                                          (int)o.g.splits, gamma, factors, row_max, row_lse,
+                                          row_entropy, row_argmax, st));
+    if (rc != SE_OK) return rc;
+  }
   return from_hip(se::launch_scaled_reduce(p, factors, st));
 }
 
@@ -774,17 +796,31 @@ se_status se_soft_embed_onepass(const float* logits, int64_t ld_logits, int64_t 
   p.stats = stats;
   p.stat_arg = stat_arg;
   p.rows_pad = o.rows_pad;
-  rc = from_hip(se::launch_soft_embed(p, false, false, st));
-  if (rc != SE_OK) return rc;
-  if (o.sweep_waves == 0)
+  if (o.sweep_waves == 0) {
+    rc = from_hip(se::launch_soft_embed(p, false, false, st));
+    if (rc != SE_OK) return rc;
     return from_hip(se::launch_onepass_reduce(p, row_max, row_lse, row_entropy, row_argmax,
                                               vocab_start, st));
-  // the sweep wrote statistics and factors with row stride n_rows
+  }
+  // the sweep wrote statistics and factors with row stride n_rows; the range merge rides in
+  // the contraction's short-split workgroups when it can
   p.rows_pad = n_rows;
-  rc = from_hip(se::launch_merge_ranges(stats, stat_arg, n_rows, (int)o.g.splits, 0,
-                                        (int)o.g.splits, gamma, factors, row_max, row_lse,
-                                        row_entropy, row_argmax, st));
+  p.merge_rows = se::contraction_can_merge(o.g, n_rows);
+  p.merge_ranges = (int)o.g.splits;
+  p.merge_r0 = 0;
+  p.factors = factors;
+  p.row_max = row_max;
+  p.row_lse = row_lse;
+  p.row_entropy = row_entropy;
+  p.row_argmax = row_argmax;
+  rc = from_hip(se::launch_soft_embed(p, false, false, st));
   if (rc != SE_OK) return rc;
+  if (!p.merge_rows) {
+    rc = from_hip(se::launch_merge_ranges(stats, stat_arg, n_rows, (int)o.g.splits, 0,
+                                          (int)o.g.splits, gamma, factors, row_max, row_lse,
+                                          row_entropy, row_argmax, st));
+    if (rc != SE_OK) return rc;
+  }
   return from_hip(se::launch_scaled_reduce(p, factors, st));
 }
 

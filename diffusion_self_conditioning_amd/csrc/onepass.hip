@@ -26,21 +26,6 @@ namespace {
 constexpr int kSweepThreads = 512;                  // one workgroup per (row, split range)
 constexpr int kSweepWaves = kSweepThreads / 64;
 
-// whole-wave reductions (64 lanes) on top of the half-wave ones
-__device__ __forceinline__ float wave_sum(float v) {
-  v = half_sum(v);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
-         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-}
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  half_argmax(v, i);
-  const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  const int i1 = __builtin_amdgcn_readlane(i, 32);
-  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  i = __builtin_amdgcn_readlane(i, 0);
-  argmax_step(v, i, v1, i1);
-}
-
 // Pass 1 reads the range (16-byte buffer loads, eight in flight per lane) and finds the
 // first maximum; pass 2 reads it again, forms the probabilities against that maximum,
 // writes them as bf16 and sums Z and S1.  Cross-wave reductions go through a small LDS
@@ -283,12 +268,7 @@ step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, 
   }
 }
 
-// One wavefront per row: the ranges merge at the overall maximum M,
-//   Z = sum_r e^(m_r - M) Z_r,  S1 = sum_r e^(m_r - M) (S1_r + (m_r - M) Z_r),
-//   lse = M + ln Z,  H = ln Z - S1 / Z,  argmax = the smallest position reaching M,
-// and split range r0 + j gets the factor gamma e^(m - M) / Z.  Lane l takes ranges
-// l, l + 64, ... in order; the lanes then combine in the fixed butterfly order, so the
-// result is bitwise repeatable.
+// The range merge as a kernel of its own: one wavefront per row (merge_ranges_row).
 constexpr int kMergeRangesThreads = 256;
 
 __global__ void __launch_bounds__(kMergeRangesThreads)
@@ -297,35 +277,10 @@ merge_ranges_kernel(const float4* __restrict__ stats, const int32_t* __restrict_
                     float* __restrict__ factors, float* __restrict__ row_max,
                     float* __restrict__ row_lse, float* __restrict__ row_entropy,
                     int32_t* __restrict__ row_argmax) {
-  const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kMergeRangesThreads / 64) + (threadIdx.x >> 6);
   if (row >= n_rows) return;                           // whole wavefronts only
-  float mx = -INFINITY;
-  int arg = INT_MAX;
-  for (int r = lane; r < n_ranges; r += 64)
-    argmax_step(mx, arg, stats[(int64_t)r * n_rows + row].x, stat_arg[(int64_t)r * n_rows + row]);
-  wave_argmax(mx, arg);
-  float z = 0.f, s1 = 0.f;
-  for (int r = lane; r < n_ranges; r += 64) {
-    const float4 st = stats[(int64_t)r * n_rows + row];
-    const float d = st.x - mx;
-    const float f = exp2_hw(d * kLog2e);
-    z = __builtin_fmaf(f, st.y, z);
-    s1 = __builtin_fmaf(f, __builtin_fmaf(d, st.y, st.z), s1);
-  }
-  z = wave_sum(z);
-  s1 = wave_sum(s1);
-  const float lz = logf(z);
-  if (lane == 0) {
-    row_max[row] = mx;
-    row_lse[row] = mx + lz;
-    row_entropy[row] = lz - s1 / z;
-    row_argmax[row] = arg;
-  }
-  const float gz = gamma / z;
-  for (int j = lane; j < splits; j += 64)
-    factors[(int64_t)j * n_rows + row] =
-        gz * exp2_hw((stats[(int64_t)(r0 + j) * n_rows + row].x - mx) * kLog2e);
+  merge_ranges_row(stats, stat_arg, n_rows, n_ranges, r0, splits, gamma, factors, row_max,
+                   row_lse, row_entropy, row_argmax, row);
 }
 
 // Merge of T slice results (one-pass calls on disjoint vocabulary slices, in vocabulary

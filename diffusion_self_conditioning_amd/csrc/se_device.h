@@ -149,6 +149,67 @@ __device__ __forceinline__ void half_argmax(float& v, int& i) {
   argmax_step(v, i, swz16_f(v), swz16_i(i));
 }
 
+// whole-wave reductions (64 lanes) on top of the half-wave ones
+__device__ __forceinline__ float wave_sum(float v) {
+  v = half_sum(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  half_argmax(v, i);
+  const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const int i1 = __builtin_amdgcn_readlane(i, 32);
+  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  i = __builtin_amdgcn_readlane(i, 0);
+  argmax_step(v, i, v1, i1);
+}
+
+// The merge of one row's range statistics, by one whole wavefront (the one-read step; the
+// partition identity of calvarado04.com, "The fix", on softmax numerators).  Range r of the
+// row holds stats[r * n_rows + row] = {m_r, Z_r, S1_r (nats), m_r} and the vocabulary id of
+// its first maximum.  At the overall maximum M:
+//   Z = sum_r e^(m_r - M) Z_r,  S1 = sum_r e^(m_r - M) (S1_r + (m_r - M) Z_r),
+//   lse = M + ln Z,  H = ln Z - S1 / Z,  argmax = the smallest id reaching M,
+// and split range r0 + j gets the factor gamma e^(m - M) / Z (factors[j * n_rows + row]).
+// Lane l takes ranges l, l + 64, ... in order; the lanes then combine in the fixed
+// butterfly order, so the result is bitwise repeatable wherever it runs.
+__device__ __forceinline__ void merge_ranges_row(const float4* __restrict__ stats,
+                                                 const int32_t* __restrict__ stat_arg,
+                                                 int64_t n_rows, int n_ranges, int r0, int splits,
+                                                 float gamma, float* __restrict__ factors,
+                                                 float* __restrict__ row_max,
+                                                 float* __restrict__ row_lse,
+                                                 float* __restrict__ row_entropy,
+                                                 int32_t* __restrict__ row_argmax, int64_t row) {
+  const int lane = threadIdx.x & 63;
+  float mx = -INFINITY;
+  int arg = 0x7fffffff;
+  for (int r = lane; r < n_ranges; r += 64)
+    argmax_step(mx, arg, stats[(int64_t)r * n_rows + row].x, stat_arg[(int64_t)r * n_rows + row]);
+  wave_argmax(mx, arg);
+  float z = 0.f, s1 = 0.f;
+  for (int r = lane; r < n_ranges; r += 64) {
+    const float4 st = stats[(int64_t)r * n_rows + row];
+    const float d = st.x - mx;
+    const float f = exp2_hw(d * kLog2e);
+    z = __builtin_fmaf(f, st.y, z);
+    s1 = __builtin_fmaf(f, __builtin_fmaf(d, st.y, st.z), s1);
+  }
+  z = wave_sum(z);
+  s1 = wave_sum(s1);
+  const float lz = logf(z);
+  if (lane == 0) {
+    row_max[row] = mx;
+    row_lse[row] = mx + lz;
+    row_entropy[row] = lz - s1 / z;
+    row_argmax[row] = arg;
+  }
+  const float gz = gamma / z;
+  for (int j = lane; j < splits; j += 64)
+    factors[(int64_t)j * n_rows + row] =
+        gz * exp2_hw((stats[(int64_t)(r0 + j) * n_rows + row].x - mx) * kLog2e);
+}
+
 // 16 OCP e4m3 codes (byte j of `c` = element j) times a power-of-two `scale`, as 16
 // bf16 values: elements 0..7 in `lo`, 8..15 in `hi`.  Every e4m3 value times a power
 // of two in the normal range is a bf16 value, so the conversion is exact.

@@ -99,7 +99,23 @@ struct GemmParams {
   const float* stats;
   const int32_t* stat_arg;
   int64_t rows_pad;
+  // The one-read calls' range merge (merge_ranges_row), run by the contraction itself when
+  // merge_rows: each workgroup of a split shorter than the longest (whose main loop ends a
+  // block earlier) merges kWaves rows after its partial store, one per wave, with the
+  // statistics of merge_ranges ranges at merge_stats (row stride M) and the slice's split
+  // ranges from merge_r0.  Only for a launch of one wave of workgroups.
+  bool merge_rows;
+  int merge_ranges, merge_r0;
+  float* factors;
+  float* row_max;
+  float* row_lse;
+  float* row_entropy;
+  int32_t* row_argmax;
 };
+
+// Whether the contraction of plan `g` for m rows can carry the range merge: one wave of
+// workgroups (at most one per CU) and enough workgroups of short splits for 8 rows each.
+bool contraction_can_merge(const GemmPlan& g, int64_t m_rows);
 
 // The host-side checks of se_soft_embed_step (and its e4m3 form, w8) short of the workspace.
 se_status check_step(const float* logits, int64_t ld_logits, int64_t n_rows, int64_t vocab,

@@ -1064,10 +1064,30 @@ soft_embed_pp_kernel(const GemmParams p) {
         for (int r = 0; r < 16; ++r)
           dst[((wave * kMF + mi * kNI + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
   }
+
+  // ---- the one-read calls' range merge, in the workgroups of the shorter splits -----------
+  // Their main loop ends a 128-position block before the longest split's, so the merge of
+  // kWaves rows (one per wave) fits in time the launch would otherwise idle; rows are dealt
+  // to those workgroups in (split, tile) order.
+  if (p.merge_rows) {
+    const int64_t longest = (p.kblocks + p.splits - 1) / p.splits;
+    auto blocks_of = [&](int q) -> int64_t {
+      return ((int64_t)(q + 1) * p.kblocks) / p.splits - ((int64_t)q * p.kblocks) / p.splits;
+    };
+    if (blocks_of(s) < longest) {
+      int before = 0;
+      for (int q = 0; q < s; ++q) before += blocks_of(q) < longest ? 1 : 0;
+      const int64_t row = ((int64_t)before * p.tiles + t) * kWaves + wave;
+      if (row < p.M)
+        merge_ranges_row(reinterpret_cast<const float4*>(p.stats), p.stat_arg, p.M,
+                         p.merge_ranges, p.merge_r0, p.splits, p.gamma, p.factors, p.row_max,
+                         p.row_lse, p.row_entropy, p.row_argmax, row);
+    }
+  }
 }
 
 template <bool FUSED, bool W8>
-void launch_contraction(const GemmParams& p, hipStream_t stream) {
+hipError_t launch_contraction(const GemmParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles * p.splits));
   // bf16 probabilities (staged super-step-tiled, or row-major): the ping-pong kernel (bit
   // for bit the same result)
@@ -1079,23 +1099,27 @@ void launch_contraction(const GemmParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((soft_embed_pp_kernel<true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((soft_embed_pp_kernel<false, W8>), grid, dim3(kGemmThreads), 0, stream, p);
-    return;
+    return hipSuccess;
   }
+  if (p.merge_rows) return hipErrorInvalidValue;   // only the ping-pong kernel merges ranges
   // whole 256-row tiles take the path with per-lane addresses fixed for the kernel
   if (p.M % kBM == 0)
     hipLaunchKernelGGL((soft_embed_kernel<FUSED, true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((soft_embed_kernel<FUSED, false, W8>), grid, dim3(kGemmThreads), 0, stream, p);
+  return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_soft_embed(const GemmParams& p, bool fused, bool w8, hipStream_t stream) {
-  if (fused && w8) launch_contraction<true, true>(p, stream);
-  else if (fused) launch_contraction<true, false>(p, stream);
-  else if (w8) launch_contraction<false, true>(p, stream);
-  else launch_contraction<false, false>(p, stream);
-  hipError_t e = launched(stream);
+  hipError_t e;
+  if (fused && w8) e = launch_contraction<true, true>(p, stream);
+  else if (fused) e = launch_contraction<true, false>(p, stream);
+  else if (w8) e = launch_contraction<false, true>(p, stream);
+  else e = launch_contraction<false, false>(p, stream);
+  if (e != hipSuccess) return e;
+  e = launched(stream);
   if (e != hipSuccess || p.splits == 1 || p.keep_partials) return e;
   const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(kReduceThreads), 0, stream, p.ws,
