@@ -3,7 +3,8 @@ E^sc = gamma * sum_r S^(r), result in the embedding dtype).
 
 CPU: the oracle's pins -- a single part is the identity, dyadic parts add exactly,
 the fixed order r = 0 .. T-1 is visible in fp32 (1e8 + 1 - 1e8 = 0), bf16 rounds to
-nearest even.  GPU (marked): bit-exact against the oracle for random parts, and the
+nearest even as torch's CPU cast does, and the fp32 sum lies within the classical bound
+(T - 1) u sum |x_r| of the exact sum (math.fsum), whatever the order.  GPU (marked): bit-exact against the oracle for random parts, and the
 partition identity end to end: four rank slices of the fused call, summed on the GPU,
 match one full-slice call.
 """
@@ -41,6 +42,42 @@ def test_bf16_ties_to_even():
     assert b[0].tolist() == [0x3F80, 0x3F82]
 
 
+def _exact_sum(parts):
+    """The exact sum over axis 0 of fp32 values, element by element (math.fsum is exact up to
+    its final rounding to double, far below fp32's)."""
+    import math
+    t = parts.shape[0]
+    flat = parts.reshape(t, -1).astype(np.float64)
+    return np.array([math.fsum(flat[:, j]) for j in range(flat.shape[1])]).reshape(parts.shape[1:])
+
+
+def _within_fp32_sum_bound(got, parts):
+    """Any order of T - 1 fp32 additions stays within (T - 1) u sum |x_r| of the exact sum
+    (u = 2^-24; the classical bound for recursive summation)."""
+    t = parts.shape[0]
+    bound = (t - 1) * 2.0 ** -24 * np.abs(parts.astype(np.float64)).sum(axis=0) * (1 + 1e-6)
+    return np.all(np.abs(got.astype(np.float64) - _exact_sum(parts)) <= bound)
+
+
+def test_sum_is_the_exact_sum_within_the_fp32_bound():
+    rng = np.random.default_rng(5)
+    for t in (1, 2, 4, 8, 23):
+        parts = (rng.standard_normal((t, 7, 33)) * 10.0 ** rng.integers(-4, 5, (t, 7, 33))).astype(np.float32)
+        s, _ = reduce_partials(parts)
+        assert _within_fp32_sum_bound(s, parts)
+        if t == 1:
+            assert np.array_equal(s, parts[0])
+
+
+def test_bf16_output_is_torch_cast_of_the_sum():
+    import torch
+    rng = np.random.default_rng(6)
+    parts = (rng.standard_normal((4, 9, 65)) * 3).astype(np.float32)
+    s, b = reduce_partials(parts)
+    want = torch.from_numpy(s).to(torch.bfloat16).view(torch.uint16).numpy().astype(np.uint16)
+    assert np.array_equal(b, want)
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("t,n,d,ld", [(1, 4, 4, 4), (2, 17, 8, 12), (4, 256, 2816, 2816),
                                       (8, 3, 64, 64)])
@@ -56,6 +93,7 @@ def test_gpu_bit_exact(t, n, d, ld):
     B.se_reduce_partials(tp[:, :, :d] if ld == d else tp, out=out, out_bf16=ob)
     torch.cuda.synchronize()
     want, wbits = reduce_partials(parts[:, :, :d])
+    assert _within_fp32_sum_bound(out.cpu().numpy(), parts[:, :, :d])
     assert np.array_equal(out.cpu().numpy(), want)
     assert np.array_equal(ob.cpu().view(torch.uint16).numpy().astype(np.uint16), wbits)
 
