@@ -176,6 +176,31 @@ def test_brute_force_exhaustive_small():
                     assert abs(st["lse"][i] - lse) < 1e-13 and abs(st["entropy"][i] - h) < 1e-13
 
 
+def test_brute_force_continuous_workload_distribution():
+    """Element values on data drawn like the workloads' (logits N(0, 9) with a planted
+    maximum 8 above the rest, table N(0, 0.02^2) rounded to bf16, gamma = fp32(sqrt(2816))):
+    the oracle's statistics and embedding against the pure-Python evaluation from the
+    definitions, on a slice in the middle of the row and on the whole row."""
+    rng = np.random.default_rng(31)
+    gamma = float(np.float32(math.sqrt(2816.0)))
+    for L, V, d in ((2, 37, 5), (3, 130, 4)):
+        x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+        for i in range(L):
+            k = int(rng.integers(V))
+            x[i, k] = np.float32(np.max(np.delete(x[i], k)) + 8)
+        bits = _bf16_table(V, d, rng)
+        table = _table_values(bits)
+        st = oracle.row_stats(x)
+        for s, e in ((0, V), (V // 3, V - 5)):
+            out = oracle.soft_embed(x, s, e, bits[s:], gamma)
+            for i in range(L):
+                m, am, lse, h, bo = _brute([float(t) for t in x[i]],
+                                           [[float(t) for t in r] for r in table[s:]], s, e, gamma, d)
+                np.testing.assert_allclose(out[i], bo, rtol=1e-12, atol=1e-15)
+                assert st["max"][i] == m and st["argmax"][i] == am
+                assert abs(st["lse"][i] - lse) < 1e-12 and abs(st["entropy"][i] - h) < 1e-12
+
+
 # --- invariants --------------------------------------------------------------------
 def test_invariants_bounds_shift_linearity_permutation():
     V, d = 777, 12
