@@ -12,7 +12,9 @@ must give the full-row oracle.  Bars as the two-pass path:
 Cases: whole vocabularies and slices of 1, 63 and 4097 positions; ragged rows and
 hidden sizes; 1, a few and 256 split ranges; rows whose maximum sits in any range;
 one-hot rows, uniform rows, rows with a dynamic range of thousands of nats; a
-near-converged canvas; and at full size the whole vocabulary and a four-rank merge.
+near-converged canvas; the rows' range merge inside the contraction (one wave of
+workgroups, the workgroups of the splits one block shorter merging 8 rows each); and at
+full size the whole vocabulary and a four-rank merge.
 """
 import sys
 
@@ -96,12 +98,33 @@ CASES = {
     "256-splits": (16, 65536, 0, 65536, 256, 7),
     "whole-tile-ragged": (256, 20008, 8, 12353, 264, 8),  # ping-pong contraction, tail
     "two-whole-tiles": (512, 4104, 0, 4104, 128, 9),
+    # the range merge inside the contraction: 13 rows on 16 merging waves; 511 rows over
+    # 2 x 3 output tiles with ragged rows and columns
+    "merge-in-contraction": (13, 20008, 8, 20008, 48, 11),
+    "merge-row-tiles": (511, 100008, 8, 100008, 520, 12),
 }
+
+
+def merges_in_contraction(L, K, d):
+    """Whether the contraction of an L x K x d one-pass call carries the range merge: one
+    wave of workgroups (256 x 256 tiles times the split count at most the CU count), at
+    least two splits, and 8 rows per workgroup of the splits one 128-block shorter."""
+    splits = B.se_soft_embed_splits(L, 0, K, d)
+    tiles = -(-L // 256) * -(-d // 256)
+    kb = -(-K // 128)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if splits < 2 or tiles * splits > cus:
+        return False
+    longest = -(-kb // splits)
+    short = sum(((r + 1) * kb // splits - r * kb // splits) < longest for r in range(splits))
+    return short * tiles * 8 >= L
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_onepass_parity(case):
     L, V, s, e, d, seed = CASES[case]
+    if case.startswith("merge"):
+        assert merges_in_contraction(L, e - s, d), case
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
     # plant each row's maximum in a different place (any split range may hold it)

@@ -14,7 +14,10 @@ row, slices of 1 and 63 positions, vocabularies and slice ends that are not mult
 of 4 (ranges with scalar heads and tails), whole and partial 256-row tiles, a row
 maximum in the slice or outside it, one-hot / uniform / wide-range / tied rows, the
 empty slice and split ranges too long for the sweep (both the two-pass step, bit for
-bit), repeatability, and the one-rank workload at full size.
+bit), repeatability, and the one-rank workload at full size.  Two cases run the rows'
+range merge inside the contraction (one wave of workgroups; the workgroups of the
+splits one block shorter each merge 8 rows): 13 rows on 16 merging waves, and 511 rows
+over 2 x 3 output tiles with ragged rows and columns.
 """
 import sys
 
@@ -107,12 +110,31 @@ CASES = {
     "two-row-tiles": (300, 2048, 1024, 2048, 512, 7),
     "many-pre-chunks": (8, 120000, 96000, 100003, 32, 8),
     "whole-tile": (256, 30003, 1000, 13337, 272, 10),   # ping-pong contraction, tail
+    "merge-in-contraction": (13, 20008, 8, 20008, 48, 11),
+    "merge-row-tiles": (511, 100011, 8, 100008, 520, 12),
 }
+
+
+def merges_in_contraction(L, K, d):
+    """Whether the contraction of an L x K x d one-read step carries the range merge: one
+    wave of workgroups (256 x 256 tiles times the split count at most the CU count), at
+    least two splits, and 8 rows per workgroup of the splits one 128-block shorter."""
+    splits = B.se_soft_embed_splits(L, 0, K, d)
+    tiles = -(-L // 256) * -(-d // 256)
+    kb = -(-K // 128)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if splits < 2 or tiles * splits > cus:
+        return False
+    longest = -(-kb // splits)
+    short = sum(((r + 1) * kb // splits - r * kb // splits) < longest for r in range(splits))
+    return short * tiles * 8 >= L
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_step_onepass_parity(case):
     L, V, s, e, d, seed = CASES[case]
+    if case.startswith("merge"):
+        assert merges_in_contraction(L, e - s, d), case
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
     # half the rows peak inside the slice, half anywhere in the row
