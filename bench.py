@@ -22,12 +22,13 @@ Inputs are seeded synthetic data, resident in HBM before the timed region starts
 anything is timed the step runs back to back for 60 ms: after an idle gap of a few
 milliseconds the GPU's power control drops below its sustained clock for tens of
 milliseconds, and a sampler runs its steps back to back.  Then --warmup W steps and
---steps K timed steps.
+--steps K timed steps, back to back with nothing recorded between them.
 
 Prints ONE JSON line.  ``value`` is soft-embed GFLOP/s over whole steps (2 L (e - s) d
-FLOP per step / ms_per_step).  The line also carries: steps/s; the per-kernel times of
-one step from HIP events recorded between the library's own launches
-(se_set_launch_events); ``roofline`` of the dominant kernel (the contraction) and
+FLOP per step / ms_per_step).  The line also carries: steps/s; the duration of each
+kernel of one step, from start and end events that the dispatch stamps for the library's
+launches (se_set_launch_events), and the gaps between them; ``roofline`` of the dominant
+kernel (the contraction) and
 ``roofline_step`` of the whole step, both on measured times; ``parity`` of the timed
 step's outputs against the fp64 oracle on every row (the rows the CPU baseline
 computes); ``cpu_baseline`` (that oracle's time on this host's cores); every other path
@@ -222,8 +223,11 @@ def condition(st: Step, path: str, min_ms: float = 60.0, min_calls: int = 20):
 
 
 def timed_steps(st: Step, path: str, K: int, W: int):
-    """W warmup steps, then K timed steps bracketed by synchronisations, each with events
-    on the launch stream.  Returns (ms_per_step, per-step µs list, wall seconds)."""
+    """W warmup steps, then K timed steps back to back, bracketed by synchronisations and by
+    two events on the launch stream (nothing is recorded between the steps: an event between
+    two steps delays the next one by several µs).  Then K more steps with an event after each,
+    for the spread of single steps.  Returns (ms_per_step, per-step µs list, wall seconds of
+    the timed steps)."""
     import torch
     for _ in range(W):
         st.call(path)
@@ -233,46 +237,96 @@ def timed_steps(st: Step, path: str, K: int, W: int):
     ev[0].record()
     for k in range(K):
         st.call(path)
-        ev[k + 1].record()
+    ev[K].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[K]) / K
+    ev[0].record()
+    for k in range(K):
+        st.call(path)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
     per = [ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(K)]
-    return ev[0].elapsed_time(ev[K]) / K, per, wall
+    return ms, per, wall
+
+
+class HipEvents:
+    """Timing events of the HIP runtime this process already runs (the one torch loaded and
+    the library uses), created with hipEventDisableSystemFence: completing one performs no
+    system-scope cache writeback and invalidation, which would slow the kernel after it."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        import torch
+        torch.cuda.init()
+        path = next(ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln)
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.live = []
+
+    def create(self, n: int) -> list:
+        out = []
+        for _ in range(n):
+            h = self.ct.c_void_p()
+            if self.hip.hipEventCreateWithFlags(self.ct.byref(h),
+                                                self.ct.c_uint(self.DISABLE_SYSTEM_FENCE)):
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            out.append(h.value)
+        self.live += out
+        return out
+
+    def record(self, ev: int, stream: int) -> None:
+        if self.hip.hipEventRecord(self.ct.c_void_p(ev), self.ct.c_void_p(stream)):
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_us(self, a: int, b: int) -> float:
+        t = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(t), self.ct.c_void_p(a), self.ct.c_void_p(b)):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value * 1e3
+
+    def destroy_all(self) -> None:
+        for h in self.live:
+            self.hip.hipEventDestroy(self.ct.c_void_p(h))
+        self.live = []
 
 
 def kernel_times(st: Step, path: str, K: int):
-    """Per-launch times of one step, averaged over K back-to-back steps: an event recorded
-    before each call, then one marker after each of the library's launches
-    (se_set_launch_events); nothing synchronises between the steps, so the first kernel of
-    a step starts right after the last one of the step before."""
+    """Per-launch kernel durations of one step, averaged over K back-to-back steps: the
+    library's launch markers (se_set_launch_events) have the dispatch stamp each kernel's
+    start and end into two events, so a duration is the kernel alone and the steps run as
+    in the timed region (no command between them, nothing synchronises).  Also the gaps
+    between consecutive kernels of a step.  Returns ([(name, µs)], [gap µs])."""
     import torch
     from diffusion_self_conditioning_amd import _binding as B
-    n_max = 8
-    steps = []
-    for _ in range(K):
-        start = torch.cuda.Event(enable_timing=True)
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_max)]
-        steps.append((start, marks))
-    for _, marks in steps:                   # create the underlying HIP events
-        for m in marks:
-            m.record()
+    n_max = 16
+    hev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    steps = [hev.create(n_max) for _ in range(K)]
+    bracket = hev.create(2)
     torch.cuda.synchronize()
     used = []
-    for start, marks in steps:
-        start.record()
-        B.se_set_launch_events([m.cuda_event for m in marks])
+    hev.record(bracket[0], stream)
+    for marks in steps:
+        B.se_set_launch_events(marks)
         st.call(path)
         used.append(B.se_launch_events_used())
         B.se_set_launch_events([])
+    hev.record(bracket[1], stream)
     torch.cuda.synchronize()
-    n_used = used[0]
-    if any(u != n_used for u in used):
+    n_used = used[0] // 2
+    if any(u != 2 * n_used for u in used) or n_used == 0:
+        hev.destroy_all()
         raise RuntimeError("launch count changed between steps")
-    sums = [0.0] * n_used
-    for start, marks in steps:
-        t = [start.elapsed_time(marks[0]) * 1e3] + [
-            marks[j - 1].elapsed_time(marks[j]) * 1e3 for j in range(1, n_used)]
+    sums, gaps = [0.0] * n_used, [0.0] * max(0, n_used - 1)
+    for marks in steps:
+        t = [hev.elapsed_us(marks[2 * j], marks[2 * j + 1]) for j in range(n_used)]
+        g = [hev.elapsed_us(marks[2 * j - 1], marks[2 * j]) for j in range(1, n_used)]
         sums = [a + b for a, b in zip(sums, t)]
+        gaps = [a + b for a, b in zip(gaps, g)]
+    marked_us = hev.elapsed_us(bracket[0], bracket[1]) / K
+    hev.destroy_all()
     names = LAUNCHES.get(path, [])
     if path in ("step_onepass", "onepass") and n_used == 3:
         from diffusion_self_conditioning_amd import _binding as B
@@ -285,7 +339,7 @@ def kernel_times(st: Step, path: str, K: int):
                  else ["step_sweep_kernel", "soft_embed_pp_kernel", "scaled_reduce_kernel"])
     if len(names) != n_used:
         names = [f"launch_{j}" for j in range(n_used)]
-    return [(names[j], sums[j] / K) for j in range(n_used)]
+    return [(names[j], sums[j] / K) for j in range(n_used)], [v / K for v in gaps], marked_us
 
 
 def step_report(st: Step, path: str, K: int, W: int) -> dict:
@@ -293,7 +347,7 @@ def step_report(st: Step, path: str, K: int, W: int) -> dict:
     w = st.w
     condition(st, path)
     ms, per, wall = timed_steps(st, path, K, W)
-    kt = kernel_times(st, path, K)
+    kt, gaps, marked_us = kernel_times(st, path, K)
     flops = w.flops()
     dom_i = max(range(len(kt)), key=lambda j: kt[j][1] if "soft_embed" in kt[j][0] else -1)
     dom_name, dom_us = kt[dom_i]
@@ -305,7 +359,8 @@ def step_report(st: Step, path: str, K: int, W: int) -> dict:
                  "algorithmic_bytes": contraction_bytes(w, fused),
                  "algorithmic_flops": flops, "traffic_source": source,
                  "basis": "algorithmic bytes (bf16 table slice + staged bf16 probabilities) "
-                          "or FLOP of one launch / its event-timed duration"})
+                          "or FLOP of one launch / its duration between the start and end "
+                          "events the dispatch stamps"})
     once, two = step_bytes_logits_once(w), step_bytes_two_pass(w)
     t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12) * 1e6
 
@@ -325,6 +380,8 @@ def step_report(st: Step, path: str, K: int, W: int) -> dict:
         "step_us_median": round(srt[len(srt) // 2], 2), "step_us_min": round(srt[0], 2),
         "wall_s_timed": round(wall, 4),
         "kernel_us": {name: round(us, 2) for name, us in kt},
+        "gaps_between_kernels_us": [round(g, 2) for g in gaps],
+        "marked_step_us": round(marked_us, 2),
         "roofline": roof,
         "roofline_step": {
             "basis": "whole-step algorithmic bytes (or the statistics pass plus the MFMA "
@@ -504,7 +561,9 @@ def main():
                           "n_gpus": 1, "steps": K, "warmup": W,
                           "ms_per_step": rep["ms_per_step"], "minimal": True,
                           "config": {"workload": w.name, "path": path},
-                          "kernel_us": rep["kernel_us"], "roofline": rep["roofline"]}),
+                          "kernel_us": rep["kernel_us"],
+                          "gaps_between_kernels_us": rep["gaps_between_kernels_us"],
+                          "marked_step_us": rep["marked_step_us"], "roofline": rep["roofline"]}),
               flush=True)
         return
 
@@ -655,6 +714,8 @@ def main():
         "canvas_steps_per_s": main_rep["canvas_steps_per_s"],
         "step_us_median": main_rep["step_us_median"], "step_us_min": main_rep["step_us_min"],
         "kernel_us": main_rep["kernel_us"],
+        "gaps_between_kernels_us": main_rep["gaps_between_kernels_us"],
+        "marked_step_us": main_rep["marked_step_us"],
         "roofline": main_rep["roofline"],
         "roofline_step": main_rep["roofline_step"],
         "parity": par,

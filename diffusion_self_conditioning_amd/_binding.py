@@ -396,8 +396,9 @@ def se_soft_embed_step(logits, vocab_start, vocab_end, w_shard, gamma, out, row_
 
 def se_set_launch_events(events) -> None:
     """Arm the calling thread's per-launch timing markers with HIP event handles (ints, e.g.
-    ``torch.cuda.Event.cuda_event`` after a first record); an empty list disarms them.  The
-    handle array is kept alive here until the next call."""
+    ``torch.cuda.Event.cuda_event`` after a first record): each later launch takes two, its
+    kernel's start and end.  An empty list disarms them.  The handle array is kept alive
+    here until the next call."""
     global _armed
     handles = [int(e) for e in events]
     _armed = (ctypes.c_void_p * max(1, len(handles)))(*handles)

@@ -20,6 +20,7 @@
 //      budget, but holds at least one position when any is left;
 //   5. per canvas: stable-step counter, step counter, converged flag.
 #include "se_device.h"
+#include "se_dispatch.h"
 #include "se_launch.h"
 
 namespace se {
@@ -145,7 +146,7 @@ hipError_t launch_accept_converge(const float* row_entropy, const int32_t* row_a
                                   hipStream_t stream) {
   int nt = 64;
   while (nt < len) nt <<= 1;
-  hipLaunchKernelGGL(accept_converge_kernel, dim3((unsigned)n_canvas), dim3(nt), 0,
+  SE_LAUNCH(accept_converge_kernel, dim3((unsigned)n_canvas), dim3(nt), 0,
                      stream, row_entropy, row_argmax, len, budget, stable_steps, tau, step_limit,
                      accepted, prev_argmax, stable_count, step_count, newly, converged);
   return launched(stream);

@@ -45,7 +45,8 @@ int device_cu_count() {
 
 // ---- launch markers ------------------------------------------------------------------
 // Per-thread list of caller-created HIP events armed by se_set_launch_events; each kernel
-// launch the thread makes afterwards records the next one on the launch's stream.
+// launch the thread makes afterwards takes the next two, stamped by the dispatch with the
+// kernel's start and end.
 namespace {
 struct LaunchMarkers {
   void* const* events = nullptr;
@@ -55,13 +56,14 @@ struct LaunchMarkers {
 thread_local LaunchMarkers t_markers;
 }  // namespace
 
-void mark_launch(hipStream_t stream) {
+bool next_launch_events(hipEvent_t* start, hipEvent_t* end) {
   LaunchMarkers& m = t_markers;
-  if (m.events == nullptr || m.used >= m.n) return;
-  if (hipEventRecord(static_cast<hipEvent_t>(m.events[m.used]), stream) == hipSuccess)
-    ++m.used;
-  else
-    (void)hipGetLastError();
+  *start = *end = nullptr;
+  if (m.events == nullptr || m.n - m.used < 2) return false;
+  *start = static_cast<hipEvent_t>(m.events[m.used]);
+  *end = static_cast<hipEvent_t>(m.events[m.used + 1]);
+  m.used += 2;
+  return true;
 }
 
 // The split count minimises a makespan model of the contraction:

@@ -18,6 +18,7 @@
 // second pass reads it again, forms the probabilities, writes them as bf16 and sums Z_s
 // and S1_s in fp32.
 #include "se_device.h"
+#include "se_dispatch.h"
 #include "se_launch.h"
 
 namespace se {
@@ -343,7 +344,7 @@ hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_
                                float* row_entropy, int32_t* row_argmax, hipStream_t stream) {
   const int64_t groups = (d + 3) / 4;
   const dim3 grid((unsigned)((groups + kMergeThreads - 1) / kMergeThreads), (unsigned)n_rows);
-  hipLaunchKernelGGL(merge_slices_kernel, grid, dim3(kMergeThreads), 0, stream, outs,
+  SE_LAUNCH(merge_slices_kernel, grid, dim3(kMergeThreads), 0, stream, outs,
                      (int)n_parts, part_stride, n_rows, d, ld_part, part_max, part_lse,
                      part_entropy, part_argmax, out, ld_out, row_max, row_lse, row_entropy,
                      row_argmax);
@@ -358,7 +359,7 @@ hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
   auto go = [&](auto kernel, int w) {
     const int per_block = (sweep_threads(w) / 64) / w;          // (row, range) items
     const dim3 grid((unsigned)((n_rows * n_ranges + per_block - 1) / per_block));
-    hipLaunchKernelGGL(kernel, grid, dim3(sweep_threads(w)), 0, stream, logits, ld, n_rows, g,
+    SE_LAUNCH(kernel, grid, dim3(sweep_threads(w)), 0, stream, logits, ld, n_rows, g,
                        n_ranges, probs, st, stat_arg);
     return launched(stream);
   };
@@ -377,7 +378,7 @@ hipError_t launch_merge_ranges(const float* stats, const int32_t* stat_arg, int6
                                int32_t* row_argmax, hipStream_t stream) {
   const int per_block = kMergeRangesThreads / 64;
   const dim3 grid((unsigned)((n_rows + per_block - 1) / per_block));
-  hipLaunchKernelGGL(merge_ranges_kernel, grid, dim3(kMergeRangesThreads), 0, stream,
+  SE_LAUNCH(merge_ranges_kernel, grid, dim3(kMergeRangesThreads), 0, stream,
                      reinterpret_cast<const float4*>(stats), stat_arg, n_rows, n_ranges, r0,
                      splits, gamma, factors, row_max, row_lse, row_entropy, row_argmax);
   return launched(stream);
@@ -388,7 +389,7 @@ hipError_t launch_split_sweep(const float* logits, int64_t ld, int64_t col0, int
                               float* stats, int32_t* stat_arg, int64_t rows_pad,
                               hipStream_t stream) {
   const dim3 grid((unsigned)(n_rows * splits));
-  hipLaunchKernelGGL(split_sweep_kernel, grid, dim3(kSweepThreads), 0, stream, logits, ld, col0,
+  SE_LAUNCH(split_sweep_kernel, grid, dim3(kSweepThreads), 0, stream, logits, ld, col0,
                      K, n_rows, splits, kblocks, probs, reinterpret_cast<float4*>(stats),
                      stat_arg, rows_pad);
   return launched(stream);

@@ -5,6 +5,7 @@
 // Each thread converts 8 consecutive columns: two 16-byte loads, one 16-byte
 // store.  Grid: x over column groups, y over rows.
 #include "se_device.h"
+#include "se_dispatch.h"
 #include "se_launch.h"
 
 namespace se {
@@ -49,7 +50,7 @@ hipError_t launch_probs_bf16(const float* logits, int64_t ld, const float* row_l
                              int64_t ldp, hipStream_t stream) {
   const int64_t groups = (K + 7) / 8;
   const dim3 grid((unsigned)((groups + kProbThreads - 1) / kProbThreads), (unsigned)n_rows);
-  hipLaunchKernelGGL(probs_bf16_kernel<false>, grid, dim3(kProbThreads), 0, stream, logits, ld,
+  SE_LAUNCH(probs_bf16_kernel<false>, grid, dim3(kProbThreads), 0, stream, logits, ld,
                      row_lse, col0, K, probs, ldp, n_rows, (int64_t)0);
   return launched(stream);
 }
@@ -62,7 +63,7 @@ hipError_t launch_probs_bf16_tiled(const float* logits, int64_t ld, const float*
   for (int64_t r0 = 0; r0 < n_rows; r0 += kMaxRows) {
     const int64_t nr = n_rows - r0 < kMaxRows ? n_rows - r0 : kMaxRows;
     const dim3 grid((unsigned)((groups + kProbThreads - 1) / kProbThreads), (unsigned)nr);
-    hipLaunchKernelGGL(probs_bf16_kernel<true>, grid, dim3(kProbThreads), 0, stream, logits, ld,
+    SE_LAUNCH(probs_bf16_kernel<true>, grid, dim3(kProbThreads), 0, stream, logits, ld,
                        row_lse, col0, K, probs, (int64_t)0, n_rows, r0);
     const hipError_t e = launched(stream);
     if (e != hipSuccess) return e;

@@ -16,6 +16,7 @@
 // the bf16 magnitude bits, exact), then a pass that scales and converts (hardware
 // round-to-nearest-even conversion to e4m3).
 #include "se_device.h"
+#include "se_dispatch.h"
 #include "se_launch.h"
 
 namespace se {
@@ -82,7 +83,7 @@ hipError_t launch_quantize_fp8(const uint16_t* w, int64_t ldw, int64_t rows, int
                                uint8_t* codes, int64_t ldq, float* row_scale,
                                hipStream_t stream) {
   const int64_t blocks = (rows + kQuantRows - 1) / kQuantRows;
-  hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
+  SE_LAUNCH(quantize_fp8_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
                      w, ldw, rows, (int)d, codes, ldq, row_scale);
   return launched(stream);
 }

@@ -7,6 +7,7 @@
 // added in the order r = 0, 1, ..., T-1 in fp32, and the sum is written as fp32
 // and / or rounded to bf16 (nearest even), the pages' output dtype.
 #include "se_device.h"
+#include "se_dispatch.h"
 #include "se_launch.h"
 
 namespace se {
@@ -43,7 +44,7 @@ hipError_t launch_reduce_parts(const float* parts, int64_t n_parts, int64_t part
                                int64_t ld_out, uint16_t* out_bf16, int64_t ld_bf16,
                                hipStream_t stream) {
   const dim3 grid((unsigned)((d / 4 + kReduceThreads - 1) / kReduceThreads), (unsigned)n_rows);
-  hipLaunchKernelGGL(reduce_parts_kernel, grid, dim3(kReduceThreads), 0, stream, parts, n_parts,
+  SE_LAUNCH(reduce_parts_kernel, grid, dim3(kReduceThreads), 0, stream, parts, n_parts,
                      part_stride, d, ld_part, out, ld_out, out_bf16, ld_bf16);
   return launched(stream);
 }

@@ -23,6 +23,7 @@
 // contraction streams: position k of row i at
 // probs[(k / kSuperStep) * n_rows * kSuperStep + i * kSuperStep + k % kSuperStep].
 #include "se_device.h"
+#include "se_dispatch.h"
 #include "se_launch.h"
 
 #include <climits>
@@ -289,7 +290,7 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
 hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int vocab,
                             float* row_max, float* row_lse, float* row_entropy,
                             int32_t* row_argmax, hipStream_t stream) {
-  hipLaunchKernelGGL((row_stats_kernel<false, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
+  SE_LAUNCH((row_stats_kernel<false, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
                      stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax,
                      (int64_t)0, (int64_t)0, nullptr, n_rows);
   return launched(stream);
@@ -306,11 +307,11 @@ hipError_t launch_row_stats_probs(const float* logits, int64_t ld, int64_t n_row
   const int64_t g_held = min((col0 + K + gpos - 1) / gpos, g0 + kHoldGroups);
   const bool hold = K > 0 && g_held <= (vocab / 4) / kGroupF4;
   if (hold)
-    hipLaunchKernelGGL((row_stats_kernel<true, kHoldGroups>), dim3((unsigned)n_rows),
+    SE_LAUNCH((row_stats_kernel<true, kHoldGroups>), dim3((unsigned)n_rows),
                        dim3(kRowThreads), 0, stream, logits, ld, vocab, row_max, row_lse,
                        row_entropy, row_argmax, col0, K, probs, n_rows);
   else
-    hipLaunchKernelGGL((row_stats_kernel<true, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
+    SE_LAUNCH((row_stats_kernel<true, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
                        stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax, col0,
                        K, probs, n_rows);
   return launched(stream);

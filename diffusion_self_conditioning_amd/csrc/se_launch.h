@@ -11,15 +11,13 @@
 namespace se {
 
 // ---- launch markers (se_set_launch_events) ----------------------------------------------
-// Records the calling thread's next armed event, if any, on `stream` (right after a kernel
-// launch on that stream).
-void mark_launch(hipStream_t stream);
-// The status of the launch just made; a successful launch is then marked.
-inline hipError_t launched(hipStream_t stream) {
-  const hipError_t e = hipGetLastError();
-  if (e == hipSuccess) mark_launch(stream);
-  return e;
-}
+// Hands out the calling thread's next two armed events, for the start and the end of the
+// kernel about to be launched; false (and nulls) when fewer than two remain.  The .hip
+// files launch every kernel through SE_LAUNCH (se_dispatch.h), which passes them to the
+// dispatch.
+bool next_launch_events(hipEvent_t* start, hipEvent_t* end);
+// The status of the launch just made on `stream`.
+inline hipError_t launched(hipStream_t) { return hipGetLastError(); }
 
 // ---- work decomposition of the slice contraction (pure host logic) -------------
 // The output [M, N] is cut into BM x BN tiles; the contracted (vocab) axis into

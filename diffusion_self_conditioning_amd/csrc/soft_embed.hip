@@ -55,6 +55,7 @@
 // the LDS write is the bf16 kernel and the two agree bit for bit on the dequantized
 // table.
 #include "se_device.h"
+#include "se_dispatch.h"
 #include "se_launch.h"
 
 #ifndef SE_W_LOAD
@@ -1096,17 +1097,17 @@ hipError_t launch_contraction(const GemmParams& p, hipStream_t stream) {
   if (!FUSED && (p.a_ss == p.M * (int64_t)kSuperStep * 2 || p.a_ss == (int64_t)kSuperStep * 2) &&
       (!W8 || p.tiles == p.tiles_n)) {
     if (p.tiles == p.tiles_n)                   // one row tile
-      hipLaunchKernelGGL((soft_embed_pp_kernel<true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
+      SE_LAUNCH((soft_embed_pp_kernel<true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((soft_embed_pp_kernel<false, W8>), grid, dim3(kGemmThreads), 0, stream, p);
+      SE_LAUNCH((soft_embed_pp_kernel<false, W8>), grid, dim3(kGemmThreads), 0, stream, p);
     return hipSuccess;
   }
   if (p.merge_rows) return hipErrorInvalidValue;   // only the ping-pong kernel merges ranges
   // whole 256-row tiles take the path with per-lane addresses fixed for the kernel
   if (p.M % kBM == 0)
-    hipLaunchKernelGGL((soft_embed_kernel<FUSED, true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
+    SE_LAUNCH((soft_embed_kernel<FUSED, true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((soft_embed_kernel<FUSED, false, W8>), grid, dim3(kGemmThreads), 0, stream, p);
+    SE_LAUNCH((soft_embed_kernel<FUSED, false, W8>), grid, dim3(kGemmThreads), 0, stream, p);
   return hipSuccess;
 }
 
@@ -1122,7 +1123,7 @@ hipError_t launch_soft_embed(const GemmParams& p, bool fused, bool w8, hipStream
   e = launched(stream);
   if (e != hipSuccess || p.splits == 1 || p.keep_partials) return e;
   const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(kReduceThreads), 0, stream, p.ws,
+  SE_LAUNCH(splitk_reduce_kernel, dim3(blocks), dim3(kReduceThreads), 0, stream, p.ws,
                      p.tiles, p.tiles_n, p.splits, p.M, p.N, p.gamma, p.out, p.ldo);
   return launched(stream);
 }
@@ -1131,7 +1132,7 @@ hipError_t launch_onepass_reduce(const GemmParams& p, float* row_max, float* row
                                  float* row_entropy, int32_t* row_argmax, int64_t col0,
                                  hipStream_t stream) {
   const int blocks = p.tiles * (int)(kTileFloats / (4 * 256));
-  hipLaunchKernelGGL(onepass_reduce_kernel, dim3(blocks), dim3(256), 0, stream, p.ws,
+  SE_LAUNCH(onepass_reduce_kernel, dim3(blocks), dim3(256), 0, stream, p.ws,
                      reinterpret_cast<const float4*>(p.stats), p.stat_arg, p.rows_pad, p.tiles,
                      p.tiles_n, p.splits, p.M, p.N, p.gamma, col0, p.out, p.ldo, row_max,
                      row_lse, row_entropy, row_argmax);
@@ -1140,7 +1141,7 @@ hipError_t launch_onepass_reduce(const GemmParams& p, float* row_max, float* row
 
 hipError_t launch_scaled_reduce(const GemmParams& p, const float* factors, hipStream_t stream) {
   const int blocks = p.tiles * (int)(kTileFloats / (4 * kReduceThreads));
-  hipLaunchKernelGGL(scaled_reduce_kernel, dim3(blocks), dim3(kReduceThreads), 0, stream, p.ws,
+  SE_LAUNCH(scaled_reduce_kernel, dim3(blocks), dim3(kReduceThreads), 0, stream, p.ws,
                      factors, p.rows_pad, p.tiles, p.tiles_n, p.splits, p.M, p.N, p.out, p.ldo);
   return launched(stream);
 }
@@ -1148,7 +1149,7 @@ hipError_t launch_scaled_reduce(const GemmParams& p, const float* factors, hipSt
 hipError_t launch_zero_rows(float* out, int64_t ldo, int64_t M, int64_t N, hipStream_t stream) {
   const int64_t groups = (N + 3) / 4;
   const dim3 grid((unsigned)((groups + 255) / 256), (unsigned)M);
-  hipLaunchKernelGGL(zero_rows_kernel, grid, dim3(256), 0, stream, out, ldo, N);
+  SE_LAUNCH(zero_rows_kernel, grid, dim3(256), 0, stream, out, ldo, N);
   return launched(stream);
 }
 

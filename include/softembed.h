@@ -90,21 +90,21 @@ const char* se_version(void);
  *
  * events: n_events HIP events (hipEvent_t, passed as void*), created by the caller
  * (with timing enabled, to read durations) and owned by it; they must stay valid until
- * the markers are disarmed or exhausted.  After this call, every kernel launch the
- * calling thread makes through this library records the next event of the list on the
- * launch's stream, right after the launch, until n_events have been recorded; later
- * launches record nothing.  An entry point that makes k launches thus records k events
- * in launch order, and the time from the previous marker (or an event the caller
- * recorded just before the call) to marker j is kernel j plus the gap before it.
- * n_events == 0 (events may then be NULL) disarms the markers.  The markers are
- * thread-local: other threads' calls are unaffected.  A failed record is skipped
- * silently (the event is not counted).  Not for use under graph capture.
+ * the kernels that use them have run.  After this call, every kernel the calling thread
+ * launches through this library takes the next two events of the list, in launch order:
+ * the dispatch itself stamps the first with the kernel's start and the second with its
+ * end (hipExtLaunchKernel), so the time between them is that kernel's own duration and
+ * the stream carries no extra command.  Once fewer than two events remain, launches take
+ * none.  An entry point that makes k launches thus uses 2k events.  n_events == 0
+ * (events may then be NULL) disarms the markers.  The markers are thread-local: other
+ * threads' calls are unaffected.  Not for use under graph capture.
  * Errors: SE_ERR_SHAPE if n_events < 0; SE_ERR_NULL if events is NULL with
  * n_events > 0.
  */
 se_status se_set_launch_events(void* const* events, int32_t n_events);
 
-/* Markers recorded since the calling thread last armed them with se_set_launch_events. */
+/* Events handed to launches (two per launch) since the calling thread last armed them
+ * with se_set_launch_events. */
 int32_t se_launch_events_used(void);
 
 /*

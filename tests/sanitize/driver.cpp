@@ -11,6 +11,7 @@
 
 extern int g_launches;
 extern int g_event_records;
+extern int g_marked_launches;
 
 extern "C" {
 int oracle_row_stats(const float* logits, int64_t ld, int64_t n_rows, int64_t vocab,
@@ -108,14 +109,16 @@ static void abi() {
                             I(4), I(5), I(6), static_cast<uint8_t*>(P(7)),
                             static_cast<uint8_t*>(P(8)), nullptr) == SE_ERR_SHAPE);
   EXPECT(se_reduce_partials(F(1), 4, L * d, L, d, d, F(2), d, H(3), d, nullptr) == SE_OK);
-  // launch markers: one event per launch, in order, until the list is used up
-  std::vector<void*> ev(2, P(20));
-  EXPECT(se_set_launch_events(ev.data(), 2) == SE_OK);
-  const int rec0 = g_event_records;
+  // launch markers: two events (start, end) per launch, in order, until fewer than two
+  // remain; the dispatch stamps them, so nothing is recorded on the stream
+  std::vector<void*> ev(5, P(20));
+  EXPECT(se_set_launch_events(ev.data(), 5) == SE_OK);
+  const int rec0 = g_event_records, marked0 = g_marked_launches;
   EXPECT(se_soft_embed_step_onepass(F(1), V, L, V, s, e, H(3), e - s, d, d, 53.f, F(4), d, F(6),
                                     F(7), F(8), I(9), P(5), ws1, nullptr) == SE_OK);
-  EXPECT(se_launch_events_used() == 2);
-  EXPECT(g_event_records - rec0 == 2);
+  EXPECT(se_launch_events_used() == 4);
+  EXPECT(g_marked_launches - marked0 == 2);
+  EXPECT(g_event_records - rec0 == 0);
   EXPECT(se_set_launch_events(nullptr, 0) == SE_OK && se_launch_events_used() == 0);
   EXPECT(se_set_launch_events(nullptr, -1) == SE_ERR_SHAPE);
   EXPECT(g_launches > 30);

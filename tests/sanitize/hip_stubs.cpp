@@ -2,7 +2,8 @@
 // reaches, so that the C ABI's host code (argument checks, work decomposition, workspace
 // layouts, launch markers) can be built with AddressSanitizer and UndefinedBehaviorSanitizer
 // and driven on a machine without a GPU.  Each launcher records that it was reached and,
-// like the real ones, marks the launch; none touches the pointers it is given.
+// like the real ones, takes the next two armed launch events; none touches the pointers it
+// is given.
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
@@ -11,6 +12,7 @@
 
 int g_launches = 0;
 int g_event_records = 0;
+int g_marked_launches = 0;
 
 extern "C" {
 hipError_t hipGetDevice(int* d) {
@@ -30,9 +32,10 @@ hipError_t hipEventRecord(hipEvent_t, hipStream_t) {
 
 namespace se {
 namespace {
-hipError_t launched_stub(hipStream_t s) {
+hipError_t launched_stub(hipStream_t) {
   ++g_launches;
-  mark_launch(s);
+  hipEvent_t start, end;
+  if (next_launch_events(&start, &end)) ++g_marked_launches;
   return hipSuccess;
 }
 }  // namespace
