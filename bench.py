@@ -52,7 +52,7 @@ METRIC = "soft-embed GFLOP/s + steps/s at L_c=256,V=262144,d=2816; % of roofline
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 KERNEL_SOURCES = ["soft_embed.hip", "row_stats.hip", "probs.hip", "onepass.hip", "se_device.h",
-                  "se_launch.h", "api.cpp"]
+                  "se_launch.h", "se_dispatch.h", "api.cpp"]
 # fastest whole-step path of each workload (measured on MI355X)
 BEST_PATH = {"tiny": "step", "rank": "step", "full": "step_onepass", "conv": "step_onepass",
              "batch": "step_onepass"}
