@@ -197,9 +197,9 @@ se_status se_soft_embed(const uint16_t* probs, int64_t ld_probs, int64_t n_rows,
  * se_probs_bf16 (bf16 nearest-even of exp(l - lse)), same accumulation.
  * Not the fast path on MI355X: each 256-column tile of the output pulls the fp32
  * logits through its compute unit again (4 bytes per probability, against 2 for
- * staged bf16), and the per-CU memory path, not HBM, bounds this contraction; the
- * same result comes faster from se_soft_embed_staged (and, with the statistics, from
- * se_soft_embed_step / se_soft_embed_step_onepass).
+ * staged bf16), and the bytes all compute units pull together through L2 and HBM
+ * bound this contraction; the same result comes faster from se_soft_embed_staged
+ * (and, with the statistics, from se_soft_embed_step / se_soft_embed_step_onepass).
  *
  * logits:  fp32 [n_rows, ld_logits]; columns [s, e) are read.
  * row_lse: fp32 [n_rows] from se_row_stats over the FULL width [0, vocab).
