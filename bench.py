@@ -82,8 +82,9 @@ def kernel_hash() -> str:
 
 
 def event_time_us(fn, K: int, warmup: int, settle_ms: float = 0.0) -> float:
-    """Average time of fn() over K back-to-back calls, from events on the current stream,
-    after `warmup` calls (and, with settle_ms, after running fn back to back for that long)."""
+    """Average time of fn() over K back-to-back calls, from two events on the current stream
+    around them (nothing recorded in between), after `warmup` calls (and, with settle_ms,
+    after running fn back to back for that long)."""
     import torch
     if settle_ms > 0:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -97,14 +98,14 @@ def event_time_us(fn, K: int, warmup: int, settle_ms: float = 0.0) -> float:
             spent += e0.elapsed_time(e1)
     for _ in range(warmup):
         fn()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    ev[0].record()
-    for k in range(K):
+    e0.record()
+    for _ in range(K):
         fn()
-        ev[k + 1].record()
+    e1.record()
     torch.cuda.synchronize()
-    return sum(ev[k].elapsed_time(ev[k + 1]) for k in range(K)) * 1e3 / K
+    return e0.elapsed_time(e1) * 1e3 / K
 
 
 def step_bytes_logits_once(w) -> int:
