@@ -668,11 +668,27 @@ def main():
     pb = st.shard.view(torch.bfloat16)
     vend_us = event_time_us(lambda: torch.mm(pa, pb, out_dtype=torch.float32), 10, 5)
     del pa, pb
+    # a read-only stream: the full-width statistics pass over this workload's logits
+    stats_us = event_time_us(lambda: B.se_row_stats(st.x, st.mx, st.lse, st.ent, st.am), K, W,
+                             settle_ms=30)
+    # the matrix cores alone: one workgroup per CU, 8 chains of 32x32x16 bf16 MFMAs per wave
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    loop_iters = 20000
+    loop_out = torch.empty(cus * 256, device=dev)
+    loop_us = event_time_us(lambda: B.se_mfma_loop(loop_out, cus, loop_iters), 10, 3,
+                            settle_ms=60)
+    loop_flop = cus * 4 * 8 * loop_iters * 32 * 32 * 16 * 2
+    del loop_out
     ceilings = {"cold_step_us_median": round(sorted(cold)[len(cold) // 2], 2),
                 "hbm_copy_gbs": round(2 * (1 << 28) * 4 / (copy_us * 1e-6) / 1e9, 1),
+                "hbm_read_gbs": round((4 * L * w.vocab + 16 * L) / (stats_us * 1e-6) / 1e9, 1),
+                "mfma_loop_tflops": round(loop_flop / (loop_us * 1e-6) / 1e12, 1),
                 "bf16_gemm_8192_tflops": round(2 * 8192 ** 3 / (mm_us * 1e-6) / 1e12, 1),
                 "vendor_gemm_same_shape_us": round(vend_us, 2),
-                "vendor_gemm_same_shape_tflops": round(flops / (vend_us * 1e-6) / 1e12, 1)}
+                "vendor_gemm_same_shape_tflops": round(flops / (vend_us * 1e-6) / 1e12, 1),
+                "note": "achievable rates on this box beside the nominal peaks: a device copy "
+                        "(read + write), the statistics pass (read only), se_mfma_loop (bf16 "
+                        "MFMA chains, no memory) and the vendor GEMM"}
 
     cpu, par = None, None
     if not args.no_cpu_baseline:

@@ -29,7 +29,7 @@ EXPORTS = ("se_status_string", "se_version", "se_row_stats", "se_probs_bf16",
            "se_soft_embed_step_onepass_workspace_bytes", "se_soft_embed_step_onepass",
            "se_soft_embed_step_fp8", "se_set_launch_events", "se_launch_events_used",
            "se_soft_embed_splits", "se_soft_embed_step_noalloc_max_bytes",
-           "se_soft_embed_step_noalloc")
+           "se_soft_embed_step_noalloc", "se_mfma_loop")
 
 
 class SoftEmbedError(RuntimeError):
@@ -88,7 +88,8 @@ def _declare(lib):
     lib.se_set_launch_events.argtypes = [vp, i32]
     lib.se_launch_events_used.argtypes = []
     lib.se_launch_events_used.restype = i32
-    for fn in ("se_soft_embed_step_noalloc", "se_set_launch_events", "se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
+    lib.se_mfma_loop.argtypes = [vp, i64, i64, ctypes.c_float, vp]
+    for fn in ("se_mfma_loop", "se_soft_embed_step_noalloc", "se_set_launch_events", "se_row_stats", "se_probs_bf16", "se_soft_embed", "se_soft_embed_fused",
                "se_accept_converge", "se_reduce_partials", "se_quantize_table_fp8",
                "se_soft_embed_fp8", "se_soft_embed_fp8_fused", "se_soft_embed_onepass",
                "se_merge_slices", "se_soft_embed_staged", "se_soft_embed_step",
@@ -243,6 +244,14 @@ def se_reduce_partials(parts, out=None, out_bf16=None, *, stream=None):
         _ptr(parts), t, parts.stride(0), n, d, parts.stride(1), _ptr(out),
         _ld(out) if out is not None else 0, _ptr(out_bf16),
         _ld(out_bf16) if out_bf16 is not None else 0, _stream(stream)))
+
+
+def se_mfma_loop(out, blocks: int, iters: int, unit: float = 1.0, *, stream=None):
+    """The MFMA-rate probe: ``blocks`` workgroups, 8 chains of ``iters`` 32x32x16 bf16 MFMAs
+    per wave, one float per lane into ``out`` (fp32, at least blocks * 256)."""
+    if out.numel() < blocks * 256:
+        raise ValueError("out holds fewer than blocks * 256 floats")
+    _check("se_mfma_loop", lib.se_mfma_loop(_ptr(out), blocks, iters, float(unit), _stream(stream)))
 
 
 def se_quantize_table_fp8(w, codes, row_scale, *, d=None, stream=None):

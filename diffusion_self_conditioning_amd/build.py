@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsoftembed.so")
 SOURCES = ["api.cpp", "row_stats.hip", "probs.hip", "soft_embed.hip", "accept.hip", "reduce.hip",
-           "quant.hip", "onepass.hip", "scratch.hip"]
+           "quant.hip", "onepass.hip", "scratch.hip", "probe.hip"]
 ARCH = os.environ.get("SOFTEMBED_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -515,6 +515,24 @@ se_status se_reduce_partials(const float* parts, int64_t n_parts, int64_t part_s
                              int64_t n_rows, int64_t d, int64_t ld_part, float* out,
                              int64_t ld_out, uint16_t* out_bf16, int64_t ld_bf16, void* stream);
 
+/*
+ * se_mfma_loop -- measurement aid: the bf16 matrix-core rate this device sustains, the
+ * achievable ceiling read beside the nominal peak when the contraction's roofline is
+ * judged (the nominal 2.5 PFLOP/s assumes the 2.4 GHz peak clock; under load the clock
+ * runs lower).  Not part of the soft embedding.
+ *
+ * Launches `blocks` workgroups of 256 threads (4 waves).  Each wave runs 8 independent
+ * chains of `iters` v_mfma_f32_32x32x16_bf16 (32 x 32 x 16, fp32 accumulate) on register
+ * operands whose every element is bf16(unit) (unit's top 16 bits), reads no memory, and
+ * stores one float per lane: the sum of its 8 x 16 accumulator elements, so
+ *     out[b * 256 + t] = 8 * 16 * iters * (16 * bf16(unit)^2)   (fp32, exact when small).
+ * Work per call: blocks * 4 * 8 * iters * 32,768 FLOP.
+ * out: fp32 [blocks * 256], 4-byte aligned, written.
+ * Errors: SE_ERR_SHAPE unless 1 <= blocks <= 65,536 and 1 <= iters <= 2^24; SE_ERR_NULL
+ * if out is NULL; SE_ERR_ALIGN if out is not 4-byte aligned.
+ */
+se_status se_mfma_loop(float* out, int64_t blocks, int64_t iters, float unit, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

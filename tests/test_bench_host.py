@@ -77,8 +77,8 @@ def test_traffic_lookup_requires_the_current_kernel_sources(tmp_path, monkeypatc
 def test_kernel_hash_covers_every_source_of_the_timed_kernels():
     csrc = os.path.join(ROOT, "diffusion_self_conditioning_amd", "csrc")
     # kernels no timed step launches: the sampler, the e4m3 quantiser, the partial sum
-    # across ranks and the no-allocation entry point's array
-    outside = {"accept.hip", "quant.hip", "reduce.hip", "scratch.hip"}
+    # across ranks, the no-allocation entry point's array and the MFMA-rate probe
+    outside = {"accept.hip", "quant.hip", "reduce.hip", "scratch.hip", "probe.hip"}
     sources = {f for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp"))}
     assert sources - outside == set(bench.KERNEL_SOURCES)
 

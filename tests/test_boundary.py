@@ -496,3 +496,12 @@ def test_launch_markers_and_split_query():
     assert b.se_soft_embed_splits(16, 0, 64, 256) == 1
     assert b.se_soft_embed_ranges(16, 0, 100, 256) == [0, 100]
     assert b.se_soft_embed_splits(0, 0, 64, 256) == 0 and b.se_soft_embed_splits(4, 8, 8, 16) == 0
+
+
+def test_mfma_loop_errors():
+    assert lib.se_mfma_loop(P1, 0, 10, 1.0, None) == b.SE_ERR_SHAPE
+    assert lib.se_mfma_loop(P1, 65537, 10, 1.0, None) == b.SE_ERR_SHAPE
+    assert lib.se_mfma_loop(P1, 1, 0, 1.0, None) == b.SE_ERR_SHAPE
+    assert lib.se_mfma_loop(P1, 1, (1 << 24) + 1, 1.0, None) == b.SE_ERR_SHAPE
+    assert lib.se_mfma_loop(None, 1, 1, 1.0, None) == b.SE_ERR_NULL
+    assert lib.se_mfma_loop(P1 + 2, 1, 1, 1.0, None) == b.SE_ERR_ALIGN
