@@ -2,7 +2,8 @@
 
 The library allocates nothing, never synchronises and never reads device data on the
 host, so a caller can capture a whole step into a graph (torch.cuda.graph drives the
-capture on its own stream).  Every replay here is checked bit for bit against an eager
+capture on its own stream); se_soft_embed_step_noalloc, the entry point for callers that
+cannot allocate, is captured too.  Every replay here is checked bit for bit against an eager
 call on the same inputs; the inputs change between replays (new logits copied into the
 captured buffer), with the program's own eager work and synchronisations in between.
 """
@@ -28,7 +29,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("which", ["step", "step_onepass", "staged", "step_held_slice", "step_fp8"])
+@pytest.mark.parametrize("which", ["step", "step_onepass", "staged", "step_held_slice", "step_fp8",
+                                   "step_noalloc"])
 def test_captured_step_replays_match_eager_calls(which):
     L, V, s, e, d = 256, 30000, 8000, 20000, 512
     if which == "step_held_slice":          # two whole 16,384-position groups: kept in registers
@@ -52,6 +54,8 @@ def test_captured_step_replays_match_eager_calls(which):
     def call():
         if which in ("step", "step_held_slice"):
             B.se_soft_embed_step(x_t, s, e, w_t, 2.0, out, mx, lse, ent, am, ws)
+        elif which == "step_noalloc":           # the library's own workspace: nothing to pass
+            B.se_soft_embed_step_noalloc(x_t, s, e, w_t, 2.0, out, mx, lse, ent, am)
         elif which == "step_onepass":
             B.se_soft_embed_step_onepass(x_t, s, e, w_t, 2.0, out, mx, lse, ent, am, ws)
         elif which == "step_fp8":
