@@ -663,10 +663,22 @@ namespace {
 //   - group 1 loads table step s + 3 in M(s) into the buffer of step s - 1 (released by its
 //     own M(s - 1)) and, keeping its last 8 loads in flight, has step s + 1 in LDS at the
 //     end of M(s).
+// Splits of at least kThreeStageMin super-steps (bf16 table) take a third probability
+// stage buffer, in the 32 KB the e4m3 code ring uses otherwise: group 0 then loads stage
+// t + 2 in two halves, in M(2 t) and M(2 t + 1), into the buffer stage t - 1 held, and waits
+// for stage t + 1 at the end of C(2 t + 1) with stage t + 2's 8 loads still in flight.  Half
+// a stage per M phase instead of a whole one every other phase keeps group 0's M phases
+// short of the other group's MFMAs, and the stage arrives a step earlier.  The loop is
+// unrolled over the three-buffer cycle so that every buffer is a distinct LDS array at
+// compile time (with run-time buffer offsets the compiler cannot tell the stage loads from
+// the fragment reads and serialises them).  Same MFMAs in the same order: bitwise equal.
+// Short splits (the one-rank slice) keep two buffers: there the longer prologue and the
+// extra tail loads cost more than the schedule gains (measured).
 constexpr int kPPStage = 64;                      // positions per probability stage
 constexpr int kPPStageBytes = kBM * kPPStage * 2; // [256 rows][64 positions] bf16
 constexpr int kPPStepBytes = kBK * kBN * 2;       // [32 rows][256 columns] bf16
-static_assert(2 * kPPStageBytes + 4 * kPPStepBytes <= 160 * 1024, "LDS budget of one CU");
+constexpr int kThreeStageMin = 32;                // super-steps of a split for three stages
+static_assert(3 * kPPStageBytes + 4 * kPPStepBytes <= 160 * 1024, "LDS budget of one CU");
 // probability stage: row m at 128 m bytes, 16-byte chunk c (8 positions) at c ^ pp_swz(m).
 // A fragment read takes one chunk of 32 consecutive rows; the swizzle gives every 8 (and
 // every 16) consecutive rows distinct 16-byte slots of a 128-byte (256-byte) bank line.
@@ -694,7 +706,7 @@ __device__ __forceinline__ void phase_end() {
 }
 constexpr int kNoVmWait = 63;
 constexpr int kPP8RawBytes = kBK * kBN;           // [32 rows][256 columns] e4m3 codes
-static_assert(2 * kPPStageBytes + 4 * kPPStepBytes + 4 * kPP8RawBytes <= 160 * 1024, "LDS budget");
+static_assert(4 * kPP8RawBytes == kPPStageBytes, "the e4m3 code ring fills the third stage buffer");
 // s_waitcnt with vmcnt(n) only
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -718,9 +730,14 @@ soft_embed_pp_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char P0[kPPStageBytes], P1[kPPStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char W0[kPPStepBytes], W1[kPPStepBytes];
   __shared__ __attribute__((aligned(16))) unsigned char W2[kPPStepBytes], W3[kPPStepBytes];
-  // e4m3 table: the codes of four steps as loaded ([32 rows][256 codes], row r at 256 r)
-  __shared__ __attribute__((aligned(16))) unsigned char R0[W8 ? kPP8RawBytes : 16], R1[W8 ? kPP8RawBytes : 16];
-  __shared__ __attribute__((aligned(16))) unsigned char R2[W8 ? kPP8RawBytes : 16], R3[W8 ? kPP8RawBytes : 16];
+  // the third probability stage (bf16 table, long splits), or the e4m3 codes of four steps
+  // as loaded ([32 rows][256 codes], row r at 256 r)
+  __shared__ __attribute__((aligned(16))) unsigned char X[kPPStageBytes];
+  unsigned char* const P2 = X;
+  unsigned char* const R0 = X;
+  unsigned char* const R1 = X + kPP8RawBytes;
+  unsigned char* const R2 = X + 2 * kPP8RawBytes;
+  unsigned char* const R3 = X + 3 * kPP8RawBytes;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave >> 2, q = wave & 3;
   const int wm = wave / kWN, wn = wave % kWN;
@@ -736,6 +753,7 @@ soft_embed_pp_kernel(const GemmParams p) {
   const int64_t k_hi = min((((int64_t)(s + 1) * p.kblocks) / p.splits) * kSplitQuantum, p.K);
   const int nq = (int)((min(k_hi, (p.K / kSS) * kSS) - k_lo) / kSS);
   const int nsteps = kQ * nq;
+  const bool three = !W8 && nq >= kThreeStageMin;   // the same for every wave of the workgroup
   // rows of this tile that exist; rows past them load row tile_rows - 1 again (finite data,
   // every load in bounds) and are never written out
   const int tile_rows = min(kBM, (int)p.M - m0);
@@ -802,6 +820,15 @@ soft_embed_pp_kernel(const GemmParams p) {
     const uint32_t soff = (uint32_t)((k0 / kSuperStep) * a_blk + 2 * (k0 % kSuperStep));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(buf + 1024 * (8 * q + i)),
+                                               16, voff[i], soff, 0, 0);
+  };
+  // half h of that stage: each wave's rows 64 q + 32 h .. + 31
+  auto load_half = [&](unsigned char* buf, int ps, int h) {
+    const int64_t k0 = k_lo + (int64_t)kPPStage * min(ps, 2 * nq - 1);
+    const uint32_t soff = (uint32_t)((k0 / kSuperStep) * a_blk + 2 * (k0 % kSuperStep));
+#pragma unroll
+    for (int i = 4 * h; i < 4 * h + 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(buf + 1024 * (8 * q + i)),
                                                16, voff[i], soff, 0, 0);
   };
@@ -889,9 +916,58 @@ soft_embed_pp_kernel(const GemmParams p) {
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // three stages: super-step qd with stage 2 qd in pa, 2 qd + 1 in pb, and stage 2 qd + 2
+  // loaded into pc (the buffer stage 2 qd - 1 held), stage 2 qd + 3 into pa
+  auto g0_super = [&](int qd, unsigned char* pa, unsigned char* pb, unsigned char* pc) {
+    load_half(pc, 2 * qd + 2, 0);
+    m_phase(pa, W0, 0);
+    phase_end<kNoVmWait>();
+    c_phase();
+    phase_end<kNoVmWait>();
+    load_half(pc, 2 * qd + 2, 1);
+    m_phase(pa, W1, 1);
+    phase_end<kNoVmWait>();
+    c_phase();
+    phase_end<8>();                             // stage 2 qd + 1 in LDS
+    load_half(pa, 2 * qd + 3, 0);
+    m_phase(pb, W2, 0);
+    phase_end<kNoVmWait>();
+    c_phase();
+    phase_end<kNoVmWait>();
+    load_half(pa, 2 * qd + 3, 1);
+    m_phase(pb, W3, 1);
+    phase_end<kNoVmWait>();
+    c_phase();
+    phase_end<8>();                             // stage 2 qd + 2 in LDS
+  };
+  auto g1_super = [&](int qd, unsigned char* pa, unsigned char* pb) {
+    const int s0 = kQ * qd;
+    load_step(W3, s0 + 3);
+    m_phase(pa, W0, 0);
+    phase_end<8>();                             // table step s0 + 1 in LDS
+    c_phase();
+    phase_end<kNoVmWait>();
+    load_step(W0, s0 + 4);
+    m_phase(pa, W1, 1);
+    phase_end<8>();
+    c_phase();
+    phase_end<kNoVmWait>();
+    load_step(W1, s0 + 5);
+    m_phase(pb, W2, 0);
+    phase_end<8>();
+    c_phase();
+    phase_end<kNoVmWait>();
+    load_step(W2, s0 + 6);
+    m_phase(pb, W3, 1);
+    phase_end<8>();
+    c_phase();
+    phase_end<kNoVmWait>();
+  };
+
   if (nq > 0) {
     if (grp == 0) {
       load_stage(P0, 0);
+      if (three) load_stage(P1, 1);
     } else if constexpr (!W8) {
       load_step(W0, 0);
       load_step(W1, 1);
@@ -901,12 +977,37 @@ soft_embed_pp_kernel(const GemmParams p) {
       load_step8(R1, 1, sc1);
       load_step8(R2, 2, sc2);
     }
-    phase_end<0>();
+    if (three && grp == 0)
+      phase_end<8>();                           // stage 0 in LDS; stage 1 may be in flight
+    else
+      phase_end<0>();
     if constexpr (W8) {                         // table step 0 as bf16 before anyone reads it
       if (grp == 1) convert8(R0, W0, sc0);
       phase_end<0>();
     }
-    if (grp == 0) {
+    if (three) {
+      // buffers of stages 2 qd, 2 qd + 1, 2 qd + 2 for qd = 0, 1, 2 (mod 3)
+      int qd = 0;
+      if (grp == 0) {
+        for (; qd + 3 <= nq; qd += 3) {
+          g0_super(qd, P0, P1, P2);
+          g0_super(qd + 1, P2, P0, P1);
+          g0_super(qd + 2, P1, P2, P0);
+        }
+        if (qd < nq) g0_super(qd, P0, P1, P2);
+        if (qd + 1 < nq) g0_super(qd + 1, P2, P0, P1);
+        phase_end<kNoVmWait>();                 // pairs with group 1's first barrier
+      } else {
+        phase_end<kNoVmWait>();                 // one phase behind group 0
+        for (; qd + 3 <= nq; qd += 3) {
+          g1_super(qd, P0, P1);
+          g1_super(qd + 1, P2, P0);
+          g1_super(qd + 2, P1, P2);
+        }
+        if (qd < nq) g1_super(qd, P0, P1);
+        if (qd + 1 < nq) g1_super(qd + 1, P2, P0);
+      }
+    } else if (grp == 0) {
       for (int qd = 0; qd < nq; ++qd) {         // steps 4 qd .. 4 qd + 3: stages 2 qd, 2 qd + 1
         load_stage(P1, 2 * qd + 1);
         m_phase(P0, W0, 0);

@@ -23,6 +23,7 @@ from diffusion_self_conditioning_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
+    from diffusion_self_conditioning_amd import _binding as B
     from diffusion_self_conditioning_amd import api
 
 DEV = "cuda:0"
@@ -89,12 +90,27 @@ TILE_CASES = {
     "k12345": (512, 50000, 12344, 24689, 520, 66),
     "k65553": (256, 70000, 0, 65553, 256, 67),
     "d16": (256, 5000, 0, 4097, 16, 68),          # one n-tile of 16 columns: clamped loads
+    # splits of at least 32 super-steps take three probability stage buffers, the loop
+    # unrolled over their cycle: split lengths of every remainder mod 3 (50/51, 113/114,
+    # 48/49 super-steps), ragged tails, two row tiles, 64 splits
+    "three-stages": (256, 150012, 8, 150003, 2816, 69),
+    "three-stages-two-tiles": (512, 160012, 8, 160011, 2816, 70),
+    "three-stages-64-splits": (256, 400012, 8, 400011, 512, 71),
 }
+
+
+def three_stage_splits(L, s, e, d):
+    """Whether every split of this contraction holds at least 32 whole super-steps (of 128
+    positions), the length from which the contraction keeps three probability stages."""
+    bounds = B.se_soft_embed_ranges(L, s, e, d)
+    return min((b - a) // 128 for a, b in zip(bounds, bounds[1:])) >= 32
 
 
 @pytest.mark.parametrize("case", sorted(TILE_CASES))
 def test_staged_whole_tiles_equals_fused(case):
     L, V, s, e, d, seed = TILE_CASES[case]
+    if case.startswith("three-stages"):
+        assert three_stage_splits(L, s, e, d), case
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
     x[np.arange(L), rng.integers(0, V, L)] += 8.0

@@ -112,6 +112,9 @@ CASES = {
     "whole-tile": (256, 30003, 1000, 13337, 272, 10),   # ping-pong contraction, tail
     "merge-in-contraction": (13, 20008, 8, 20008, 48, 11),
     "merge-row-tiles": (511, 100011, 8, 100008, 520, 12),
+    # splits of at least 32 super-steps: three probability stage buffers in the contraction
+    "three-stages": (17, 150011, 8, 150003, 2816, 13),
+    "three-stages-two-tiles": (300, 160011, 8, 160011, 2816, 14),
 }
 
 
@@ -135,6 +138,9 @@ def test_step_onepass_parity(case):
     L, V, s, e, d, seed = CASES[case]
     if case.startswith("merge"):
         assert merges_in_contraction(L, e - s, d), case
+    if case.startswith("three-stages"):
+        bounds = B.se_soft_embed_ranges(L, s, e, d)
+        assert min((b - a) // 128 for a, b in zip(bounds, bounds[1:])) >= 32, case
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
     # half the rows peak inside the slice, half anywhere in the row
