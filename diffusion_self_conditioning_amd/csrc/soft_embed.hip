@@ -686,6 +686,15 @@ __device__ __forceinline__ int pp_swz(int m) { return ((m >> 1) ^ ((m & 1) << 2)
 __device__ __forceinline__ int pp_off(int m, int c) { return m * 128 + 16 * (c ^ pp_swz(m)); }
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// An LDS array of its own for each tag.  Loads into one and reads of another stay apart: the
+// compiler tells LDS objects apart, but not two ranges of one object that a buffer load
+// fills, and it would wait for such loads before every read.
+template <int Tag, int Bytes>
+__device__ __forceinline__ unsigned char* lds_array() {
+  __shared__ __attribute__((aligned(16))) unsigned char a[Bytes];
+  return a;
+}
+
 // s_waitcnt with vmcnt(n) and lgkmcnt(0) (expcnt not waited on)
 template <int n>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -731,13 +740,17 @@ soft_embed_pp_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char W0[kPPStepBytes], W1[kPPStepBytes];
   __shared__ __attribute__((aligned(16))) unsigned char W2[kPPStepBytes], W3[kPPStepBytes];
   // the third probability stage (bf16 table, long splits), or the e4m3 codes of four steps
-  // as loaded ([32 rows][256 codes], row r at 256 r)
-  __shared__ __attribute__((aligned(16))) unsigned char X[kPPStageBytes];
-  unsigned char* const P2 = X;
-  unsigned char* const R0 = X;
-  unsigned char* const R1 = X + kPP8RawBytes;
-  unsigned char* const R2 = X + 2 * kPP8RawBytes;
-  unsigned char* const R3 = X + 3 * kPP8RawBytes;
+  // as loaded ([32 rows][256 codes], row r at 256 r): each its own LDS array, declared only
+  // in the form that uses it
+  unsigned char *P2 = nullptr, *R0 = nullptr, *R1 = nullptr, *R2 = nullptr, *R3 = nullptr;
+  if constexpr (W8) {
+    R0 = lds_array<10, kPP8RawBytes>();
+    R1 = lds_array<11, kPP8RawBytes>();
+    R2 = lds_array<12, kPP8RawBytes>();
+    R3 = lds_array<13, kPP8RawBytes>();
+  } else {
+    P2 = lds_array<2, kPPStageBytes>();
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave >> 2, q = wave & 3;
   const int wm = wave / kWN, wn = wave % kWN;
