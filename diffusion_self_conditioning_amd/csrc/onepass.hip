@@ -155,19 +155,17 @@ __device__ __forceinline__ void step_range(const StepRanges& g, int r, int64_t& 
 }
 
 // W wavefronts (1, 2, 4 or 8) of a workgroup share one (row, range); wave k of the group
-// takes the k-th of W near-equal, 4-aligned pieces, at most 3072 positions (12 16-byte
-// groups per lane, held in registers between the maximum and the sums).  The group
-// combines its maxima and then its sums through LDS in wave order.
-constexpr int kSweepNF4 = 12;
-static_assert(kSweepPiece == 64 * 4 * kSweepNF4, "a wave holds 12 groups of 4 per lane");
+// takes the k-th of W near-equal, 4-aligned pieces, at most 64 NF4 positions (NF4 = 12 or
+// 16 16-byte groups per lane, held in registers between the maximum and the sums).  The
+// group combines its maxima and then its sums through LDS in wave order.
+static_assert(kSweepPiece == 64 * 4 * 12 && kSweepPieceWide == 64 * 4 * 16, "sweep pieces");
 
-template <int W>
+template <int W, int NF4>
 __global__ void __launch_bounds__(sweep_threads(W))
 step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, StepRanges g,
                   int n_ranges, uint16_t* __restrict__ probs, float4* __restrict__ stats,
                   int32_t* __restrict__ stat_arg) {
   constexpr int kWaves = sweep_threads(W) / 64;
-  constexpr int NF4 = kSweepNF4;
   __shared__ float grp_v[kWaves], grp_z[kWaves], grp_s[kWaves];
   __shared__ int grp_i[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -352,7 +350,7 @@ hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_
 }
 
 hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
-                             const StepRanges& g, int waves, uint16_t* probs, float* stats,
+                             const StepRanges& g, SweepShape sw, uint16_t* probs, float* stats,
                              int32_t* stat_arg, hipStream_t stream) {
   const int n_ranges = g.n_pre + g.splits + g.n_post;
   float4* st = reinterpret_cast<float4*>(stats);
@@ -363,11 +361,16 @@ hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
                        n_ranges, probs, st, stat_arg);
     return launched(stream);
   };
-  switch (waves) {
-    case 1: return go(step_sweep_kernel<1>, 1);
-    case 2: return go(step_sweep_kernel<2>, 2);
-    case 4: return go(step_sweep_kernel<4>, 4);
-    case 8: return go(step_sweep_kernel<8>, 8);
+  if (sw.groups == 16) {
+    if (sw.waves == 4) return go(step_sweep_kernel<4, 16>, 4);
+    return hipErrorInvalidValue;
+  }
+  if (sw.groups != 12) return hipErrorInvalidValue;
+  switch (sw.waves) {
+    case 1: return go(step_sweep_kernel<1, 12>, 1);
+    case 2: return go(step_sweep_kernel<2, 12>, 2);
+    case 4: return go(step_sweep_kernel<4, 12>, 4);
+    case 8: return go(step_sweep_kernel<8, 12>, 8);
     default: return hipErrorInvalidValue;
   }
 }

@@ -49,18 +49,24 @@ struct GemmPlan {
 int device_cu_count();
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 
+// Positions one wave of the sweep holds in registers: 12 16-byte groups per lane, or 16
+// (the wide form, taken only where it lets 4 waves hold a range that would take 8).
+constexpr int kSweepPiece = 64 * 4 * 12;
+constexpr int kSweepPieceWide = 64 * 4 * 16;
+
+// Waves per range (1, 2, 4 or 8; 0 when the ranges are too long) and 16-byte groups per
+// lane (12 or 16) of the register sweep over the split ranges of `g`.
+struct SweepShape {
+  int waves, groups;
+};
+SweepShape sweep_shape(const GemmPlan& g, int64_t K);
+
 struct OnepassLayout {
   GemmPlan g;
   int64_t rows_pad;
-  int sweep_waves;        // waves per range of the register sweep (0: ranges too long)
+  SweepShape sweep;
   size_t off_probs, off_parts, off_stats, off_arg, off_fac, total;
 };
-
-// Positions one wave of the sweep holds in registers (12 16-byte groups per lane).
-constexpr int kSweepPiece = 64 * 4 * 12;
-
-// Waves per range (1, 2, 4 or 8) that hold the longest split range of `g`, or 0.
-int sweep_waves(const GemmPlan& g, int64_t K);
 
 OnepassLayout onepass_layout(int64_t n_rows, int64_t K, int64_t d);
 
@@ -171,10 +177,11 @@ struct StepRanges {
 // One read of every logit: per (row, range) maximum, first argmax (a vocabulary id),
 // Z and S1 against the range maximum (stats[r * n_rows + row] = {m, Z, S1 nats, m},
 // stat_arg likewise), and for the slice's split ranges the bf16 probabilities against
-// the range maximum in the super-step-tiled layout.  `waves` (1, 2, 4 or 8) wavefronts
-// share a range of at most waves * kSweepPiece positions.
+// the range maximum in the super-step-tiled layout.  sw.waves (1, 2, 4 or 8) wavefronts
+// share a range of at most waves * 256 * sw.groups positions (sw.groups 16 only with 4
+// waves).
 hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
-                             const StepRanges& g, int waves, uint16_t* probs, float* stats,
+                             const StepRanges& g, SweepShape sw, uint16_t* probs, float* stats,
                              int32_t* stat_arg, hipStream_t stream);
 
 // Merge of each row's range statistics: row max / lse / entropy / argmax, and the

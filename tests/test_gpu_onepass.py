@@ -102,6 +102,8 @@ CASES = {
     # 2 x 3 output tiles with ragged rows and columns
     "merge-in-contraction": (13, 20008, 8, 20008, 48, 11),
     "merge-row-tiles": (511, 100008, 8, 100008, 520, 12),
+    # split ranges of 12,289 .. 16,384 positions: the sweep's 4-wave, 16-group form
+    "wide-sweep": (16, 330008, 8, 330008, 2816, 13),
 }
 
 
@@ -125,6 +127,9 @@ def test_onepass_parity(case):
     L, V, s, e, d, seed = CASES[case]
     if case.startswith("merge"):
         assert merges_in_contraction(L, e - s, d), case
+    if case == "wide-sweep":
+        bounds = B.se_soft_embed_ranges(L, s, e, d)
+        assert 4 * 3072 < max(b - a for a, b in zip(bounds, bounds[1:])) <= 4 * 4096, case
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
     # plant each row's maximum in a different place (any split range may hold it)

@@ -115,6 +115,10 @@ CASES = {
     # splits of at least 32 super-steps: three probability stage buffers in the contraction
     "three-stages": (17, 150011, 8, 150003, 2816, 13),
     "three-stages-two-tiles": (300, 160011, 8, 160011, 2816, 14),
+    # split ranges of 12,289 .. 16,384 positions: the sweep's 4-wave, 16-group form, with
+    # ranges before and after the slice cut at 16,384
+    "wide-sweep": (16, 330011, 8, 330008, 2816, 15),
+    "wide-sweep-mid-slice": (16, 400011, 40000, 370000, 2816, 16),
 }
 
 
@@ -138,6 +142,9 @@ def test_step_onepass_parity(case):
     L, V, s, e, d, seed = CASES[case]
     if case.startswith("merge"):
         assert merges_in_contraction(L, e - s, d), case
+    if case.startswith("wide-sweep"):
+        bounds = B.se_soft_embed_ranges(L, s, e, d)
+        assert 4 * 3072 < max(b - a for a, b in zip(bounds, bounds[1:])) <= 4 * 4096, case
     if case.startswith("three-stages"):
         bounds = B.se_soft_embed_ranges(L, s, e, d)
         assert min((b - a) // 128 for a, b in zip(bounds, bounds[1:])) >= 32, case
