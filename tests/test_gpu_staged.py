@@ -90,27 +90,34 @@ TILE_CASES = {
     "k12345": (512, 50000, 12344, 24689, 520, 66),
     "k65553": (256, 70000, 0, 65553, 256, 67),
     "d16": (256, 5000, 0, 4097, 16, 68),          # one n-tile of 16 columns: clamped loads
-    # splits of at least 32 super-steps take three probability stage buffers, the loop
-    # unrolled over their cycle: split lengths of every remainder mod 3 (50/51, 113/114,
-    # 48/49 super-steps), ragged tails, two row tiles, 64 splits
-    "three-stages": (256, 150012, 8, 150003, 2816, 69),
-    "three-stages-two-tiles": (512, 160012, 8, 160011, 2816, 70),
-    "three-stages-64-splits": (256, 400012, 8, 400011, 512, 71),
+    # the contraction cycles three probability stage buffers, its loop unrolled over the
+    # cycle: long splits with lengths of every remainder mod 3 (50/51, 113/114, 48/49
+    # super-steps), ragged tails, two row tiles, 64 splits
+    "long-splits": (256, 150012, 8, 150003, 2816, 69),
+    "long-splits-two-tiles": (512, 160012, 8, 160011, 2816, 70),
+    "long-splits-64-splits": (256, 400012, 8, 400011, 512, 71),
+    # splits of one to five super-steps: the stage loads past a split's end clamped to its
+    # last stage, the cycle cut after one or two super-steps
+    "short-splits-1-2": (256, 1500, 8, 1011, 2816, 72),
+    "short-splits-2-3": (256, 3500, 8, 3011, 2816, 73),
+    "short-splits-4-5": (512, 5600, 8, 5011, 2816, 74),
 }
 
 
-def three_stage_splits(L, s, e, d):
-    """Whether every split of this contraction holds at least 32 whole super-steps (of 128
-    positions), the length from which the contraction keeps three probability stages."""
+def split_super_steps(L, s, e, d):
+    """The whole super-steps (of 128 positions) of each split of this contraction."""
     bounds = B.se_soft_embed_ranges(L, s, e, d)
-    return min((b - a) // 128 for a, b in zip(bounds, bounds[1:])) >= 32
+    return [(b - a) // 128 for a, b in zip(bounds, bounds[1:])]
 
 
 @pytest.mark.parametrize("case", sorted(TILE_CASES))
 def test_staged_whole_tiles_equals_fused(case):
     L, V, s, e, d, seed = TILE_CASES[case]
-    if case.startswith("three-stages"):
-        assert three_stage_splits(L, s, e, d), case
+    if case.startswith("long-splits"):
+        assert min(split_super_steps(L, s, e, d)) >= 32, case
+    if case.startswith("short-splits"):
+        n = split_super_steps(L, s, e, d)
+        assert 1 <= min(n) <= max(n) <= 5, case
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
     x[np.arange(L), rng.integers(0, V, L)] += 8.0

@@ -112,9 +112,9 @@ CASES = {
     "whole-tile": (256, 30003, 1000, 13337, 272, 10),   # ping-pong contraction, tail
     "merge-in-contraction": (13, 20008, 8, 20008, 48, 11),
     "merge-row-tiles": (511, 100011, 8, 100008, 520, 12),
-    # splits of at least 32 super-steps: three probability stage buffers in the contraction
-    "three-stages": (17, 150011, 8, 150003, 2816, 13),
-    "three-stages-two-tiles": (300, 160011, 8, 160011, 2816, 14),
+    # splits of at least 32 super-steps: the contraction's unrolled three-buffer cycle
+    "long-splits": (17, 150011, 8, 150003, 2816, 13),
+    "long-splits-two-tiles": (300, 160011, 8, 160011, 2816, 14),
     # split ranges of 12,289 .. 16,384 positions: the sweep's 4-wave, 16-group form, with
     # ranges before and after the slice cut at 16,384
     "wide-sweep": (16, 330011, 8, 330008, 2816, 15),
@@ -145,7 +145,7 @@ def test_step_onepass_parity(case):
     if case.startswith("wide-sweep"):
         bounds = B.se_soft_embed_ranges(L, s, e, d)
         assert 4 * 3072 < max(b - a for a, b in zip(bounds, bounds[1:])) <= 4 * 4096, case
-    if case.startswith("three-stages"):
+    if case.startswith("long-splits"):
         bounds = B.se_soft_embed_ranges(L, s, e, d)
         assert min((b - a) // 128 for a, b in zip(bounds, bounds[1:])) >= 32, case
     rng = np.random.default_rng(seed)
