@@ -650,32 +650,34 @@ namespace {
 //     while the other wave waits on LDS and memory.  Every phase ends with a workgroup
 //     barrier; group 1 takes one extra barrier before its loop and group 0 one after it.
 //   - Operands go from memory to LDS with buffer_load ... lds: no staging registers and no
-//     LDS writes in the loop.  Group 0 loads the probability stages (64 positions, 32 KB;
-//     with the e4m3 table two buffers, a whole stage in the M phase of every other step,
-//     with the bf16 table three buffers, below); group 1 the table steps (32 positions,
-//     16 KB, ring of four, three steps ahead).
+//     LDS writes in the loop.  Group 0 loads the probability stages (64 positions, 32 KB,
+//     two buffers, a whole stage in the M phase of every other step); group 1 the table
+//     steps (32 positions, 16 KB, ring of four, three steps ahead).
 //   - Every buffer is its own LDS array and the barriers are plain s_barrier with the wait
 //     counts written out (empty asm memory clobbers keep LDS accesses on their side), so a
 //     wave waits only for the loads the next phases read.
 // When a step's data lands, for step s (group 0's M(s) follows barrier 2 s, group 1's one
 // barrier later):
-//   - two stage buffers: group 0 loads stage t + 1 in M(2 t) into the buffer stage t - 1 held (released by
+//   - group 0 loads stage t + 1 in M(2 t) into the buffer stage t - 1 held (released by
 //     group 1's M(2 t - 1)) and waits for it at the end of C(2 t + 1);
 //   - group 1 loads table step s + 3 in M(s) into the buffer of step s - 1 (released by its
 //     own M(s - 1)) and, keeping its last 8 loads in flight, has step s + 1 in LDS at the
 //     end of M(s).
-// With the bf16 table the contraction keeps a third probability stage buffer, in the
-// 32 KB the e4m3 code ring uses otherwise: group 0 then loads stage t + 2 in two halves, in
-// M(2 t) and M(2 t + 1), into the buffer stage t - 1 held, and waits for stage t + 1 at the
-// end of C(2 t + 1) with stage t + 2's 8 loads still in flight.  Half a stage per M phase
-// instead of a whole one every other phase keeps group 0's M phases short of the other
-// group's MFMAs, and the stage arrives a step earlier.  The loop is unrolled over the
-// three-buffer cycle so that every buffer is a distinct LDS array at compile time (with
-// run-time buffer offsets the compiler cannot tell the stage loads from the fragment reads
-// and serialises them).  Same MFMAs in the same order: bitwise equal to two buffers.
+// Splits of at least kThreeStageMin super-steps (bf16 table) take a third probability
+// stage buffer, in the 32 KB the e4m3 code ring uses otherwise: group 0 then loads stage
+// t + 2 in two halves, in M(2 t) and M(2 t + 1), into the buffer stage t - 1 held, and waits
+// for stage t + 1 at the end of C(2 t + 1) with stage t + 2's 8 loads still in flight.  Half
+// a stage per M phase instead of a whole one every other phase keeps group 0's M phases
+// short of the other group's MFMAs, and the stage arrives a step earlier.  The loop is
+// unrolled over the three-buffer cycle so that every buffer is a distinct LDS array at
+// compile time (with run-time buffer offsets the compiler cannot tell the stage loads from
+// the fragment reads and serialises them).  Same MFMAs in the same order: bitwise equal.
+// Short splits (the one-rank slice) keep two buffers: there the longer prologue and the
+// extra tail loads cost more than the schedule gains (measured).
 constexpr int kPPStage = 64;                      // positions per probability stage
 constexpr int kPPStageBytes = kBM * kPPStage * 2; // [256 rows][64 positions] bf16
 constexpr int kPPStepBytes = kBK * kBN * 2;       // [32 rows][256 columns] bf16
+constexpr int kThreeStageMin = 32;                // super-steps of a split for three stages
 static_assert(3 * kPPStageBytes + 4 * kPPStepBytes <= 160 * 1024, "LDS budget of one CU");
 // probability stage: row m at 128 m bytes, 16-byte chunk c (8 positions) at c ^ pp_swz(m).
 // A fragment read takes one chunk of 32 consecutive rows; the swizzle gives every 8 (and
@@ -737,7 +739,7 @@ soft_embed_pp_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char P0[kPPStageBytes], P1[kPPStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char W0[kPPStepBytes], W1[kPPStepBytes];
   __shared__ __attribute__((aligned(16))) unsigned char W2[kPPStepBytes], W3[kPPStepBytes];
-  // the third probability stage (bf16 table), or the e4m3 codes of four steps
+  // the third probability stage (bf16 table, long splits), or the e4m3 codes of four steps
   // as loaded ([32 rows][256 codes], row r at 256 r): each its own LDS array, declared only
   // in the form that uses it
   unsigned char *P2 = nullptr, *R0 = nullptr, *R1 = nullptr, *R2 = nullptr, *R3 = nullptr;
@@ -764,7 +766,7 @@ soft_embed_pp_kernel(const GemmParams p) {
   const int64_t k_hi = min((((int64_t)(s + 1) * p.kblocks) / p.splits) * kSplitQuantum, p.K);
   const int nq = (int)((min(k_hi, (p.K / kSS) * kSS) - k_lo) / kSS);
   const int nsteps = kQ * nq;
-  constexpr bool three = !W8;                    // three probability stage buffers
+  const bool three = !W8 && nq >= kThreeStageMin;   // the same for every wave of the workgroup
   // rows of this tile that exist; rows past them load row tile_rows - 1 again (finite data,
   // every load in bounds) and are never written out
   const int tile_rows = min(kBM, (int)p.M - m0);
@@ -996,7 +998,7 @@ soft_embed_pp_kernel(const GemmParams p) {
       if (grp == 1) convert8(R0, W0, sc0);
       phase_end<0>();
     }
-    if constexpr (three) {
+    if (three) {
       // buffers of stages 2 qd, 2 qd + 1, 2 qd + 2 for qd = 0, 1, 2 (mod 3)
       int qd = 0;
       if (grp == 0) {
@@ -1018,7 +1020,7 @@ soft_embed_pp_kernel(const GemmParams p) {
         if (qd < nq) g1_super(qd, P0, P1);
         if (qd + 1 < nq) g1_super(qd + 1, P2, P0);
       }
-    } else if (grp == 0) {                      // e4m3 table: two stage buffers
+    } else if (grp == 0) {
       for (int qd = 0; qd < nq; ++qd) {         // steps 4 qd .. 4 qd + 3: stages 2 qd, 2 qd + 1
         load_stage(P1, 2 * qd + 1);
         m_phase(P0, W0, 0);
@@ -1040,40 +1042,63 @@ soft_embed_pp_kernel(const GemmParams p) {
         phase_end<0>();                         // stage 2 qd + 2 in LDS
       }
       phase_end<kNoVmWait>();                   // pairs with group 1's first barrier
-    } else {                                    // e4m3 table, group 1
+    } else {
       phase_end<kNoVmWait>();                   // one phase behind group 0
       for (int qd = 0; qd < nq; ++qd) {
         const int s0 = kQ * qd;
-        // step s: codes of step s + 3 requested; step s + 1's (requested two M phases
-        // ago: at most the 8 later loads may be in flight) converted into its buffer
-        load_step8(R3, s0 + 3, sc3);
-        m_phase(P0, W0, 0);
-        wait_vm<8>();
-        convert8(R1, W1, sc1);
-        phase_end<kNoVmWait>();
-        c_phase();
-        phase_end<kNoVmWait>();
-        load_step8(R0, s0 + 4, sc0);
-        m_phase(P0, W1, 1);
-        wait_vm<8>();
-        convert8(R2, W2, sc2);
-        phase_end<kNoVmWait>();
-        c_phase();
-        phase_end<kNoVmWait>();
-        load_step8(R1, s0 + 5, sc1);
-        m_phase(P1, W2, 0);
-        wait_vm<8>();
-        convert8(R3, W3, sc3);
-        phase_end<kNoVmWait>();
-        c_phase();
-        phase_end<kNoVmWait>();
-        load_step8(R2, s0 + 6, sc2);
-        m_phase(P1, W3, 1);
-        wait_vm<8>();
-        convert8(R0, W0, sc0);
-        phase_end<kNoVmWait>();
-        c_phase();
-        phase_end<kNoVmWait>();
+        if constexpr (!W8) {
+          load_step(W3, s0 + 3);
+          m_phase(P0, W0, 0);
+          phase_end<8>();                       // table step s0 + 1 in LDS
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step(W0, s0 + 4);
+          m_phase(P0, W1, 1);
+          phase_end<8>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step(W1, s0 + 5);
+          m_phase(P1, W2, 0);
+          phase_end<8>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step(W2, s0 + 6);
+          m_phase(P1, W3, 1);
+          phase_end<8>();
+          c_phase();
+          phase_end<kNoVmWait>();
+        } else {
+          // step s: codes of step s + 3 requested; step s + 1's (requested two M phases
+          // ago: at most the 8 later loads may be in flight) converted into its buffer
+          load_step8(R3, s0 + 3, sc3);
+          m_phase(P0, W0, 0);
+          wait_vm<8>();
+          convert8(R1, W1, sc1);
+          phase_end<kNoVmWait>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step8(R0, s0 + 4, sc0);
+          m_phase(P0, W1, 1);
+          wait_vm<8>();
+          convert8(R2, W2, sc2);
+          phase_end<kNoVmWait>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step8(R1, s0 + 5, sc1);
+          m_phase(P1, W2, 0);
+          wait_vm<8>();
+          convert8(R3, W3, sc3);
+          phase_end<kNoVmWait>();
+          c_phase();
+          phase_end<kNoVmWait>();
+          load_step8(R2, s0 + 6, sc2);
+          m_phase(P1, W3, 1);
+          wait_vm<8>();
+          convert8(R0, W0, sc0);
+          phase_end<kNoVmWait>();
+          c_phase();
+          phase_end<kNoVmWait>();
+        }
       }
     }
   }

@@ -90,14 +90,14 @@ TILE_CASES = {
     "k12345": (512, 50000, 12344, 24689, 520, 66),
     "k65553": (256, 70000, 0, 65553, 256, 67),
     "d16": (256, 5000, 0, 4097, 16, 68),          # one n-tile of 16 columns: clamped loads
-    # the contraction cycles three probability stage buffers, its loop unrolled over the
-    # cycle: long splits with lengths of every remainder mod 3 (50/51, 113/114, 48/49
-    # super-steps), ragged tails, two row tiles, 64 splits
+    # splits of at least 32 super-steps take three probability stage buffers, the loop
+    # unrolled over their cycle: split lengths of every remainder mod 3 (50/51, 113/114,
+    # 48/49 super-steps), ragged tails, two row tiles, 64 splits
     "long-splits": (256, 150012, 8, 150003, 2816, 69),
     "long-splits-two-tiles": (512, 160012, 8, 160011, 2816, 70),
     "long-splits-64-splits": (256, 400012, 8, 400011, 512, 71),
-    # splits of one to five super-steps: the stage loads past a split's end clamped to its
-    # last stage, the cycle cut after one or two super-steps
+    # splits of one to five super-steps (two stage buffers): the stage load past a split's
+    # end clamped to its last stage, several splits per tile, two row tiles
     "short-splits-1-2": (256, 1500, 8, 1011, 2816, 72),
     "short-splits-2-3": (256, 3500, 8, 3011, 2816, 73),
     "short-splits-4-5": (512, 5600, 8, 5011, 2816, 74),

@@ -112,7 +112,7 @@ CASES = {
     "whole-tile": (256, 30003, 1000, 13337, 272, 10),   # ping-pong contraction, tail
     "merge-in-contraction": (13, 20008, 8, 20008, 48, 11),
     "merge-row-tiles": (511, 100011, 8, 100008, 520, 12),
-    # splits of at least 32 super-steps: the contraction's unrolled three-buffer cycle
+    # splits of at least 32 super-steps: three probability stage buffers in the contraction
     "long-splits": (17, 150011, 8, 150003, 2816, 13),
     "long-splits-two-tiles": (300, 160011, 8, 160011, 2816, 14),
     # split ranges of 12,289 .. 16,384 positions: the sweep's 4-wave, 16-group form, with
