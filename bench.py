@@ -628,17 +628,31 @@ def main():
     us_s8 = event_time_us(lambda: B.se_soft_embed_step_fp8(
         st.x, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8, *s8, st.wss), K, W,
         settle_ms=60.0)
+    out8o = torch.empty_like(st.out)
+    s8o = [torch.empty(L, device=dev) for _ in range(3)] + [
+        torch.empty(L, device=dev, dtype=torch.int32)]
+    us_s8o = event_time_us(lambda: B.se_soft_embed_step_onepass_fp8(
+        st.x, w.vocab_start, w.vocab_end, codes, wscale, w.gamma, out8o, *s8o, st.ws1), K, W,
+        settle_ms=60.0)
     s8_bytes = 4 * L * w.vocab + w.k * d + 4 * w.k + 4 * L * d + 16 * L
     us_q = event_time_us(lambda: B.se_quantize_table_fp8(st.shard, codes, wscale), 3, 1)
+
+    def fp8_roof(us):
+        return {"bound": "hbm", "algorithmic_bytes": s8_bytes,
+                "achieved": round(s8_bytes / (us * 1e-6) / 1e9, 2), "peak": PEAK_HBM_GBS,
+                "frac": round(s8_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     fp8_side = {"step_us": round(us_s8, 2), "gflops_step": round(flops / (us_s8 * 1e-6) / 1e9, 2),
-                "roofline_step": {"bound": "hbm", "algorithmic_bytes": s8_bytes,
-                                  "achieved": round(s8_bytes / (us_s8 * 1e-6) / 1e9, 2),
-                                  "peak": PEAK_HBM_GBS,
-                                  "frac": round(s8_bytes / (us_s8 * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                                                4)},
+                "roofline_step": fp8_roof(us_s8),
+                "onepass_step_us": round(us_s8o, 2),
+                "onepass_gflops_step": round(flops / (us_s8o * 1e-6) / 1e9, 2),
+                "onepass_roofline_step": fp8_roof(us_s8o),
                 "quantize_shard_us": round(us_q, 2),
-                "note": "a different numerical contract (the dequantized e4m3 table); not value"}
-    del codes, wscale, out8, s8
+                "note": "a different numerical contract (the dequantized e4m3 table); not value. "
+                        "step: se_soft_embed_step_fp8 (two passes over the logits, the codes "
+                        "converted to bf16 in LDS); onepass_step: se_soft_embed_step_onepass_fp8 "
+                        "(one read, row scales carried by the staged probabilities, codes read "
+                        "in place)"}
+    del codes, wscale, out8, s8, out8o, s8o
 
     # cold step, and the box's achievable ceilings beside the peaks
     scrub = torch.empty(1 << 28, device=dev)

@@ -27,7 +27,8 @@ EXPORTS = ("se_status_string", "se_version", "se_row_stats", "se_probs_bf16",
            "se_soft_embed_onepass", "se_merge_slices", "se_soft_embed_staged_workspace_bytes",
            "se_soft_embed_staged", "se_soft_embed_step",
            "se_soft_embed_step_onepass_workspace_bytes", "se_soft_embed_step_onepass",
-           "se_soft_embed_step_fp8", "se_set_launch_events", "se_launch_events_used",
+           "se_soft_embed_step_fp8", "se_soft_embed_step_onepass_fp8", "se_set_launch_events",
+           "se_launch_events_used",
            "se_soft_embed_splits", "se_soft_embed_step_noalloc_max_bytes",
            "se_soft_embed_step_noalloc", "se_mfma_loop")
 
@@ -79,6 +80,7 @@ def _declare(lib):
     lib.se_soft_embed_step_onepass.argtypes = lib.se_soft_embed_step.argtypes
     lib.se_soft_embed_step_fp8.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, i64, i64, i64, f32,
                                            vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.se_soft_embed_step_onepass_fp8.argtypes = lib.se_soft_embed_step_fp8.argtypes
     lib.se_soft_embed_step_noalloc_max_bytes.argtypes = []
     lib.se_soft_embed_step_noalloc_max_bytes.restype = sz
     lib.se_soft_embed_step_noalloc.argtypes = [vp, i64, i64, i64, i64, i64, vp, i64, i64, i64,
@@ -93,7 +95,8 @@ def _declare(lib):
                "se_accept_converge", "se_reduce_partials", "se_quantize_table_fp8",
                "se_soft_embed_fp8", "se_soft_embed_fp8_fused", "se_soft_embed_onepass",
                "se_merge_slices", "se_soft_embed_staged", "se_soft_embed_step",
-               "se_soft_embed_step_onepass", "se_soft_embed_step_fp8"):
+               "se_soft_embed_step_onepass", "se_soft_embed_step_fp8",
+               "se_soft_embed_step_onepass_fp8"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -382,6 +385,21 @@ def se_soft_embed_step_fp8(logits, vocab_start, vocab_end, w_codes, w_scale, gam
     w_rows = w_codes.shape[0] if w_rows is None else w_rows
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("se_soft_embed_step_fp8", lib.se_soft_embed_step_fp8(
+        _ptr(logits), _ld(logits), n, vocab, vocab_start, vocab_end, _ptr(w_codes), _ptr(w_scale),
+        w_rows, _ld(w_codes), d, float(gamma), _ptr(out), _ld(out), _ptr(row_max), _ptr(row_lse),
+        _ptr(row_entropy), _ptr(row_argmax), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def se_soft_embed_step_onepass_fp8(logits, vocab_start, vocab_end, w_codes, w_scale, gamma, out,
+                                   row_max, row_lse, row_entropy, row_argmax, workspace, *,
+                                   vocab=None, d=None, w_rows=None, stream=None):
+    """se_soft_embed_step_onepass against an e4m3 table (codes + per-row scales)."""
+    n, v = logits.shape
+    vocab = v if vocab is None else vocab
+    d = w_codes.shape[1] if d is None else d
+    w_rows = w_codes.shape[0] if w_rows is None else w_rows
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("se_soft_embed_step_onepass_fp8", lib.se_soft_embed_step_onepass_fp8(
         _ptr(logits), _ld(logits), n, vocab, vocab_start, vocab_end, _ptr(w_codes), _ptr(w_scale),
         w_rows, _ld(w_codes), d, float(gamma), _ptr(out), _ld(out), _ptr(row_max), _ptr(row_lse),
         _ptr(row_entropy), _ptr(row_argmax), _ptr(workspace), ws_bytes, _stream(stream)))

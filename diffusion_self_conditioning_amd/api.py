@@ -13,7 +13,7 @@ from ._binding import (SoftEmbedError, se_merge_slices, se_probs_bf16,  # noqa: 
                        se_soft_embed_fp8_fused, se_soft_embed_fused, se_soft_embed_onepass,
                        se_soft_embed_onepass_workspace_bytes, se_soft_embed_staged,
                        se_soft_embed_step, se_soft_embed_step_fp8, se_soft_embed_step_onepass,
-                       se_soft_embed_step_onepass_workspace_bytes,
+                       se_soft_embed_step_onepass_fp8, se_soft_embed_step_onepass_workspace_bytes,
                        se_soft_embed_staged_workspace_bytes, se_soft_embed_workspace_bytes,
                        se_status_string, se_version)
 
@@ -116,14 +116,23 @@ def soft_embed_onepass(logits, vocab_start, vocab_end, w_shard, gamma, *, ws=Non
 
 
 def soft_embed_step_fp8(logits, vocab_start, vocab_end, w_codes, w_scale, gamma, *, ws=None,
-                        stream=None):
+                        stream=None, onepass=False):
     """se_soft_embed_step_fp8: the whole step against an e4m3 table; returns
-    (out, row_max, row_lse, row_entropy, row_argmax)."""
+    (out, row_max, row_lse, row_entropy, row_argmax).  ``onepass=True`` runs
+    se_soft_embed_step_onepass_fp8 (one read of the logits, the row scales carried by the
+    staged probabilities; w_scale 16-byte aligned)."""
     n, d = logits.shape[0], w_codes.shape[1]
     f = dict(device=logits.device, dtype=torch.float32)
     out = torch.empty((n, d), **f)
     mx, lse, ent = torch.empty(n, **f), torch.empty(n, **f), torch.empty(n, **f)
     am = torch.empty(n, device=logits.device, dtype=torch.int32)
+    if onepass:
+        if ws is None:
+            ws = step_onepass_workspace(n, logits.shape[1], vocab_start, vocab_end, d,
+                                        logits.device)
+        se_soft_embed_step_onepass_fp8(logits, vocab_start, vocab_end, w_codes, w_scale, gamma,
+                                       out, mx, lse, ent, am, ws, stream=stream)
+        return out, mx, lse, ent, am
     if ws is None:
         ws = staged_workspace(n, vocab_start, vocab_end, d, logits.device)
     se_soft_embed_step_fp8(logits, vocab_start, vocab_end, w_codes, w_scale, gamma, out, mx, lse,

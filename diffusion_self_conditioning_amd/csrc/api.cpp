@@ -586,34 +586,47 @@ size_t se_soft_embed_step_onepass_workspace_bytes(int64_t n_rows, int64_t vocab,
   return se::step_onepass_layout(n_rows, vocab, vocab_start, vocab_end, d).total;
 }
 
-se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int64_t n_rows,
-                                     int64_t vocab, int64_t vocab_start, int64_t vocab_end,
-                                     const uint16_t* w_shard, int64_t w_rows, int64_t ld_w,
-                                     int64_t d, float gamma, float* out, int64_t ld_out,
-                                     float* row_max, float* row_lse, float* row_entropy,
-                                     int32_t* row_argmax, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The one-read step: one sweep over the logits (per-range statistics, the slice's staged
+// probabilities), the contraction with the range merge, and the factor-scaled split
+// reduction.  w8: the table is e4m3 codes with per-row power-of-two scales; the sweep
+// stores each probability times its row's scale and the contraction reads the codes as
+// they are.  Shapes the sweep cannot take run as the two-pass step, in the same workspace.
+se_status run_step_onepass(const float* logits, int64_t ld_logits, int64_t n_rows,
+                           int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                           const void* w_shard, const float* w_scale, int64_t w_rows,
+                           int64_t ld_w, int64_t d, float gamma, float* out, int64_t ld_out,
+                           float* row_max, float* row_lse, float* row_entropy,
+                           int32_t* row_argmax, void* workspace, size_t workspace_bytes,
+                           void* stream, bool w8) {
   se_status rc = check_slice_shape(n_rows, vocab, vocab_start, vocab_end, w_rows, d, ld_w, ld_out);
   if (rc != SE_OK) return rc;
   if (ld_logits < vocab) return SE_ERR_SHAPE;
   if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
   const se::StepOnepassLayout o =
       se::step_onepass_layout(n_rows, vocab, vocab_start, vocab_end, d);
-  if (o.sweep.waves == 0)                  // empty slice, or split ranges too long: two passes
-    return se_soft_embed_step(logits, ld_logits, n_rows, vocab, vocab_start, vocab_end, w_shard,
-                              w_rows, ld_w, d, gamma, out, ld_out, row_max, row_lse,
-                              row_entropy, row_argmax, workspace, workspace_bytes, stream);
+  if (o.sweep.waves == 0)          // empty slice, or split ranges too long: two passes
+    return run_step(logits, ld_logits, n_rows, vocab, vocab_start, vocab_end, w_shard,
+                    w8 ? w_scale : nullptr, w_rows, ld_w, d, gamma, out, ld_out, row_max,
+                    row_lse, row_entropy, row_argmax, workspace, workspace_bytes, stream, w8);
   if (!logits || !w_shard || !out || !row_max || !row_lse || !row_entropy || !row_argmax)
     return SE_ERR_NULL;
   rc = check_slice_layout(vocab_start, d, ld_w, ld_out, w_shard, out);
   if (rc != SE_OK) return rc;
+  if (w8) {
+    rc = check_fp8_layout(d, ld_w, w_scale);
+    if (rc != SE_OK) return rc;
+    if (!aligned16(w_scale)) return SE_ERR_ALIGN;   // the sweep reads 4 scales at a time
+  }
   if (!aligned16(logits) || (ld_logits % 4) != 0) return SE_ERR_ALIGN;
   if (!aligned4(row_max) || !aligned4(row_lse) || !aligned4(row_entropy) || !aligned4(row_argmax))
     return SE_ERR_ALIGN;
   const int64_t K = vocab_end - vocab_start;
   if (o.g.grid > INT32_MAX || n_rows * o.n_ranges > INT32_MAX) return SE_ERR_SHAPE;
   if ((int64_t)se::tiled_probs_bytes(n_rows, K) > (int64_t)UINT32_MAX ||
-      K * ld_w * 2 > (int64_t)UINT32_MAX)
+      K * ld_w * (w8 ? 1 : 2) > (int64_t)UINT32_MAX)
     return SE_ERR_SHAPE;
   if (workspace_bytes < o.total) return SE_ERR_WORKSPACE;
   if (!workspace) return SE_ERR_NULL;
@@ -625,7 +638,7 @@ se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int
   float* factors = reinterpret_cast<float*>(ws + o.off_fac);
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = from_hip(se::launch_step_sweep(logits, ld_logits, n_rows, o.rg, o.sweep, probs, stats,
-                                      stat_arg, st));
+                                      stat_arg, w8 ? w_scale : nullptr, st));
   if (rc != SE_OK) return rc;
   se::GemmParams p{};
   p.a = probs;                       // super-step-tiled: [K / 128][n_rows][128]
@@ -633,6 +646,8 @@ se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int
   p.a_ss = n_rows * se::kSuperStep * 2;
   p.col0 = 0;
   p.w = w_shard;
+  p.wscale = w8 ? w_scale : nullptr;
+  p.w8_direct = w8;                  // the scales are in the probabilities
   p.ldw = ld_w;
   p.M = n_rows;
   p.N = d;
@@ -658,7 +673,7 @@ se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int
   p.row_lse = row_lse;
   p.row_entropy = row_entropy;
   p.row_argmax = row_argmax;
-  rc = from_hip(se::launch_soft_embed(p, false, false, st));
+  rc = from_hip(se::launch_soft_embed(p, false, w8, st));
   if (rc != SE_OK) return rc;
   if (!p.merge_rows) {
     rc = from_hip(se::launch_merge_ranges(stats, stat_arg, n_rows, o.n_ranges, o.rg.n_pre,
@@ -667,6 +682,34 @@ se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int
     if (rc != SE_OK) return rc;
   }
   return from_hip(se::launch_scaled_reduce(p, factors, st));
+}
+}  // namespace
+
+extern "C" {
+
+se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int64_t n_rows,
+                                     int64_t vocab, int64_t vocab_start, int64_t vocab_end,
+                                     const uint16_t* w_shard, int64_t w_rows, int64_t ld_w,
+                                     int64_t d, float gamma, float* out, int64_t ld_out,
+                                     float* row_max, float* row_lse, float* row_entropy,
+                                     int32_t* row_argmax, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return run_step_onepass(logits, ld_logits, n_rows, vocab, vocab_start, vocab_end, w_shard,
+                          nullptr, w_rows, ld_w, d, gamma, out, ld_out, row_max, row_lse,
+                          row_entropy, row_argmax, workspace, workspace_bytes, stream, false);
+}
+
+se_status se_soft_embed_step_onepass_fp8(const float* logits, int64_t ld_logits,
+                                         int64_t n_rows, int64_t vocab, int64_t vocab_start,
+                                         int64_t vocab_end, const uint8_t* w_codes,
+                                         const float* w_scale, int64_t w_rows, int64_t ld_w,
+                                         int64_t d, float gamma, float* out, int64_t ld_out,
+                                         float* row_max, float* row_lse, float* row_entropy,
+                                         int32_t* row_argmax, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return run_step_onepass(logits, ld_logits, n_rows, vocab, vocab_start, vocab_end, w_codes,
+                          w_scale, w_rows, ld_w, d, gamma, out, ld_out, row_max, row_lse,
+                          row_entropy, row_argmax, workspace, workspace_bytes, stream, true);
 }
 
 se_status se_quantize_table_fp8(const uint16_t* w, int64_t ld_w, int64_t rows, int64_t d,
@@ -775,7 +818,7 @@ se_status se_soft_embed_onepass(const float* logits, int64_t ld_logits, int64_t 
   rg.kblocks = (int)o.g.kblocks;
   if (o.sweep.waves > 0)
     rc = from_hip(se::launch_step_sweep(logits, ld_logits, n_rows, rg, o.sweep, probs, stats,
-                                        stat_arg, st));
+                                        stat_arg, nullptr, st));
   else
     rc = from_hip(se::launch_split_sweep(logits, ld_logits, vocab_start, K, n_rows,
                                          (int)o.g.splits, (int)o.g.kblocks, probs, stats,

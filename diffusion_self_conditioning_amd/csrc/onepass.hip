@@ -17,6 +17,8 @@
 // below holds: a first pass reads the range and finds its maximum and first position; a
 // second pass reads it again, forms the probabilities, writes them as bf16 and sums Z_s
 // and S1_s in fp32.
+#include <type_traits>
+
 #include "se_device.h"
 #include "se_dispatch.h"
 #include "se_launch.h"
@@ -160,11 +162,13 @@ __device__ __forceinline__ void step_range(const StepRanges& g, int r, int64_t& 
 // group combines its maxima and then its sums through LDS in wave order.
 static_assert(kSweepPiece == 64 * 4 * 12 && kSweepPieceWide == 64 * 4 * 16, "sweep pieces");
 
-template <int W, int NF4>
+// SCALED: slice position j's probability is stored times pscale[j] (a power of two, so the
+// bf16 value is the unscaled one times pscale[j] exactly); the statistics stay unscaled.
+template <int W, int NF4, bool SCALED>
 __global__ void __launch_bounds__(sweep_threads(W))
 step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, StepRanges g,
                   int n_ranges, uint16_t* __restrict__ probs, float4* __restrict__ stats,
-                  int32_t* __restrict__ stat_arg) {
+                  int32_t* __restrict__ stat_arg, const float* __restrict__ pscale) {
   constexpr int kWaves = sweep_threads(W) / 64;
   __shared__ float grp_v[kWaves], grp_z[kWaves], grp_s[kWaves];
   __shared__ int grp_i[kWaves];
@@ -196,6 +200,17 @@ step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, 
   if (lane < (int)(a0 - p0)) rs = (int)(p0 - c0) + lane;
   else if (lane >= 4 && lane < 4 + (int)(p1 - a1)) rs = (int)(a1 - c0) + lane - 4;
   const float xs = rs >= 0 ? x[c0 + rs] : 0.f;
+  // the scales of the same positions (slice positions js + base + 4 gi ..; 16-byte aligned)
+  float4 sv[SCALED ? NF4 : 1];
+  float ss = 1.f;
+  if constexpr (SCALED) {
+    if (active && in_slice) {
+      const __amdgpu_buffer_rsrc_t sr = make_rsrc(pscale + (c0 - g.s) + base, (uint32_t)ng * 16u);
+#pragma unroll
+      for (int u = 0; u < NF4; ++u) sv[u] = buffer_load_f4(sr, (uint32_t)(u * 64 + lane) * 16u, 0u);
+      if (rs >= 0) ss = pscale[c0 - g.s + rs];
+    }
+  }
 
   float mv = -INFINITY;
   int mi = INT_MAX;
@@ -240,7 +255,11 @@ step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, 
       z += (q0 + q1) + (q2 + q3);
       s1 = __builtin_fmaf(q0, t0, __builtin_fmaf(q1, t1, __builtin_fmaf(q2, t2, __builtin_fmaf(q3, t3, s1))));
       if (active && in_slice) {                         // 4 positions in one super-step
-        store_stream_u2(prow + tiled(js + base + 4 * gi), pack_bf16x2(q0, q1), pack_bf16x2(q2, q3));
+        if constexpr (SCALED)
+          store_stream_u2(prow + tiled(js + base + 4 * gi), pack_bf16x2(q0 * sv[u].x, q1 * sv[u].y),
+                          pack_bf16x2(q2 * sv[u].z, q3 * sv[u].w));
+        else
+          store_stream_u2(prow + tiled(js + base + 4 * gi), pack_bf16x2(q0, q1), pack_bf16x2(q2, q3));
       }
     }
   }
@@ -249,7 +268,7 @@ step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, 
     const float q = exp2_hw(t);
     z += q;
     s1 = __builtin_fmaf(q, t, s1);
-    if (active && in_slice) store_stream_u16(prow + tiled(js + rs), __builtin_bit_cast(uint16_t, (__bf16)q));
+    if (active && in_slice) store_stream_u16(prow + tiled(js + rs), __builtin_bit_cast(uint16_t, (__bf16)(q * ss)));
   }
   z = wave_sum(z);
   s1 = wave_sum(s1);
@@ -351,28 +370,32 @@ hipError_t launch_merge_slices(const float* outs, int64_t n_parts, int64_t part_
 
 hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
                              const StepRanges& g, SweepShape sw, uint16_t* probs, float* stats,
-                             int32_t* stat_arg, hipStream_t stream) {
+                             int32_t* stat_arg, const float* pscale, hipStream_t stream) {
   const int n_ranges = g.n_pre + g.splits + g.n_post;
   float4* st = reinterpret_cast<float4*>(stats);
   auto go = [&](auto kernel, int w) {
     const int per_block = (sweep_threads(w) / 64) / w;          // (row, range) items
     const dim3 grid((unsigned)((n_rows * n_ranges + per_block - 1) / per_block));
     SE_LAUNCH(kernel, grid, dim3(sweep_threads(w)), 0, stream, logits, ld, n_rows, g,
-                       n_ranges, probs, st, stat_arg);
+                       n_ranges, probs, st, stat_arg, pscale);
     return launched(stream);
   };
-  if (sw.groups == 16) {
-    if (sw.waves == 4) return go(step_sweep_kernel<4, 16>, 4);
-    return hipErrorInvalidValue;
-  }
-  if (sw.groups != 12) return hipErrorInvalidValue;
-  switch (sw.waves) {
-    case 1: return go(step_sweep_kernel<1, 12>, 1);
-    case 2: return go(step_sweep_kernel<2, 12>, 2);
-    case 4: return go(step_sweep_kernel<4, 12>, 4);
-    case 8: return go(step_sweep_kernel<8, 12>, 8);
-    default: return hipErrorInvalidValue;
-  }
+  auto pick = [&](auto scaled) -> hipError_t {
+    constexpr bool S = decltype(scaled)::value;
+    if (sw.groups == 16) {
+      if (sw.waves == 4) return go(step_sweep_kernel<4, 16, S>, 4);
+      return hipErrorInvalidValue;
+    }
+    if (sw.groups != 12) return hipErrorInvalidValue;
+    switch (sw.waves) {
+      case 1: return go(step_sweep_kernel<1, 12, S>, 1);
+      case 2: return go(step_sweep_kernel<2, 12, S>, 2);
+      case 4: return go(step_sweep_kernel<4, 12, S>, 4);
+      case 8: return go(step_sweep_kernel<8, 12, S>, 8);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  return pscale ? pick(std::true_type{}) : pick(std::false_type{});
 }
 
 hipError_t launch_merge_ranges(const float* stats, const int32_t* stat_arg, int64_t n_rows,

@@ -88,6 +88,8 @@ struct GemmParams {
   int64_t col0;           // vocab_start: column of `a` holding slice position 0
   const void* w;          // shard, row 0 = slice position 0: bf16, or e4m3 codes
   const float* wscale;    // e4m3 table only: power-of-two scale of each shard row
+  bool w8_direct;         // e4m3 codes read as they are: the probabilities arrive multiplied
+                          // by the row scales (staged, super-step-tiled); wscale unused
   int64_t ldw;            // elements (bytes for e4m3 codes)
   int64_t M, N, K;
   float gamma;
@@ -179,10 +181,11 @@ struct StepRanges {
 // stat_arg likewise), and for the slice's split ranges the bf16 probabilities against
 // the range maximum in the super-step-tiled layout.  sw.waves (1, 2, 4 or 8) wavefronts
 // share a range of at most waves * 256 * sw.groups positions (sw.groups 16 only with 4
-// waves).
+// waves).  pscale (optional, 16-byte aligned, one power of two per slice position): the
+// probabilities are stored times pscale[j].
 hipError_t launch_step_sweep(const float* logits, int64_t ld, int64_t n_rows,
                              const StepRanges& g, SweepShape sw, uint16_t* probs, float* stats,
-                             int32_t* stat_arg, hipStream_t stream);
+                             int32_t* stat_arg, const float* pscale, hipStream_t stream);
 
 // Merge of each row's range statistics: row max / lse / entropy / argmax, and the
 // factor gamma e^(m_r - lse) of every split range r0 + j (factors[j * n_rows + row]).

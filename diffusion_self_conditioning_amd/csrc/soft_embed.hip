@@ -716,6 +716,14 @@ __device__ __forceinline__ void phase_end() {
 constexpr int kNoVmWait = 63;
 constexpr int kPP8RawBytes = kBK * kBN;           // [32 rows][256 columns] e4m3 codes
 static_assert(4 * kPP8RawBytes == kPPStageBytes, "the e4m3 code ring fills the third stage buffer");
+static_assert(3 * kPPStageBytes + 4 * kPP8RawBytes <= 160 * 1024, "LDS budget of the D8 form");
+// codes read in place (D8): step row k at 256 k bytes, 16-byte chunk c (16 columns) at
+// c ^ d8_swz(k).  A transpose read of 16 lanes takes 8 consecutive rows (k = 8 j .. 8 j + 7)
+// of one chunk; the swizzle puts those rows in 8 chunks distinct modulo 8, and the rows of
+// the neighbouring chunk (c ^ 1) in the 8 other chunks of the 256-byte line.
+__device__ __forceinline__ int d8_swz(int k) { return (k & 7) | ((k & 1) << 3); }
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i32_t* lds_v2i32_ptr;
 // s_waitcnt with vmcnt(n) only
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -731,26 +739,37 @@ __device__ __forceinline__ void wait_vm() {
 // registers; two M phases later each wave converts the rows it loaded itself (so a wait on
 // its own loads suffices) to bf16, exactly as soft_embed_kernel's e4m3 producer does, into
 // the step's table buffer, one step before anyone reads it.
-template <bool TABLE_NT, bool W8>
+// D8: e4m3 codes again, with the probabilities already multiplied by the row scales (the
+// product P[m, k] s_k is exact in bf16, as s_k is a power of two).  Group 1 loads a step's
+// codes like a bf16 step, and the M phases read the fragments from the codes themselves
+// with transpose reads of 8 codes, turned into bf16 by unscaled conversions in registers:
+// no conversion pass and half the table bytes in LDS.
+template <bool TABLE_NT, bool W8, bool D8>
 __global__ void __launch_bounds__(kGemmThreads)
 __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 soft_embed_pp_kernel(const GemmParams p) {
   static_assert(kWaves == 8 && kMI == 4 && kNI == 2 && kWN == 4, "the 8-wave layout");
+  static_assert(!(W8 && D8), "one e4m3 form");
+  constexpr bool RAW = W8 || D8;                  // the table as e4m3 codes
   __shared__ __attribute__((aligned(16))) unsigned char P0[kPPStageBytes], P1[kPPStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char W0[kPPStepBytes], W1[kPPStepBytes];
   __shared__ __attribute__((aligned(16))) unsigned char W2[kPPStepBytes], W3[kPPStepBytes];
-  // the third probability stage (bf16 table, long splits), or the e4m3 codes of four steps
-  // as loaded ([32 rows][256 codes], row r at 256 r): each its own LDS array, declared only
-  // in the form that uses it
+  // the third probability stage (bf16 table and D8, long splits), and the e4m3 codes of
+  // four steps ([32 rows][256 codes]; W8: row r at 256 r as loaded, D8: swizzled): each its
+  // own LDS array, declared only in the forms that use it
   unsigned char *P2 = nullptr, *R0 = nullptr, *R1 = nullptr, *R2 = nullptr, *R3 = nullptr;
-  if constexpr (W8) {
+  if constexpr (RAW) {
     R0 = lds_array<10, kPP8RawBytes>();
     R1 = lds_array<11, kPP8RawBytes>();
     R2 = lds_array<12, kPP8RawBytes>();
     R3 = lds_array<13, kPP8RawBytes>();
-  } else {
-    P2 = lds_array<2, kPPStageBytes>();
   }
+  if constexpr (!W8) P2 = lds_array<2, kPPStageBytes>();
+  // the table buffers the fragments read: bf16 steps (W8: converted), or D8's codes
+  unsigned char* const T0 = D8 ? R0 : W0;
+  unsigned char* const T1 = D8 ? R1 : W1;
+  unsigned char* const T2 = D8 ? R2 : W2;
+  unsigned char* const T3 = D8 ? R3 : W3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave >> 2, q = wave & 3;
   const int wm = wave / kWN, wn = wave % kWN;
@@ -786,7 +805,7 @@ soft_embed_pp_kernel(const GemmParams p) {
                                           (int64_t)kBM * kSuperStep * 2
                                     : (kBM - 1) * a_rs + p.K * 2,
                             (int64_t)UINT32_MAX));
-  const int64_t w_ld = p.ldw * (W8 ? 1 : 2);
+  const int64_t w_ld = p.ldw * (RAW ? 1 : 2);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       make_rsrc(static_cast<const unsigned char*>(p.w) + k_lo * w_ld,
                 (uint32_t)min((k_hi - k_lo) * w_ld, (int64_t)UINT32_MAX));
@@ -806,7 +825,7 @@ soft_embed_pp_kernel(const GemmParams p) {
       const int r = 64 * q + 8 * i + (lane >> 3);
       voff[i] = (uint32_t)(min(r, tile_rows - 1) * a_rs) + 16u * (uint32_t)((lane & 7) ^ pp_swz(r));
     }
-  } else if constexpr (!W8) {
+  } else if constexpr (!RAW) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = 8 * q + 2 * i + (lane >> 5);
@@ -815,6 +834,17 @@ soft_embed_pp_kernel(const GemmParams p) {
     }
 #pragma unroll
     for (int i = 4; i < 8; ++i) voff[i] = 0u;
+  } else if constexpr (D8) {
+    // wave q loads step rows 8 q .. + 7, 4 rows per load: lane l of load i writes row
+    // k = 8 q + 4 i + l / 16, stored chunk l % 16, which holds column chunk (l % 16) ^ d8_swz(k)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k = 8 * q + 4 * i + (lane >> 4);
+      const int col = n0 + 16 * ((lane & 15) ^ d8_swz(k));
+      voff[i] = (uint32_t)(k * w_ld) + (uint32_t)min(col, N - 16);
+    }
+#pragma unroll
+    for (int i = 2; i < 8; ++i) voff[i] = 0u;
   } else {
     // e4m3: wave q loads step rows 8 q .. + 7 as codes, 4 rows per load (lane l of load i:
     // row 8 q + 4 i + l / 16, columns 16 (l % 16) .. + 15), and the scales of its rows
@@ -852,6 +882,21 @@ soft_embed_pp_kernel(const GemmParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(buf + 1024 * (4 * q + i)),
                                                16, voff[i], soff, 0, TABLE_NT ? 2 : 0);
   };
+  // D8: codes of step st, 2 loads per wave
+  auto load_step_d8 = [&](unsigned char* raw, int st) {
+    const uint32_t soff = (uint32_t)((int64_t)kBK * min(st, nsteps - 1) * w_ld);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(raw + 1024 * (2 * q + i)),
+                                               16, voff[i], soff, 0, TABLE_NT ? 2 : 0);
+  };
+  // a table step into its buffer (bf16 or D8); group 1's wait for the step after the one in
+  // use leaves the two later steps' loads in flight
+  auto load_tab = [&](unsigned char* buf, int st) {
+    if constexpr (D8) load_step_d8(buf, st);
+    else load_step(buf, st);
+  };
+  constexpr int kTabWait = D8 ? 4 : 8;
   // e4m3: codes of step st into a raw buffer, the scales of the wave's rows into sc
   auto load_step8 = [&](unsigned char* raw, int st, float (&sc)[2]) {
     const int64_t k0 = (int64_t)kBK * min(st, nsteps - 1);
@@ -893,8 +938,17 @@ soft_embed_pp_kernel(const GemmParams p) {
   {
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
-      b_rd[ni] = (uint32_t)w_off(8 * (g >> 1) + (i >> 2), kTN * wn + 32 * ni + 16 * (g & 1) + 4 * (i & 3));
+    for (int ni = 0; ni < kNI; ++ni) {
+      if constexpr (D8) {
+        // 16 lanes read rows 8 (g / 2) + i / 2 (8 codes each, half i % 2 of the chunk);
+        // lane 16 g + j receives column j of the chunk's 8 rows
+        const int k = 8 * (g >> 1) + (i >> 1);
+        const int c = (kTN * wn + 32 * ni) / 16 + (g & 1);
+        b_rd[ni] = (uint32_t)(256 * k + 16 * (c ^ d8_swz(k)) + 8 * (i & 1));
+      } else {
+        b_rd[ni] = (uint32_t)w_off(8 * (g >> 1) + (i >> 2), kTN * wn + 32 * ni + 16 * (g & 1) + 4 * (i & 3));
+      }
+    }
   }
   bf16x8 a0[kMI], b0[kNI], a1[kMI], b1[kNI];
   auto frag = [&](const unsigned char* pb, const unsigned char* wb, int h, int u, bf16x8 (&af)[kMI],
@@ -904,11 +958,22 @@ soft_embed_pp_kernel(const GemmParams p) {
       af[mi] = *reinterpret_cast<const bf16x8*>(pb + pp_off(a_row + 32 * mi, 4 * h + 2 * u + (lane >> 5)));
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
-      const unsigned char* wp = wb + b_rd[ni] + 8192 * u;
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp + 2048));
-      bf[ni] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
-                                       __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+      if constexpr (D8) {
+        // 8 codes (rows 16 u + 8 (lane / 32) .. + 7 of one column), exact in bf16
+        const v2i32_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_v2i32_ptr)(wb + b_rd[ni] + 4096 * u));
+        const uint4 v = make_uint4(fp8x2_to_bf16x2((uint32_t)c.x, 1.f, false),
+                                   fp8x2_to_bf16x2((uint32_t)c.x, 1.f, true),
+                                   fp8x2_to_bf16x2((uint32_t)c.y, 1.f, false),
+                                   fp8x2_to_bf16x2((uint32_t)c.y, 1.f, true));
+        bf[ni] = __builtin_bit_cast(bf16x8, v);
+      } else {
+        const unsigned char* wp = wb + b_rd[ni] + 8192 * u;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(wp + 2048));
+        bf[ni] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
+                                         __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     }
   };
   auto mfmas = [&](const bf16x8 (&af)[kMI], const bf16x8 (&bf)[kNI]) {
@@ -933,46 +998,46 @@ soft_embed_pp_kernel(const GemmParams p) {
   // loaded into pc (the buffer stage 2 qd - 1 held), stage 2 qd + 3 into pa
   auto g0_super = [&](int qd, unsigned char* pa, unsigned char* pb, unsigned char* pc) {
     load_half(pc, 2 * qd + 2, 0);
-    m_phase(pa, W0, 0);
+    m_phase(pa, T0, 0);
     phase_end<kNoVmWait>();
     c_phase();
     phase_end<kNoVmWait>();
     load_half(pc, 2 * qd + 2, 1);
-    m_phase(pa, W1, 1);
+    m_phase(pa, T1, 1);
     phase_end<kNoVmWait>();
     c_phase();
     phase_end<8>();                             // stage 2 qd + 1 in LDS
     load_half(pa, 2 * qd + 3, 0);
-    m_phase(pb, W2, 0);
+    m_phase(pb, T2, 0);
     phase_end<kNoVmWait>();
     c_phase();
     phase_end<kNoVmWait>();
     load_half(pa, 2 * qd + 3, 1);
-    m_phase(pb, W3, 1);
+    m_phase(pb, T3, 1);
     phase_end<kNoVmWait>();
     c_phase();
     phase_end<8>();                             // stage 2 qd + 2 in LDS
   };
   auto g1_super = [&](int qd, unsigned char* pa, unsigned char* pb) {
     const int s0 = kQ * qd;
-    load_step(W3, s0 + 3);
-    m_phase(pa, W0, 0);
-    phase_end<8>();                             // table step s0 + 1 in LDS
+    load_tab(T3, s0 + 3);
+    m_phase(pa, T0, 0);
+    phase_end<kTabWait>();                      // table step s0 + 1 in LDS
     c_phase();
     phase_end<kNoVmWait>();
-    load_step(W0, s0 + 4);
-    m_phase(pa, W1, 1);
-    phase_end<8>();
+    load_tab(T0, s0 + 4);
+    m_phase(pa, T1, 1);
+    phase_end<kTabWait>();
     c_phase();
     phase_end<kNoVmWait>();
-    load_step(W1, s0 + 5);
-    m_phase(pb, W2, 0);
-    phase_end<8>();
+    load_tab(T1, s0 + 5);
+    m_phase(pb, T2, 0);
+    phase_end<kTabWait>();
     c_phase();
     phase_end<kNoVmWait>();
-    load_step(W2, s0 + 6);
-    m_phase(pb, W3, 1);
-    phase_end<8>();
+    load_tab(T2, s0 + 6);
+    m_phase(pb, T3, 1);
+    phase_end<kTabWait>();
     c_phase();
     phase_end<kNoVmWait>();
   };
@@ -982,9 +1047,9 @@ soft_embed_pp_kernel(const GemmParams p) {
       load_stage(P0, 0);
       if (three) load_stage(P1, 1);
     } else if constexpr (!W8) {
-      load_step(W0, 0);
-      load_step(W1, 1);
-      load_step(W2, 2);
+      load_tab(T0, 0);
+      load_tab(T1, 1);
+      load_tab(T2, 2);
     } else {
       load_step8(R0, 0, sc0);
       load_step8(R1, 1, sc1);
@@ -1023,20 +1088,20 @@ soft_embed_pp_kernel(const GemmParams p) {
     } else if (grp == 0) {
       for (int qd = 0; qd < nq; ++qd) {         // steps 4 qd .. 4 qd + 3: stages 2 qd, 2 qd + 1
         load_stage(P1, 2 * qd + 1);
-        m_phase(P0, W0, 0);
+        m_phase(P0, T0, 0);
         phase_end<kNoVmWait>();
         c_phase();
         phase_end<kNoVmWait>();
-        m_phase(P0, W1, 1);
+        m_phase(P0, T1, 1);
         phase_end<kNoVmWait>();
         c_phase();
         phase_end<0>();                         // stage 2 qd + 1 in LDS
         load_stage(P0, 2 * qd + 2);
-        m_phase(P1, W2, 0);
+        m_phase(P1, T2, 0);
         phase_end<kNoVmWait>();
         c_phase();
         phase_end<kNoVmWait>();
-        m_phase(P1, W3, 1);
+        m_phase(P1, T3, 1);
         phase_end<kNoVmWait>();
         c_phase();
         phase_end<0>();                         // stage 2 qd + 2 in LDS
@@ -1047,24 +1112,24 @@ soft_embed_pp_kernel(const GemmParams p) {
       for (int qd = 0; qd < nq; ++qd) {
         const int s0 = kQ * qd;
         if constexpr (!W8) {
-          load_step(W3, s0 + 3);
-          m_phase(P0, W0, 0);
-          phase_end<8>();                       // table step s0 + 1 in LDS
+          load_tab(T3, s0 + 3);
+          m_phase(P0, T0, 0);
+          phase_end<kTabWait>();                // table step s0 + 1 in LDS
           c_phase();
           phase_end<kNoVmWait>();
-          load_step(W0, s0 + 4);
-          m_phase(P0, W1, 1);
-          phase_end<8>();
+          load_tab(T0, s0 + 4);
+          m_phase(P0, T1, 1);
+          phase_end<kTabWait>();
           c_phase();
           phase_end<kNoVmWait>();
-          load_step(W1, s0 + 5);
-          m_phase(P1, W2, 0);
-          phase_end<8>();
+          load_tab(T1, s0 + 5);
+          m_phase(P1, T2, 0);
+          phase_end<kTabWait>();
           c_phase();
           phase_end<kNoVmWait>();
-          load_step(W2, s0 + 6);
-          m_phase(P1, W3, 1);
-          phase_end<8>();
+          load_tab(T2, s0 + 6);
+          m_phase(P1, T3, 1);
+          phase_end<kTabWait>();
           c_phase();
           phase_end<kNoVmWait>();
         } else {
@@ -1121,7 +1186,17 @@ soft_embed_pp_kernel(const GemmParams p) {
       *reinterpret_cast<uint4*>(P0 + pp_off(row, c)) =
           make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
     }
-    if constexpr (!W8) {
+    if constexpr (D8) {
+      // codes: 32 rows x 16 chunks of 16 columns, one per thread, in the swizzled layout
+      // (rows past the slice: zero codes)
+      const int k = tid >> 4, c = tid & 15;
+      const int64_t kr = k0 + k;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (kr < p.K)
+        v = *reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(p.w) + kr * w_ld +
+                                            min(n0 + 16 * c, N - 16));
+      *reinterpret_cast<uint4*>(R0 + 256 * k + 16 * (c ^ d8_swz(k))) = v;
+    } else if constexpr (!W8) {
       // table: 32 rows x 32 chunks of 8 columns, 2 per thread
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -1149,7 +1224,7 @@ soft_embed_pp_kernel(const GemmParams p) {
       *reinterpret_cast<uint4*>(W0 + w_off(k, col + 8)) = hi;
     }
     __syncthreads();
-    m_phase(P0, W0, 0);
+    m_phase(P0, T0, 0);
     mfmas(a0, b0);
     mfmas(a1, b1);
     __syncthreads();
@@ -1208,12 +1283,20 @@ hipError_t launch_contraction(const GemmParams& p, hipStream_t stream) {
   // for bit the same result)
   // (e4m3 table: one row tile only; with several, the conversion, all in group 1's M
   // phase, outlasts the other group's MFMAs and the register-staged kernel is faster)
-  if (!FUSED && (p.a_ss == p.M * (int64_t)kSuperStep * 2 || p.a_ss == (int64_t)kSuperStep * 2) &&
-      (!W8 || p.tiles == p.tiles_n)) {
-    if (p.tiles == p.tiles_n)                   // one row tile
-      SE_LAUNCH((soft_embed_pp_kernel<true, W8>), grid, dim3(kGemmThreads), 0, stream, p);
+  const bool staged = p.a_ss == p.M * (int64_t)kSuperStep * 2 || p.a_ss == (int64_t)kSuperStep * 2;
+  if (p.w8_direct) {                            // pre-scaled probabilities, codes read in place
+    if (FUSED || !W8 || !staged) return hipErrorInvalidValue;
+    if (p.tiles == p.tiles_n)
+      SE_LAUNCH((soft_embed_pp_kernel<true, false, true>), grid, dim3(kGemmThreads), 0, stream, p);
     else
-      SE_LAUNCH((soft_embed_pp_kernel<false, W8>), grid, dim3(kGemmThreads), 0, stream, p);
+      SE_LAUNCH((soft_embed_pp_kernel<false, false, true>), grid, dim3(kGemmThreads), 0, stream, p);
+    return hipSuccess;
+  }
+  if (!FUSED && staged && (!W8 || p.tiles == p.tiles_n)) {
+    if (p.tiles == p.tiles_n)                   // one row tile
+      SE_LAUNCH((soft_embed_pp_kernel<true, W8, false>), grid, dim3(kGemmThreads), 0, stream, p);
+    else
+      SE_LAUNCH((soft_embed_pp_kernel<false, W8, false>), grid, dim3(kGemmThreads), 0, stream, p);
     return hipSuccess;
   }
   if (p.merge_rows) return hipErrorInvalidValue;   // only the ping-pong kernel merges ranges

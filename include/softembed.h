@@ -335,6 +335,33 @@ se_status se_soft_embed_step_onepass(const float* logits, int64_t ld_logits, int
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * se_soft_embed_step_onepass_fp8 -- se_soft_embed_step_onepass against an e4m3 table with
+ * per-row power-of-two scales 2^k_v, as se_quantize_table_fp8 writes them (the FP8
+ * weights of the agentlenshq overview of DiffusionGemma in vLLM, section on performance
+ * and quantization).  The sweep stores each slice probability times its table row's
+ * scale, bf16_rne(e^(l - m_r) 2^k_v) = bf16_rne(e^(l - m_r)) 2^k_v, and the contraction
+ * multiplies those by the codes themselves (every e4m3 value is exact in bf16): the
+ * partition identity of calvarado04.com, "The fix", with each term's scale moved from the
+ * table row to the probability.  The result is se_soft_embed_step_onepass's on the
+ * dequantized table (codes times scales) bit for bit wherever every stored probability
+ * stays in bf16's normal range (a probability below 2^-126 / 2^k_v may round differently;
+ * such a term is below 2^-117 in magnitude).
+ * Arguments as se_soft_embed_step_fp8, with w_scale 16-byte aligned, and a workspace of
+ * se_soft_embed_step_onepass_workspace_bytes() bytes (16-byte aligned).  Shapes the sweep
+ * cannot take (empty slice, a split range longer than 24,576 positions) run as
+ * se_soft_embed_step_fp8 in the same workspace.  Errors as se_soft_embed_step_fp8, and
+ * SE_ERR_ALIGN for a w_scale that is not 16-byte aligned.
+ */
+se_status se_soft_embed_step_onepass_fp8(const float* logits, int64_t ld_logits,
+                                         int64_t n_rows, int64_t vocab, int64_t vocab_start,
+                                         int64_t vocab_end, const uint8_t* w_codes,
+                                         const float* w_scale, int64_t w_rows, int64_t ld_w,
+                                         int64_t d, float gamma, float* out, int64_t ld_out,
+                                         float* row_max, float* row_lse, float* row_entropy,
+                                         int32_t* row_argmax, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
  * se_quantize_table_fp8 -- the e4m3 form of a bf16 embedding table (the pages serve
  * the model with FP8 weights: agentlenshq overview of DiffusionGemma in vLLM,
  * section on performance and quantization, quantized checkpoints).

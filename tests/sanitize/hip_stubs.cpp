@@ -63,7 +63,7 @@ hipError_t launch_split_sweep(const float*, int64_t, int64_t, int64_t, int64_t, 
 hipError_t launch_onepass_reduce(const GemmParams&, float*, float*, float*, int32_t*, int64_t,
                                  hipStream_t s) { return launched_stub(s); }
 hipError_t launch_step_sweep(const float*, int64_t, int64_t, const StepRanges&, SweepShape sw,
-                             uint16_t*, float*, int32_t*, hipStream_t s) {
+                             uint16_t*, float*, int32_t*, const float*, hipStream_t s) {
   const bool narrow = sw.groups == 12 && (sw.waves == 1 || sw.waves == 2 || sw.waves == 4 ||
                                           sw.waves == 8);
   if (!narrow && !(sw.groups == 16 && sw.waves == 4)) return hipErrorInvalidValue;

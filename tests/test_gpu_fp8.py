@@ -1,5 +1,6 @@
-"""GPU parity of the e4m3 table path: se_quantize_table_fp8, se_soft_embed_fp8 and
-se_soft_embed_fp8_fused (MI355X), all through the C ABI.
+"""GPU parity of the e4m3 table path: se_quantize_table_fp8, se_soft_embed_fp8,
+se_soft_embed_fp8_fused, se_soft_embed_step_fp8 and se_soft_embed_step_onepass_fp8
+(MI355X), all through the C ABI.
 
 Bars:
   quantizer                codes and scales bit-exact with oracle.fp8.quantize_table
@@ -10,6 +11,10 @@ Bars:
                            power-of-two scale is exact in bf16; same accumulation order)
   decode                   a one-hot probability row returns code value x scale exactly,
                            for every finite code
+  one-read e4m3 step       bit-exact with the bf16 one-read step on the dequantized table
+                           (the sweep stores each probability times its row's power-of-two
+                           scale and the contraction reads the codes as they are), and the
+                           oracle gate
 The table inputs of the GPU contraction are the oracle's codes, never the GPU
 quantizer's, so no expected value depends on the HIP path.
 """
@@ -318,3 +323,137 @@ def test_fp8_step_rank_full_size():
     for a, b in ((mx, mx2), (lse, lse2), (ent, ent2), (am, am2), (out, ref)):
         assert torch.equal(a, b)
     np.testing.assert_array_equal(am.cpu().numpy(), wl.planted_index(w))
+
+
+# ---- se_soft_embed_step_onepass_fp8: the row scales carried by the staged probabilities --
+
+def dev_logits(x):
+    """x in a buffer whose row pitch is a multiple of 4, padded with huge values past V."""
+    L, V = x.shape
+    ld = ((V + 3) // 4) * 4
+    buf = np.full((L, ld), np.float32(1e30), np.float32)
+    buf[:, :V] = x
+    return dev(buf)[:, :V]
+
+
+ONEPASS_CASES = {
+    # name: (L, V, s, e, d, seed)
+    "tiny": (16, 4096, 0, 4096, 256, 31),
+    "ragged": (17, 20008, 8, 20008, 48, 32),
+    "slice-1": (5, 1000, 16, 17, 16, 33),
+    "slice-63": (33, 1003, 64, 127, 2816, 34),        # V not a multiple of 4
+    "slice-in-middle": (64, 50000, 12344, 37001, 128, 35),
+    "two-row-tiles": (300, 2048, 1024, 2048, 512, 36),
+    "whole-tile-tail": (256, 30003, 1000, 13337, 272, 37),
+    "merge-in-contraction": (13, 20008, 8, 20008, 48, 38),
+    "merge-row-tiles": (511, 100011, 8, 100008, 528, 39),
+    "long-splits": (17, 150011, 8, 150003, 2816, 40),
+    "long-splits-two-tiles": (300, 160011, 8, 160011, 2816, 41),
+    "short-splits": (256, 3500, 8, 3011, 2816, 42),
+    "d16": (256, 5000, 0, 4097, 16, 43),
+}
+
+
+def fp8_inputs(L, V, s, e, d, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    x[np.arange(L), rng.integers(0, V, L)] += 8.0
+    if e == s:                                    # an empty slice reads no table rows
+        return x, np.zeros((8, d), np.uint8), np.ones(8, np.float32)
+    bits = wl.fp32_to_bf16_bits((rng.standard_normal((e - s, d)) * 0.02).astype(np.float32))
+    codes, scale = fp8.quantize_table(bits)
+    return x, codes, scale
+
+
+@pytest.mark.parametrize("case", sorted(ONEPASS_CASES))
+def test_fp8_onepass_step_equals_bf16_onepass_on_the_dequantized_table(case):
+    """se_soft_embed_step_onepass_fp8 on the oracle's codes (codes and scales past the slice:
+    NaN, never read): statistics and embedding bit for bit se_soft_embed_step_onepass's on
+    the oracle's dequantized table (a power-of-two scale moves exactly from the table row to
+    the probability), and within the gate of the fp64 oracle on the dequantized table."""
+    L, V, s, e, d, seed = ONEPASS_CASES[case]
+    x, codes, scale = fp8_inputs(L, V, s, e, d, seed)
+    dq = fp8.dequantize_bf16_bits(codes, scale)
+    c_t = dev(np.concatenate([codes, np.full((24, d), 0x7F, np.uint8)]))
+    s_t = dev(np.concatenate([scale, np.full(24, np.nan, np.float32)]))
+    dq_t = dev(np.concatenate([dq, np.full((24, d), 0x7FC0, np.uint16)]))
+    x_t = dev_logits(x)
+    say("fp8 one-read step", case, (L, V, s, e, d))
+    got = api.soft_embed_step_fp8(x_t, s, e, c_t, s_t, 7.5, onepass=True)
+    ref = api.soft_embed_step(x_t, s, e, dq_t, 7.5, onepass=True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("out", "max", "lse", "entropy", "argmax"), got, ref):
+        assert torch.equal(a, b), name
+    r = rel_fro(got[0].cpu().numpy(),
+                oracle.soft_embed(x, s, e, fp8.dequantize(codes, scale).astype(np.float32), 7.5))
+    say("rel_fro", f"{r:.3e}")
+    assert r <= GATE
+
+
+def test_fp8_onepass_step_repeats():
+    L, V, s, e, d = 64, 50000, 8, 40008, 256
+    x, codes, scale = fp8_inputs(L, V, s, e, d, 44)
+    c_t, s_t, x_t = dev(codes), dev(scale), dev_logits(x)
+    say("fp8 one-read step: repeat")
+    a = api.soft_embed_step_fp8(x_t, s, e, c_t, s_t, 2.0, onepass=True)
+    b = api.soft_embed_step_fp8(x_t, s, e, c_t, s_t, 2.0, onepass=True)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("shape", [(8, 512, 16, 16, 16), (4096, 110000, 0, 110000, 1024)],
+                         ids=["empty-slice", "long-split-ranges"])
+def test_fp8_onepass_step_falls_back_to_the_two_pass_step(shape):
+    """An empty slice, or split ranges longer than 24,576 positions (4096 rows x 4 n-tiles,
+    4 splits of 27,520 positions): the call is se_soft_embed_step_fp8 in the same
+    workspace, bit for bit."""
+    L, V, s, e, d = shape
+    x, codes, scale = fp8_inputs(L, V, s, e, d, 45)
+    c_t, s_t, x_t = dev(codes), dev(scale), dev(x)
+    ws = api.step_onepass_workspace(L, V, s, e, d, DEV)
+    say("fp8 one-read step fallback", shape)
+    a = api.soft_embed_step_fp8(x_t, s, e, c_t, s_t, 1.5, onepass=True, ws=ws)
+    b = api.soft_embed_step_fp8(x_t, s, e, c_t, s_t, 1.5)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_fp8_onepass_step_rejects_an_unaligned_scale_array():
+    L, V, s, e, d = 8, 4096, 0, 4096, 64
+    x, codes, scale = fp8_inputs(L, V, s, e, d, 46)
+    s_t = dev(np.concatenate([[0.0], scale]).astype(np.float32))[1:]     # 4 bytes past 16
+    with pytest.raises(B.SoftEmbedError) as err:
+        api.soft_embed_step_fp8(dev_logits(x), s, e, dev(codes), s_t, 1.0, onepass=True)
+    assert err.value.status == B.SE_ERR_ALIGN
+
+
+def test_fp8_onepass_step_rank_full_size():
+    """The one-rank shape (L=256, slice [65536, 131072), d=2816) on the oracle's codes: bit
+    for bit se_soft_embed_step_onepass on the oracle's dequantized shard, the planted argmax,
+    and sampled rows against the fp64 oracle."""
+    w = wl.get("rank")
+    bits, _ = wl.make_table(w)
+    shard = np.ascontiguousarray(bits[w.vocab_start:w.vocab_end])
+    del bits
+    say("fp8 one-read rank: oracle quantize")
+    codes, scale = fp8.quantize_table(shard)
+    del shard
+    dq = fp8.dequantize_bf16_bits(codes, scale)
+    x = wl.make_logits(w)
+    x_t = dev(x)
+    say("fp8 one-read rank: gpu calls")
+    got = api.soft_embed_step_fp8(x_t, w.vocab_start, w.vocab_end, dev(codes), dev(scale),
+                                  w.gamma, onepass=True)
+    ref = api.soft_embed_step(x_t, w.vocab_start, w.vocab_end, dev(dq), w.gamma, onepass=True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("out", "max", "lse", "entropy", "argmax"), got, ref):
+        assert torch.equal(a, b), name
+    np.testing.assert_array_equal(got[4].cpu().numpy(), wl.planted_index(w))
+    rows = np.array([0, 77, 255])
+    say("fp8 one-read rank: oracle rows", list(rows))
+    r = rel_fro(got[0].cpu().numpy()[rows],
+                oracle.soft_embed(x[rows], w.vocab_start, w.vocab_end, dq, w.gamma))
+    say("rel_fro", f"{r:.3e}")
+    assert r <= GATE
