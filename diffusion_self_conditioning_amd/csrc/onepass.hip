@@ -200,14 +200,13 @@ step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, 
   if (lane < (int)(a0 - p0)) rs = (int)(p0 - c0) + lane;
   else if (lane >= 4 && lane < 4 + (int)(p1 - a1)) rs = (int)(a1 - c0) + lane - 4;
   const float xs = rs >= 0 ? x[c0 + rs] : 0.f;
-  // the scales of the same positions (slice positions js + base + 4 gi ..; 16-byte aligned)
-  float4 sv[SCALED ? NF4 : 1];
+  // the scales of the same positions (slice positions js + base + 4 gi ..; 16-byte aligned),
+  // each loaded where it is used (held for the whole loop they would cost occupancy)
   float ss = 1.f;
+  __amdgpu_buffer_rsrc_t sr = make_rsrc(pscale, 0u);
   if constexpr (SCALED) {
     if (active && in_slice) {
-      const __amdgpu_buffer_rsrc_t sr = make_rsrc(pscale + (c0 - g.s) + base, (uint32_t)ng * 16u);
-#pragma unroll
-      for (int u = 0; u < NF4; ++u) sv[u] = buffer_load_f4(sr, (uint32_t)(u * 64 + lane) * 16u, 0u);
+      sr = make_rsrc(pscale + (c0 - g.s) + base, (uint32_t)ng * 16u);
       if (rs >= 0) ss = pscale[c0 - g.s + rs];
     }
   }
@@ -255,11 +254,13 @@ step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, 
       z += (q0 + q1) + (q2 + q3);
       s1 = __builtin_fmaf(q0, t0, __builtin_fmaf(q1, t1, __builtin_fmaf(q2, t2, __builtin_fmaf(q3, t3, s1))));
       if (active && in_slice) {                         // 4 positions in one super-step
-        if constexpr (SCALED)
-          store_stream_u2(prow + tiled(js + base + 4 * gi), pack_bf16x2(q0 * sv[u].x, q1 * sv[u].y),
-                          pack_bf16x2(q2 * sv[u].z, q3 * sv[u].w));
-        else
+        if constexpr (SCALED) {
+          const float4 sc = buffer_load_f4(sr, (uint32_t)gi * 16u, 0u);
+          store_stream_u2(prow + tiled(js + base + 4 * gi), pack_bf16x2(q0 * sc.x, q1 * sc.y),
+                          pack_bf16x2(q2 * sc.z, q3 * sc.w));
+        } else {
           store_stream_u2(prow + tiled(js + base + 4 * gi), pack_bf16x2(q0, q1), pack_bf16x2(q2, q3));
+        }
       }
     }
   }

@@ -452,6 +452,36 @@ def test_step_fp8_errors():
                 ws=None, ws_bytes=0) == b.SE_OK
 
 
+def test_step_onepass_fp8_errors():
+    """The one-read e4m3 step: the e4m3 table checks, a scale array that must be 16-byte
+    aligned (the sweep reads four scales at a time), the one-read workspace; the empty
+    slice goes to the two-pass e4m3 step (its own checks)."""
+    st = lib.se_soft_embed_step_onepass_fp8
+
+    def call(**kw):
+        a = dict(x=P1, ld=262144, n=256, vocab=262144, s=65536, e=131072, w=P3, sc=P2 + 4096,
+                 w_rows=65536, ldw=2816, d=2816, gamma=53.0, out=P4, ldo=2816, mx=P2, lse=P2 + 1024,
+                 ent=P2 + 2048, am=P2 + 3072, ws=P5, ws_bytes=1 << 40)
+        a.update(kw)
+        return st(a["x"], a["ld"], a["n"], a["vocab"], a["s"], a["e"], a["w"], a["sc"],
+                  a["w_rows"], a["ldw"], a["d"], a["gamma"], a["out"], a["ldo"], a["mx"], a["lse"],
+                  a["ent"], a["am"], a["ws"], a["ws_bytes"], None)
+    assert call(w_rows=1000) == b.SE_ERR_SLICE
+    assert call(ld=1000) == b.SE_ERR_SHAPE
+    assert call(sc=None) == b.SE_ERR_NULL
+    assert call(x=None) == b.SE_ERR_NULL
+    assert call(d=2808, ldw=2816, ldo=2816) == b.SE_ERR_ALIGN     # d % 16 != 0
+    assert call(ldw=2824) == b.SE_ERR_ALIGN                      # ld_w % 16 != 0
+    assert call(sc=P2 + 4100) == b.SE_ERR_ALIGN                  # 4-byte, not 16-byte aligned
+    assert call(s=65540) == b.SE_ERR_ALIGN
+    assert call(ws_bytes=1024) == b.SE_ERR_WORKSPACE
+    assert call(ws=None) == b.SE_ERR_NULL
+    assert call(n=0, x=None, w=None, sc=None, out=None, mx=None, lse=None, ent=None, am=None,
+                ws=None, ws_bytes=0) == b.SE_OK
+    # empty slice: the two-pass e4m3 step, whose statistics-only form needs no table
+    assert call(s=16, e=16, sc=None) == b.SE_ERR_NULL
+
+
 def test_32bit_offset_limits_both_sides():
     """The kernels address staged probabilities, a split's shard rows and a 256-row tile of the
     probability operand with 32-bit byte offsets, so each must stay below 4 GiB; at the limit the
