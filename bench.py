@@ -121,11 +121,11 @@ def step_bytes_two_pass(w) -> int:
                                                    + 4 * w.rows * w.d)
 
 
-def contraction_bytes(w, fused: bool) -> int:
-    """Algorithmic HBM bytes of one contraction launch: the bf16 table slice once and the
-    probability operand once (staged bf16, or fp32 logits for the fused kernel).  The
-    split partials are implementation traffic, not counted."""
-    return 2 * w.k * w.d + (4 if fused else 2) * w.rows * w.k
+def contraction_bytes(w, fused: bool, table_elem_bytes: int = 2) -> int:
+    """Algorithmic HBM bytes of one contraction launch: the table slice once (bf16, or e4m3
+    codes: table_elem_bytes 1) and the probability operand once (staged bf16, or fp32 logits
+    for the fused kernel).  The split partials are implementation traffic, not counted."""
+    return table_elem_bytes * w.k * w.d + (4 if fused else 2) * w.rows * w.k
 
 
 def roofline(flops: int, nbytes: int, us: float, traffic=None) -> dict:
@@ -171,6 +171,17 @@ class Step:
         self.ws1 = api.step_onepass_workspace(L, w.vocab, w.vocab_start, w.vocab_end, d, dev)
         self.wso = None
         self.probs = None
+        self.codes = self.wscale = None
+
+    def quantized(self):
+        """The e4m3 codes and power-of-two row scales of the shard (quantized once)."""
+        if self.codes is None:
+            import torch
+            from diffusion_self_conditioning_amd import _binding as B
+            self.codes = torch.empty(tuple(self.shard.shape), dtype=torch.uint8, device=self.dev)
+            self.wscale = torch.empty(self.shard.shape[0], device=self.dev)
+            B.se_quantize_table_fp8(self.shard, self.codes, self.wscale)
+        return self.codes, self.wscale
 
     def call(self, path: str, out=None):
         from diffusion_self_conditioning_amd import _binding as B
@@ -182,6 +193,10 @@ class Step:
             B.se_soft_embed_step(self.x, s, e, self.shard, w.gamma, o, *stats, self.wss)
         elif path == "step_onepass":
             B.se_soft_embed_step_onepass(self.x, s, e, self.shard, w.gamma, o, *stats, self.ws1)
+        elif path == "step_onepass_fp8":
+            codes, wscale = self.quantized()
+            B.se_soft_embed_step_onepass_fp8(self.x, s, e, codes, wscale, w.gamma, o, *stats,
+                                             self.ws1)
         elif path == "onepass":
             if self.wso is None:
                 self.wso = api.onepass_workspace(w.rows, s, e, w.d, self.dev)
@@ -353,13 +368,16 @@ def step_report(st: Step, path: str, K: int, W: int) -> dict:
     dom_i = max(range(len(kt)), key=lambda j: kt[j][1] if "soft_embed" in kt[j][0] else -1)
     dom_name, dom_us = kt[dom_i]
     fused = "fused" in dom_name
-    traffic, source = measured_traffic("soft_embed_pp_kernel" if not fused else
-                                       "soft_embed_kernel_fused", w.name)
-    roof = roofline(flops, contraction_bytes(w, fused), dom_us, traffic)
+    e4m3 = path.endswith("_fp8")
+    traffic, source = measured_traffic("soft_embed_kernel_fused" if fused else
+                                       "soft_embed_pp_kernel_e4m3" if e4m3 else
+                                       "soft_embed_pp_kernel", w.name)
+    nbytes = contraction_bytes(w, fused, 1 if e4m3 else 2)
+    roof = roofline(flops, nbytes, dom_us, traffic)
     roof.update({"kernel": dom_name, "kernel_us": round(dom_us, 2),
-                 "algorithmic_bytes": contraction_bytes(w, fused),
+                 "algorithmic_bytes": nbytes,
                  "algorithmic_flops": flops, "traffic_source": source,
-                 "basis": "algorithmic bytes (bf16 table slice + staged bf16 probabilities) "
+                 "basis": "algorithmic bytes (table slice + staged bf16 probabilities) "
                           "or FLOP of one launch / its duration between the start and end "
                           "events the dispatch stamps"})
     once, two = step_bytes_logits_once(w), step_bytes_two_pass(w)
@@ -497,8 +515,9 @@ def main():
     ap.add_argument("--workload", default="full", choices=["full", "rank", "conv", "batch", "tiny"])
     ap.add_argument("--path", default="auto",
                     choices=["auto", "step", "step_onepass", "onepass", "unfused", "staged",
-                             "fused"],
-                    help="how the step runs (auto: the workload's fastest whole-step path)")
+                             "fused", "step_onepass_fp8"],
+                    help="how the step runs (auto: the workload's fastest whole-step path; "
+                         "step_onepass_fp8, the e4m3-table step, with --minimal only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--side-workloads", default="rank,conv,batch",
                     help="comma-separated workloads timed beside the main one on their fastest "
@@ -542,6 +561,10 @@ def main():
     w = wl.get(args.workload)
     path = BEST_PATH[w.name] if args.path == "auto" else args.path
     whole = w.vocab_start == 0 and w.vocab_end == w.vocab
+    if path == "step_onepass_fp8" and not args.minimal:
+        print("--path step_onepass_fp8 (another numerical contract: the e4m3 table) runs with "
+              "--minimal only; the full run reports it under paths.fp8_table", file=sys.stderr)
+        sys.exit(2)
     if path == "onepass" and not whole:
         print("--path onepass needs a workload whose slice is the whole vocabulary (its row "
               "statistics are those of the slice)", file=sys.stderr)
@@ -561,7 +584,8 @@ def main():
         print(json.dumps({"metric": METRIC, "value": rep["gflops"], "unit": "GFLOP/s",
                           "n_gpus": 1, "steps": K, "warmup": W,
                           "ms_per_step": rep["ms_per_step"], "minimal": True,
-                          "config": {"workload": w.name, "path": path},
+                          "config": {"workload": w.name, "path": path,
+                                     "table": "e4m3" if path.endswith("_fp8") else "bf16"},
                           "kernel_us": rep["kernel_us"],
                           "gaps_between_kernels_us": rep["gaps_between_kernels_us"],
                           "marked_step_us": rep["marked_step_us"], "roofline": rep["roofline"]}),

@@ -34,6 +34,8 @@ def test_byte_counts_of_the_whole_vocabulary_step():
     out = 256 * 2816 * 4
     assert bench.contraction_bytes(w, fused=False) == table + staged == 1_610_612_736
     assert bench.contraction_bytes(w, fused=True) == table + logits
+    # the e4m3 table: one byte per code
+    assert bench.contraction_bytes(w, False, 1) == table // 2 + staged
     assert bench.step_bytes_logits_once(w) == logits + table + out + 16 * 256 == 1_747_718_144
     assert bench.step_bytes_two_pass(w) == (logits + 16 * 256) + (table + logits + out) \
         == 2_016_153_600
