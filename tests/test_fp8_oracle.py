@@ -135,3 +135,25 @@ def test_quantization_commutes_with_power_of_two_row_scaling():
     c2, s2 = quantize_table(bits2)
     assert np.array_equal(c1, c2)
     assert np.array_equal(s2, s1 * np.float32(32.0))
+
+
+def test_moving_a_row_scale_onto_the_probability_is_exact():
+    """The reading behind the one-read e4m3 step: for a power of two 2^k (the row scales,
+    k in [-126, 0] here) and a probability p in (0, 1], bf16(p 2^k) = bf16(p) 2^k whenever
+    p 2^k stays in bf16's normal range, so each product p 2^k code equals bf16(p) times the
+    dequantized entry code 2^k exactly.  Checked with torch's CPU bfloat16 cast (round to
+    nearest even) on random and boundary probabilities."""
+    rng = np.random.default_rng(5)
+    p = np.concatenate([rng.random(20000), np.exp(-rng.random(20000) * 80.0),
+                        [1.0, 0.5, 2.0 ** -20, 1 - 2.0 ** -24, 1.00390625 / 2]]).astype(np.float32)
+    for k in (-126, -100, -40, -14, -12, -7, -1, 0):
+        s = np.float32(2.0 ** k)
+        scaled = torch.from_numpy(p * s).to(torch.bfloat16).to(torch.float64).numpy()
+        moved = torch.from_numpy(p).to(torch.bfloat16).to(torch.float64).numpy() * float(s)
+        normal = p.astype(np.float64) * float(s) >= 2.0 ** -126
+        assert normal.sum() > 0
+        np.testing.assert_array_equal(scaled[normal], moved[normal])
+        # and the code products agree exactly in fp64 (bf16 x e4m3 values are exact there)
+        code_vals = decode_e4m3(np.arange(0, 0x7F, dtype=np.uint8))
+        c = code_vals[rng.integers(0, len(code_vals), normal.sum())]
+        np.testing.assert_array_equal(scaled[normal] * c, moved[normal] * c)
