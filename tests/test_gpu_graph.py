@@ -30,7 +30,7 @@ def say(*a):
 
 
 @pytest.mark.parametrize("which", ["step", "step_onepass", "staged", "step_held_slice", "step_fp8",
-                                   "step_noalloc"])
+                                   "step_onepass_fp8", "step_noalloc"])
 def test_captured_step_replays_match_eager_calls(which):
     L, V, s, e, d = 256, 30000, 8000, 20000, 512
     if which == "step_held_slice":          # two whole 16,384-position groups: kept in registers
@@ -43,11 +43,11 @@ def test_captured_step_replays_match_eager_calls(which):
     out = torch.empty((L, d), **f)
     mx, lse, ent = torch.empty(L, **f), torch.empty(L, **f), torch.empty(L, **f)
     am = torch.empty(L, device=DEV, dtype=torch.int32)
-    if which == "step_onepass":
+    if which in ("step_onepass", "step_onepass_fp8"):
         ws = api.step_onepass_workspace(L, V, s, e, d, DEV)
     else:
         ws = api.staged_workspace(L, s, e, d, DEV)
-    if which == "step_fp8":                 # e4m3 table, quantized once before the capture
+    if which.endswith("fp8"):               # e4m3 table, quantized once before the capture
         codes, wscale = api.quantize_table_fp8(w_t)
         torch.cuda.synchronize()
 
@@ -60,6 +60,9 @@ def test_captured_step_replays_match_eager_calls(which):
             B.se_soft_embed_step_onepass(x_t, s, e, w_t, 2.0, out, mx, lse, ent, am, ws)
         elif which == "step_fp8":
             B.se_soft_embed_step_fp8(x_t, s, e, codes, wscale, 2.0, out, mx, lse, ent, am, ws)
+        elif which == "step_onepass_fp8":
+            B.se_soft_embed_step_onepass_fp8(x_t, s, e, codes, wscale, 2.0, out, mx, lse, ent, am,
+                                             ws)
         else:                                   # statistics call, then the staged contraction
             B.se_row_stats(x_t, mx, lse, ent, am)
             B.se_soft_embed_staged(x_t, lse, s, e, w_t, 2.0, out, ws)
