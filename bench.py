@@ -563,7 +563,7 @@ def main():
     whole = w.vocab_start == 0 and w.vocab_end == w.vocab
     if path == "step_onepass_fp8" and not args.minimal:
         print("--path step_onepass_fp8 (another numerical contract: the e4m3 table) runs with "
-              "--minimal only; the full run reports it under paths.fp8_table", file=sys.stderr)
+              "--minimal only; the full run reports it under fp8_table", file=sys.stderr)
         sys.exit(2)
     if path == "onepass" and not whole:
         print("--path onepass needs a workload whose slice is the whole vocabulary (its row "

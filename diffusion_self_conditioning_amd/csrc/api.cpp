@@ -290,10 +290,11 @@ se_status run_soft_embed(bool fused, const void* a, int64_t lda, const float* ls
 // The contraction of super-step-tiled bf16 probabilities ([K / 128][n_rows][128], slice
 // position 0 first) in the workspace of a staged call.
 se_status run_staged_gemm(const se::StagedLayout& o, const uint16_t* probs, int64_t n_rows,
-                          int64_t K, const void* w_shard, const float* w_scale, int64_t ld_w,
-                          int64_t d, float gamma, float* out, int64_t ld_out, unsigned char* ws,
-                          hipStream_t st) {
+                          int64_t K, const void* w_shard, const float* w_scale, bool w8_direct,
+                          int64_t ld_w, int64_t d, float gamma, float* out, int64_t ld_out,
+                          unsigned char* ws, hipStream_t st) {
   se::GemmParams p{};
+  p.w8_direct = w8_direct;           // e4m3 codes read as they are: the scales are in probs
   p.a = probs;
   p.lda = se::kSuperStep;
   p.a_ss = n_rows * se::kSuperStep * 2;
@@ -471,7 +472,8 @@ se_status se_soft_embed_staged(const float* logits, int64_t ld_logits, const flo
   rc = from_hip(se::launch_probs_bf16_tiled(logits, ld_logits, row_lse, n_rows, vocab_start, K,
                                             probs, st));
   if (rc != SE_OK) return rc;
-  return run_staged_gemm(o, probs, n_rows, K, w_shard, nullptr, ld_w, d, gamma, out, ld_out, ws, st);
+  return run_staged_gemm(o, probs, n_rows, K, w_shard, nullptr, false, ld_w, d, gamma, out, ld_out,
+                         ws, st);
 }
 
 }  // extern "C"
@@ -542,12 +544,15 @@ se_status run_step(const float* logits, int64_t ld_logits, int64_t n_rows, int64
   if (!aligned16(workspace)) return SE_ERR_ALIGN;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   uint16_t* probs = reinterpret_cast<uint16_t*>(ws + o.off_probs);
+  // e4m3 table with 16-byte aligned scales: the statistics pass stores the probabilities times
+  // their rows' scales and the contraction reads the codes as they are
+  const bool direct = w8 && aligned16(w_scale);
   rc = from_hip(se::launch_row_stats_probs(logits, ld_logits, n_rows, (int)vocab, row_max,
                                            row_lse, row_entropy, row_argmax, vocab_start, K,
-                                           probs, st));
+                                           probs, direct ? w_scale : nullptr, st));
   if (rc != SE_OK) return rc;
-  return run_staged_gemm(o, probs, n_rows, K, w_shard, w8 ? w_scale : nullptr, ld_w, d, gamma,
-                         out, ld_out, ws, st);
+  return run_staged_gemm(o, probs, n_rows, K, w_shard, w8 ? w_scale : nullptr, direct, ld_w, d,
+                         gamma, out, ld_out, ws, st);
 }
 }  // namespace
 

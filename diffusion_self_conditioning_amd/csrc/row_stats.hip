@@ -99,12 +99,15 @@ constexpr int kGroupF4 = kUnroll * kRowThreads;
 constexpr int kHoldGroups = 16 / kUnroll;        // 16 float4 (64 VGPRs) per thread
 static_assert(kHoldGroups >= 1, "at most 16 chunks per group");
 
-template <bool PROBS, int HOLD>
+// SCALED (with PROBS): slice position k's probability is stored times pscale[k] (a power of
+// two, so the bf16 value is the unscaled one times pscale[k] exactly; 16-byte aligned).
+template <bool PROBS, int HOLD, bool SCALED>
 __global__ void __launch_bounds__(kRowThreads)
 row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
                  float* __restrict__ row_max, float* __restrict__ row_lse,
                  float* __restrict__ row_entropy, int32_t* __restrict__ row_argmax,
-                 int64_t col0, int64_t K, uint16_t* __restrict__ probs, int64_t n_rows) {
+                 int64_t col0, int64_t K, uint16_t* __restrict__ probs, int64_t n_rows,
+                 const float* __restrict__ pscale) {
   const int64_t row = blockIdx.x;
   const float* __restrict__ x = logits + row * ld;
   const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x);
@@ -220,13 +223,30 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
     const float* __restrict__ xs = x + col0;
     uint16_t* __restrict__ prow = probs + row * kSuperStep;
     // the slice's positions [k_begin, K) read again (k_begin a multiple of 8)
+    // the scales of slice positions k .. k + 3 (k a multiple of 4), or of position k alone
+    auto scale4 = [&](int64_t k) -> float4 {
+      if constexpr (SCALED) return reinterpret_cast<const float4*>(pscale + k)[0];
+      else return make_float4(1.f, 1.f, 1.f, 1.f);
+    };
+    auto scale1 = [&](int64_t k) -> float {
+      if constexpr (SCALED) return pscale[k];
+      else return 1.f;
+    };
     auto reread = [&](int64_t k_begin) {
       auto put8 = [&](int64_t k, const float4& a, const float4& b) {
         uint4 o;
-        o.x = pack_bf16x2(prob_from_logit(a.x, nl), prob_from_logit(a.y, nl));
-        o.y = pack_bf16x2(prob_from_logit(a.z, nl), prob_from_logit(a.w, nl));
-        o.z = pack_bf16x2(prob_from_logit(b.x, nl), prob_from_logit(b.y, nl));
-        o.w = pack_bf16x2(prob_from_logit(b.z, nl), prob_from_logit(b.w, nl));
+        if constexpr (SCALED) {
+          const float4 sa = scale4(k), sb = scale4(k + 4);
+          o.x = pack_bf16x2(prob_from_logit(a.x, nl) * sa.x, prob_from_logit(a.y, nl) * sa.y);
+          o.y = pack_bf16x2(prob_from_logit(a.z, nl) * sa.z, prob_from_logit(a.w, nl) * sa.w);
+          o.z = pack_bf16x2(prob_from_logit(b.x, nl) * sb.x, prob_from_logit(b.y, nl) * sb.y);
+          o.w = pack_bf16x2(prob_from_logit(b.z, nl) * sb.z, prob_from_logit(b.w, nl) * sb.w);
+        } else {
+          o.x = pack_bf16x2(prob_from_logit(a.x, nl), prob_from_logit(a.y, nl));
+          o.y = pack_bf16x2(prob_from_logit(a.z, nl), prob_from_logit(a.w, nl));
+          o.z = pack_bf16x2(prob_from_logit(b.x, nl), prob_from_logit(b.y, nl));
+          o.w = pack_bf16x2(prob_from_logit(b.z, nl), prob_from_logit(b.w, nl));
+        }
         store_stream_u4(prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep, o);
       };
       // four 8-position groups per thread in flight, then the remaining groups one by one
@@ -248,7 +268,8 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
         } else {
           uint16_t* __restrict__ pp = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
           for (int64_t j = 0; j < K - k; ++j)
-            store_stream_u16(pp + j, __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(xs[k + j], nl)));
+            store_stream_u16(pp + j, __builtin_bit_cast(
+                                         uint16_t, (__bf16)(prob_from_logit(xs[k + j], nl) * scale1(k + j))));
         }
       }
     };
@@ -266,12 +287,19 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
             uint16_t* dst = prow + (k / kSuperStep) * n_rows * kSuperStep + k % kSuperStep;
             const float4 v = held[h][u];
             if (k + 4 <= K) {
-              store_stream_u2(dst, pack_bf16x2(prob_from_logit(v.x, nl), prob_from_logit(v.y, nl)),
-                              pack_bf16x2(prob_from_logit(v.z, nl), prob_from_logit(v.w, nl)));
+              if constexpr (SCALED) {
+                const float4 sv = scale4(k);
+                store_stream_u2(dst, pack_bf16x2(prob_from_logit(v.x, nl) * sv.x, prob_from_logit(v.y, nl) * sv.y),
+                                pack_bf16x2(prob_from_logit(v.z, nl) * sv.z, prob_from_logit(v.w, nl) * sv.w));
+              } else {
+                store_stream_u2(dst, pack_bf16x2(prob_from_logit(v.x, nl), prob_from_logit(v.y, nl)),
+                                pack_bf16x2(prob_from_logit(v.z, nl), prob_from_logit(v.w, nl)));
+              }
             } else {
               const float e4[4] = {v.x, v.y, v.z, v.w};
               for (int j = 0; j < (int)(K - k); ++j)
-                store_stream_u16(dst + j, __builtin_bit_cast(uint16_t, (__bf16)prob_from_logit(e4[j], nl)));
+                store_stream_u16(dst + j, __builtin_bit_cast(
+                                              uint16_t, (__bf16)(prob_from_logit(e4[j], nl) * scale1(k + j))));
             }
           }
         }
@@ -290,31 +318,30 @@ row_stats_kernel(const float* __restrict__ logits, int64_t ld, int vocab,
 hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int vocab,
                             float* row_max, float* row_lse, float* row_entropy,
                             int32_t* row_argmax, hipStream_t stream) {
-  SE_LAUNCH((row_stats_kernel<false, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
+  SE_LAUNCH((row_stats_kernel<false, 0, false>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
                      stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax,
-                     (int64_t)0, (int64_t)0, nullptr, n_rows);
+                     (int64_t)0, (int64_t)0, nullptr, n_rows, nullptr);
   return launched(stream);
 }
 
 hipError_t launch_row_stats_probs(const float* logits, int64_t ld, int64_t n_rows, int vocab,
                                   float* row_max, float* row_lse, float* row_entropy,
                                   int32_t* row_argmax, int64_t col0, int64_t K,
-                                  uint16_t* probs, hipStream_t stream) {
+                                  uint16_t* probs, const float* pscale, hipStream_t stream) {
   // the slice's first kHoldGroups groups, when they lie inside the main loop's range: kept
   // in registers (the rest of a longer slice is read again); otherwise all read again
   const int64_t gpos = 4 * (int64_t)kGroupF4;
   const int64_t g0 = col0 / gpos;
   const int64_t g_held = min((col0 + K + gpos - 1) / gpos, g0 + kHoldGroups);
   const bool hold = K > 0 && g_held <= (vocab / 4) / kGroupF4;
-  if (hold)
-    SE_LAUNCH((row_stats_kernel<true, kHoldGroups>), dim3((unsigned)n_rows),
-                       dim3(kRowThreads), 0, stream, logits, ld, vocab, row_max, row_lse,
-                       row_entropy, row_argmax, col0, K, probs, n_rows);
-  else
-    SE_LAUNCH((row_stats_kernel<true, 0>), dim3((unsigned)n_rows), dim3(kRowThreads), 0,
-                       stream, logits, ld, vocab, row_max, row_lse, row_entropy, row_argmax, col0,
-                       K, probs, n_rows);
-  return launched(stream);
+  auto go = [&](auto kernel) {
+    SE_LAUNCH(kernel, dim3((unsigned)n_rows), dim3(kRowThreads), 0, stream, logits, ld, vocab,
+              row_max, row_lse, row_entropy, row_argmax, col0, K, probs, n_rows, pscale);
+    return launched(stream);
+  };
+  if (pscale)
+    return hold ? go(row_stats_kernel<true, kHoldGroups, true>) : go(row_stats_kernel<true, 0, true>);
+  return hold ? go(row_stats_kernel<true, kHoldGroups, false>) : go(row_stats_kernel<true, 0, false>);
 }
 
 }  // namespace se

@@ -136,11 +136,12 @@ hipError_t launch_row_stats(const float* logits, int64_t ld, int64_t n_rows, int
                             int32_t* row_argmax, hipStream_t stream);
 
 // se_row_stats, and in the same pass the bf16 probabilities of slice [col0, col0 + K)
-// in the super-step-tiled layout (see launch_probs_bf16_tiled)
+// in the super-step-tiled layout (see launch_probs_bf16_tiled); pscale (optional, 16-byte
+// aligned, one power of two per slice position): the probabilities are stored times pscale[k]
 hipError_t launch_row_stats_probs(const float* logits, int64_t ld, int64_t n_rows, int vocab,
                                   float* row_max, float* row_lse, float* row_entropy,
                                   int32_t* row_argmax, int64_t col0, int64_t K,
-                                  uint16_t* probs, hipStream_t stream);
+                                  uint16_t* probs, const float* pscale, hipStream_t stream);
 
 hipError_t launch_probs_bf16(const float* logits, int64_t ld, const float* row_lse,
                              int64_t n_rows, int64_t col0, int64_t K, uint16_t* probs,

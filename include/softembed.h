@@ -287,10 +287,14 @@ se_status se_soft_embed_step_noalloc(const float* logits, int64_t ld_logits, int
  * power-of-two scales (as se_quantize_table_fp8 writes them; the pages serve FP8
  * weights: agentlenshq overview of DiffusionGemma in vLLM, performance and
  * quantization).  Outputs are bit for bit those of se_row_stats followed by
- * se_soft_embed_fp8_fused.  Arguments: those of se_soft_embed_step with the table given
- * as w_codes (uint8 [w_rows, ld_w]) and w_scale (fp32 [w_rows]) as in se_soft_embed_fp8;
- * workspace of se_soft_embed_staged_workspace_bytes() bytes.  Errors as
- * se_soft_embed_step, and those of se_soft_embed_fp8's table checks.
+ * se_soft_embed_fp8_fused.  With a 16-byte aligned w_scale the statistics pass stores each
+ * slice probability times its row's scale and the contraction reads the codes as they are
+ * (as se_soft_embed_step_onepass_fp8 does; the same bits wherever every stored probability
+ * stays in bf16's normal range); otherwise the contraction turns the codes into bf16 rows.
+ * Arguments: those of se_soft_embed_step with the table given as w_codes (uint8
+ * [w_rows, ld_w]) and w_scale (fp32 [w_rows]) as in se_soft_embed_fp8; workspace of
+ * se_soft_embed_staged_workspace_bytes() bytes.  Errors as se_soft_embed_step, and those
+ * of se_soft_embed_fp8's table checks.
  */
 se_status se_soft_embed_step_fp8(const float* logits, int64_t ld_logits, int64_t n_rows,
                                  int64_t vocab, int64_t vocab_start, int64_t vocab_end,

@@ -43,7 +43,8 @@ hipError_t launched_stub(hipStream_t) {
 hipError_t launch_row_stats(const float*, int64_t, int64_t, int, float*, float*, float*,
                             int32_t*, hipStream_t s) { return launched_stub(s); }
 hipError_t launch_row_stats_probs(const float*, int64_t, int64_t, int, float*, float*, float*,
-                                  int32_t*, int64_t, int64_t, uint16_t*, hipStream_t s) {
+                                  int32_t*, int64_t, int64_t, uint16_t*, const float*,
+                                  hipStream_t s) {
   return launched_stub(s);
 }
 hipError_t launch_probs_bf16(const float*, int64_t, const float*, int64_t, int64_t, int64_t,

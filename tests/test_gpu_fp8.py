@@ -457,3 +457,27 @@ def test_fp8_onepass_step_rank_full_size():
                 oracle.soft_embed(x[rows], w.vocab_start, w.vocab_end, dq, w.gamma))
     say("rel_fro", f"{r:.3e}")
     assert r <= GATE
+
+
+@pytest.mark.parametrize("case", ["ragged", "two-whole-tiles", "whole-tile-held-slice",
+                                  "slice-4097"])
+def test_fp8_step_scale_alignment_forms_agree(case):
+    """se_soft_embed_step_fp8 with a 16-byte aligned scale array (the statistics pass carries
+    the scales, codes read in place) and with one 4 bytes past such an address (the codes
+    turned into bf16 rows): the same outputs bit for bit."""
+    L, V, s, e, d, seed = CASES[case]
+    rng = np.random.default_rng(seed + 70)
+    x = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    x[np.arange(L), rng.integers(0, V, L)] += 8.0
+    bits = wl.fp32_to_bf16_bits((rng.standard_normal((e - s, d)) * 0.02).astype(np.float32))
+    codes, scale = fp8.quantize_table(bits)
+    c_t, x_t = dev(codes), dev(x)
+    s_al = dev(scale)
+    s_un = dev(np.concatenate([[np.float32(0)], scale]).astype(np.float32))[1:]
+    assert s_al.data_ptr() % 16 == 0 and s_un.data_ptr() % 16 == 4
+    say("fp8 step scale forms", case, (L, V, s, e, d))
+    a = api.soft_embed_step_fp8(x_t, s, e, c_t, s_al, 7.5)
+    b = api.soft_embed_step_fp8(x_t, s, e, c_t, s_un, 7.5)
+    torch.cuda.synchronize()
+    for name, u, v in zip(("out", "max", "lse", "entropy", "argmax"), a, b):
+        assert torch.equal(u, v), name
