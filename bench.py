@@ -64,6 +64,8 @@ LAUNCHES = {
                      "scaled_reduce_kernel"],
     "onepass": ["step_sweep_kernel", "soft_embed_pp_kernel", "merge_ranges_kernel",
                 "scaled_reduce_kernel"],
+    "step_onepass_fp8": ["step_sweep_kernel<scaled>", "soft_embed_pp_kernel<e4m3 in place>",
+                         "merge_ranges_kernel", "scaled_reduce_kernel"],
     "staged": ["row_stats_kernel", "probs_bf16_kernel<tiled>", "soft_embed_pp_kernel",
                "splitk_reduce_kernel"],
     "fused": ["row_stats_kernel", "soft_embed_kernel<fused>", "splitk_reduce_kernel"],
@@ -344,15 +346,17 @@ def kernel_times(st: Step, path: str, K: int):
     marked_us = hev.elapsed_us(bracket[0], bracket[1]) / K
     hev.destroy_all()
     names = LAUNCHES.get(path, [])
-    if path in ("step_onepass", "onepass") and n_used == 3:
+    if path in ("step_onepass", "onepass", "step_onepass_fp8") and n_used == 3:
         from diffusion_self_conditioning_amd import _binding as B
         w = st.w
-        two_pass = path == "step_onepass" and (
+        two_pass = path != "onepass" and (
             B.se_soft_embed_step_onepass_workspace_bytes(w.rows, w.vocab, w.vocab_start,
                                                          w.vocab_end, w.d)
             == B.se_soft_embed_staged_workspace_bytes(w.rows, w.vocab_start, w.vocab_end, w.d))
-        names = (LAUNCHES["step"] if two_pass       # the one-read call ran the two-pass step
-                 else ["step_sweep_kernel", "soft_embed_pp_kernel", "scaled_reduce_kernel"])
+        one = LAUNCHES[path]
+        names = ([] if two_pass and path.endswith("_fp8")   # the two-pass e4m3 step: unnamed
+                 else LAUNCHES["step"] if two_pass          # the one-read call ran the two-pass step
+                 else [one[0], one[1], one[3]])
     if len(names) != n_used:
         names = [f"launch_{j}" for j in range(n_used)]
     return [(names[j], sums[j] / K) for j in range(n_used)], [v / K for v in gaps], marked_us
