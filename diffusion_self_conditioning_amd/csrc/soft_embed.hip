@@ -1280,8 +1280,9 @@ template <bool FUSED, bool W8>
 hipError_t launch_contraction(const GemmParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles * p.splits));
   // bf16 probabilities (staged super-step-tiled, or row-major): the ping-pong kernel (bit
-  // for bit the same result)
-  // (e4m3 table: one row tile only; with several, the conversion, all in group 1's M
+  // for bit the same result).  Probabilities that carry the row scales: its form that reads
+  // the codes in place, at any number of row tiles.  An e4m3 table with unscaled
+  // probabilities: one row tile only (with several, the conversion, all in group 1's M
   // phase, outlasts the other group's MFMAs and the register-staged kernel is faster)
   const bool staged = p.a_ss == p.M * (int64_t)kSuperStep * 2 || p.a_ss == (int64_t)kSuperStep * 2;
   if (p.w8_direct) {                            // pre-scaled probabilities, codes read in place
