@@ -99,6 +99,13 @@ static void abi() {
                                 nullptr) == SE_OK);
   EXPECT(se_soft_embed_fp8(H(1), V, L, V, s, e, static_cast<uint8_t*>(P(3)), nullptr, e - s, d,
                            d, 53.f, F(4), d, P(5), big, nullptr) == SE_ERR_NULL);
+  // the one-read e4m3 step: 16-byte aligned scales, its workspace; a 4-byte offset is refused
+  EXPECT(se_soft_embed_step_onepass_fp8(F(1), V, L, V, s, e, static_cast<uint8_t*>(P(3)), F(10),
+                                        e - s, d, d, 53.f, F(4), d, F(6), F(7), F(8), I(9), P(5),
+                                        ws1, nullptr) == SE_OK);
+  EXPECT(se_soft_embed_step_onepass_fp8(F(1), V, L, V, s, e, static_cast<uint8_t*>(P(3)),
+                                        F(10) + 1, e - s, d, d, 53.f, F(4), d, F(6), F(7), F(8),
+                                        I(9), P(5), ws1, nullptr) == SE_ERR_ALIGN);
   // slices, sampler, partial sums
   EXPECT(se_merge_slices(F(1), 4, L * d, L, d, d, F(2), F(3), F(4), I(5), F(6), d, F(7), F(8),
                          F(9), I(10), nullptr) == SE_OK);
