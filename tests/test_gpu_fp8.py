@@ -481,3 +481,48 @@ def test_fp8_step_scale_alignment_forms_agree(case):
     torch.cuda.synchronize()
     for name, u, v in zip(("out", "max", "lse", "entropy", "argmax"), a, b):
         assert torch.equal(u, v), name
+
+
+def random_shapes(n, seed):
+    """Seeded shapes within the calls' layout rules (vocab_start a multiple of 8, d a
+    multiple of 16): rows 1..600 (one to three row tiles), vocabularies up to 60,000,
+    slices from one position to the whole row, d 16..1024."""
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        L = int(r.integers(1, 601))
+        V = int(r.integers(64, 60001))
+        s = 8 * int(r.integers(0, V // 8))
+        e = int(r.integers(s + 1, V + 1))
+        d = 16 * int(r.integers(1, 65))
+        out.append((L, V, s, e, d))
+    return out
+
+
+@pytest.mark.parametrize("shape", random_shapes(16, 2026), ids=lambda sh: "x".join(map(str, sh)))
+def test_fp8_steps_on_random_shapes(shape):
+    """On seeded random shapes: the one-read e4m3 step bit for bit the bf16 one-read step on
+    the oracle's dequantized table; the two-pass e4m3 step with 16-byte aligned scales (codes
+    read in place) bit for bit its form with unaligned scales (codes converted); both within
+    the gate of the fp64 oracle."""
+    L, V, s, e, d = shape
+    seed = L * 7919 + V * 31 + s + e + d
+    x, codes, scale = fp8_inputs(L, V, s, e, d, seed)
+    dq = fp8.dequantize_bf16_bits(codes, scale)
+    c_t, dq_t, x_t = dev(codes), dev(dq), dev_logits(x)
+    s_al = dev(scale)
+    s_un = dev(np.concatenate([[np.float32(0)], scale]).astype(np.float32))[1:]
+    say("fp8 random shape", shape)
+    one = api.soft_embed_step_fp8(x_t, s, e, c_t, s_al, 3.0, onepass=True)
+    one_bf = api.soft_embed_step(x_t, s, e, dq_t, 3.0, onepass=True)
+    two = api.soft_embed_step_fp8(x_t, s, e, c_t, s_al, 3.0)
+    two_cv = api.soft_embed_step_fp8(x_t, s, e, c_t, s_un, 3.0)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("out", "max", "lse", "entropy", "argmax"), one, one_bf):
+        assert torch.equal(a, b), ("one-read", name)
+    for name, a, b in zip(("out", "max", "lse", "entropy", "argmax"), two, two_cv):
+        assert torch.equal(a, b), ("two-pass", name)
+    ref = oracle.soft_embed(x, s, e, fp8.dequantize(codes, scale).astype(np.float32), 3.0)
+    for o in (one[0], two[0]):
+        r = rel_fro(o.cpu().numpy(), ref)
+        assert r <= GATE, r
