@@ -29,8 +29,10 @@ def row_stats(logits: torch.Tensor, stream=None):
 
 
 def probs_bf16(logits, row_lse, vocab_start, vocab_end, stream=None):
-    """bf16 probability matrix [L, V]; only columns [vocab_start, vocab_end) are written."""
-    p = torch.zeros(logits.shape, device=logits.device, dtype=torch.bfloat16)
+    """bf16 probability matrix [L, V] (a view of a buffer whose row pitch is V rounded up to
+    8, as se_probs_bf16 requires); only columns [vocab_start, vocab_end) are written."""
+    n, v = logits.shape
+    p = torch.zeros((n, (v + 7) // 8 * 8), device=logits.device, dtype=torch.bfloat16)[:, :v]
     se_probs_bf16(logits, row_lse, vocab_start, vocab_end, p, stream=stream)
     return p
 
