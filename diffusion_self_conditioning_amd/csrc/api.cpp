@@ -610,6 +610,8 @@ se_status run_step_onepass(const float* logits, int64_t ld_logits, int64_t n_row
   if (rc != SE_OK) return rc;
   if (ld_logits < vocab) return SE_ERR_SHAPE;
   if (n_rows == 0) return SE_OK;   // nothing to read or write: buffers may be NULL
+  // the sweep reads 4 scales at a time; the same rule whichever pass runs
+  if (w8 && w_scale && !aligned16(w_scale)) return SE_ERR_ALIGN;
   const se::StepOnepassLayout o =
       se::step_onepass_layout(n_rows, vocab, vocab_start, vocab_end, d);
   if (o.sweep.waves == 0)          // empty slice, or split ranges too long: two passes
@@ -623,7 +625,6 @@ se_status run_step_onepass(const float* logits, int64_t ld_logits, int64_t n_row
   if (w8) {
     rc = check_fp8_layout(d, ld_w, w_scale);
     if (rc != SE_OK) return rc;
-    if (!aligned16(w_scale)) return SE_ERR_ALIGN;   // the sweep reads 4 scales at a time
   }
   if (!aligned16(logits) || (ld_logits % 4) != 0) return SE_ERR_ALIGN;
   if (!aligned4(row_max) || !aligned4(row_lse) || !aligned4(row_entropy) || !aligned4(row_argmax))

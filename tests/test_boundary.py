@@ -478,8 +478,9 @@ def test_step_onepass_fp8_errors():
     assert call(ws=None) == b.SE_ERR_NULL
     assert call(n=0, x=None, w=None, sc=None, out=None, mx=None, lse=None, ent=None, am=None,
                 ws=None, ws_bytes=0) == b.SE_OK
-    # empty slice: the two-pass e4m3 step, whose statistics-only form needs no table
+    # empty slice: the two-pass e4m3 step, with the same scale checks
     assert call(s=16, e=16, sc=None) == b.SE_ERR_NULL
+    assert call(s=16, e=16, sc=P2 + 4100) == b.SE_ERR_ALIGN
 
 
 def test_32bit_offset_limits_both_sides():
