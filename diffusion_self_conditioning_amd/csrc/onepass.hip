@@ -177,12 +177,14 @@ step_sweep_kernel(const float* __restrict__ logits, int64_t ld, int64_t n_rows, 
   const int64_t item = (int64_t)blockIdx.x * (kWaves / W) + wave / W;
   const bool active = item < n_rows * n_ranges;
   if (W == 1 && !active) return;                      // whole wavefronts; no barrier below
-  // items in range-major order: workgroups launched together take one range of neighbouring
-  // rows, whose staged probabilities are neighbouring 256-byte runs of one super-step
-  // (measured: sweep 78 -> 76 us at the whole vocabulary; row-major order spreads the
-  // stores over all super-steps)
-  const int64_t row = active ? item % n_rows : 0;
-  const int r = active ? (int)(item / n_rows) : 0;
+  // Unscaled: items in range-major order, so that workgroups launched together take one
+  // range of neighbouring rows, whose staged probabilities are neighbouring 256-byte runs of
+  // one super-step (measured: sweep 78 -> 76 us at the whole vocabulary; row-major order
+  // spreads the stores over all super-steps).  Scaled: row-major order, so that workgroups
+  // launched together read the scales of different ranges (all reading one range's scales
+  // at once, the sweep measured 86 -> 92 us).
+  const int64_t row = active ? (SCALED ? item / n_ranges : item % n_rows) : 0;
+  const int r = active ? (int)(SCALED ? item % n_ranges : item / n_rows) : 0;
   int64_t c0 = 0, c1 = 0;
   if (active) step_range(g, r, c0, c1);
   const bool in_slice = r >= g.n_pre && r < g.n_pre + g.splits;
