@@ -549,7 +549,7 @@ se_status se_reduce_partials(const float* parts, int64_t n_parts, int64_t part_s
 /*
  * se_mfma_loop -- measurement aid: the bf16 matrix-core rate this device sustains, the
  * achievable ceiling read beside the nominal peak when the contraction's roofline is
- * judged (the nominal 2.5 PFLOP/s assumes the 2.4 GHz peak clock; under load the clock
+ * assessed (the nominal 2.5 PFLOP/s assumes the 2.4 GHz peak clock; under load the clock
  * runs lower).  Not part of the soft embedding.
  *
  * Launches `blocks` workgroups of 256 threads (4 waves).  Each wave runs 8 independent
